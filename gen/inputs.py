@@ -1,0 +1,284 @@
+"""Seeded input generators and the record packer.
+
+Recipe (every draw is seeded; the same call on the same device gives the same
+tensor):
+  x         fp32 ~ N(0, 1); prefill activations are that value rounded to bf16
+  Wr        router weights ~ N(0, 0.05), rounded once to bf16, [E][H] per layer
+  bias      optional popularity term b_e = ln p_e, p_e proportional to
+            rank_e^-s (Zipf, s = 1.1), rank a seeded permutation of 1..E
+  experts   Wg, Wu [F][H] and Wd [H][F] ~ N(0, 0.02), then quantised:
+            int4: per block of 32 along the input dim, s = fp16(max|w| / 7),
+                  q = clamp(round_half_even(w / s), -8, 7)
+            int2: per block of 16, m = fp16(min w), s = fp16((max w - min w)/3),
+                  q = clamp(round_half_even((w - m) / s), 0, 3)
+            (a block whose scale is 0 gets q = 0, resp. q = 0)
+  pool      one uint8 tensor of n_slots * record_bytes; the record of
+            (layer l, expert e) sits at slot S[l][e], S a seeded permutation,
+            column E of S being the shared expert.
+
+Random numbers come from torch generators: on the CPU for small cases and on
+the GPU for the large pools (the two devices give different streams for the
+same seed; every test states where its inputs were drawn).
+"""
+import numpy as np
+import torch
+
+__all__ = [
+    "QFMT_INT4", "QFMT_INT2", "record_bytes", "seed_of", "make_gen",
+    "normal", "draw_x", "draw_x_rejecting", "to_bf16_bits", "draw_router",
+    "zipf_bias", "quantize_int4", "quantize_int2", "pack_int4", "pack_int2",
+    "pack_record", "draw_expert_weights", "make_slot_table", "build_pool",
+    "LayerInputs", "make_layer_inputs",
+]
+
+QFMT_INT4 = 0
+QFMT_INT2 = 1
+EXPERT_CHUNK = 16  # experts drawn per generator call (part of the recipe)
+
+
+def record_bytes(qfmt, H, F):
+    """Bytes of one expert record (include/moe.h, "Expert weight records")."""
+    if qfmt == QFMT_INT4:
+        return 27 * H * F // 16
+    if qfmt == QFMT_INT2:
+        return 3 * H * F // 2
+    raise ValueError(qfmt)
+
+
+def seed_of(*parts):
+    """A 63-bit seed from a tuple of ints / strings (numpy SeedSequence)."""
+    ints = []
+    for p in parts:
+        if isinstance(p, str):
+            ints.extend(p.encode())
+        else:
+            ints.append(int(p))
+    st = np.random.SeedSequence(ints).generate_state(2, dtype=np.uint32)
+    return int((int(st[0]) << 31) ^ int(st[1])) & ((1 << 63) - 1)
+
+
+def make_gen(device, *parts):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_of(*parts))
+    return g
+
+
+def normal(shape, std, gen, device):
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * std
+
+
+def to_bf16_bits(t):
+    """fp32 -> bf16 (round to nearest even) bit patterns as int16."""
+    return t.to(torch.bfloat16).view(torch.int16)
+
+
+def draw_x(seed, T, H, device="cpu", tag="x", attempt=0):
+    g = make_gen(device, seed, tag, attempt)
+    return normal((T, H), 1.0, g, device)
+
+
+def draw_x_rejecting(seed, T, H, accept, device="cpu", tag="x", max_attempts=64):
+    """Draw x token by token: token t keeps the row of the first attempt a for
+    which accept(rows)[t] is true.  `accept` maps an fp32 [T][H] CPU tensor to
+    a bool numpy array [T]; the caller supplies it (the generator holds no
+    layer arithmetic).  Returns (x, attempts_per_token)."""
+    x = draw_x(seed, T, H, device, tag, 0)
+    ok = np.asarray(accept(x.cpu()), dtype=bool)
+    att = np.zeros(T, dtype=np.int64)
+    a = 0
+    while not ok.all():
+        a += 1
+        if a >= max_attempts:
+            raise RuntimeError("rejection sampling did not converge")
+        xa = draw_x(seed, T, H, device, tag, a)
+        bad = np.nonzero(~ok)[0]
+        bad_t = torch.as_tensor(bad, device=x.device)
+        x[bad_t] = xa[bad_t]
+        att[bad] = a
+        ok = np.asarray(accept(x.cpu()), dtype=bool)
+    return x, att
+
+
+def draw_router(seed, layer, E, H, device="cpu"):
+    """Router weights as bf16 bits int16 [E][H]."""
+    g = make_gen(device, seed, "router", layer)
+    return to_bf16_bits(normal((E, H), 0.05, g, device))
+
+
+def zipf_bias(seed, layer, E, s=1.1):
+    """fp32 [E]: b_e = ln p_e, p_e = rank_e^-s / sum_r r^-s."""
+    rng = np.random.default_rng(seed_of(seed, "zipf", layer))
+    rank = rng.permutation(E) + 1
+    p = rank.astype(np.float64) ** (-s)
+    p /= p.sum()
+    return torch.from_numpy(np.log(p).astype(np.float32))
+
+
+# ----------------------------------------------------------------------------
+# quantisers (weights arrive quantised; these only build inputs)
+
+def quantize_int4(W):
+    """W fp32 [rows][K] -> (q int8 [rows][K] in [-8,7], s fp16 [rows][K/32])."""
+    rows, K = W.shape
+    Wb = W.reshape(rows, K // 32, 32)
+    s = (Wb.abs().amax(-1) / 7.0).to(torch.float16)
+    sf = s.float().unsqueeze(-1)
+    q = torch.where(sf > 0, torch.round(Wb / torch.where(sf > 0, sf, torch.ones_like(sf))),
+                    torch.zeros_like(Wb))
+    q = q.clamp(-8, 7).to(torch.int8).reshape(rows, K)
+    return q, s
+
+
+def quantize_int2(W):
+    """W fp32 [rows][K] -> (q uint8 [rows][K] in [0,3], s fp16, m fp16 [rows][K/16])."""
+    rows, K = W.shape
+    Wb = W.reshape(rows, K // 16, 16)
+    lo = Wb.amin(-1)
+    hi = Wb.amax(-1)
+    m = lo.to(torch.float16)
+    s = ((hi - lo) / 3.0).to(torch.float16)
+    sf = s.float().unsqueeze(-1)
+    q = torch.where(sf > 0,
+                    torch.round((Wb - m.float().unsqueeze(-1)) / torch.where(sf > 0, sf, torch.ones_like(sf))),
+                    torch.zeros_like(Wb))
+    q = q.clamp(0, 3).to(torch.uint8).reshape(rows, K)
+    return q, s, m
+
+
+# ----------------------------------------------------------------------------
+# packers (byte layout of include/moe.h)
+
+def _gu_rows(G, U):
+    """[..., F, H] gate/up -> [..., 2F, H] in runs of 32 rows: gate 32, up 32."""
+    *lead, F, H = G.shape
+    g = G.reshape(*lead, F // 32, 32, H)
+    u = U.reshape(*lead, F // 32, 32, H)
+    return torch.stack([g, u], dim=-3).reshape(*lead, 2 * F, H)
+
+
+def _nibble_words(n):
+    """n int32 [rows][K] (values 0..15) -> int32 words [rows][K/8]:
+    word j holds values 8j+2i at bits 4i and 8j+2i+1 at bits 16+4i."""
+    rows, K = n.shape
+    v = n.reshape(rows, K // 8, 4, 2).to(torch.int64)
+    sh = torch.arange(4, device=n.device, dtype=torch.int64) * 4
+    w = (v[..., 0] << sh).sum(-1) | (v[..., 1] << (sh + 16)).sum(-1)
+    return w.to(torch.int64)
+
+
+def _crumb_words(n):
+    """n [rows][K] (values 0..3) -> words [rows][K/16]: value 2i at bits 2i and
+    value 2i+1 at bits 16+2i."""
+    rows, K = n.shape
+    v = n.reshape(rows, K // 16, 8, 2).to(torch.int64)
+    sh = torch.arange(8, device=n.device, dtype=torch.int64) * 2
+    w = (v[..., 0] << sh).sum(-1) | (v[..., 1] << (sh + 16)).sum(-1)
+    return w.to(torch.int64)
+
+
+def _words_to_bytes(w):
+    """int64 words holding uint32 values -> uint8 little-endian bytes."""
+    w = w.reshape(-1)
+    b = torch.stack([(w >> (8 * i)) & 0xFF for i in range(4)], dim=-1)
+    return b.to(torch.uint8).reshape(-1)
+
+
+def _f16_bytes(h):
+    return h.contiguous().view(torch.uint8).reshape(-1)
+
+
+def pack_int4(Wg_q, Wg_s, Wu_q, Wu_s, Wd_q, Wd_s):
+    """Quantised int4 matrices of one expert -> record bytes (uint8)."""
+    F, H = Wg_q.shape
+    gu_q = _gu_rows(Wg_q, Wu_q)                           # [2F][H] int8
+    gu_s = _gu_rows(Wg_s, Wu_s)                           # [2F][H/32]
+    KBg, KBd = H // 32, F // 32
+    wgu = _nibble_words(gu_q.to(torch.int32) + 8)         # [2F][H/8]
+    wgu = wgu.reshape(2 * F, KBg, 4).permute(1, 0, 2)     # [kb][r][4]
+    wd = _nibble_words(Wd_q.to(torch.int32) + 8).reshape(H, KBd, 4).permute(1, 0, 2)
+    sgu = gu_s.reshape(2 * F, KBg // 4, 4).permute(1, 0, 2)  # [kb/4][r][4]
+    sd = Wd_s.reshape(H, KBd // 4, 4).permute(1, 0, 2)
+    out = torch.cat([_words_to_bytes(wgu.contiguous()), _words_to_bytes(wd.contiguous()),
+                     _f16_bytes(sgu), _f16_bytes(sd)])
+    assert out.numel() == record_bytes(QFMT_INT4, H, F)
+    return out
+
+
+def pack_int2(Wg_q, Wg_s, Wg_m, Wu_q, Wu_s, Wu_m, Wd_q, Wd_s, Wd_m):
+    """Quantised int2 matrices of one expert -> record bytes (uint8)."""
+    F, H = Wg_q.shape
+    gu_q = _gu_rows(Wg_q, Wu_q)
+    gu_s = _gu_rows(Wg_s, Wu_s)
+    gu_m = _gu_rows(Wg_m, Wu_m)
+    Ug, Ud = H // 64, F // 64
+    wgu = _crumb_words(gu_q.to(torch.int32)).reshape(2 * F, Ug, 4).permute(1, 0, 2)
+    wd = _crumb_words(Wd_q.to(torch.int32)).reshape(H, Ud, 4).permute(1, 0, 2)
+    mgu = torch.stack([gu_s, gu_m], dim=-1).reshape(2 * F, Ug, 4, 2).permute(1, 0, 2, 3)
+    md = torch.stack([Wd_s, Wd_m], dim=-1).reshape(H, Ud, 4, 2).permute(1, 0, 2, 3)
+    out = torch.cat([_words_to_bytes(wgu.contiguous()), _words_to_bytes(wd.contiguous()),
+                     _f16_bytes(mgu), _f16_bytes(md)])
+    assert out.numel() == record_bytes(QFMT_INT2, H, F)
+    return out
+
+
+def pack_record(qfmt, Wg, Wu, Wd):
+    """fp32 weights of one expert -> record bytes."""
+    if qfmt == QFMT_INT4:
+        return pack_int4(*quantize_int4(Wg), *quantize_int4(Wu), *quantize_int4(Wd))
+    return pack_int2(*quantize_int2(Wg), *quantize_int2(Wu), *quantize_int2(Wd))
+
+
+def draw_expert_weights(seed, layer, n_experts, H, F, device="cpu", std=0.02):
+    """Yield (e, Wg, Wu, Wd) for experts 0..n_experts-1 of one layer (the
+    last one, index E, is the layer's shared expert when n_experts = E+1).
+    Experts are drawn EXPERT_CHUNK at a time from one generator per layer."""
+    g = make_gen(device, seed, "experts", layer)
+    for c0 in range(0, n_experts, EXPERT_CHUNK):
+        n = min(EXPERT_CHUNK, n_experts - c0)
+        Wg = normal((n, F, H), std, g, device)
+        Wu = normal((n, F, H), std, g, device)
+        Wd = normal((n, H, F), std, g, device)
+        for i in range(n):
+            yield c0 + i, Wg[i], Wu[i], Wd[i]
+
+
+def make_slot_table(seed, L, E, n_slots=None):
+    """int32 [L][E+1]: a seeded permutation of the L*(E+1) slots."""
+    n = L * (E + 1)
+    rng = np.random.default_rng(seed_of(seed, "slots"))
+    perm = rng.permutation(n if n_slots is None else n_slots)[:n]
+    return torch.from_numpy(perm.astype(np.int32).reshape(L, E + 1))
+
+
+def build_pool(seed, L, E, H, F, qfmt, device="cpu", rec_bytes=None,
+               slot_table=None, std=0.02, progress=None):
+    """Draw and pack all L*(E+1) records.  Returns (pool uint8 [n*R], S, R)."""
+    R = record_bytes(qfmt, H, F) if rec_bytes is None else rec_bytes
+    S = make_slot_table(seed, L, E) if slot_table is None else slot_table
+    n_slots = int(S.max().item()) + 1
+    pool = torch.zeros(n_slots * R, dtype=torch.uint8, device=device)
+    for l in range(L):
+        for e, Wg, Wu, Wd in draw_expert_weights(seed, l, E + 1, H, F, device, std):
+            s = int(S[l, e])
+            rec = pack_record(qfmt, Wg, Wu, Wd)
+            pool[s * R: s * R + rec.numel()] = rec
+        if progress is not None:
+            progress(l)
+    return pool, S, R
+
+
+class LayerInputs:
+    """Everything one layer (or a stack) needs, as torch tensors."""
+
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+def make_layer_inputs(seed, L, E, H, F, qfmt=QFMT_INT4, bias=False,
+                      device="cpu", progress=None):
+    """Routers [L][E][H] (bf16 bits), bias [L][E] or None, pool, slot table."""
+    Wr = torch.stack([draw_router(seed, l, E, H, device) for l in range(L)])
+    b = torch.stack([zipf_bias(seed, l, E) for l in range(L)]).to(device) if bias else None
+    pool, S, R = build_pool(seed, L, E, H, F, qfmt, device, progress=progress)
+    return LayerInputs(seed=seed, L=L, E=E, H=H, F=F, qfmt=qfmt, Wr=Wr, bias=b,
+                       pool=pool, S=S.to(device), R=R)

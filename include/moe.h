@@ -1,0 +1,284 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed-expert MoE-FFN layer library
+ * (libmoe.so).
+ *
+ * What the layer computes.  Pages describing the Strata engine for the
+ * Qwen3.8-Flash-Next model:
+ *   - "Strata开源运行时：12GB显卡跑动125B参数Qwen3模型", section
+ *     "模型本身：稀疏MoE带来的计算与存储鸿沟": in every layer a router picks
+ *     10 of 512 experts for each token, and one shared expert always runs;
+ *     the model has 48 layers.
+ *   - "为什么 Strata 在小显存显卡上这么快", section "问题：1250 亿参数，12 GB
+ *     显存": 48 x 512 = 24,576 experts, 10 chosen per layer per token, so a
+ *     token touches 480 routed experts.
+ *   - same page, section "一个 token，三路工人": after the router, the chosen
+ *     experts' results are summed on the GPU before the next layer starts.
+ *   - same page, section "读长提示词：大块流式读取": prompts are read in
+ *     chunks of up to 8,192 (or 16,384) tokens, and a chunk routes to nearly
+ *     every expert of a layer.
+ * The pages do not spell out the expert network or the quantisation; this
+ * library fixes them as follows (all are part of the contract below):
+ *   router   l[t,e] = sum_h x[t,h] * Wr[e,h] + b[e]       (fp32 accumulation)
+ *   top-k    the k largest l[t,.], larger logit first, equal logits broken
+ *            towards the lower expert index; w[t,j] = softmax over the k
+ *            chosen logits (sums to 1).
+ *   expert   SwiGLU: y_e(x) = Wd_e ( silu(Wg_e x) * (Wu_e x) ),
+ *            silu(z) = z / (1 + exp(-z)).
+ *   layer    y[t] = sum_{j<k} w[t,j] * y_{idx[t,j]}(x_t) + y_shared(x_t)
+ *            (shared expert weight 1), summed in the order j = 0..k-1, then
+ *            the shared expert.  A stack of layers chains x_{l+1} = x_l + y_l.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions (all entry points)
+ *   - Every data pointer is DEVICE memory owned by the caller.  The library
+ *     never allocates, frees or retains device memory.  Scratch memory is the
+ *     caller's `ws` buffer of `ws_bytes` bytes, sized by moe_workspace_size().
+ *   - Work is enqueued asynchronously on the caller's HIP stream `stream`
+ *     (a hipStream_t passed as void*; NULL = the null stream).  No entry point
+ *     synchronises the device.
+ *   - Return value: MOE_OK (0) or a negative MOE_E* code.  On error nothing
+ *     has been enqueued and moe_last_error() (thread-local) describes it.
+ *     Arguments are validated on the host before any launch.  Index contents
+ *     of device arrays (expert ids, slots, rows) are preconditions that are
+ *     not checked on the host; an out-of-range value is undefined behaviour.
+ *   - bf16 and fp16 values are passed as uint16_t bit patterns.
+ *   - Entry points keep no state between calls: calls on different streams
+ *     with different workspaces may run concurrently.
+ *   - Results are deterministic: no floating-point atomics are used, so a
+ *     repeated call on the same inputs gives bit-identical outputs.
+ *
+ * ---------------------------------------------------------------------------
+ * Expert weight records
+ *   One expert = gate Wg [F][H], up Wu [F][H], down Wd [H][F] (row-major
+ *   [out][in]).  Quantisation blocks run along the input (K) dimension.
+ *   Shapes must satisfy H % 128 == 0 and F % 128 == 0.
+ *
+ *   The gate and up matrices are stored as one "GU" matrix of 2F rows:
+ *   GU row r, with g = r / 64 and i = r % 64, is gate row 32g+i when i < 32
+ *   and up row 32g+i-32 otherwise (gate and up alternate in runs of 32 rows).
+ *   The down matrix is stored as its H rows.
+ *
+ *   MOE_Q4_B32 (qfmt 0): blocks of 32 values, each with one fp16 scale s;
+ *   value = s * q, q in [-8, 7], stored as the nibble q + 8.
+ *     A 16-byte block holds four little-endian 32-bit words; word j holds
+ *     block values 8j..8j+7: value 8j+2i in bits [4i, 4i+4) and value 8j+2i+1
+ *     in bits [16+4i, 16+4i+4), i = 0..3.
+ *     Planes of one record (byte offsets from the record start):
+ *       GU_Q  at 0           : block (kb, r), kb < H/32, r < 2F, at 16*(kb*2F + r)
+ *       D_Q   at H*F         : block (kb, r), kb < F/32, r < H,  at 16*(kb*H + r)
+ *       GU_S  at 3HF/2       : scale (kb, r) at 2*((kb/4)*2F*4 + 4r + kb%4)
+ *       D_S   at 3HF/2+HF/8  : scale (kb, r) at 2*((kb/4)*H*4 + 4r + kb%4)
+ *     Record size 27HF/16 bytes (2,654,208 B at H=2048, F=768).
+ *
+ *   MOE_Q2_B16 (qfmt 1): blocks of 16 values, each with an fp16 scale s and an
+ *   fp16 offset m; value = s * q + m, q in [0, 3] stored as 2 bits.
+ *     A 32-bit little-endian word holds one block: value 2i in bits
+ *     [2i, 2i+2) and value 2i+1 in bits [16+2i, 16+2i+2), i = 0..7.
+ *     A 16-byte q-unit holds 4 consecutive blocks (word j = block 4u+j).
+ *     A 16-byte meta-unit holds (s, m) of 4 consecutive blocks: block 4u+j's
+ *     s at byte 4j and m at byte 4j+2.
+ *       GU_Q  at 0           : q-unit (u, r), u < H/64, at 16*(u*2F + r)
+ *       D_Q   at HF/2        : q-unit (u, r), u < F/64, at 16*(u*H + r)
+ *       GU_M  at 3HF/4       : meta-unit (u, r), u < H/64, at 16*(u*2F + r)
+ *       D_M   at 5HF/4       : meta-unit (u, r), u < F/64, at 16*(u*H + r)
+ *     Record size 3HF/2 bytes (2,359,296 B at H=2048, F=768).
+ *
+ *   Pool and slot table.  All records live in one caller-owned pool; the
+ *   record in slot s starts at pool + s * record_bytes.  pool must be 256-byte
+ *   aligned; record_bytes must be a multiple of 256 and at least
+ *   moe_record_bytes(qfmt, H, F).  The slot table S is int32 [L][E+1]:
+ *   S[l][e] is the slot of routed expert e of layer l, S[l][E] the slot of
+ *   layer l's shared expert.
+ *
+ *   Router weights Wr are bf16 [E][H] row-major per layer ([L][E][H] for a
+ *   stack); the optional bias b is fp32 [E] per layer ([L][E] for a stack).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* return codes */
+#define MOE_OK            0
+#define MOE_EINVAL       (-1) /* null pointer or meaningless argument      */
+#define MOE_ESHAPE       (-2) /* size outside the supported range          */
+#define MOE_EALIGN       (-3) /* misaligned pointer or record size         */
+#define MOE_EUNSUPPORTED (-4) /* unknown dtype / format / op               */
+#define MOE_EWORKSPACE   (-5) /* ws too small (or NULL when needed)        */
+#define MOE_EHIP         (-6) /* the HIP runtime reported a launch error    */
+
+/* activation dtypes */
+#define MOE_F32  0
+#define MOE_BF16 1
+
+/* weight formats */
+#define MOE_Q4_B32 0
+#define MOE_Q2_B16 1
+
+/* op ids for moe_workspace_size */
+#define MOE_OP_ROUTE_TOPK     0
+#define MOE_OP_PERMUTE        1
+#define MOE_OP_EXPERT_GEMV_Q  2
+#define MOE_OP_GROUPED_GEMM_Q 3
+#define MOE_OP_COMBINE        4
+#define MOE_OP_USAGE_UPDATE   5
+#define MOE_OP_DECODE_STACK   6
+
+/* Supported ranges (checked on the host). */
+#define MOE_MAX_E        1024  /* routed experts per layer                  */
+#define MOE_MAX_K        16    /* top-k                                     */
+#define MOE_MAX_DECODE_T 8     /* tokens per decode / verify call           */
+#define MOE_MAX_H        8192
+#define MOE_MAX_F        8192
+
+/* Version of this ABI (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Thread-local description of the last error returned on this thread
+ * ("" if none).  The string stays valid until the next call on the thread. */
+const char* moe_last_error(void);
+
+/* Minimum record size in bytes for format qfmt (0 if the shape or format is
+ * unsupported). */
+int64_t moe_record_bytes(int qfmt, int H, int F);
+
+/* Workspace bytes that entry point `op` needs for these sizes (0 = none).
+ * Arguments that an op does not use are ignored (pass 0).  For
+ * MOE_OP_DECODE_STACK, F is the FFN size and E the routed expert count;
+ * the layer count does not change the size.  Returns 0 for unknown ops. */
+size_t moe_workspace_size(int op, int T, int k, int E, int H, int F, int qfmt);
+
+/* --------------------------------------------------------------------------
+ * moe_route_topk -- router logits, top-k selection and softmax weights.
+ *   x        [T][H] activations, dtype x_dtype (MOE_F32 or MOE_BF16)
+ *   w_router bf16 [E][H], bias fp32 [E] or NULL
+ *   topk_idx int32 [T][k] out: chosen experts, larger logit first, ties to
+ *            the lower index
+ *   topk_w   fp32 [T][k] out: softmax of the chosen logits
+ *   logits_out fp32 [T][E] out, or NULL
+ * Requires 1 <= k <= MOE_MAX_K, k <= E <= MOE_MAX_E, H % 128 == 0, T >= 0.
+ * A NaN logit is a caller error (the choice is then unspecified). */
+int moe_route_topk(const void* x, int x_dtype, int T, int H,
+                   const uint16_t* w_router, const float* bias, int E, int k,
+                   int32_t* topk_idx, float* topk_w, float* logits_out,
+                   void* stream);
+
+/* --------------------------------------------------------------------------
+ * moe_permute -- group the T*k (token, choice) pairs by expert; stable.
+ *   counts  int32 [E]   out: counts[e] = #{(t,j) : topk_idx[t][j] == e}
+ *   offsets int32 [E+1] out: exclusive prefix sum, offsets[E] = T*k
+ *   row_src int32 [T*k] out: row_src[r] = t*k+j of the pair placed at row r;
+ *           rows of one expert keep ascending t*k+j order
+ *   inv_row int32 [T*k] out: inv_row[row_src[r]] = r
+ *   x_perm  optional [T*k][H] out (dtype x_dtype): x_perm[r] = x[row_src[r]/k]
+ *           (pass x = x_perm = NULL to skip)
+ * Requires 1 <= k <= MOE_MAX_K, k <= E <= MOE_MAX_E, T*k < 2^31, and
+ * topk_idx entries in [0, E).  ws: moe_workspace_size(MOE_OP_PERMUTE, ...). */
+int moe_permute(const int32_t* topk_idx, int T, int k, int E,
+                int32_t* counts, int32_t* offsets, int32_t* row_src,
+                int32_t* inv_row, const void* x, int x_dtype, int H,
+                void* x_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------------------
+ * moe_expert_gemv_q -- decode / verify experts (1 <= T <= MOE_MAX_DECODE_T).
+ *   x        fp32 [T][H]
+ *   topk_idx int32 [T][k] (from moe_route_topk)
+ *   y_parts  fp32 [T][k+1][H] out: y_parts[t][j] = y_{topk_idx[t][j]}(x_t)
+ *            for j < k, y_parts[t][k] = y_shared(x_t); not weighted.
+ * Each distinct expert of the call is read from the pool once.
+ * ws: moe_workspace_size(MOE_OP_EXPERT_GEMV_Q, T, k, E, H, F, qfmt). */
+int moe_expert_gemv_q(const float* x, int T, int H, int F,
+                      const int32_t* topk_idx, int k, int E,
+                      const int32_t* slot_table, int layer, const void* pool,
+                      int64_t record_bytes, int qfmt, float* y_parts,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------------------
+ * moe_grouped_gemm_q -- prefill experts over a permuted chunk.
+ *   x        bf16 [T][H]; every |x| must be finite in fp16 (< 65504)
+ *   row_src, offsets: from moe_permute (rows of expert e are
+ *            [offsets[e], offsets[e+1]))
+ *   y_perm   fp32 [T*k][H] out: y_perm[r] = y_e(x[row_src[r]/k])
+ *   y_shared fp32 [T][H]   out: y_shared[t] = y_shared(x[t])
+ * Experts with no rows are skipped.  Internally x is multiplied in fp16
+ * (exact for bf16 values of magnitude >= 2^-14), weights are dequantised to
+ * fp16 (one rounding of s*q, resp. s*q+m), the SiLU*mul intermediate is
+ * rounded to fp16 and all sums are fp32.
+ * ws: moe_workspace_size(MOE_OP_GROUPED_GEMM_Q, T, k, E, H, F, qfmt). */
+int moe_grouped_gemm_q(const uint16_t* x, int T, int H, int F,
+                       const int32_t* row_src, const int32_t* offsets, int k,
+                       int E, const int32_t* slot_table, int layer,
+                       const void* pool, int64_t record_bytes, int qfmt,
+                       float* y_perm, float* y_shared, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------------------
+ * moe_combine -- weighted sum of the expert outputs of each token.
+ *   inv_row == NULL: decode layout, y_rows is [T][k+1][H] as written by
+ *     moe_expert_gemv_q (slot k = shared expert) and y_shared must be NULL.
+ *   inv_row != NULL: prefill layout, y_rows is y_perm [T*k][H] and y_shared
+ *     is [T][H].
+ *   y_out[t] = sum_{j<k} topk_w[t][j] * row(t,j) + shared(t) (+ residual[t])
+ *   summed in that order in fp32.  residual may be NULL; y_out may alias
+ *   residual.
+ */
+int moe_combine(const float* y_rows, const int32_t* inv_row,
+                const float* y_shared, const float* topk_w,
+                const float* residual, int T, int k, int H, float* y_out,
+                void* stream);
+
+/* --------------------------------------------------------------------------
+ * moe_usage_update -- per-step expert usage with exponential decay and a
+ * periodic global re-rank.  Pages: "Strata：12GB 显卡跑 125B 模型，MoE 专家
+ * 热缓存打破 VRAM 限制", section "工作原理" (exponential decay: the more an
+ * expert is used the harder it is to evict); "为什么 Strata 在小显存显卡上
+ * 这么快", section "由粗到细" (the adaptive tier swaps in at most 96 experts
+ * every four rounds).
+ *   hits[e]  = number of the T tokens whose topk_idx row contains e
+ *   scores[layer][e] <- fp32( fp32(decay * scores[layer][e]) + hits[e] ),
+ *              for every e < E, each operation rounded to fp32 (no FMA)
+ *   When layer == L-1, top_out != NULL and (step+1) % rerank_every == 0:
+ *   top_out[i] = flat index l*E+e of the i-th largest score over all L*E
+ *   entries, larger score first, equal scores by lower flat index.
+ *   hits_ws  int32 [E] scratch (device).
+ * Requires scores >= 0 and finite, 1 <= top_n <= min(L*E, 1024),
+ * L*E <= 65536, rerank_every >= 1. */
+int moe_usage_update(const int32_t* topk_idx, int T, int k, int layer, int L,
+                     int E, float decay, int64_t step, int rerank_every,
+                     int top_n, int32_t* hits_ws, float* scores,
+                     int32_t* top_out, void* stream);
+
+/* --------------------------------------------------------------------------
+ * moe_decode_stack -- one decode / verify step through L chained layers
+ * (1 <= T <= MOE_MAX_DECODE_T), the whole step enqueued as a single
+ * persistent kernel.  Pages: "为什么 Strata 在小显存显卡上这么快", section
+ * "一个 token，三路工人" (the whole 48-layer forward is recorded once and
+ * replayed so that the host never waits inside a step); section "先猜，再检查"
+ * (a verify step runs 1 real + up to 3 drafted tokens through all 48 layers).
+ *   x_in     fp32 [T][H];  x_out fp32 [T][H] (may not alias x_in)
+ *   w_router bf16 [L][E][H];  bias fp32 [L][E] or NULL
+ *   slot_table int32 [L][E+1]
+ *   topk_idx_out int32 [L][T][k] or NULL; topk_w_out fp32 [L][T][k] or NULL
+ *   x_hist   fp32 [L][T][H] or NULL: x_hist[l] = input of layer l
+ * Per layer it computes exactly what moe_route_topk + moe_expert_gemv_q +
+ * moe_combine(residual = x_l) compute.
+ * ws: moe_workspace_size(MOE_OP_DECODE_STACK, T, k, E, H, F, qfmt). */
+int moe_decode_stack(const float* x_in, int T, int H, int F, int E, int k,
+                     int L, const uint16_t* w_router, const float* bias,
+                     const int32_t* slot_table, const void* pool,
+                     int64_t record_bytes, int qfmt, float* x_out,
+                     int32_t* topk_idx_out, float* topk_w_out, float* x_hist,
+                     void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

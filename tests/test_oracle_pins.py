@@ -1,0 +1,327 @@
+"""Pins of the CPU oracle against things other than itself: hand-derived
+fixtures of the byte format, closed forms, brute force on tiny inputs,
+identities and library routines.  CPU only."""
+import json
+import math
+import os
+import struct
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import gen as G
+import oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _fixture(name):
+    with open(os.path.join(GOLD, name)) as f:
+        d = json.load(f)
+    rec = np.zeros(d["record_bytes"], np.uint8)
+    for w in d["writes"]:
+        b = np.frombuffer(bytes.fromhex(w["hex"]), np.uint8)
+        rec[w["offset"]:w["offset"] + b.size] = b
+    return d, rec
+
+
+# ---------------------------------------------------------------- format
+
+def test_record_sizes():
+    # 27HF/16 and 3HF/2 bytes; at H=2048, F=768: 648 and 576 pages of 4 KiB
+    assert G.record_bytes(0, 2048, 768) == 2_654_208 == 648 * 4096
+    assert G.record_bytes(1, 2048, 768) == 2_359_296 == 576 * 4096
+    assert G.record_bytes(0, 256, 128) == 55_296
+
+
+@pytest.mark.parametrize("name", ["format_int4.json", "format_int2.json"])
+def test_decode_hand_made_record(name):
+    d, rec = _fixture(name)
+    assert rec.size == G.record_bytes(d["qfmt"], d["H"], d["F"])
+    Wg, Wu, Wd = O.decode_record(rec, d["qfmt"], d["H"], d["F"])
+    assert Wg.shape == (d["F"], d["H"]) and Wu.shape == (d["F"], d["H"]) and Wd.shape == (d["H"], d["F"])
+    mats = {"gate": Wg, "up": Wu, "down": Wd}
+    listed = {m: np.zeros(M.shape, bool) for m, M in mats.items()}
+    for ex in d["expect"]:
+        vals = ex["values"] if "values" in ex else [ex["fill"]] * ex["n"]
+        got = mats[ex["m"]][ex["row"], ex["col0"]:ex["col0"] + len(vals)]
+        np.testing.assert_array_equal(got, np.array(vals, np.float64), err_msg=str(ex))
+        listed[ex["m"]][ex["row"], ex["col0"]:ex["col0"] + len(vals)] = True
+    for m, M in mats.items():
+        assert np.all(M[~listed[m]] == 0), m
+
+
+@pytest.mark.parametrize("qfmt", [0, 1])
+def test_quantise_decode_round_trip(qfmt):
+    H, F = 256, 128
+    g = G.make_gen("cpu", 123, "rt", qfmt)
+    Wg, Wu, Wd = (G.normal(s, 0.02, g, "cpu") for s in [(F, H), (F, H), (H, F)])
+    rec = G.pack_record(qfmt, Wg, Wu, Wd).numpy()
+    dec = O.decode_record(rec, qfmt, H, F)
+    for W, D in zip((Wg, Wu, Wd), dec):
+        if qfmt == 0:
+            q, s = G.quantize_int4(W)
+            blk = 32
+            exact = q.double().numpy() * np.repeat(s.double().numpy(), blk, axis=1)
+            bound = np.repeat(s.double().numpy(), blk, axis=1) / 2
+        else:
+            q, s, m = G.quantize_int2(W)
+            blk = 16
+            sr = np.repeat(s.double().numpy(), blk, axis=1)
+            mr = np.repeat(m.double().numpy(), blk, axis=1)
+            exact = q.double().numpy() * sr + mr
+            lo = W.double().numpy().reshape(W.shape[0], -1, blk).min(-1)
+            hi = W.double().numpy().reshape(W.shape[0], -1, blk).max(-1)
+            # s/2 plus what the fp16 rounding of m and s moves the grid ends
+            slack = np.abs(np.repeat(lo, blk, 1) - mr) + np.abs(3 * sr - np.repeat(hi - lo, blk, 1))
+            bound = sr / 2 + slack
+        np.testing.assert_array_equal(D, exact)  # decoder == quantiser's (q, s[, m])
+        assert np.all(np.abs(W.double().numpy() - D) <= bound * (1 + 1e-6) + 1e-12)
+
+
+# ---------------------------------------------------------------- router / top-k
+
+def _brute_topk(x, Wr, b, k):
+    T, E = len(x), len(Wr)
+    idx, w = [], []
+    for t in range(T):
+        l = [math.fsum(x[t][h] * Wr[e][h] for h in range(len(x[t]))) + (b[e] if b is not None else 0.0)
+             for e in range(E)]
+        order = sorted(range(E), key=lambda e: (-l[e], e))[:k]
+        z = [math.exp(l[e] - l[order[0]]) for e in order]
+        idx.append(order)
+        w.append([v / math.fsum(z) for v in z])
+    return np.array(idx), np.array(w)
+
+
+def test_topk_brute_force_tiny():
+    rng = np.random.default_rng(5)
+    for trial in range(20):
+        T, E, H = 3, int(rng.integers(2, 9)), 5
+        k = int(rng.integers(1, E + 1))
+        x = rng.normal(size=(T, H))
+        Wr = rng.normal(size=(E, H))
+        b = rng.normal(size=E) if trial % 2 else None
+        idx, w = O.topk_select(O.router_logits(x, Wr, b), k)
+        bi, bw = _brute_topk(x.tolist(), Wr.tolist(), None if b is None else b.tolist(), k)
+        np.testing.assert_array_equal(idx, bi)
+        np.testing.assert_allclose(w, bw, rtol=0, atol=1e-14)
+
+
+def test_ties_go_to_lower_index():
+    H, E, k = 8, 6, 3
+    Wr = np.zeros((E, H))
+    Wr[5] = Wr[2] = np.arange(1, H + 1)   # identical best rows 2 and 5
+    Wr[4] = 0.5 * np.arange(1, H + 1)
+    x = np.ones((1, H))
+    idx, w = O.topk_select(O.router_logits(x, Wr), k)
+    assert idx.tolist() == [[2, 5, 4]]
+    assert w[0, 0] == w[0, 1]
+
+
+def test_all_zero_router_picks_first_k_uniformly():
+    idx, w = O.topk_select(O.router_logits(np.ones((2, 16)), np.zeros((10, 16))), 4)
+    assert idx.tolist() == [[0, 1, 2, 3]] * 2
+    assert np.all(w == 0.25)
+
+
+def test_k2_closed_form_and_full_softmax_renormalised():
+    rng = np.random.default_rng(1)
+    l = rng.normal(size=(50, 12)) * 2
+    idx, w = O.topk_select(l, 2)
+    l0 = l[np.arange(50), idx[:, 0]]
+    l1 = l[np.arange(50), idx[:, 1]]
+    np.testing.assert_allclose(w[:, 0], 1.0 / (1.0 + np.exp(l1 - l0)), rtol=1e-14)
+    # softmax over all experts, then renormalised over the chosen k
+    for k in (1, 3, 7, 12):
+        idx, w = O.topk_select(l, k)
+        p = scipy.special.softmax(l, axis=1)
+        pk = np.take_along_axis(p, idx, 1)
+        np.testing.assert_allclose(w, pk / pk.sum(1, keepdims=True), rtol=1e-12)
+        assert np.all([len(set(r)) == k for r in idx.tolist()])
+        np.testing.assert_allclose(w.sum(1), 1.0, rtol=0, atol=1e-15)
+        assert np.all(np.diff(np.take_along_axis(l, idx, 1), axis=1) <= 0)
+
+
+def test_gap_helpers():
+    l = np.array([[5.0, 4.0, 4.0005, 1.0], [3.0, 2.0, 1.0, 0.0]])
+    np.testing.assert_allclose(O.topk_gaps(l, 2), [0.0005, 1.0])
+    assert O.gap_ok(l, 2).tolist() == [False, True]
+    assert O.gap_ok(l, 1).tolist() == [True, True]
+
+
+# ---------------------------------------------------------------- experts
+
+def test_silu_identities_and_library():
+    z = np.linspace(-30, 30, 1001)
+    np.testing.assert_allclose(O.silu(z) - O.silu(-z), z, rtol=0, atol=1e-12)
+    assert O.silu(0.0) == 0.0
+    assert abs(O.silu(60.0) - 60.0) < 1e-20 and abs(O.silu(-60.0)) < 1e-20
+    ref = torch.nn.functional.silu(torch.from_numpy(z)).numpy()
+    np.testing.assert_allclose(O.silu(z), ref, rtol=1e-15, atol=1e-300)
+
+
+def test_swiglu_hand_example():
+    # Wg = I, Wu = 2I, Wd = I, x = (ln3, -ln3, 0):
+    # silu(ln3) = ln3 * 3/4, silu(-ln3) = -ln3 / 4, so y = (1.5 ln^2 3, 0.5 ln^2 3, 0)
+    L3 = math.log(3.0)
+    I = np.eye(3)
+    y = O.expert_ffn(I, 2 * I, I, np.array([[L3, -L3, 0.0]]))
+    np.testing.assert_allclose(y[0], [1.5 * L3 * L3, 0.5 * L3 * L3, 0.0], rtol=1e-15, atol=1e-300)
+
+
+def test_expert_operand_orientation():
+    # rectangular shapes: Wg, Wu are [F][H], Wd is [H][F]
+    H, F = 4, 2
+    Wg = np.zeros((F, H)); Wg[1, 2] = 1.0      # g1 = x2
+    Wu = np.zeros((F, H)); Wu[1, 0] = 1.0      # u1 = x0
+    Wd = np.zeros((H, F)); Wd[3, 1] = 5.0      # y3 = 5 h1
+    x = np.array([[2.0, 0.0, math.log(3.0), 0.0]])
+    y = O.expert_ffn(Wg, Wu, Wd, x)
+    np.testing.assert_allclose(y[0], [0, 0, 0, 5 * 0.75 * math.log(3.0) * 2.0], rtol=1e-15)
+
+
+def _scaled_identity_experts(a, b, H):
+    """Expert e: Wg = a_e I, Wu = I, Wd = b_e I, so y_e(x) = b_e silu(a_e x) x."""
+    I = np.eye(H)
+    return lambda e: (a[e] * I, I, b[e] * I)
+
+
+def test_dense_mixture_when_k_equals_E():
+    rng = np.random.default_rng(7)
+    T, H, E = 5, 6, 4
+    a = rng.normal(size=E + 1); b = rng.normal(size=E + 1)
+    x = rng.normal(size=(T, H)); Wr = rng.normal(size=(E, H))
+    y, idx, w, _, l = O.moe_layer(x, Wr, None, E, _scaled_identity_experts(a, b, H), E)
+    xt = torch.from_numpy(x)
+    p = torch.softmax(torch.from_numpy(x @ Wr.T), dim=1)
+    ref = sum(p[:, e:e + 1] * b[e] * torch.nn.functional.silu(a[e] * xt) * xt for e in range(E))
+    ref = ref + b[E] * torch.nn.functional.silu(a[E] * xt) * xt
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_single_expert_and_zero_down():
+    rng = np.random.default_rng(8)
+    T, H = 3, 5
+    a = rng.normal(size=2); b = rng.normal(size=2)
+    x = rng.normal(size=(T, H))
+    get = _scaled_identity_experts(a, b, H)
+    y, idx, w, parts, _ = O.moe_layer(x, rng.normal(size=(1, H)), None, 1, get, 1)
+    assert np.all(idx == 0) and np.all(w == 1.0)
+    np.testing.assert_allclose(y, b[0] * O.silu(a[0] * x) * x + b[1] * O.silu(a[1] * x) * x, rtol=1e-13)
+    # routed experts with a zero down matrix leave only the shared expert
+    E = 6
+    b2 = np.zeros(E + 1); b2[E] = 1.5
+    a2 = rng.normal(size=E + 1)
+    y, *_ = O.moe_layer(x, rng.normal(size=(E, H)), None, 3, _scaled_identity_experts(a2, b2, H), E)
+    np.testing.assert_allclose(y, 1.5 * O.silu(a2[E] * x) * x, rtol=1e-14)
+
+
+def test_combine_hand_example():
+    yr = np.array([[[1.0, 2.0], [10.0, 20.0]]])
+    ys = np.array([[100.0, 200.0]])
+    w = np.array([[0.25, 0.75]])
+    np.testing.assert_array_equal(O.combine(yr, w, ys), [[107.75, 215.5]])
+    np.testing.assert_array_equal(O.combine(yr, w, ys, residual=np.array([[1.0, -1.0]])), [[108.75, 214.5]])
+
+
+# ---------------------------------------------------------------- permutation
+
+def test_permute_brute_force_and_invariants():
+    rng = np.random.default_rng(3)
+    for T, k, E in [(1, 1, 1), (7, 2, 5), (40, 4, 9), (100, 10, 512), (3, 3, 1000)]:
+        idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
+        counts, offsets, row_src, inv_row = O.permute(idx, E)
+        flat = idx.reshape(-1).tolist()
+        brute = sorted(range(T * k), key=lambda i: (flat[i], i))
+        assert row_src.tolist() == brute
+        assert counts.sum() == T * k and offsets[0] == 0 and offsets[-1] == T * k
+        assert counts.tolist() == [flat.count(e) for e in range(E)]
+        assert np.all(inv_row[row_src] == np.arange(T * k))
+        X = rng.normal(size=(T, 3))
+        xp = X[row_src // k]                                   # permute
+        back = xp[inv_row].reshape(T, k, 3)                    # unpermute
+        assert np.all(back == X[:, None, :])
+        for e in range(E):
+            seg = row_src[offsets[e]:offsets[e + 1]]
+            assert np.all(idx.reshape(-1)[seg] == e) and np.all(np.diff(seg) > 0)
+
+
+# ---------------------------------------------------------------- usage
+
+def _r32(v):
+    return struct.unpack("f", struct.pack("f", v))[0]
+
+
+def test_usage_emulates_fp32_one_rounding_per_op():
+    rng = np.random.default_rng(11)
+    L, E = 3, 20
+    s = rng.uniform(0, 50, size=(L, E)).astype(np.float32)
+    idx = np.stack([rng.choice(E, 4, replace=False) for _ in range(6)])
+    new, top = O.usage_update(s, idx, 1, 0.99, 0, 4, 5)
+    hits = [sum(1 for row in idx.tolist() if e in row) for e in range(E)]
+    d32 = _r32(0.99)
+    for e in range(E):
+        assert new[1, e] == _r32(_r32(d32 * float(s[1, e])) + hits[e])
+    assert np.array_equal(new[[0, 2]], s[[0, 2]]) and top is None
+
+
+def test_usage_closed_form_and_rerank():
+    L, E, h = 2, 8, 3
+    s = np.zeros((L, E), np.float32)
+    idx = np.array([[0, 1]] * h)  # experts 0 and 1 get h hits per step
+    tops = {}
+    for n in range(1, 41):
+        for layer in range(L):
+            s, top = O.usage_update(s, idx if layer == 0 else idx + 2, layer, 0.99, n - 1, 4, 5)
+            if top is not None:
+                tops[n] = top
+        expect = h * (1 - 0.99 ** n) / 0.01
+        assert abs(float(s[0, 0]) - expect) <= 1e-5 * expect
+    assert sorted(tops) == list(range(4, 41, 4))
+    # ties between equal scores go to the lower flat index: 0,1 (layer 0), 10,11 (layer 1)
+    assert tops[40].tolist() == [0, 1, 10, 11, 2]
+
+
+def test_usage_topn_brute_force():
+    rng = np.random.default_rng(2)
+    L, E = 4, 30
+    s = rng.integers(0, 6, size=(L, E)).astype(np.float32)   # many ties
+    new, top = O.usage_update(s, np.zeros((0, 3), np.int64), L - 1, 0.5, 3, 4, 17)
+    flat = new.reshape(-1).tolist()
+    brute = sorted(range(L * E), key=lambda i: (-flat[i], i))[:17]
+    assert top.tolist() == brute
+
+
+# ---------------------------------------------------------------- stack
+
+def test_stack_chaining_and_identity():
+    rng = np.random.default_rng(4)
+    T, H, E, L, k = 2, 6, 5, 3, 2
+    x = rng.normal(size=(T, H))
+    Wr = rng.normal(size=(L, E, H))
+    getters = [_scaled_identity_experts(rng.normal(size=E + 1), rng.normal(size=E + 1), H) for _ in range(L)]
+    xo, idx, w, hist = O.moe_stack_decode(x, Wr, None, k, getters, E)
+    assert np.array_equal(hist[0], x)
+    for l in range(L):
+        y, i2, w2, _, _ = O.moe_layer(hist[l], Wr[l], None, k, getters[l], E)
+        nxt = hist[l + 1] if l + 1 < L else xo
+        np.testing.assert_array_equal(nxt, hist[l] + y)
+        assert np.array_equal(i2, idx[l])
+    zero = [_scaled_identity_experts(np.ones(E + 1), np.zeros(E + 1), H)] * L
+    xo, *_ = O.moe_stack_decode(x, Wr, None, k, zero, E)
+    np.testing.assert_array_equal(xo, x)
+
+
+def test_pages_structural_constants():
+    with open(os.path.join(GOLD, "pages_constants.json")) as f:
+        c = json.load(f)
+    assert c["layers"] * c["experts_per_layer"] == c["total_experts"]
+    assert c["layers"] * c["top_k"] == c["experts_per_token"]
+    # one token's routed rows over 48 layers: permuting a single token per
+    # layer gives exactly k rows per layer, all distinct experts
+    idx = np.arange(c["top_k"])[None, :]
+    counts, *_ = O.permute(idx, c["experts_per_layer"])
+    assert counts.sum() == c["top_k"] and counts.max() == 1
