@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE-FFN layer on one MI355X.
+
+Headline (the JSON `value`): decode tokens/s through a 48-layer MoE-only stack
+(512 experts top-10 + 1 shared expert per layer, hidden 2048, FFN 768, int4
+blocks of 32 with fp16 scales, Zipf(1.1) router bias), batch 1, every weight
+resident in HBM behind the (layer, expert) -> slot table.  One step = one
+token through all 48 layers (router, top-k, expert gather-GEMV, combine),
+enqueued as one HIP graph replay.  Inputs are synthetic and seeded (gen/).
+
+Also measured and reported under "extra": the speculative-verify step (4
+tokens per step) and one 8,192-token prefill chunk through one layer (route,
+permute, grouped GEMM on the matrix cores, combine).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+MFMA_F16_PEAK_TFS = 2500.0  # MI355X dense fp16 / bf16 matrix peak
+
+METRIC = "MoE decode tokens/s over 48 layers (HBM GB/s, % peak); prefill tok/s (% MFMA)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "routed_expert_ffn_moe_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_tag, per_launch_units):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("source_hash") != source_hash():
+        return None
+    return d.get("bytes_per_" + per_launch_units)
+
+
+class LazyPool:
+    def __init__(self, pool):
+        self.pool = pool
+
+    def __getitem__(self, sl):
+        return self.pool[sl].cpu().numpy()
+
+
+def cpu_baseline(li, x_tok, budget_s):
+    """The oracle (as it stands) on the host: one token through as many of the
+    48 layers as fit in the time budget (at least 2), scaled to 48 layers."""
+    import numpy as np
+    import oracle as O
+    S = li.S.cpu().numpy()
+    x = x_tok.detach().cpu().double().numpy()
+    t0, c0 = time.perf_counter(), os.times()
+    n = 0
+    while n < li.L and (n < 2 or time.perf_counter() - t0 < budget_s):
+        Wr = O.bf16_to_f64(li.Wr[n].cpu().numpy())
+        b = None if li.bias is None else li.bias[n].cpu().double().numpy()
+        get = O.expert_getter(LazyPool(li.pool), S, n, li.qfmt, li.H, li.F, li.R)
+        y, *_ = O.moe_layer(O.rms_normalize(x), Wr, b, li.k, get, li.E)
+        x = x + y
+        n += 1
+    wall = time.perf_counter() - t0
+    c1 = os.times()
+    cpu = (c1.user - c0.user) + (c1.system - c0.system)
+    per_token = wall / n * li.L
+    return {"value": round(1.0 / per_token, 6), "unit": "tokens/s", "cores": round(cpu / wall, 2),
+            "cores_available": os.cpu_count(), "kind": "oracle",
+            "sample": f"1 token through the first {n} of {li.L} layers (fp64 NumPy, records decoded per layer), "
+                      f"{wall:.1f} s, scaled to {li.L} layers"}, np
+
+
+def decode_bench(M, li, T, steps, warmup, use_graph, seed_tag):
+    """Times `steps` decode steps of T tokens.  Returns a dict of results."""
+    import torch
+    import gen as G
+    dev = li.pool.device
+    L, E, H, F, k = li.L, li.E, li.H, li.F, li.k
+    xs = G.draw_x(2, (steps + warmup) * T, H, dev, tag=seed_tag).view(steps + warmup, T, H)
+    x_in = torch.empty((T, H), dtype=torch.float32, device=dev)
+    x_out = torch.empty_like(x_in)
+    idx_out = torch.empty((L, T, k), dtype=torch.int32, device=dev)
+    ws = M.workspace(M.MOE_OP_DECODE_STACK, dev, T, k, E, H, F, li.qfmt)
+
+    def step():
+        M.moe_decode_stack(x_in, F, E, k, li.Wr, li.bias, li.S, li.pool, li.R, li.qfmt, x_out=x_out,
+                           topk_idx_out=idx_out, ws=ws)
+
+    x_in.copy_(xs[0])
+    step()
+    torch.cuda.synchronize()
+    ref = x_out.clone()
+    if not torch.isfinite(ref).all():
+        raise RuntimeError("decode step produced non-finite values")
+    graph = None
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                step()
+        torch.cuda.current_stream().wait_stream(s)
+        for rep in range(2):  # replays must match the eager step bit for bit
+            x_out.zero_()
+            x_in.copy_(xs[0])
+            graph.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(x_out, ref):
+                raise RuntimeError("graph replay differs from the eager step")
+    run = graph.replay if graph is not None else step
+    for i in range(warmup):
+        x_in.copy_(xs[i])
+        run()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(steps):
+        x_in.copy_(xs[warmup + i])
+        run()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    # distinct experts per layer of every timed step (re-run untimed to read the routing)
+    uniq = []
+    for i in range(steps):
+        x_in.copy_(xs[warmup + i])
+        run()
+        torch.cuda.synchronize()
+        ids = idx_out.cpu()
+        uniq.append([len(set(ids[l].reshape(-1).tolist())) for l in range(L)])
+    return {"ms": ms, "uniq": uniq, "steps": steps, "T": T}
+
+
+def decode_bytes(li, uniq_step, T):
+    """Algorithmic HBM bytes of one step: every distinct expert's record plus
+    the shared expert's, the router matrix, and the activations read and
+    written (x in, x out) per layer."""
+    return sum((u + 1) * li.R + li.E * li.H * 2 + 2 * T * li.H * 4 for u in uniq_step)
+
+
+def prefill_bench(M, li, reps, warmup):
+    """One 8,192-token bf16 chunk through layer 0 (no bias: near-uniform routing)."""
+    import torch
+    import gen as G
+    dev = li.pool.device
+    T, H, E, k, F = 8192, li.H, li.E, li.k, li.F
+    x = G.draw_x(3, T, H, dev, tag="bench-prefill").to(torch.bfloat16)
+    Wr0 = li.Wr[0].contiguous()
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    ws_r = M.workspace(M.MOE_OP_ROUTE_TOPK, dev, T=T, E=E)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_src = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv_row = torch.empty(T * k, dtype=torch.int32, device=dev)
+    ws_p = M.workspace(M.MOE_OP_PERMUTE, dev, T=T, k=k, E=E)
+    y_perm = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+    y_sh = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws_g = M.workspace(M.MOE_OP_GROUPED_GEMM_Q, dev, T, k, E, H, F, li.qfmt)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream()
+    names = ["route", "permute", "grouped_gemm", "combine"]
+    ops = [
+        lambda: M.moe_route_topk(x, Wr0, None, k, topk_idx=idx, topk_w=w, ws=ws_r),
+        lambda: M.moe_permute(idx, E, counts, offsets, row_src, inv_row, ws=ws_p),
+        lambda: M.moe_grouped_gemm_q(x, row_src, offsets, k, E, F, li.S, 0, li.pool, li.R, li.qfmt, y_perm=y_perm,
+                                     y_shared=y_sh, ws=ws_g),
+        lambda: M.moe_combine(y_perm, w, inv_row=inv_row, y_shared=y_sh, y_out=y),
+    ]
+    for _ in range(warmup):
+        for op in ops:
+            op()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(reps)]
+    for r in range(reps):
+        ev[r][0].record(st)
+        for i, op in enumerate(ops):
+            op()
+            ev[r][i + 1].record(st)
+    torch.cuda.synchronize()
+    per_op = {n: sorted(ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps))[reps // 2]
+              for i, n in enumerate(names)}
+    total = sorted(ev[r][0].elapsed_time(ev[r][-1]) for r in range(reps))[reps // 2]
+    experts_hit = int((counts > 0).sum().item())
+    flop_routed = 2.0 * T * k * 3 * H * F
+    flop_shared = 2.0 * T * 3 * H * F
+    gemm_s = per_op["grouped_gemm"] / 1e3
+    tf_routed_equiv = (flop_routed + flop_shared) / gemm_s / 1e12
+    return {
+        "workload": "8,192-token bf16 chunk, 1 layer, 512 experts top-10 + shared, int4 (median of "
+                    f"{reps})",
+        "tokens_per_s": round(T / (total / 1e3), 1),
+        "ms_layer": round(total, 4),
+        "ms_per_op": {n: round(v, 4) for n, v in per_op.items()},
+        "grouped_gemm_tflops": round(tf_routed_equiv, 2),
+        "grouped_gemm_mfma_frac": round(tf_routed_equiv / MFMA_F16_PEAK_TFS, 4),
+        "grouped_gemm_gflop": {"routed": round(flop_routed / 1e9, 1), "shared": round(flop_shared / 1e9, 1)},
+        "routed_gemm_target_ms": round(flop_routed / 1e9 / (0.5 * MFMA_F16_PEAK_TFS), 4),
+        "experts_hit": experts_hit,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-graph", action="store_true", help="launch the step eagerly instead of a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the verify and prefill measurements")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the layer is data-parallel with a "
+              "replicated expert pool; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gen as G
+    import routed_expert_ffn_moe_amd as M
+    M.load(build_if_missing=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    L, E, H, F, k = 48, 512, 2048, 768, 10
+    t0 = time.perf_counter()
+    li = G.make_layer_inputs(2, L, E, H, F, qfmt=0, bias=True, device=dev,
+                             progress=lambda l: log(f"pool: layer {l + 1}/{L}") if (l + 1) % 8 == 0 else None)
+    li.k = k
+    torch.cuda.synchronize()
+    log(f"pool of {li.pool.numel() / 1e9:.1f} GB built in {time.perf_counter() - t0:.1f} s")
+
+    d1 = decode_bench(M, li, 1, args.steps, args.warmup, not args.no_graph, "bench-x")
+    ms_step = d1["ms"] / args.steps
+    bytes_steps = [decode_bytes(li, u, 1) for u in d1["uniq"]]
+    bytes_per_step = sum(bytes_steps) / len(bytes_steps)
+    gbs = bytes_per_step / (ms_step / 1e3) / 1e9
+    value = args.steps / (d1["ms"] / 1e3)
+    log(f"decode T=1: {ms_step:.4f} ms/step, {value:.1f} tok/s, {gbs:.1f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of peak)")
+
+    traffic = measured_traffic("decode_stack_t1", "step")
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int4-weights x fp16 dot2 -> fp32", "data": "synthetic",
+        "config": {"workload": "48-layer MoE-only stack decode, batch 1 (1 token per step)", "layers": L,
+                   "experts": E, "top_k": k, "shared_experts": 1, "hidden": H, "ffn": F,
+                   "weights": "int4 blocks of 32, fp16 scale", "router_bias": "Zipf(1.1)",
+                   "pool_gb": round(li.pool.numel() / 1e9, 2),
+                   "launch": "hip-graph replay per step" if not args.no_graph else "eager"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "whole decode step (router + top-k + expert GEMV + combine, 48 layers)",
+                     "algorithmic_bytes_per_step": round(bytes_per_step)},
+    }
+    if not args.no_extra:
+        d4 = decode_bench(M, li, 4, args.steps, args.warmup, not args.no_graph, "bench-x4")
+        ms4 = d4["ms"] / args.steps
+        b4 = sum(decode_bytes(li, u, 4) for u in d4["uniq"]) / len(d4["uniq"])
+        u4 = sum(sum(u) for u in d4["uniq"]) / (len(d4["uniq"]) * L)
+        pf = prefill_bench(M, li, reps=10, warmup=3)
+        out["extra"] = {
+            "verify_t4": {"token_positions_per_s": round(4 * args.steps / (d4["ms"] / 1e3), 1),
+                          "ms_per_step": round(ms4, 5), "gbs": round(b4 / (ms4 / 1e3) / 1e9, 1),
+                          "hbm_frac": round(b4 / (ms4 / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "mean_distinct_experts_per_layer": round(u4, 2)},
+            "prefill_c4": pf,
+        }
+        log(f"verify T=4: {ms4:.4f} ms/step; prefill: {json.dumps(pf)}")
+    if not args.no_cpu_baseline:
+        xs = G.draw_x(2, 1, H, dev, tag="bench-x")
+        cb, _ = cpu_baseline(li, xs, args.cpu_budget)
+        out["cpu_baseline"] = cb
+        log(f"cpu baseline: {cb}")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

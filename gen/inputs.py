@@ -28,7 +28,7 @@ __all__ = [
     "normal", "draw_x", "draw_x_rejecting", "to_bf16_bits", "draw_router",
     "zipf_bias", "quantize_int4", "quantize_int2", "pack_int4", "pack_int2",
     "pack_record", "draw_expert_weights", "make_slot_table", "build_pool",
-    "LayerInputs", "make_layer_inputs",
+    "LayerInputs", "make_layer_inputs", "draw_expert_chunks",
 ]
 
 QFMT_INT4 = 0
@@ -118,21 +118,21 @@ def zipf_bias(seed, layer, E, s=1.1):
 # quantisers (weights arrive quantised; these only build inputs)
 
 def quantize_int4(W):
-    """W fp32 [rows][K] -> (q int8 [rows][K] in [-8,7], s fp16 [rows][K/32])."""
-    rows, K = W.shape
-    Wb = W.reshape(rows, K // 32, 32)
+    """W fp32 [..., rows, K] -> (q int8 [..., rows, K] in [-8,7], s fp16 [..., rows, K/32])."""
+    *lead, K = W.shape
+    Wb = W.reshape(*lead, K // 32, 32)
     s = (Wb.abs().amax(-1) / 7.0).to(torch.float16)
     sf = s.float().unsqueeze(-1)
     q = torch.where(sf > 0, torch.round(Wb / torch.where(sf > 0, sf, torch.ones_like(sf))),
                     torch.zeros_like(Wb))
-    q = q.clamp(-8, 7).to(torch.int8).reshape(rows, K)
+    q = q.clamp(-8, 7).to(torch.int8).reshape(*lead, K)
     return q, s
 
 
 def quantize_int2(W):
-    """W fp32 [rows][K] -> (q uint8 [rows][K] in [0,3], s fp16, m fp16 [rows][K/16])."""
-    rows, K = W.shape
-    Wb = W.reshape(rows, K // 16, 16)
+    """W fp32 [..., rows, K] -> (q uint8 [..., rows, K] in [0,3], s fp16, m fp16 [..., rows, K/16])."""
+    *lead, K = W.shape
+    Wb = W.reshape(*lead, K // 16, 16)
     lo = Wb.amin(-1)
     hi = Wb.amax(-1)
     m = lo.to(torch.float16)
@@ -141,7 +141,7 @@ def quantize_int2(W):
     q = torch.where(sf > 0,
                     torch.round((Wb - m.float().unsqueeze(-1)) / torch.where(sf > 0, sf, torch.ones_like(sf))),
                     torch.zeros_like(Wb))
-    q = q.clamp(0, 3).to(torch.uint8).reshape(rows, K)
+    q = q.clamp(0, 3).to(torch.uint8).reshape(*lead, K)
     return q, s, m
 
 
@@ -157,88 +157,100 @@ def _gu_rows(G, U):
 
 
 def _nibble_words(n):
-    """n int32 [rows][K] (values 0..15) -> int32 words [rows][K/8]:
+    """n int [..., K] (values 0..15) -> int64 words [..., K/8]:
     word j holds values 8j+2i at bits 4i and 8j+2i+1 at bits 16+4i."""
-    rows, K = n.shape
-    v = n.reshape(rows, K // 8, 4, 2).to(torch.int64)
+    *lead, K = n.shape
+    v = n.reshape(*lead, K // 8, 4, 2).to(torch.int64)
     sh = torch.arange(4, device=n.device, dtype=torch.int64) * 4
-    w = (v[..., 0] << sh).sum(-1) | (v[..., 1] << (sh + 16)).sum(-1)
-    return w.to(torch.int64)
+    return (v[..., 0] << sh).sum(-1) | (v[..., 1] << (sh + 16)).sum(-1)
 
 
 def _crumb_words(n):
-    """n [rows][K] (values 0..3) -> words [rows][K/16]: value 2i at bits 2i and
-    value 2i+1 at bits 16+2i."""
-    rows, K = n.shape
-    v = n.reshape(rows, K // 16, 8, 2).to(torch.int64)
+    """n [..., K] (values 0..3) -> int64 words [..., K/16]: value 2i at bits 2i
+    and value 2i+1 at bits 16+2i."""
+    *lead, K = n.shape
+    v = n.reshape(*lead, K // 16, 8, 2).to(torch.int64)
     sh = torch.arange(8, device=n.device, dtype=torch.int64) * 2
-    w = (v[..., 0] << sh).sum(-1) | (v[..., 1] << (sh + 16)).sum(-1)
-    return w.to(torch.int64)
+    return (v[..., 0] << sh).sum(-1) | (v[..., 1] << (sh + 16)).sum(-1)
 
 
 def _words_to_bytes(w):
-    """int64 words holding uint32 values -> uint8 little-endian bytes."""
-    w = w.reshape(-1)
-    b = torch.stack([(w >> (8 * i)) & 0xFF for i in range(4)], dim=-1)
-    return b.to(torch.uint8).reshape(-1)
+    """int64 words holding uint32 values [n, ...] -> uint8 little-endian [n, bytes]."""
+    n = w.shape[0]
+    w = torch.where(w >= (1 << 31), w - (1 << 32), w)  # uint32 bit pattern as int32
+    return w.to(torch.int32).contiguous().view(torch.uint8).reshape(n, -1)
 
 
 def _f16_bytes(h):
-    return h.contiguous().view(torch.uint8).reshape(-1)
+    n = h.shape[0]
+    return h.contiguous().view(torch.uint8).reshape(n, -1)
 
 
 def pack_int4(Wg_q, Wg_s, Wu_q, Wu_s, Wd_q, Wd_s):
-    """Quantised int4 matrices of one expert -> record bytes (uint8)."""
-    F, H = Wg_q.shape
-    gu_q = _gu_rows(Wg_q, Wu_q)                           # [2F][H] int8
-    gu_s = _gu_rows(Wg_s, Wu_s)                           # [2F][H/32]
+    """Quantised int4 matrices of n experts ([n, ...], or one expert without
+    the leading n) -> record bytes uint8 [n, R] (resp. [R])."""
+    single = Wg_q.dim() == 2
+    if single:
+        Wg_q, Wg_s, Wu_q, Wu_s, Wd_q, Wd_s = (t.unsqueeze(0) for t in (Wg_q, Wg_s, Wu_q, Wu_s, Wd_q, Wd_s))
+    n, F, H = Wg_q.shape
+    gu_q = _gu_rows(Wg_q, Wu_q)                                    # [n][2F][H]
+    gu_s = _gu_rows(Wg_s, Wu_s)                                    # [n][2F][H/32]
     KBg, KBd = H // 32, F // 32
-    wgu = _nibble_words(gu_q.to(torch.int32) + 8)         # [2F][H/8]
-    wgu = wgu.reshape(2 * F, KBg, 4).permute(1, 0, 2)     # [kb][r][4]
-    wd = _nibble_words(Wd_q.to(torch.int32) + 8).reshape(H, KBd, 4).permute(1, 0, 2)
-    sgu = gu_s.reshape(2 * F, KBg // 4, 4).permute(1, 0, 2)  # [kb/4][r][4]
-    sd = Wd_s.reshape(H, KBd // 4, 4).permute(1, 0, 2)
-    out = torch.cat([_words_to_bytes(wgu.contiguous()), _words_to_bytes(wd.contiguous()),
-                     _f16_bytes(sgu), _f16_bytes(sd)])
-    assert out.numel() == record_bytes(QFMT_INT4, H, F)
-    return out
+    wgu = _nibble_words(gu_q.to(torch.int32) + 8).reshape(n, 2 * F, KBg, 4).permute(0, 2, 1, 3)  # [n][kb][r][4]
+    wd = _nibble_words(Wd_q.to(torch.int32) + 8).reshape(n, H, KBd, 4).permute(0, 2, 1, 3)
+    sgu = gu_s.reshape(n, 2 * F, KBg // 4, 4).permute(0, 2, 1, 3)  # [n][kb/4][r][4]
+    sd = Wd_s.reshape(n, H, KBd // 4, 4).permute(0, 2, 1, 3)
+    out = torch.cat([_words_to_bytes(wgu), _words_to_bytes(wd), _f16_bytes(sgu), _f16_bytes(sd)], dim=1)
+    assert out.shape[1] == record_bytes(QFMT_INT4, H, F)
+    return out[0] if single else out
 
 
 def pack_int2(Wg_q, Wg_s, Wg_m, Wu_q, Wu_s, Wu_m, Wd_q, Wd_s, Wd_m):
-    """Quantised int2 matrices of one expert -> record bytes (uint8)."""
-    F, H = Wg_q.shape
+    """Quantised int2 matrices of n experts -> record bytes uint8 [n, R] (or [R])."""
+    single = Wg_q.dim() == 2
+    ts = (Wg_q, Wg_s, Wg_m, Wu_q, Wu_s, Wu_m, Wd_q, Wd_s, Wd_m)
+    if single:
+        ts = tuple(t.unsqueeze(0) for t in ts)
+    Wg_q, Wg_s, Wg_m, Wu_q, Wu_s, Wu_m, Wd_q, Wd_s, Wd_m = ts
+    n, F, H = Wg_q.shape
     gu_q = _gu_rows(Wg_q, Wu_q)
     gu_s = _gu_rows(Wg_s, Wu_s)
     gu_m = _gu_rows(Wg_m, Wu_m)
     Ug, Ud = H // 64, F // 64
-    wgu = _crumb_words(gu_q.to(torch.int32)).reshape(2 * F, Ug, 4).permute(1, 0, 2)
-    wd = _crumb_words(Wd_q.to(torch.int32)).reshape(H, Ud, 4).permute(1, 0, 2)
-    mgu = torch.stack([gu_s, gu_m], dim=-1).reshape(2 * F, Ug, 4, 2).permute(1, 0, 2, 3)
-    md = torch.stack([Wd_s, Wd_m], dim=-1).reshape(H, Ud, 4, 2).permute(1, 0, 2, 3)
-    out = torch.cat([_words_to_bytes(wgu.contiguous()), _words_to_bytes(wd.contiguous()),
-                     _f16_bytes(mgu), _f16_bytes(md)])
-    assert out.numel() == record_bytes(QFMT_INT2, H, F)
-    return out
+    wgu = _crumb_words(gu_q.to(torch.int32)).reshape(n, 2 * F, Ug, 4).permute(0, 2, 1, 3)
+    wd = _crumb_words(Wd_q.to(torch.int32)).reshape(n, H, Ud, 4).permute(0, 2, 1, 3)
+    mgu = torch.stack([gu_s, gu_m], dim=-1).reshape(n, 2 * F, Ug, 4, 2).permute(0, 2, 1, 3, 4)
+    md = torch.stack([Wd_s, Wd_m], dim=-1).reshape(n, H, Ud, 4, 2).permute(0, 2, 1, 3, 4)
+    out = torch.cat([_words_to_bytes(wgu), _words_to_bytes(wd), _f16_bytes(mgu), _f16_bytes(md)], dim=1)
+    assert out.shape[1] == record_bytes(QFMT_INT2, H, F)
+    return out[0] if single else out
 
 
 def pack_record(qfmt, Wg, Wu, Wd):
-    """fp32 weights of one expert -> record bytes."""
+    """fp32 weights of one expert ([F][H], [F][H], [H][F]) or of n experts
+    (leading dim n) -> record bytes."""
     if qfmt == QFMT_INT4:
         return pack_int4(*quantize_int4(Wg), *quantize_int4(Wu), *quantize_int4(Wd))
     return pack_int2(*quantize_int2(Wg), *quantize_int2(Wu), *quantize_int2(Wd))
 
 
-def draw_expert_weights(seed, layer, n_experts, H, F, device="cpu", std=0.02):
-    """Yield (e, Wg, Wu, Wd) for experts 0..n_experts-1 of one layer (the
-    last one, index E, is the layer's shared expert when n_experts = E+1).
-    Experts are drawn EXPERT_CHUNK at a time from one generator per layer."""
+def draw_expert_chunks(seed, layer, n_experts, H, F, device="cpu", std=0.02):
+    """Yield (e0, Wg [n,F,H], Wu [n,F,H], Wd [n,H,F]) for the experts of one
+    layer, EXPERT_CHUNK at a time from one generator per layer (the last
+    expert, index E, is the layer's shared expert when n_experts = E+1)."""
     g = make_gen(device, seed, "experts", layer)
     for c0 in range(0, n_experts, EXPERT_CHUNK):
         n = min(EXPERT_CHUNK, n_experts - c0)
         Wg = normal((n, F, H), std, g, device)
         Wu = normal((n, F, H), std, g, device)
         Wd = normal((n, H, F), std, g, device)
-        for i in range(n):
+        yield c0, Wg, Wu, Wd
+
+
+def draw_expert_weights(seed, layer, n_experts, H, F, device="cpu", std=0.02):
+    """Yield (e, Wg, Wu, Wd) per expert (same draws as draw_expert_chunks)."""
+    for c0, Wg, Wu, Wd in draw_expert_chunks(seed, layer, n_experts, H, F, device, std):
+        for i in range(Wg.shape[0]):
             yield c0 + i, Wg[i], Wu[i], Wd[i]
 
 
@@ -257,11 +269,14 @@ def build_pool(seed, L, E, H, F, qfmt, device="cpu", rec_bytes=None,
     S = make_slot_table(seed, L, E) if slot_table is None else slot_table
     n_slots = int(S.max().item()) + 1
     pool = torch.zeros(n_slots * R, dtype=torch.uint8, device=device)
+    view = pool.view(n_slots, R)
+    Rq = record_bytes(qfmt, H, F)
     for l in range(L):
-        for e, Wg, Wu, Wd in draw_expert_weights(seed, l, E + 1, H, F, device, std):
-            s = int(S[l, e])
-            rec = pack_record(qfmt, Wg, Wu, Wd)
-            pool[s * R: s * R + rec.numel()] = rec
+        for c0, Wg, Wu, Wd in draw_expert_chunks(seed, l, E + 1, H, F, device, std):
+            recs = pack_record(qfmt, Wg, Wu, Wd)                      # [n][Rq]
+            slots = S[l, c0:c0 + recs.shape[0]].to(device=device, dtype=torch.long)
+            view[slots, :Rq] = recs
+            del Wg, Wu, Wd, recs
         if progress is not None:
             progress(l)
     return pool, S, R

@@ -26,7 +26,8 @@
  *            silu(z) = z / (1 + exp(-z)).
  *   layer    y[t] = sum_{j<k} w[t,j] * y_{idx[t,j]}(x_t) + y_shared(x_t)
  *            (shared expert weight 1), summed in the order j = 0..k-1, then
- *            the shared expert.  A stack of layers chains x_{l+1} = x_l + y_l.
+ *            the shared expert.  A stack of layers is a pre-norm residual
+ *            chain (see moe_decode_stack).
  *
  * ---------------------------------------------------------------------------
  * Conventions (all entry points)
@@ -162,13 +163,15 @@ size_t moe_workspace_size(int op, int T, int k, int E, int H, int F, int qfmt);
  *   topk_idx int32 [T][k] out: chosen experts, larger logit first, ties to
  *            the lower index
  *   topk_w   fp32 [T][k] out: softmax of the chosen logits
- *   logits_out fp32 [T][E] out, or NULL
+ *   logits_out fp32 [T][E] out, or NULL (the logits then go to ws)
  * Requires 1 <= k <= MOE_MAX_K, k <= E <= MOE_MAX_E, H % 128 == 0, T >= 0.
- * A NaN logit is a caller error (the choice is then unspecified). */
+ * A NaN logit is a caller error (the choice is then unspecified).
+ * ws: moe_workspace_size(MOE_OP_ROUTE_TOPK, T, k, E, H, 0, 0) bytes; may be
+ * NULL when logits_out is given. */
 int moe_route_topk(const void* x, int x_dtype, int T, int H,
                    const uint16_t* w_router, const float* bias, int E, int k,
                    int32_t* topk_idx, float* topk_w, float* logits_out,
-                   void* stream);
+                   void* ws, size_t ws_bytes, void* stream);
 
 /* --------------------------------------------------------------------------
  * moe_permute -- group the T*k (token, choice) pairs by expert; stable.
@@ -257,8 +260,8 @@ int moe_usage_update(const int32_t* topk_idx, int T, int k, int layer, int L,
 
 /* --------------------------------------------------------------------------
  * moe_decode_stack -- one decode / verify step through L chained layers
- * (1 <= T <= MOE_MAX_DECODE_T), the whole step enqueued as a single
- * persistent kernel.  Pages: "为什么 Strata 在小显存显卡上这么快", section
+ * (1 <= T <= MOE_MAX_DECODE_T), the whole step enqueued on `stream` with no
+ * host synchronisation (it may be captured into a HIP graph).  Pages: "为什么 Strata 在小显存显卡上这么快", section
  * "一个 token，三路工人" (the whole 48-layer forward is recorded once and
  * replayed so that the host never waits inside a step); section "先猜，再检查"
  * (a verify step runs 1 real + up to 3 drafted tokens through all 48 layers).
@@ -266,9 +269,15 @@ int moe_usage_update(const int32_t* topk_idx, int T, int k, int layer, int L,
  *   w_router bf16 [L][E][H];  bias fp32 [L][E] or NULL
  *   slot_table int32 [L][E+1]
  *   topk_idx_out int32 [L][T][k] or NULL; topk_w_out fp32 [L][T][k] or NULL
- *   x_hist   fp32 [L][T][H] or NULL: x_hist[l] = input of layer l
- * Per layer it computes exactly what moe_route_topk + moe_expert_gemv_q +
- * moe_combine(residual = x_l) compute.
+ *   x_hist   fp32 [L][T][H] or NULL: x_hist[l] = x_l, the residual stream
+ *            entering layer l
+ * Layers chain as a pre-norm residual stream (the pages do not describe the
+ * non-MoE parts of a layer; without a norm a chain of SwiGLU layers, which
+ * are quadratic in x, overflows within a few layers):
+ *   xn_l = x_l / sqrt(mean_h(x_l^2) + 1e-6)          (unit gain)
+ *   x_{l+1} = x_l + MoE_l(xn_l)
+ * where MoE_l(xn_l) is exactly what moe_route_topk + moe_expert_gemv_q +
+ * moe_combine compute on xn_l with layer l's router, bias and slots.
  * ws: moe_workspace_size(MOE_OP_DECODE_STACK, T, k, E, H, F, qfmt). */
 int moe_decode_stack(const float* x_in, int T, int H, int F, int E, int k,
                      int L, const uint16_t* w_router, const float* bias,

@@ -20,7 +20,8 @@ What it follows (pages about the Strata engine for Qwen3.8-Flash-Next):
     decayed usage score.
 Where the pages are silent, the readings are the ones stated in include/moe.h
 (SwiGLU experts, softmax over the chosen logits, ties to the lower index,
-shared expert with weight 1, the record byte format, x_{l+1} = x_l + y_l).
+shared expert with weight 1, the record byte format, and a stack of layers
+as a pre-norm residual chain x_{l+1} = x_l + MoE_l(x_l / rms(x_l))).
 
 Pins: every function here is checked in tests/test_oracle_pins.py against
 hand-derived values, closed forms, brute force or library routines.  No
@@ -32,7 +33,7 @@ __all__ = [
     "bf16_to_f64", "f16_to_f64", "decode_record", "expert_getter",
     "router_logits", "topk_select", "topk_gaps", "gap_ok", "silu",
     "expert_ffn", "moe_layer", "combine", "permute", "usage_update",
-    "moe_stack_decode",
+    "moe_stack_decode", "rms_normalize",
 ]
 
 QFMT_INT4 = 0
@@ -209,15 +210,22 @@ def moe_layer(x, Wr, bias, k, get_expert, E):
     return y, idx, w, y_parts, logits
 
 
-def moe_stack_decode(x, Wr_layers, bias_layers, k, getters, E):
-    """Chain layers: x_{l+1} = x_l + y_l.  getters[l] is layer l's expert
-    getter.  Returns (x_out, idx [L][T][k], w [L][T][k], x_hist [L][T][H])."""
+def rms_normalize(x, eps=1e-6):
+    """x / sqrt(mean(x^2) + eps) per token (unit gain)."""
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def moe_stack_decode(x, Wr_layers, bias_layers, k, getters, E, eps=1e-6):
+    """Chain layers with a pre-norm residual: x_{l+1} = x_l + MoE_l(rms(x_l)).
+    getters[l] is layer l's expert getter.  Returns (x_out, idx [L][T][k],
+    w [L][T][k], x_hist [L][T][H]) where x_hist[l] is x_l (before the norm)."""
     x = np.asarray(x, np.float64)
     idxs, ws, hist = [], [], []
     for l, get in enumerate(getters):
         hist.append(x.copy())
         b = None if bias_layers is None else bias_layers[l]
-        y, idx, w, _, _ = moe_layer(x, Wr_layers[l], b, k, get, E)
+        y, idx, w, _, _ = moe_layer(rms_normalize(x, eps), Wr_layers[l], b, k, get, E)
         idxs.append(idx)
         ws.append(w)
         x = x + y

@@ -1,0 +1,13 @@
+// Internal launchers shared between the entry points (not part of the ABI).
+#pragma once
+#include "moe_common.h"
+
+int moe_launch_route(const void* x, int x_dtype, int T, int H, const uint16_t* w_router, const float* bias,
+                     int E, int k, int32_t* topk_idx, float* topk_w, float* logits, hipStream_t st);
+
+int moe_launch_gemv(const float* x, int T, int H, int F, const int32_t* topk_idx, int k, int E,
+                    const int32_t* slot_table, int layer, const void* pool, int64_t record_bytes, int qfmt,
+                    float* y_parts, void* ws, hipStream_t st);
+
+int moe_launch_combine(const float* y_rows, const int32_t* inv_row, const float* y_shared, const float* topk_w,
+                       const float* residual, int T, int k, int H, float* y_out, hipStream_t st);

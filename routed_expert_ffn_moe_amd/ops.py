@@ -1,0 +1,174 @@
+"""Python binding of libmoe: one function per C entry point, same names.
+
+Only argument marshalling happens here: tensors are checked for device,
+dtype and contiguity, missing outputs and workspaces are allocated with
+torch (device memory is torch's job), and the C function is called with the
+raw device pointers and torch's current HIP stream.  Every step of the layer
+runs in the library's kernels; nothing here computes.
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (MOE_BF16, MOE_F32, MOE_OP_DECODE_STACK, MOE_OP_EXPERT_GEMV_Q, MOE_OP_GROUPED_GEMM_Q,
+                   MOE_OP_PERMUTE, MOE_OP_ROUTE_TOPK, MOE_Q2_B16, MOE_Q4_B32, MoeError, check)
+
+__all__ = [
+    "moe_abi_version", "moe_record_bytes", "moe_workspace_size", "workspace", "moe_route_topk", "moe_permute",
+    "moe_expert_gemv_q", "moe_grouped_gemm_q", "moe_combine", "moe_usage_update", "moe_decode_stack",
+    "MOE_Q4_B32", "MOE_Q2_B16", "MoeError", "MOE_OP_ROUTE_TOPK", "MOE_OP_PERMUTE", "MOE_OP_EXPERT_GEMV_Q",
+    "MOE_OP_GROUPED_GEMM_Q", "MOE_OP_DECODE_STACK",
+]
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("libmoe takes device tensors only")
+            if not t.is_contiguous():
+                raise ValueError("libmoe takes contiguous tensors only")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _x_dtype(x):
+    if x.dtype == torch.float32:
+        return MOE_F32
+    if x.dtype in (torch.bfloat16, torch.int16):  # bf16 values or their bit patterns
+        return MOE_BF16
+    raise ValueError(f"unsupported activation dtype {x.dtype}")
+
+
+def _half_bits(t):
+    if t.dtype not in (torch.bfloat16, torch.float16, torch.int16):
+        raise ValueError(f"expected 16-bit tensor, got {t.dtype}")
+    return t
+
+
+def moe_abi_version():
+    return _lib.load().moe_abi_version()
+
+
+def moe_record_bytes(qfmt, H, F):
+    return _lib.load().moe_record_bytes(qfmt, H, F)
+
+
+def moe_workspace_size(op, T=0, k=0, E=0, H=0, F=0, qfmt=0):
+    return _lib.load().moe_workspace_size(op, T, k, E, H, F, qfmt)
+
+
+def workspace(op, device, T=0, k=0, E=0, H=0, F=0, qfmt=0):
+    n = moe_workspace_size(op, T, k, E, H, F, qfmt)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def moe_route_topk(x, w_router, bias, k, topk_idx=None, topk_w=None, logits_out=None, ws=None, stream=None):
+    """x [T][H] fp32/bf16, w_router bf16 [E][H], bias fp32 [E] or None."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    _half_bits(w_router)
+    dev = x.device
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if logits_out is None and ws is None:
+        ws = workspace(MOE_OP_ROUTE_TOPK, dev, T=T, E=E)
+    _dev(x, w_router, bias, topk_idx, topk_w, logits_out, ws)
+    check(_lib.load().moe_route_topk(_p(x), _x_dtype(x), T, H, _p(w_router), _p(bias), E, k, _p(topk_idx),
+                                     _p(topk_w), _p(logits_out), _p(ws), 0 if ws is None else ws.numel(),
+                                     _stream(stream)))
+    return topk_idx, topk_w
+
+
+def moe_permute(topk_idx, E, counts=None, offsets=None, row_src=None, inv_row=None, x=None, x_perm=None, ws=None,
+                stream=None):
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    row_src = torch.empty(T * k, dtype=torch.int32, device=dev) if row_src is None else row_src
+    inv_row = torch.empty(T * k, dtype=torch.int32, device=dev) if inv_row is None else inv_row
+    if x is not None and x_perm is None:
+        x_perm = torch.empty((T * k, x.shape[1]), dtype=x.dtype, device=dev)
+    ws = workspace(MOE_OP_PERMUTE, dev, T=T, k=k, E=E) if ws is None else ws
+    _dev(topk_idx, counts, offsets, row_src, inv_row, x, x_perm, ws)
+    H = 0 if x is None else x.shape[1]
+    xd = 0 if x is None else _x_dtype(x)
+    check(_lib.load().moe_permute(_p(topk_idx), T, k, E, _p(counts), _p(offsets), _p(row_src), _p(inv_row), _p(x),
+                                  xd, H, _p(x_perm), _p(ws), ws.numel(), _stream(stream)))
+    return counts, offsets, row_src, inv_row, x_perm
+
+
+def moe_expert_gemv_q(x, topk_idx, E, F, slot_table, layer, pool, record_bytes, qfmt, y_parts=None, ws=None,
+                      stream=None):
+    """x fp32 [T][H]; returns y_parts fp32 [T][k+1][H]."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    dev = x.device
+    if y_parts is None:
+        y_parts = torch.empty((T, k + 1, H), dtype=torch.float32, device=dev)
+    ws = workspace(MOE_OP_EXPERT_GEMV_Q, dev, T, k, E, H, F, qfmt) if ws is None else ws
+    _dev(x, topk_idx, slot_table, pool, y_parts, ws)
+    check(_lib.load().moe_expert_gemv_q(_p(x), T, H, F, _p(topk_idx), k, E, _p(slot_table), layer, _p(pool),
+                                        record_bytes, qfmt, _p(y_parts), _p(ws), ws.numel(), _stream(stream)))
+    return y_parts
+
+
+def moe_grouped_gemm_q(x, row_src, offsets, k, E, F, slot_table, layer, pool, record_bytes, qfmt, y_perm=None,
+                       y_shared=None, ws=None, stream=None):
+    """x bf16 [T][H]; returns (y_perm fp32 [T*k][H], y_shared fp32 [T][H])."""
+    T, H = x.shape
+    dev = x.device
+    _half_bits(x)
+    y_perm = torch.empty((T * k, H), dtype=torch.float32, device=dev) if y_perm is None else y_perm
+    y_shared = torch.empty((T, H), dtype=torch.float32, device=dev) if y_shared is None else y_shared
+    ws = workspace(MOE_OP_GROUPED_GEMM_Q, dev, T, k, E, H, F, qfmt) if ws is None else ws
+    _dev(x, row_src, offsets, slot_table, pool, y_perm, y_shared, ws)
+    check(_lib.load().moe_grouped_gemm_q(_p(x), T, H, F, _p(row_src), _p(offsets), k, E, _p(slot_table), layer,
+                                         _p(pool), record_bytes, qfmt, _p(y_perm), _p(y_shared), _p(ws), ws.numel(),
+                                         _stream(stream)))
+    return y_perm, y_shared
+
+
+def moe_combine(y_rows, topk_w, inv_row=None, y_shared=None, residual=None, y_out=None, stream=None):
+    T, k = topk_w.shape
+    H = y_rows.shape[-1]
+    y_out = torch.empty((T, H), dtype=torch.float32, device=y_rows.device) if y_out is None else y_out
+    _dev(y_rows, topk_w, inv_row, y_shared, residual, y_out)
+    check(_lib.load().moe_combine(_p(y_rows), _p(inv_row), _p(y_shared), _p(topk_w), _p(residual), T, k, H, _p(y_out),
+                                  _stream(stream)))
+    return y_out
+
+
+def moe_usage_update(topk_idx, layer, L, E, decay, step, rerank_every, top_n, hits_ws, scores, top_out=None,
+                     stream=None):
+    T, k = topk_idx.shape
+    _dev(topk_idx, hits_ws, scores, top_out)
+    check(_lib.load().moe_usage_update(_p(topk_idx), T, k, layer, L, E, float(decay), int(step), rerank_every, top_n,
+                                       _p(hits_ws), _p(scores), _p(top_out), _stream(stream)))
+    return scores, top_out
+
+
+def moe_decode_stack(x_in, F, E, k, w_router, bias, slot_table, pool, record_bytes, qfmt, x_out=None,
+                     topk_idx_out=None, topk_w_out=None, x_hist=None, ws=None, stream=None):
+    """x_in fp32 [T][H], w_router bf16 [L][E][H]; returns x_out fp32 [T][H]."""
+    T, H = x_in.shape
+    L = w_router.shape[0]
+    dev = x_in.device
+    x_out = torch.empty_like(x_in) if x_out is None else x_out
+    ws = workspace(MOE_OP_DECODE_STACK, dev, T, k, E, H, F, qfmt) if ws is None else ws
+    _dev(x_in, w_router, bias, slot_table, pool, x_out, topk_idx_out, topk_w_out, x_hist, ws)
+    check(_lib.load().moe_decode_stack(_p(x_in), T, H, F, E, k, L, _p(w_router), _p(bias), _p(slot_table), _p(pool),
+                                       record_bytes, qfmt, _p(x_out), _p(topk_idx_out), _p(topk_w_out), _p(x_hist),
+                                       _p(ws), ws.numel(), _stream(stream)))
+    return x_out

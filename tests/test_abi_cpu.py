@@ -1,0 +1,127 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared
+entry point, answers size queries, and rejects bad arguments with the
+documented codes before launching anything (no GPU is touched).  Every call
+below carries at least one invalid argument, so validation fails before any
+HIP call; the dummy addresses are never dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from routed_expert_ffn_moe_amd import _lib
+import gen as G
+
+HEADER = os.path.join(os.path.dirname(__file__), "..", "include", "moe.h")
+FAKE = 0x10000  # non-null, 256-byte aligned dummy "device" address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(moe_\w+)\s*\(", txt, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 11, names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+
+
+def test_version_and_sizes(lib):
+    assert lib.moe_abi_version() == 1
+    assert lib.moe_record_bytes(0, 2048, 768) == G.record_bytes(0, 2048, 768) == 2_654_208
+    assert lib.moe_record_bytes(1, 2048, 768) == G.record_bytes(1, 2048, 768) == 2_359_296
+    assert lib.moe_record_bytes(0, 256, 128) == 55_296
+    assert lib.moe_record_bytes(0, 200, 128) == 0 and lib.moe_record_bytes(7, 256, 128) == 0
+    assert lib.moe_workspace_size(_lib.MOE_OP_COMBINE, 4, 2, 16, 256, 128, 0) == 0
+    assert lib.moe_workspace_size(_lib.MOE_OP_ROUTE_TOPK, 8192, 10, 512, 2048, 0, 0) >= 8192 * 512 * 4
+    assert lib.moe_workspace_size(_lib.MOE_OP_GROUPED_GEMM_Q, 8192, 10, 512, 2048, 768, 0) >= 90112 * 768 * 2
+    assert lib.moe_workspace_size(_lib.MOE_OP_EXPERT_GEMV_Q, 1, 10, 512, 2048, 768, 0) > 0
+    assert lib.moe_workspace_size(99, 1, 1, 1, 1, 1, 0) == 0
+
+
+def _err(lib):
+    return lib.moe_last_error().decode()
+
+
+def test_route_topk_rejects(lib):
+    f = lib.moe_route_topk
+    ok = dict(x=FAKE, xd=0, T=4, H=256, wr=FAKE, b=None, E=16, k=2, idx=FAKE, w=FAKE, lg=FAKE, ws=None, wsb=0, s=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["xd"], a["T"], a["H"], a["wr"], a["b"], a["E"], a["k"], a["idx"], a["w"], a["lg"],
+                 a["ws"], a["wsb"], a["s"])
+    assert call(k=17) == _lib.MOE_ESHAPE and "k=17" in _err(lib)
+    assert call(k=20, E=16) == _lib.MOE_ESHAPE
+    assert call(E=2000) == _lib.MOE_ESHAPE
+    assert call(H=200) == _lib.MOE_ESHAPE
+    assert call(xd=5) == _lib.MOE_EUNSUPPORTED
+    assert call(x=None) == _lib.MOE_EINVAL
+    assert call(x=FAKE + 4) == _lib.MOE_EALIGN
+    assert call(lg=None) == _lib.MOE_EWORKSPACE           # no logits_out and no ws
+    assert call(lg=None, ws=FAKE, wsb=16) == _lib.MOE_EWORKSPACE
+    assert call(T=0, x=None, wr=None) == _lib.MOE_OK       # nothing to do, nothing launched
+
+
+def test_expert_ops_reject(lib):
+    g = lib.moe_expert_gemv_q
+    base = [FAKE, 1, 2048, 768, FAKE, 10, 512, FAKE, 0, FAKE, 2_654_208, 0, FAKE, FAKE, 1 << 20, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return g(*a)
+    assert call(1, 9) == _lib.MOE_ESHAPE             # T > 8
+    assert call(1, 0) == _lib.MOE_ESHAPE
+    assert call(11, 3) == _lib.MOE_EUNSUPPORTED      # qfmt
+    assert call(9, FAKE + 64) == _lib.MOE_EALIGN     # pool alignment
+    assert call(10, 2_654_208 - 256) == _lib.MOE_EALIGN  # record too small
+    assert call(10, 2_654_208 + 1) == _lib.MOE_EALIGN
+    assert call(13, None) == _lib.MOE_EWORKSPACE
+    assert call(14, 100) == _lib.MOE_EWORKSPACE
+    assert call(7, None) == _lib.MOE_EINVAL          # slot table
+    assert call(3, 700) == _lib.MOE_ESHAPE           # F % 128
+    assert call(5, 17) == _lib.MOE_ESHAPE            # k > 16
+    h = lib.moe_grouped_gemm_q
+    gb = [FAKE, 8192, 2048, 768, FAKE, FAKE, 10, 512, FAKE, 0, FAKE, 2_654_208, 0, FAKE, FAKE, FAKE, 0, None]
+    assert h(*gb) == _lib.MOE_EWORKSPACE
+    gb2 = list(gb); gb2[0] = FAKE + 2
+    gb2[16] = 1 << 40
+    assert h(*gb2) == _lib.MOE_EALIGN
+    gb3 = list(gb); gb3[7] = 4096
+    assert h(*gb3) == _lib.MOE_ESHAPE
+
+
+def test_permute_combine_usage_reject(lib):
+    assert lib.moe_permute(FAKE, 10, 2, 0, FAKE, FAKE, FAKE, FAKE, None, 0, 0, None, FAKE, 1 << 20, None) == _lib.MOE_ESHAPE
+    assert lib.moe_permute(FAKE, 10, 2, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 256, None, FAKE, 1 << 20, None) == _lib.MOE_EINVAL
+    assert lib.moe_permute(FAKE, 1000, 10, 512, FAKE, FAKE, FAKE, FAKE, None, 0, 0, None, FAKE, 8, None) == _lib.MOE_EWORKSPACE
+    assert lib.moe_combine(FAKE, FAKE, None, FAKE, None, 4, 2, 256, FAKE, None) == _lib.MOE_EINVAL
+    assert lib.moe_combine(FAKE, None, None, FAKE, None, 4, 2, 254, FAKE, None) == _lib.MOE_ESHAPE
+    assert lib.moe_combine(FAKE + 4, None, None, FAKE, None, 4, 2, 256, FAKE, None) == _lib.MOE_EALIGN
+    u = lib.moe_usage_update
+    assert u(FAKE, 1, 10, 48, 48, 512, ctypes.c_float(0.99), 0, 4, 96, FAKE, FAKE, FAKE, None) == _lib.MOE_EINVAL
+    assert u(FAKE, 1, 10, 0, 200, 512, ctypes.c_float(0.99), 0, 4, 96, FAKE, FAKE, FAKE, None) == _lib.MOE_ESHAPE
+    assert u(FAKE, 1, 10, 0, 48, 512, ctypes.c_float(0.99), 0, 4, 2000, FAKE, FAKE, FAKE, None) == _lib.MOE_ESHAPE
+    assert u(FAKE, 1, 10, 0, 48, 512, ctypes.c_float(float("nan")), 0, 4, 96, FAKE, FAKE, FAKE, None) == _lib.MOE_EINVAL
+    assert u(FAKE, 1, 10, 0, 48, 512, ctypes.c_float(0.99), 0, 0, 96, FAKE, FAKE, FAKE, None) == _lib.MOE_EINVAL
+
+
+def test_decode_stack_rejects(lib):
+    f = lib.moe_decode_stack
+    a = [FAKE, 1, 2048, 768, 512, 10, 48, FAKE, None, FAKE, FAKE, 2_654_208, 0, FAKE + 256, None, None, None, FAKE,
+         1024, None]
+    b = list(a); b[13] = FAKE
+    assert f(*b) == _lib.MOE_EINVAL                   # x_out aliases x_in
+    b = list(a); b[6] = 0
+    assert f(*b) == _lib.MOE_ESHAPE
+    assert f(*a) == _lib.MOE_EWORKSPACE               # 1 KiB is too small

@@ -1,0 +1,337 @@
+"""GPU parity of every entry point against the CPU oracle, through the C ABI.
+
+Bars: routing indices, counts, offsets, permutation rows and usage scores /
+re-rank bit-exact; routing weights |dw| <= 2e-5 (fp32 dot-product rounding
+of the logits); MoE outputs rel-L2 <= 2e-3 and max-abs <=
+1e-2 * max|y|.  Inputs are seeded (gen/); sizes span several tiles, ragged
+tails and empty expert groups, plus the full-size shapes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen as G
+import oracle as O
+from tests import cases as C
+
+pytestmark = pytest.mark.gpu
+
+W_ATOL = 2e-5
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import routed_expert_ffn_moe_amd as M
+    M.load(build_if_missing=False)
+    return M
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _check_routing(idx_gpu, w_gpu, idx_ref, w_ref):
+    assert np.array_equal(_np(idx_gpu).astype(np.int64), idx_ref)
+    assert np.max(np.abs(_np(w_gpu) - w_ref)) <= W_ATOL
+    assert np.max(np.abs(_np(w_gpu).sum(1) - 1.0)) <= 1e-6
+
+
+# ---------------------------------------------------------------- router / top-k
+
+@pytest.mark.parametrize("T,E,k,bias,bf16", [(4, 16, 2, False, False), (4, 16, 2, True, True),
+                                            (67, 16, 2, False, False), (200, 37, 5, True, True),
+                                            (3, 1000, 16, False, False), (5, 16, 16, False, False)])
+def test_route_topk_small(moe, T, E, k, bias, bf16):
+    H = 256
+    Wr = G.draw_router(0, 0, E, H)
+    b = G.zipf_bias(0, 0, E) if bias else None
+    x, _ = G.draw_x_rejecting(0, T, H, C.gap_acceptor(Wr, b, k, as_bf16=bf16))
+    if bf16:
+        x = x.to(torch.bfloat16)
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    idx, w = moe.moe_route_topk(x.cuda(), Wr.cuda(), None if b is None else b.cuda(), k, logits_out=logits)
+    ref_l = O.router_logits(C.x_as_f64(x), C.router_f64(Wr), None if b is None else b.double().numpy())
+    ref_i, ref_w = O.topk_select(ref_l, k)
+    _check_routing(idx, w, ref_i, ref_w)
+    assert np.max(np.abs(_np(logits) - ref_l)) <= 1e-4
+
+
+def test_route_topk_ties_and_zero_router(moe):
+    H, E, k, T = 128, 64, 6, 5
+    Wr = torch.zeros((E, H), dtype=torch.bfloat16)
+    idx, w = moe.moe_route_topk(torch.ones((T, H), device="cuda"), Wr.cuda(), None, k)
+    assert _np(idx).tolist() == [list(range(k))] * T
+    assert np.all(_np(w) == np.float32(1.0 / k))
+    # duplicated rows: equal logits, lower index first
+    Wr = G.draw_router(9, 0, E, H)
+    Wr[40] = Wr[7]
+    Wr[50] = Wr[7]
+    x = Wr[7].view(torch.bfloat16).float().unsqueeze(0).repeat(T, 1) * 3.0  # row 7 wins
+    idx, w = moe.moe_route_topk(x.cuda(), Wr.cuda(), None, k)
+    assert np.all(_np(idx)[:, :3] == [7, 40, 50])
+    assert np.all(_np(w)[:, 0] == _np(w)[:, 1])
+
+
+@pytest.mark.parametrize("T", [1, 4, 8])
+def test_route_topk_full_decode(moe, T):
+    li_Wr = G.draw_router(1, 0, 512, 2048)
+    b = G.zipf_bias(1, 0, 512)
+    x, _ = G.draw_x_rejecting(1, T, 2048, C.gap_acceptor(li_Wr, b, 10))
+    idx, w = moe.moe_route_topk(x.cuda(), li_Wr.cuda(), b.cuda(), 10)
+    ref_i, ref_w = O.topk_select(O.router_logits(C.x_as_f64(x), C.router_f64(li_Wr), b.double().numpy()), 10)
+    _check_routing(idx, w, ref_i, ref_w)
+
+
+def test_route_topk_full_prefill(moe):
+    """8,192 bf16 tokens, 512 experts, top-10, no bias (near-uniform routing)."""
+    T, H, E, k = 8192, 2048, 512, 10
+    Wr = G.draw_router(3, 0, E, H)
+    x, att = G.draw_x_rejecting(3, T, H, C.gap_acceptor(Wr, None, k, as_bf16=True))
+    x = x.to(torch.bfloat16)
+    idx, w = moe.moe_route_topk(x.cuda(), Wr.cuda(), None, k)
+    ref_i, ref_w = O.topk_select(O.router_logits(C.x_as_f64(x), C.router_f64(Wr)), k)
+    _check_routing(idx, w, ref_i, ref_w)
+    counts = np.bincount(ref_i.ravel(), minlength=E)
+    assert counts.min() > 0  # a chunk routes to every expert
+
+
+# ---------------------------------------------------------------- permutation
+
+def _random_idx(rng, T, k, E, skew=0.0):
+    p = np.arange(1, E + 1, dtype=np.float64) ** (-skew)
+    p /= p.sum()
+    return np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("T,k,E,skew", [(1, 1, 1, 0), (7, 2, 5, 0), (300, 4, 16, 1.5), (1025, 3, 9, 0),
+                                        (8192, 10, 512, 0), (16384, 10, 512, 1.1), (50, 16, 1000, 0)])
+def test_permute(moe, T, k, E, skew):
+    rng = np.random.default_rng(T * 31 + k)
+    idx = _random_idx(rng, T, k, E, skew)
+    x = torch.randn((T, 64), generator=torch.Generator().manual_seed(T)).to(torch.bfloat16)
+    counts, offsets, row_src, inv_row, xp = moe.moe_permute(torch.from_numpy(idx).cuda(), E, x=x.cuda())
+    rc, ro, rs, ri = O.permute(idx, E)
+    assert np.array_equal(_np(counts), rc)
+    assert np.array_equal(_np(offsets), ro)
+    assert np.array_equal(_np(row_src), rs)
+    assert np.array_equal(_np(inv_row), ri)
+    assert torch.equal(xp.cpu(), x[torch.from_numpy(rs) // k])
+
+
+def test_permute_empty(moe):
+    idx = torch.zeros((0, 3), dtype=torch.int32, device="cuda")
+    counts, offsets, *_ = moe.moe_permute(idx, 7)
+    assert _np(counts).tolist() == [0] * 7 and _np(offsets).tolist() == [0] * 8
+
+
+# ---------------------------------------------------------------- decode experts
+
+def _layer_outputs_decode(moe, li, x, layer=0):
+    idx, w = moe.moe_route_topk(x.cuda(), li.Wr[layer].cuda().contiguous(),
+                                None if li.bias is None else li.bias[layer].cuda().contiguous(), li.k)
+    yp = moe.moe_expert_gemv_q(x.cuda(), idx, li.E, li.F, li.S.cuda(), layer, li.pool.cuda(), li.R, li.qfmt)
+    y = moe.moe_combine(yp, w)
+    return idx, w, yp, y
+
+
+@pytest.mark.parametrize("qfmt", [0, 1])
+@pytest.mark.parametrize("T", [1, 4])
+def test_gemv_tiny(moe, qfmt, T):
+    li = C.layer_case(0, T, 256, 16, 2, 128, qfmt=qfmt)
+    idx, w, yp, y = _layer_outputs_decode(moe, li, li.x)
+    ry, ri, rw, rparts, _ = C.oracle_layer(li)
+    _check_routing(idx, w, ri, rw)
+    C.assert_close_moe(_np(yp), rparts, "y_parts")
+    C.assert_close_moe(_np(y), ry, "y")
+
+
+@pytest.mark.parametrize("qfmt", [0, 1])
+@pytest.mark.parametrize("T", [1, 4])
+def test_gemv_full_layer(moe, qfmt, T):
+    """One 512-expert top-10 layer at H=2048, F=768 with the Zipf bias."""
+    li = C.layer_case(1, T, 2048, 512, 10, 768, qfmt=qfmt, bias=True, device="cuda")
+    idx, w, yp, y = _layer_outputs_decode(moe, li, li.x)
+    ry, ri, rw, rparts, _ = C.oracle_layer(li)
+    _check_routing(idx, w, ri, rw)
+    C.assert_close_moe(_np(yp), rparts, "y_parts")
+    C.assert_close_moe(_np(y), ry, "y")
+
+
+def test_gemv_batch_invariance_and_determinism(moe):
+    li = C.layer_case(1, 4, 2048, 512, 10, 768, bias=True, device="cuda")
+    _, _, yp4, y4 = _layer_outputs_decode(moe, li, li.x)
+    _, _, yp4b, y4b = _layer_outputs_decode(moe, li, li.x)
+    assert torch.equal(y4, y4b)  # bit-identical rerun
+    for t in range(4):
+        idx1, _, yp1, y1 = _layer_outputs_decode(moe, li, li.x[t:t + 1])
+        assert torch.equal(yp1[0], yp4[t])  # a token's result does not depend on its batch
+        assert torch.equal(y1[0], y4[t])
+
+
+def test_gemv_slot_permutation_invariance(moe):
+    li = C.layer_case(0, 4, 256, 16, 2, 128)
+    _, _, _, y = _layer_outputs_decode(moe, li, li.x)
+    # move every record to another slot and permute the slot table alike
+    n = li.S.numel()
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(5))
+    pool2 = torch.zeros_like(li.pool)
+    S2 = torch.empty_like(li.S)
+    for l in range(li.S.shape[0]):
+        for e in range(li.S.shape[1]):
+            s_old, s_new = int(li.S[l, e]), int(perm[int(li.S[l, e])])
+            pool2[s_new * li.R:(s_new + 1) * li.R] = li.pool[s_old * li.R:(s_old + 1) * li.R]
+            S2[l, e] = s_new
+    li2 = C.layer_case(0, 4, 256, 16, 2, 128)
+    li2.pool, li2.S = pool2, S2
+    _, _, _, y2 = _layer_outputs_decode(moe, li2, li.x)
+    assert torch.equal(y, y2)
+
+
+# ---------------------------------------------------------------- prefill experts
+
+def _prefill_layer(moe, li, x_bf16):
+    idx, w = moe.moe_route_topk(x_bf16.cuda(), li.Wr[0].cuda().contiguous(),
+                                None if li.bias is None else li.bias[0].cuda().contiguous(), li.k)
+    counts, offsets, row_src, inv_row, _ = moe.moe_permute(idx, li.E)
+    y_perm, y_sh = moe.moe_grouped_gemm_q(x_bf16.cuda(), row_src, offsets, li.k, li.E, li.F, li.S.cuda(), 0,
+                                          li.pool.cuda(), li.R, li.qfmt)
+    y = moe.moe_combine(y_perm, w, inv_row=inv_row, y_shared=y_sh)
+    return idx, w, counts, inv_row, y_perm, y_sh, y
+
+
+@pytest.mark.parametrize("qfmt", [0, 1])
+@pytest.mark.parametrize("T,E,k,bias", [(4, 16, 2, False), (300, 16, 2, True), (2000, 16, 2, False),
+                                        (333, 40, 6, True)])
+def test_grouped_gemm_small(moe, qfmt, T, E, k, bias):
+    li = C.layer_case(2, T, 256, E, k, 128, qfmt=qfmt, bias=bias, x_bf16=True)
+    idx, w, counts, inv_row, y_perm, y_sh, y = _prefill_layer(moe, li, li.x)
+    ry, ri, rw, rparts, _ = C.oracle_layer(li)
+    _check_routing(idx, w, ri, rw)
+    rows = _np(y_perm)[_np(inv_row).reshape(T, k)]
+    C.assert_close_moe(rows, rparts[:, :k], "routed rows")
+    C.assert_close_moe(_np(y_sh), rparts[:, k], "shared")
+    C.assert_close_moe(_np(y), ry, "y")
+
+
+def test_grouped_gemm_empty_groups(moe):
+    """Experts 3, 7 and 11 get no rows; expert 0 gets more than two tiles."""
+    T, H, E, k, F = 300, 256, 16, 2, 128
+    li = C.layer_case(4, T, H, E, k, F, x_bf16=True, gap=False)
+    rng = np.random.default_rng(4)
+    pool_e = [e for e in range(1, E) if e not in (3, 7, 11)]
+    idx = np.stack([[0, rng.choice(pool_e)] for _ in range(T)]).astype(np.int32)
+    counts, offsets, row_src, inv_row, _ = moe.moe_permute(torch.from_numpy(idx).cuda(), E)
+    assert _np(counts)[[3, 7, 11]].tolist() == [0, 0, 0]
+    y_perm, y_sh = moe.moe_grouped_gemm_q(li.x.cuda(), row_src, offsets, k, E, F, li.S.cuda(), 0, li.pool.cuda(),
+                                          li.R, li.qfmt)
+    get = O.expert_getter(C.LazyPool(li.pool), li.S.numpy(), 0, li.qfmt, H, F, li.R)
+    xf = C.x_as_f64(li.x)
+    for e in (0, 1, 15):
+        sel = np.nonzero(idx == e)
+        ref = O.expert_ffn(*get(e), xf[sel[0]])
+        got = _np(y_perm)[_np(inv_row).reshape(T, k)[sel]]
+        C.assert_close_moe(got, ref, f"expert {e}")
+    C.assert_close_moe(_np(y_sh), O.expert_ffn(*get(E), xf), "shared")
+
+
+def test_grouped_gemm_full_size_sampled(moe):
+    """8,192-token chunk, 512 experts top-10, H=2048, F=768: routing and
+    permutation exact on every token, outputs checked on sampled tokens."""
+    T, H, E, k, F = 8192, 2048, 512, 10, 768
+    li = C.layer_case(3, T, H, E, k, F, x_bf16=True, device="cuda")
+    idx, w, counts, inv_row, y_perm, y_sh, y = _prefill_layer(moe, li, li.x)
+    xf = C.x_as_f64(li.x)
+    ref_i, ref_w = O.topk_select(O.router_logits(xf, C.router_f64(li.Wr[0])), k)
+    _check_routing(idx, w, ref_i, ref_w)
+    rc, ro, rs, ri = O.permute(ref_i, E)
+    assert np.array_equal(_np(counts), rc) and np.array_equal(_np(inv_row), ri)
+    sample = np.random.default_rng(0).choice(T, size=12, replace=False)
+    sample = np.concatenate([[0, T - 1], sample])
+    ry, ri2, rw2, rparts, _ = C.oracle_layer(li, tokens=sample)
+    C.assert_close_moe(_np(y)[sample], ry, "y (sampled)")
+    rows = _np(y_perm)[_np(inv_row).reshape(T, k)[sample]]
+    C.assert_close_moe(rows, rparts[:, :k], "routed rows (sampled)")
+
+
+# ---------------------------------------------------------------- usage
+
+def test_usage_update_steps(moe):
+    L, E, k, T = 4, 64, 6, 5
+    rng = np.random.default_rng(1)
+    scores = torch.zeros((L, E), dtype=torch.float32, device="cuda")
+    ref = np.zeros((L, E), np.float32)
+    hits = torch.empty(E, dtype=torch.int32, device="cuda")
+    top = torch.empty(40, dtype=torch.int32, device="cuda")
+    for step in range(9):
+        for layer in range(L):
+            idx = _random_idx(rng, T, k, E, skew=1.2)
+            top.fill_(-1)
+            moe.moe_usage_update(torch.from_numpy(idx).cuda(), layer, L, E, 0.99, step, 4, 40, hits, scores, top)
+            ref, rtop = O.usage_update(ref, idx, layer, 0.99, step, 4, 40)
+            assert np.array_equal(_np(scores), ref)  # bit-exact fp32
+            if rtop is not None:
+                assert np.array_equal(_np(top), rtop)
+            else:
+                assert np.all(_np(top) == -1)
+
+
+def test_usage_rerank_full_size(moe):
+    L, E = 48, 512
+    rng = np.random.default_rng(7)
+    s = (rng.integers(0, 50, size=(L, E)) * 0.25).astype(np.float32)  # many ties
+    scores = torch.from_numpy(s).cuda()
+    hits = torch.empty(E, dtype=torch.int32, device="cuda")
+    top = torch.empty(96, dtype=torch.int32, device="cuda")
+    idx = _random_idx(rng, 16384, 10, E, skew=1.1)
+    moe.moe_usage_update(torch.from_numpy(idx).cuda(), L - 1, L, E, 0.99, 3, 4, 96, hits, scores, top)
+    ref, rtop = O.usage_update(s, idx, L - 1, 0.99, 3, 4, 96)
+    assert np.array_equal(_np(scores), ref)
+    assert np.array_equal(_np(top), rtop)
+
+
+# ---------------------------------------------------------------- stacked decode
+
+@pytest.mark.parametrize("qfmt", [0, 1])
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_stack_tiny(moe, qfmt, T):
+    L = 6
+    li = C.layer_case(5, T, 256, 16, 2, 128, qfmt=qfmt, bias=True, L=L, gap=False)
+    x = li.x.cuda()
+    idx_o = torch.empty((L, T, 2), dtype=torch.int32, device="cuda")
+    w_o = torch.empty((L, T, 2), dtype=torch.float32, device="cuda")
+    hist = torch.empty((L, T, 256), dtype=torch.float32, device="cuda")
+    xo = moe.moe_decode_stack(x, li.F, li.E, li.k, li.Wr.cuda(), li.bias.cuda(), li.S.cuda(), li.pool.cuda(), li.R,
+                              qfmt, topk_idx_out=idx_o, topk_w_out=w_o, x_hist=hist)
+    assert torch.equal(hist[0], x)
+    for l in range(L):
+        xl = torch.from_numpy(O.rms_normalize(C.x_as_f64(hist[l])))
+        ry, ri, rw, _, rl = C.oracle_layer(li, layer=l, x=xl)
+        ok = O.gap_ok(rl, li.k, C.MIN_GAP)
+        assert np.array_equal(_np(idx_o[l])[ok], ri[ok])
+        nxt = hist[l + 1] if l + 1 < L else xo
+        if ok.all():
+            C.assert_close_moe(_np(nxt - hist[l]), ry, f"layer {l}")
+
+
+# ---------------------------------------------------------------- generator
+
+@pytest.mark.parametrize("qfmt", [0, 1])
+def test_packer_on_gpu_is_a_valid_encoding(moe, qfmt):
+    """The large pools are packed on the GPU.  Its bytes decode (oracle decoder)
+    to within the quantisation step of the drawn weights and match the CPU
+    packing except where a value sits on a rounding boundary (the two
+    devices' fp32 division may round such w/s differently)."""
+    g = G.make_gen("cpu", 77, qfmt)
+    Wg, Wu, Wd = (G.normal((3,) + s, 0.02, g, "cpu") for s in [(128, 256), (128, 256), (256, 128)])
+    a = G.pack_record(qfmt, Wg, Wu, Wd)
+    b = G.pack_record(qfmt, Wg.cuda(), Wu.cuda(), Wd.cuda()).cpu()
+    for e in range(3):
+        da = O.decode_record(a[e].numpy(), qfmt, 256, 128)
+        db = O.decode_record(b[e].numpy(), qfmt, 256, 128)
+        for W, A, B in zip((Wg[e], Wu[e], Wd[e]), da, db):
+            W = W.double().numpy()
+            step = np.abs(A - W).max() * 2 + 1e-12
+            assert np.abs(B - W).max() <= step * 1.01
+            assert np.mean(A != B) < 1e-3

@@ -297,6 +297,19 @@ def test_usage_topn_brute_force():
 
 # ---------------------------------------------------------------- stack
 
+def test_rms_normalize_closed_forms():
+    x = np.array([[3.0, 4.0], [1e-3, -1e-3]])
+    # mean square of (3, 4) is 12.5
+    np.testing.assert_allclose(O.rms_normalize(x, 0.0)[0], [3 / np.sqrt(12.5), 4 / np.sqrt(12.5)], rtol=1e-15)
+    rng = np.random.default_rng(0)
+    z = rng.normal(size=(5, 64)) * 7.0
+    n = O.rms_normalize(z, 0.0)
+    np.testing.assert_allclose(np.mean(n * n, axis=1), 1.0, rtol=1e-13)
+    np.testing.assert_allclose(O.rms_normalize(3.5 * z, 0.0), n, rtol=1e-13)  # scale invariance
+    # eps only matters for tiny vectors: mean square 1e-6, eps 1e-6 halves it
+    np.testing.assert_allclose(O.rms_normalize(x[1:], 1e-6), x[1:] / np.sqrt(2e-6), rtol=1e-12)
+
+
 def test_stack_chaining_and_identity():
     rng = np.random.default_rng(4)
     T, H, E, L, k = 2, 6, 5, 3, 2
@@ -306,7 +319,8 @@ def test_stack_chaining_and_identity():
     xo, idx, w, hist = O.moe_stack_decode(x, Wr, None, k, getters, E)
     assert np.array_equal(hist[0], x)
     for l in range(L):
-        y, i2, w2, _, _ = O.moe_layer(hist[l], Wr[l], None, k, getters[l], E)
+        xn = hist[l] / np.sqrt(np.mean(hist[l] ** 2, axis=1, keepdims=True) + 1e-6)
+        y, i2, w2, _, _ = O.moe_layer(xn, Wr[l], None, k, getters[l], E)
         nxt = hist[l + 1] if l + 1 < L else xo
         np.testing.assert_array_equal(nxt, hist[l] + y)
         assert np.array_equal(i2, idx[l])
