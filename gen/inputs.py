@@ -199,7 +199,7 @@ def pack_int4(Wg_q, Wg_s, Wu_q, Wu_s, Wd_q, Wd_s):
     wgu = _nibble_words(gu_q.to(torch.int32) + 8).reshape(n, 2 * F, KBg, 4).permute(0, 2, 1, 3)  # [n][kb][r][4]
     wd = _nibble_words(Wd_q.to(torch.int32) + 8).reshape(n, H, KBd, 4).permute(0, 2, 1, 3)
     sgu = gu_s.reshape(n, 2 * F, KBg // 4, 4).permute(0, 2, 1, 3)  # [n][kb/4][r][4]
-    sd = Wd_s.reshape(n, H, KBd // 4, 4).permute(0, 2, 1, 3)
+    sd = Wd_s.permute(0, 2, 1)                                     # [n][kb][r]
     out = torch.cat([_words_to_bytes(wgu), _words_to_bytes(wd), _f16_bytes(sgu), _f16_bytes(sd)], dim=1)
     assert out.shape[1] == record_bytes(QFMT_INT4, H, F)
     return out[0] if single else out
@@ -216,11 +216,11 @@ def pack_int2(Wg_q, Wg_s, Wg_m, Wu_q, Wu_s, Wu_m, Wd_q, Wd_s, Wd_m):
     gu_q = _gu_rows(Wg_q, Wu_q)
     gu_s = _gu_rows(Wg_s, Wu_s)
     gu_m = _gu_rows(Wg_m, Wu_m)
-    Ug, Ud = H // 64, F // 64
+    Ug = H // 64
     wgu = _crumb_words(gu_q.to(torch.int32)).reshape(n, 2 * F, Ug, 4).permute(0, 2, 1, 3)
-    wd = _crumb_words(Wd_q.to(torch.int32)).reshape(n, H, Ud, 4).permute(0, 2, 1, 3)
+    wd = _crumb_words(Wd_q.to(torch.int32)).permute(0, 2, 1)        # [n][blk][r]
     mgu = torch.stack([gu_s, gu_m], dim=-1).reshape(n, 2 * F, Ug, 4, 2).permute(0, 2, 1, 3, 4)
-    md = torch.stack([Wd_s, Wd_m], dim=-1).reshape(n, H, Ud, 4, 2).permute(0, 2, 1, 3, 4)
+    md = torch.stack([Wd_s, Wd_m], dim=-1).permute(0, 2, 1, 3)      # [n][blk][r][2]
     out = torch.cat([_words_to_bytes(wgu), _words_to_bytes(wd), _f16_bytes(mgu), _f16_bytes(md)], dim=1)
     assert out.shape[1] == record_bytes(QFMT_INT2, H, F)
     return out[0] if single else out

@@ -68,7 +68,7 @@
  *       GU_Q  at 0           : block (kb, r), kb < H/32, r < 2F, at 16*(kb*2F + r)
  *       D_Q   at H*F         : block (kb, r), kb < F/32, r < H,  at 16*(kb*H + r)
  *       GU_S  at 3HF/2       : scale (kb, r) at 2*((kb/4)*2F*4 + 4r + kb%4)
- *       D_S   at 3HF/2+HF/8  : scale (kb, r) at 2*((kb/4)*H*4 + 4r + kb%4)
+ *       D_S   at 3HF/2+HF/8  : scale (kb, r) at 2*(kb*H + r)
  *     Record size 27HF/16 bytes (2,654,208 B at H=2048, F=768).
  *
  *   MOE_Q2_B16 (qfmt 1): blocks of 16 values, each with an fp16 scale s and an
@@ -77,11 +77,11 @@
  *     [2i, 2i+2) and value 2i+1 in bits [16+2i, 16+2i+2), i = 0..7.
  *     A 16-byte q-unit holds 4 consecutive blocks (word j = block 4u+j).
  *     A 16-byte meta-unit holds (s, m) of 4 consecutive blocks: block 4u+j's
- *     s at byte 4j and m at byte 4j+2.
+ *     s at byte 4j and m at byte 4j+2.  The down planes are not grouped.
  *       GU_Q  at 0           : q-unit (u, r), u < H/64, at 16*(u*2F + r)
- *       D_Q   at HF/2        : q-unit (u, r), u < F/64, at 16*(u*H + r)
+ *       D_Q   at HF/2        : word of block (b, r), b < F/16, r < H, at 4*(b*H + r)
  *       GU_M  at 3HF/4       : meta-unit (u, r), u < H/64, at 16*(u*2F + r)
- *       D_M   at 5HF/4       : meta-unit (u, r), u < F/64, at 16*(u*H + r)
+ *       D_M   at 5HF/4       : (s, m) of block (b, r) at 4*(b*H + r), m at +2
  *     Record size 3HF/2 bytes (2,359,296 B at H=2048, F=768).
  *
  *   Pool and slot table.  All records live in one caller-owned pool; the
@@ -278,6 +278,15 @@ int moe_usage_update(const int32_t* topk_idx, int T, int k, int layer, int L,
  *   x_{l+1} = x_l + MoE_l(xn_l)
  * where MoE_l(xn_l) is exactly what moe_route_topk + moe_expert_gemv_q +
  * moe_combine compute on xn_l with layer l's router, bias and slots.
+ * Execution: for 1 <= T <= 4 (and shapes whose working set fits in LDS) the
+ * step runs as ONE persistent kernel whose workgroups pass data through
+ * tagged words in ws (no host synchronisation, no grid barrier); otherwise,
+ * or when the environment variable MOE_DECODE_PATH=chain is set, as a chain
+ * of kernels per layer.  The persistent path keeps a call counter and tagged
+ * buffers in ws across calls: pass the same ws to every call of a stack and
+ * do not use it for anything else in between (calls on one ws must not
+ * overlap).  Its waits are bounded; if one times out (e.g. the GPU could not
+ * keep all its workgroups resident) x_out is filled with NaN.
  * ws: moe_workspace_size(MOE_OP_DECODE_STACK, T, k, E, H, F, qfmt). */
 int moe_decode_stack(const float* x_in, int T, int H, int F, int E, int k,
                      int L, const uint16_t* w_router, const float* bias,

@@ -65,8 +65,9 @@ def _halves(rec, start, nbytes):
     return np.frombuffer(np.ascontiguousarray(rec[start:start + nbytes]).tobytes(), dtype="<u2")
 
 
-def _int4_matrix(rec, q_off, s_off, rows, K):
-    """Decode one int4 plane pair into a dense fp64 [rows][K] matrix."""
+def _int4_matrix(rec, q_off, s_off, rows, K, grouped_scales):
+    """Decode one int4 plane pair into a dense fp64 [rows][K] matrix.  Scales
+    are stored [kb/4][row][4] (grouped) or [kb][row]."""
     KB = K // 32
     w = _words(rec, q_off, rows * K // 2).reshape(KB, rows, 4)   # [kb][row][word j]
     vals = np.empty((KB, rows, 4, 8), dtype=np.int64)            # value 8j+v
@@ -74,22 +75,37 @@ def _int4_matrix(rec, q_off, s_off, rows, K):
         vals[..., 2 * i] = (w >> (4 * i)) & 0xF
         vals[..., 2 * i + 1] = (w >> (16 + 4 * i)) & 0xF
     q = vals.reshape(KB, rows, 32).transpose(1, 0, 2) - 8          # [row][kb][32]
-    s = f16_to_f64(_halves(rec, s_off, rows * KB * 2).reshape(KB // 4, rows, 4))
-    s = s.transpose(1, 0, 2).reshape(rows, KB)                     # [row][kb]
+    if grouped_scales:
+        s = f16_to_f64(_halves(rec, s_off, rows * KB * 2).reshape(KB // 4, rows, 4))
+        s = s.transpose(1, 0, 2).reshape(rows, KB)                 # [row][kb]
+    else:
+        s = f16_to_f64(_halves(rec, s_off, rows * KB * 2).reshape(KB, rows)).T
     return (q * s[:, :, None]).reshape(rows, K)
 
 
-def _int2_matrix(rec, q_off, m_off, rows, K):
-    """Decode one int2 plane pair into a dense fp64 [rows][K] matrix."""
-    U = K // 64
-    w = _words(rec, q_off, rows * K // 4).reshape(U, rows, 4)     # word j = block 4u+j
-    vals = np.empty((U, rows, 4, 16), dtype=np.int64)
+def _int2_block_values(w):
+    """words [...] of one int2 block each -> values [..., 16]."""
+    vals = np.empty(w.shape + (16,), dtype=np.int64)
     for i in range(8):
         vals[..., 2 * i] = (w >> (2 * i)) & 0x3
         vals[..., 2 * i + 1] = (w >> (16 + 2 * i)) & 0x3
-    q = vals.transpose(1, 0, 2, 3).reshape(rows, K // 16, 16)     # [row][block][16]
-    meta = f16_to_f64(_halves(rec, m_off, rows * (K // 16) * 4).reshape(U, rows, 4, 2))
-    meta = meta.transpose(1, 0, 2, 3).reshape(rows, K // 16, 2)
+    return vals
+
+
+def _int2_matrix(rec, q_off, m_off, rows, K, grouped):
+    """Decode one int2 plane pair into a dense fp64 [rows][K] matrix.  Words
+    and (s, m) pairs are stored in 4-block units [K/64][row][4] (grouped) or
+    per block [K/16][row]."""
+    NB = K // 16
+    if grouped:
+        w = _words(rec, q_off, rows * K // 4).reshape(NB // 4, rows, 4)   # word j = block 4u+j
+        q = _int2_block_values(w).transpose(1, 0, 2, 3).reshape(rows, NB, 16)
+        meta = f16_to_f64(_halves(rec, m_off, rows * NB * 4).reshape(NB // 4, rows, 4, 2))
+        meta = meta.transpose(1, 0, 2, 3).reshape(rows, NB, 2)
+    else:
+        w = _words(rec, q_off, rows * K // 4).reshape(NB, rows)
+        q = _int2_block_values(w).transpose(1, 0, 2)                      # [row][block][16]
+        meta = f16_to_f64(_halves(rec, m_off, rows * NB * 4).reshape(NB, rows, 2)).transpose(1, 0, 2)
     s, m = meta[..., 0], meta[..., 1]
     return (q * s[:, :, None] + m[:, :, None]).reshape(rows, K)
 
@@ -99,11 +115,11 @@ def decode_record(rec, qfmt, H, F):
     rec = np.asarray(rec, dtype=np.uint8)
     HF = H * F
     if qfmt == QFMT_INT4:
-        gu = _int4_matrix(rec, 0, 3 * HF // 2, 2 * F, H)
-        wd = _int4_matrix(rec, HF, 3 * HF // 2 + HF // 8, H, F)
+        gu = _int4_matrix(rec, 0, 3 * HF // 2, 2 * F, H, grouped_scales=True)
+        wd = _int4_matrix(rec, HF, 3 * HF // 2 + HF // 8, H, F, grouped_scales=False)
     elif qfmt == QFMT_INT2:
-        gu = _int2_matrix(rec, 0, 3 * HF // 4, 2 * F, H)
-        wd = _int2_matrix(rec, HF // 2, 5 * HF // 4, H, F)
+        gu = _int2_matrix(rec, 0, 3 * HF // 4, 2 * F, H, grouped=True)
+        wd = _int2_matrix(rec, HF // 2, 5 * HF // 4, H, F, grouped=False)
     else:
         raise ValueError(qfmt)
     # GU row 64g+i is gate row 32g+i (i < 32) or up row 32g+i-32 (i >= 32)

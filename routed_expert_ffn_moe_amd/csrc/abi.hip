@@ -4,6 +4,7 @@
 
 #include "moe_common.h"
 #include "moe_sizes.h"
+#include "moe_kernels.h"
 
 static thread_local char g_err[512] = "";
 
@@ -58,7 +59,7 @@ extern "C" size_t moe_workspace_size(int op, int T, int k, int E, int H, int F, 
     case MOE_OP_GROUPED_GEMM_Q: return moe_ws_gemm(T, k, E, F);
     case MOE_OP_COMBINE: return 0;
     case MOE_OP_USAGE_UPDATE: return 0;
-    case MOE_OP_DECODE_STACK: return moe_ws_stack(T, k, E, H, F, qfmt);
+    case MOE_OP_DECODE_STACK: return moe_ws_decode_stack(T, k, E, H, F, qfmt);
     default: return 0;
   }
 }

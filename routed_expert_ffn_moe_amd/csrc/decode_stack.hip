@@ -13,7 +13,28 @@
 #include "moe_sizes.h"
 #include "moe_kernels.h"
 
+#include <cstdlib>
+#include <cstring>
+
 #define MOE_STACK_EPS 1e-6f
+
+size_t moe_ws_decode_stack(int T, int k, int E, int H, int F, int qfmt) {
+  if (T < 1 || k < 1 || H < 128 || F < 128) return 0;
+  size_t a = moe_ws_stack(T, k, E, H, F, qfmt);
+  if (moe_persistent_supported(T, k, E, H, F, qfmt)) {
+    const size_t b = moe_ws_stack_persistent(T, k, E, H, F, qfmt);
+    if (b > a) a = b;
+  }
+  return a;
+}
+
+// MOE_DECODE_PATH=chain forces the per-layer kernel chain; otherwise the
+// persistent kernel is used whenever it supports the shape.
+static bool use_persistent(int T, int k, int E, int H, int F, int qfmt) {
+  const char* e = getenv("MOE_DECODE_PATH");
+  if (e && strcmp(e, "chain") == 0) return false;
+  return moe_persistent_supported(T, k, E, H, F, qfmt);
+}
 
 // xn[t] = x[t] / sqrt(mean(x[t]^2) + eps); one workgroup per token, fixed-order
 // fp32 reduction.
@@ -45,10 +66,13 @@ extern "C" int moe_decode_stack(const float* x_in, int T, int H, int F, int E, i
   MOE_REQUIRE(moe_aligned(x_in, 16) && moe_aligned(x_out, 16) && moe_aligned(w_router, 16) &&
                   (!x_hist || moe_aligned(x_hist, 16)),
               MOE_EALIGN, "x_in, x_out, x_hist and w_router must be 16-byte aligned");
-  const size_t need = moe_ws_stack(T, k, E, H, F, qfmt);
+  const size_t need = moe_ws_decode_stack(T, k, E, H, F, qfmt);
   MOE_REQUIRE(ws && ws_bytes >= need && moe_aligned(ws, 256), MOE_EWORKSPACE,
               "ws needs %zu bytes, 256-byte aligned", need);
   hipStream_t st = moe_stream(stream);
+  if (use_persistent(T, k, E, H, F, qfmt))
+    return moe_launch_decode_persistent(x_in, T, H, F, E, k, L, w_router, bias, slot_table, pool, record_bytes, qfmt,
+                                        x_out, topk_idx_out, topk_w_out, x_hist, ws, st);
   const MoeStackLayout W = moe_stack_layout(T, k, E, H, F, qfmt);
   uint8_t* w = (uint8_t*)ws;
   float* logits = (float*)(w + W.logits);

@@ -221,10 +221,13 @@ __device__ __forceinline__ void moe_q2_unit(uint4 q, uint4 meta, const uint8_t* 
 // Row r of a [kb][row]-stored matrix with `rows` rows and K columns, dotted
 // with the prepared vectors, over this wave's share of K.  Returns partials
 // in acc[i].
+// `grouped`: the gate/up planes keep scales in 4-block groups [kb/4][row][4]
+// and int2 words / (s, m) in 4-block units; the down planes store them per
+// block [kb][row].
 template <int QFMT, int MAXT>
 __device__ __forceinline__ void moe_row_dot(const uint8_t* __restrict__ rec, int64_t q_off, int64_t s_off,
                                             int rows, int K, int r, int wave, const uint8_t* const* prep,
-                                            int ntok, float* acc) {
+                                            int ntok, float* acc, bool grouped) {
   if (QFMT == MOE_Q4_B32) {
     const int KB = K / 32;
     const int per = KB / GEMV_WAVES;  // K % 128 == 0 -> KB % 4 == 0
@@ -239,8 +242,8 @@ __device__ __forceinline__ void moe_row_dot(const uint8_t* __restrict__ rec, int
       for (int u = 0; u < 4; ++u) {
         if (u < n) {
           const int kb = g + u;
-          const uint16_t sb = *reinterpret_cast<const uint16_t*>(
-              rec + s_off + 2 * ((int64_t)(kb >> 2) * rows * 4 + 4 * r + (kb & 3)));
+          const int64_t si = grouped ? (int64_t)(kb >> 2) * rows * 4 + 4 * r + (kb & 3) : (int64_t)kb * rows + r;
+          const uint16_t sb = *reinterpret_cast<const uint16_t*>(rec + s_off + 2 * si);
           moe_q4_block<MAXT>(qv[u], moe_f16_to_f32(sb), prep, kb, K, ntok, acc);
         }
       }
@@ -250,8 +253,20 @@ __device__ __forceinline__ void moe_row_dot(const uint8_t* __restrict__ rec, int
     const int per = (U4 + GEMV_WAVES - 1) / GEMV_WAVES;
     const int u0 = wave * per, u1 = min(U4, u0 + per);
     for (int u = u0; u < u1; ++u) {
-      const uint4 q = *reinterpret_cast<const uint4*>(rec + q_off + 16 * ((int64_t)u * rows + r));
-      const uint4 m = *reinterpret_cast<const uint4*>(rec + s_off + 16 * ((int64_t)u * rows + r));
+      uint4 q, m;
+      if (grouped) {
+        q = *reinterpret_cast<const uint4*>(rec + q_off + 16 * ((int64_t)u * rows + r));
+        m = *reinterpret_cast<const uint4*>(rec + s_off + 16 * ((int64_t)u * rows + r));
+      } else {
+        uint32_t qw[4], mw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          qw[j] = *reinterpret_cast<const uint32_t*>(rec + q_off + 4 * ((int64_t)(4 * u + j) * rows + r));
+          mw[j] = *reinterpret_cast<const uint32_t*>(rec + s_off + 4 * ((int64_t)(4 * u + j) * rows + r));
+        }
+        q = make_uint4(qw[0], qw[1], qw[2], qw[3]);
+        m = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+      }
       moe_q2_unit<MAXT>(q, m, prep, u, K, ntok, acc);
     }
   }
@@ -286,7 +301,7 @@ __global__ __launch_bounds__(256) void gemv_gu_kernel(int H, int F, int E, const
 #pragma unroll
   for (int i = 0; i < MOE_MAX_DECODE_T; ++i) acc[i] = 0.f;
   const int r = 64 * rg + lane;
-  moe_row_dot<QFMT, MOE_MAX_DECODE_T>(rec, pl.gu_q, pl.gu_s, 2 * F, H, r, wave, prep, ntok, acc);
+  moe_row_dot<QFMT, MOE_MAX_DECODE_T>(rec, pl.gu_q, pl.gu_s, 2 * F, H, r, wave, prep, ntok, acc, true);
 #pragma unroll
   for (int i = 0; i < MOE_MAX_DECODE_T; ++i) red[wave][i][lane] = acc[i];
   __syncthreads();
@@ -334,7 +349,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int F, int E, int
 #pragma unroll
   for (int i = 0; i < MOE_MAX_DECODE_T; ++i) acc[i] = 0.f;
   const int r = 64 * rg + lane;
-  moe_row_dot<QFMT, MOE_MAX_DECODE_T>(rec, pl.d_q, pl.d_s, H, F, r, wave, prep, ntok, acc);
+  moe_row_dot<QFMT, MOE_MAX_DECODE_T>(rec, pl.d_q, pl.d_s, H, F, r, wave, prep, ntok, acc, false);
 #pragma unroll
   for (int i = 0; i < MOE_MAX_DECODE_T; ++i) red[wave][i][lane] = acc[i];
   __syncthreads();

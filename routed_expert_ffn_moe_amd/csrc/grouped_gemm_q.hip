@@ -83,8 +83,14 @@ __device__ __forceinline__ void load_b(BRegs<MOE_Q4_B32>& b, const uint8_t* rec,
       const int kb = 2 * c + bi;
       b.q[sub][bi] = *reinterpret_cast<const uint2*>(rec + q_off + 16 * ((int64_t)kb * rows + r) + 8 * hh);
     }
-    const int kb = 2 * c;  // even -> both scales in one 4-byte word
-    b.s[sub] = *reinterpret_cast<const uint32_t*>(rec + s_off + 2 * ((int64_t)(kb >> 2) * rows * 4 + 4 * r + (kb & 3)));
+    const int kb = 2 * c;
+    if (gu) {  // 4-block groups: kb even -> both scales in one 4-byte word
+      b.s[sub] = *reinterpret_cast<const uint32_t*>(rec + s_off + 2 * ((int64_t)(kb >> 2) * rows * 4 + 4 * r + (kb & 3)));
+    } else {   // per block [kb][row]
+      const uint32_t s0 = *reinterpret_cast<const uint16_t*>(rec + s_off + 2 * ((int64_t)kb * rows + r));
+      const uint32_t s1 = *reinterpret_cast<const uint16_t*>(rec + s_off + 2 * ((int64_t)(kb + 1) * rows + r));
+      b.s[sub] = s0 | (s1 << 16);
+    }
   }
 }
 
@@ -94,8 +100,19 @@ __device__ __forceinline__ void load_b(BRegs<MOE_Q2_B16>& b, const uint8_t* rec,
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
     const int r = row0 + 32 * sub;
-    b.q[sub] = *reinterpret_cast<const uint4*>(rec + q_off + 16 * ((int64_t)c * rows + r));
-    b.m[sub] = *reinterpret_cast<const uint4*>(rec + m_off + 16 * ((int64_t)c * rows + r));
+    if (gu) {  // 4-block units
+      b.q[sub] = *reinterpret_cast<const uint4*>(rec + q_off + 16 * ((int64_t)c * rows + r));
+      b.m[sub] = *reinterpret_cast<const uint4*>(rec + m_off + 16 * ((int64_t)c * rows + r));
+    } else {   // per block [b][row]
+      uint32_t qw[4], mw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        qw[j] = *reinterpret_cast<const uint32_t*>(rec + q_off + 4 * ((int64_t)(4 * c + j) * rows + r));
+        mw[j] = *reinterpret_cast<const uint32_t*>(rec + m_off + 4 * ((int64_t)(4 * c + j) * rows + r));
+      }
+      b.q[sub] = make_uint4(qw[0], qw[1], qw[2], qw[3]);
+      b.m[sub] = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+    }
   }
   (void)hh;
 }

@@ -293,26 +293,75 @@ def test_usage_rerank_full_size(moe):
 
 # ---------------------------------------------------------------- stacked decode
 
-@pytest.mark.parametrize("qfmt", [0, 1])
-@pytest.mark.parametrize("T", [1, 4])
-def test_decode_stack_tiny(moe, qfmt, T):
-    L = 6
-    li = C.layer_case(5, T, 256, 16, 2, 128, qfmt=qfmt, bias=True, L=L, gap=False)
-    x = li.x.cuda()
-    idx_o = torch.empty((L, T, 2), dtype=torch.int32, device="cuda")
-    w_o = torch.empty((L, T, 2), dtype=torch.float32, device="cuda")
-    hist = torch.empty((L, T, 256), dtype=torch.float32, device="cuda")
-    xo = moe.moe_decode_stack(x, li.F, li.E, li.k, li.Wr.cuda(), li.bias.cuda(), li.S.cuda(), li.pool.cuda(), li.R,
-                              qfmt, topk_idx_out=idx_o, topk_w_out=w_o, x_hist=hist)
+def _stack_run(moe, li, x, path, ws=None):
+    import os
+    L, T, H, k = li.Wr.shape[0], x.shape[0], x.shape[1], li.k
+    idx_o = torch.empty((L, T, k), dtype=torch.int32, device="cuda")
+    w_o = torch.empty((L, T, k), dtype=torch.float32, device="cuda")
+    hist = torch.empty((L, T, H), dtype=torch.float32, device="cuda")
+    old = os.environ.get("MOE_DECODE_PATH")
+    os.environ["MOE_DECODE_PATH"] = path
+    try:
+        xo = moe.moe_decode_stack(x, li.F, li.E, k, li.Wr, li.bias, li.S, li.pool, li.R, li.qfmt,
+                                  topk_idx_out=idx_o, topk_w_out=w_o, x_hist=hist, ws=ws)
+    finally:
+        if old is None:
+            del os.environ["MOE_DECODE_PATH"]
+        else:
+            os.environ["MOE_DECODE_PATH"] = old
+    torch.cuda.synchronize()
+    return xo, idx_o, w_o, hist
+
+
+def _check_stack(li, x, xo, idx_o, w_o, hist, layers):
+    L = hist.shape[0]
     assert torch.equal(hist[0], x)
-    for l in range(L):
+    assert torch.isfinite(xo).all()
+    excluded = 0
+    for l in layers:
         xl = torch.from_numpy(O.rms_normalize(C.x_as_f64(hist[l])))
         ry, ri, rw, _, rl = C.oracle_layer(li, layer=l, x=xl)
         ok = O.gap_ok(rl, li.k, C.MIN_GAP)
+        excluded += int((~ok).sum())
         assert np.array_equal(_np(idx_o[l])[ok], ri[ok])
+        assert np.max(np.abs(_np(w_o[l])[ok] - rw[ok])) <= W_ATOL
         nxt = hist[l + 1] if l + 1 < L else xo
         if ok.all():
             C.assert_close_moe(_np(nxt - hist[l]), ry, f"layer {l}")
+    return excluded
+
+
+@pytest.mark.parametrize("path", ["chain", "persistent"])
+@pytest.mark.parametrize("qfmt", [0, 1])
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_stack_tiny(moe, qfmt, T, path):
+    L = 6
+    li = C.layer_case(5, T, 256, 16, 2, 128, qfmt=qfmt, bias=True, L=L, gap=False, device="cuda")
+    x = li.x.contiguous()
+    xo, idx_o, w_o, hist = _stack_run(moe, li, x, path)
+    excluded = _check_stack(li, x, xo, idx_o, w_o, hist, range(L))
+    assert excluded <= T * L // 4
+
+
+@pytest.mark.parametrize("qfmt", [0, 1])
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_stack_full_shape_persistent(moe, qfmt, T):
+    """4 layers of the full shape (512 experts top-10, H=2048, F=768), the
+    persistent kernel; layers 0 and 3 checked against the oracle, and the
+    chain path must agree within tolerance on every layer."""
+    L = 4
+    li = C.layer_case(6, T, 2048, 512, 10, 768, qfmt=qfmt, bias=True, L=L, gap=False, device="cuda")
+    x = li.x.contiguous()
+    ws = moe.workspace(moe.MOE_OP_DECODE_STACK, "cuda", T, 10, 512, 2048, 768, qfmt)
+    xo, idx_o, w_o, hist = _stack_run(moe, li, x, "persistent", ws=ws)
+    _check_stack(li, x, xo, idx_o, w_o, hist, [0, 3])
+    xc, idx_c, w_c, hist_c = _stack_run(moe, li, x, "chain")
+    assert torch.equal(idx_c, idx_o)
+    C.assert_close_moe(_np(xc), _np(xo), "chain vs persistent")
+    # repeated calls on the same workspace: new tags each call, same result
+    for rep in range(3):
+        xo2, idx2, _, _ = _stack_run(moe, li, x, "persistent", ws=ws)
+        assert torch.equal(xo2, xo) and torch.equal(idx2, idx_o)
 
 
 # ---------------------------------------------------------------- generator
