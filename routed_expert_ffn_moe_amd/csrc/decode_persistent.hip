@@ -160,60 +160,115 @@ __device__ __forceinline__ uint32_t pt_wave_max(uint32_t v) {
 }
 
 // Top-k of one token's E logits (LDS) by one wave.  Lane l holds the keys of
-// experts l + 64 * i (i < SLOTS) as 64-bit (order-preserving logit bits,
-// ~expert): distinct, and the larger key is the larger logit, on equal logits
-// the lower expert.  Each lane sorts its keys; every round takes the wave-wide
-// maximum of the lane heads and the winning lane pops its head.  Lane 0
-// writes ids[j] and the softmax weights wts[j] of the chosen logits.
+// experts l + 64 * i (i < SLOTS): the order-preserving logit bits, and on
+// equal bits the lower expert first.  Each lane sorts its keys; every round
+// takes the wave-wide maximum of the lane heads and the lane holding it pops
+// its head.  Lane j < k ends with the j-th expert and its softmax weight over
+// the k chosen logits (ids[j], wts[j]).
 template <int SLOTS>
 __device__ __forceinline__ void pt_topk(const float* lg, int E, int k, int* ids, float* wts) {
   const int lane = threadIdx.x & 63;
-  uint32_t hi[SLOTS], lo[SLOTS];
+  uint32_t hi[SLOTS], ex[SLOTS];
 #pragma unroll
   for (int i = 0; i < SLOTS; ++i) {
     const int e = lane + 64 * i;
     hi[i] = e < E ? moe_f32_order_key(lg[e < E ? e : 0]) : 0u;  // every real key has hi > 0
-    lo[i] = ~(uint32_t)e;
+    ex[i] = (uint32_t)e;
   }
-  // descending sort of the lane's keys (odd-even transposition network)
+  // descending sort of the lane's keys (odd-even transposition network); the
+  // experts of one lane ascend with i, so equal keys keep the lower expert first
 #pragma unroll
   for (int r = 0; r < SLOTS; ++r) {
 #pragma unroll
     for (int i = r & 1; i + 1 < SLOTS; i += 2) {
-      const bool sw = hi[i] < hi[i + 1] || (hi[i] == hi[i + 1] && lo[i] < lo[i + 1]);
-      const uint32_t h0 = hi[i], l0 = lo[i];
+      const bool sw = hi[i] < hi[i + 1] || (hi[i] == hi[i + 1] && ex[i] > ex[i + 1]);
+      const uint32_t h0 = hi[i], e0 = ex[i];
       hi[i] = sw ? hi[i + 1] : hi[i];
-      lo[i] = sw ? lo[i + 1] : lo[i];
+      ex[i] = sw ? ex[i + 1] : ex[i];
       hi[i + 1] = sw ? h0 : hi[i + 1];
-      lo[i + 1] = sw ? l0 : lo[i + 1];
+      ex[i + 1] = sw ? e0 : ex[i + 1];
     }
   }
+  uint32_t my_key = 0u, my_e = 0u;
   for (int j = 0; j < k; ++j) {
-    const uint32_t Mh = pt_wave_max(hi[0]);
-    const uint32_t Ml = pt_wave_max(hi[0] == Mh ? lo[0] : 0u);
-    if (hi[0] == Mh && lo[0] == Ml) {  // exactly one lane: pop its head
+    const uint32_t M = pt_wave_max(hi[0]);
+    const uint64_t cand = __ballot(hi[0] == M);
+    int wl = __ffsll((long long)cand) - 1;
+    if (__popcll(cand) > 1) {  // equal logits in several lanes: the lowest expert
+      const uint32_t ce = hi[0] == M ? ex[0] : 0xFFFFFFFFu;
+      const uint32_t emin = ~pt_wave_max(~ce);
+      wl = (int)(emin & 63);
+    }
+    const uint32_t ew = __builtin_amdgcn_readlane(ex[0], wl);
+    if (lane == j) {
+      my_key = M;
+      my_e = ew;
+    }
+    if (lane == wl) {  // pop the head
 #pragma unroll
       for (int i = 0; i + 1 < SLOTS; ++i) {
         hi[i] = hi[i + 1];
-        lo[i] = lo[i + 1];
+        ex[i] = ex[i + 1];
       }
       hi[SLOTS - 1] = 0u;
-      lo[SLOTS - 1] = 0u;
-    }
-    if (lane == 0) {
-      ids[j] = (int)~Ml;
-      wts[j] = moe_order_key_f32(Mh);
     }
   }
-  if (lane == 0) {
-    const float m0 = wts[0];
-    float sum = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const float z = expf(wts[j] - m0);
-      wts[j] = z;
-      sum += z;
+  // softmax over the chosen logits, lane j holding logit j (max is lane 0's)
+  const float m0 = moe_order_key_f32(__builtin_amdgcn_readfirstlane(my_key));
+  const float z = lane < k ? expf(moe_order_key_f32(my_key) - m0) : 0.f;
+  float sum = z;  // sum in lane order: lanes 0..k-1 are added left to right
+  {
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), j));
+    sum = acc;
+  }
+  if (lane < k) {
+    ids[lane] = (int)my_e;
+    wts[lane] = z / sum;
+  }
+}
+
+// Work plan of one layer from the T * k chosen experts (one wave): the
+// distinct experts in order of first occurrence (token-major), each with its
+// tokens and their top-k positions, then the shared expert with every token.
+// uslot[t * (k + 1) + j] = u * 4 + c names the unit u and token slot c that
+// produce token t's j-th expert output.  n = T * k <= 64.
+__device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, int* p_exp, int* p_ntok, int* p_tok,
+                                        int* p_j, int* uslot, int* p_misc) {
+  const int lane = threadIdx.x & 63, n = T * k;
+  const int e = lane < n ? topi[lane] : -1 - lane;  // distinct negatives for idle lanes
+  int first = lane, before = 0, total = 0;           // first lane with this expert; count before; count
+  for (int q = 0; q < n; ++q) {
+    const int eq = __builtin_amdgcn_readlane(e, q);
+    if (eq == e) {
+      first = min(first, q);
+      before += q < lane;
+      ++total;
     }
-    for (int j = 0; j < k; ++j) wts[j] = wts[j] / sum;
+  }
+  const uint64_t firsts = __ballot(lane < n && first == lane);
+  const int u_first = (int)__popcll(firsts & ((1ull << lane) - 1ull));  // rank among first occurrences
+  const int u = __shfl(u_first, first, 64);
+  const int U = (int)__popcll(firsts);
+  if (lane < n) {
+    const int t = lane / k, j = lane % k;
+    if (first == lane) {
+      p_exp[u] = e;
+      p_ntok[u] = total;
+    }
+    p_tok[u * 4 + before] = t;
+    p_j[u * 4 + before] = j;
+    uslot[t * (k + 1) + j] = u * 4 + before;
+  }
+  if (lane < T) {
+    p_tok[U * 4 + lane] = lane;
+    p_j[U * 4 + lane] = k;
+    uslot[lane * (k + 1) + k] = U * 4 + lane;
+  }
+  if (lane == 0) {
+    p_exp[U] = E;
+    p_ntok[U] = T;
+    p_misc[0] = U + 1;
   }
 }
 
@@ -269,9 +324,9 @@ __device__ __forceinline__ void pt_prep_word(const float* v, float scale, bool v
 // Per-half sections (red, hs, hp, hc) exist twice: the two halves of the
 // workgroup run two work units side by side.
 struct PtLds {
-  size_t xs, xprep, lg, topi, topw, p_exp, p_ntok, p_tok, p_j, p_misc, red, hp, hc, inv, hs, uslot, dq, ds, poff, total;
+  size_t xs, xprep, lg, topi, topw, p_exp, p_ntok, p_tok, p_j, p_misc, red, hp, hc, inv, hs, uslot, poff, total;
 };
-__host__ __device__ inline PtLds pt_lds(int T, int k, int E, int H, int nfs, size_t prep_bytes) {
+__host__ __device__ inline PtLds pt_lds(int qfmt, int T, int k, int E, int H, int nfs, size_t prep_bytes) {
   PtLds o;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -296,8 +351,6 @@ __host__ __device__ inline PtLds pt_lds(int T, int k, int E, int H, int nfs, siz
   o.inv = take(4 * 4);
   o.hs = take(2 * 4 * 32 * 4);                // [half][token][32]
   o.uslot = take((size_t)T * (k + 1) * 4);
-  o.dq = take((size_t)2 * H * 16);  // [half][row] down block (int4) or 2 words (int2)
-  o.ds = take((size_t)2 * H * 8);   // [half][row] down scale (int4, one dword per row) or 2 metas (int2)
   o.poff = take((size_t)T * (k + 1) * nfs * 4);
   o.total = off;
   return o;
@@ -315,7 +368,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
   const MoePlanes pl = moe_planes(QFMT, H, F);  // a record is < 4 GiB: 32-bit plane offsets
   const uint32_t o_guq = (uint32_t)pl.gu_q, o_gus = (uint32_t)pl.gu_s, o_dq = (uint32_t)pl.d_q, o_ds = (uint32_t)pl.d_s;
 
-  const PtLds o = pt_lds(T, k, E, H, a.nfs, a.prep_bytes);
+  const PtLds o = pt_lds(QFMT, T, k, E, H, a.nfs, a.prep_bytes);
   float* xs = (float*)(smem + o.xs);          // [T][H]
   uint8_t* xprep = smem + o.xprep;            // [T][prep_bytes]
   float* lg = (float*)(smem + o.lg);          // [T][E]
@@ -332,8 +385,6 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
   float* inv = (float*)(smem + o.inv);        // [4]
   float* hs = (float*)(smem + o.hs);          // [2][4][32]
   int* uslot = (int*)(smem + o.uslot);        // [T][k+1] -> u * 4 + i
-  uint8_t* dq_l = smem + o.dq;                // [2][H][16]
-  uint8_t* ds_l = smem + o.ds;                // [2][H][8]
   uint32_t* poff = (uint32_t*)(smem + o.poff); // [T][(k+1) * nfs]
 
   const uint32_t call = __hip_atomic_load(a.hdr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -469,45 +520,9 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
       if (a.topk_idx_out) a.topk_idx_out[(size_t)l * T * k + tid] = topi[tid];
       if (a.topk_w_out) a.topk_w_out[(size_t)l * T * k + tid] = topw[tid];
     }
-    // plan: distinct experts in ascending order, then the shared expert
+    // plan (wave 0), then the partial-offset table
     {
-      const int n = T * k;
-      int* fl = (int*)red;  // first-occurrence flags [n] (red is free here)
-      if (tid < n) {
-        const int e = topi[tid];
-        bool first = true;
-        for (int j = 0; j < tid; ++j) first &= topi[j] != e;
-        fl[tid] = first;
-      }
-      __syncthreads();
-      if (tid < n && fl[tid]) {
-        const int e = topi[tid];
-        int u = 0;
-        for (int j = 0; j < n; ++j) u += (fl[j] && topi[j] < e);
-        p_exp[u] = e;
-        int c = 0;
-        for (int t = 0; t < T; ++t)
-          for (int j = 0; j < k; ++j)
-            if (topi[t * k + j] == e && c < 4) {
-              p_tok[u * 4 + c] = t;
-              p_j[u * 4 + c] = j;
-              uslot[t * (k + 1) + j] = u * 4 + c;
-              ++c;
-            }
-        p_ntok[u] = c;
-      }
-      if (tid == 0) {
-        int U = 0;
-        for (int j = 0; j < n; ++j) U += fl[j];
-        p_exp[U] = E;
-        p_ntok[U] = T;
-        for (int t = 0; t < T; ++t) {
-          p_tok[U * 4 + t] = t;
-          p_j[U * 4 + t] = k;
-          uslot[t * (k + 1) + k] = U * 4 + t;
-        }
-        p_misc[0] = U + 1;
-      }
+      if (wave == 0) pt_plan(topi, T, k, E, p_exp, p_ntok, p_tok, p_j, uslot, p_misc);
       __syncthreads();
       // word offset in pbuf (without the row) of partial pi = j * nfs + fs of
       // token t: unit v = u * nfs + fs, token slot i, both from uslot
@@ -538,29 +553,31 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
       float acc[MT];
 #pragma unroll
       for (int i = 0; i < MT; ++i) acc[i] = 0.f;
-      // the down block column goes straight to LDS (global_load_lds): row rr
-      // of this half's buffer holds its 16-byte block (int4) or two words
-      // (int2); it is consumed after the gate/up reduction.  Issued first.
-      uint8_t* hdq = dq_l + (size_t)half * H * 16;
-      uint8_t* hds = ds_l + (size_t)half * H * 8;
-      if (act) {
-        for (int r0 = 64 * hw; r0 < H; r0 += 256) {  // 64 rows per wave-wide load
-          const int rr = r0 + lane;
-          if (QFMT == MOE_Q4_B32) {
-            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(rec + (uint32_t)(o_dq + 16u * (uint32_t)(fs * H + rr))),
-                                             (void __attribute__((address_space(3)))*)(hdq + (size_t)r0 * 16), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(rec + (uint32_t)(o_ds + 2u * (uint32_t)(fs * H + rr))),
-                                             (void __attribute__((address_space(3)))*)(hds + (size_t)r0 * 4), 2, 0, 0);
-          } else {
+      // the down block column: thread htid holds rows htid + 256 * c (the
+      // rows it multiplies later).  With one token per unit the loads are
+      // issued right after the gate/up loads (which are needed first); with
+      // more tokens after the gate/up dot products, to bound live registers.
+      // A fixed count of 8 rows (H <= 2048); rows past H repeat the last row.
+      constexpr bool down_early = MT == 1;
+      uint4 dq[8];     // int4: the row's block; int2: two words, two metas
+      uint32_t ds[8];  // int4: the row's scale
+      auto issue_down = [&]() {
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(rec + (uint32_t)(o_dq + 4u * (uint32_t)((2 * fs + b) * H + rr))),
-                                               (void __attribute__((address_space(3)))*)(hdq + (size_t)b * H * 4 + (size_t)r0 * 4), 4, 0, 0);
-              __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(rec + (uint32_t)(o_ds + 4u * (uint32_t)((2 * fs + b) * H + rr))),
-                                               (void __attribute__((address_space(3)))*)(hds + (size_t)b * H * 4 + (size_t)r0 * 4), 4, 0, 0);
-            }
+        for (int c = 0; c < 8; ++c) {
+          const uint32_t rr = (uint32_t)(htid + 256 * min(c, H / 256 - 1));
+          if (QFMT == MOE_Q4_B32) {
+            dq[c] = *reinterpret_cast<const uint4*>(rec + (o_dq + 16u * ((uint32_t)fs * (uint32_t)H + rr)));
+            ds[c] = *reinterpret_cast<const uint16_t*>(rec + (o_ds + 2u * ((uint32_t)fs * (uint32_t)H + rr)));
+          } else {
+            const uint32_t w0 = (2u * fs) * (uint32_t)H + rr, w1 = w0 + (uint32_t)H;
+            dq[c].x = *reinterpret_cast<const uint32_t*>(rec + (o_dq + 4u * w0));
+            dq[c].y = *reinterpret_cast<const uint32_t*>(rec + (o_dq + 4u * w1));
+            dq[c].z = *reinterpret_cast<const uint32_t*>(rec + (o_ds + 4u * w0));
+            dq[c].w = *reinterpret_cast<const uint32_t*>(rec + (o_ds + 4u * w1));
           }
         }
+      };
+      if (act) {
         const int r = 64 * fs + lane;  // gate/up row
         // wave hw takes a quarter of the K blocks, in groups of 4 blocks (the
         // unit of the scale planes); indices are clamped so that every load
@@ -577,20 +594,25 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
             for (int b = 0; b < 4; ++b)
               q[4 * c + b] = *reinterpret_cast<const uint4*>(rec + (o_guq + 16u * ((4u * gg + b) * 2u * (uint32_t)F + (uint32_t)r)));
           }
+          if (down_early) issue_down();
+          // with one token every use is unconditional (a group past g1 gets
+          // scale 0), so the loads stay together ahead of the first dot
+          // product and the down loads behind them stay in flight
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            if (g0 + c < g1) {
-              const uint32_t sw[2] = {sc[c].x, sc[c].y};
+            const int gg = min(g0 + c, NG - 1);
+            const bool gv = g0 + c < g1;
+            if (MT > 1 && !gv) continue;
+            const uint32_t sw[2] = {sc[c].x, sc[c].y};
 #pragma unroll
-              for (int b = 0; b < 4; ++b) {
-                const int kb = 4 * (g0 + c) + b;
-                const float s = moe_f16_to_f32((uint16_t)(sw[b >> 1] >> (16 * (b & 1))));
+            for (int b = 0; b < 4; ++b) {
+              const int kb = 4 * gg + b;
+              const float s = gv ? moe_f16_to_f32((uint16_t)(sw[b >> 1] >> (16 * (b & 1)))) : 0.f;
 #pragma unroll
-                for (int i = 0; i < MT; ++i) {
-                  if (i < ntok) {
-                    const float cc = ((const float2*)(xpt[i] + 2 * (size_t)H))[kb].x;
-                    acc[i] = fmaf(s, pt_q4_dot(q[4 * c + b], (const uint32_t*)xpt[i] + 16 * kb, cc), acc[i]);
-                  }
+              for (int i = 0; i < MT; ++i) {
+                if ((MT == 1 && i == 0) || i < ntok) {
+                  const float cc = ((const float2*)(xpt[i] + 2 * (size_t)H))[kb].x;
+                  acc[i] = fmaf(s, pt_q4_dot(q[4 * c + b], (const uint32_t*)xpt[i] + 16 * kb, cc), acc[i]);
                 }
               }
             }
@@ -604,28 +626,30 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
             q[c] = *reinterpret_cast<const uint4*>(rec + (o_guq + 16u * (uu * 2u * (uint32_t)F + (uint32_t)r)));
             m[c] = *reinterpret_cast<const uint4*>(rec + (o_gus + 16u * (uu * 2u * (uint32_t)F + (uint32_t)r)));
           }
+          if (down_early) issue_down();
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
-            const int uu = u0 + c;
-            if (uu < u1) {
-              const uint32_t qw[4] = {q[c].x, q[c].y, q[c].z, q[c].w}, mw[4] = {m[c].x, m[c].y, m[c].z, m[c].w};
+            const int uu = min(u0 + c, U4 - 1);
+            const bool uv = u0 + c < u1;  // past u1: scale and min 0
+            if (MT > 1 && !uv) continue;
+            const uint32_t qw[4] = {q[c].x, q[c].y, q[c].z, q[c].w}, mw[4] = {m[c].x, m[c].y, m[c].z, m[c].w};
 #pragma unroll
-              for (int jb = 0; jb < 4; ++jb) {
-                const int b = 4 * uu + jb;
-                const float s = moe_f16_to_f32((uint16_t)(mw[jb] & 0xffff));
-                const float mm = moe_f16_to_f32((uint16_t)(mw[jb] >> 16));
+            for (int jb = 0; jb < 4; ++jb) {
+              const int b = 4 * uu + jb;
+              const float s = uv ? moe_f16_to_f32((uint16_t)(mw[jb] & 0xffff)) : 0.f;
+              const float mm = uv ? moe_f16_to_f32((uint16_t)(mw[jb] >> 16)) : 0.f;
 #pragma unroll
-                for (int i = 0; i < MT; ++i) {
-                  if (i < ntok) {
-                    const float2 cc = ((const float2*)(xpt[i] + 2 * (size_t)H))[b];
-                    acc[i] += pt_q2_dot(qw[jb], s, mm, (const uint32_t*)xpt[i] + 8 * b, cc);
-                  }
+              for (int i = 0; i < MT; ++i) {
+                if ((MT == 1 && i == 0) || i < ntok) {
+                  const float2 cc = ((const float2*)(xpt[i] + 2 * (size_t)H))[b];
+                  acc[i] += pt_q2_dot(qw[jb], s, mm, (const uint32_t*)xpt[i] + 8 * b, cc);
                 }
               }
             }
           }
         }
       }
+      if (!down_early && act) issue_down();
 #pragma unroll
       for (int i = 0; i < MT; ++i) hred[(hw * 4 + i) * 64 + lane] = acc[i];
       __syncthreads();
@@ -643,8 +667,6 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         pt_prep_block<QFMT>(hhs + i * 32 + 16 * b, 1.0f, hhp + i * 16 + 8 * b, hhc + i * 2 + b);
       }
       __syncthreads();
-      __builtin_amdgcn_s_waitcnt(0);  // this thread's LDS-bound loads have landed
-      __syncthreads();
       if (act) {
         float wgt[MT];
 #pragma unroll
@@ -655,26 +677,26 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
             if (j < k) wgt[i] = topw[t * k + j];
           }
         }
-        for (int rr = htid; rr < H; rr += 256) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          if (c >= H / 256) break;
+          const int rr = htid + 256 * c;
           float y[MT];
 #pragma unroll
           for (int i = 0; i < MT; ++i) y[i] = 0.f;
           if (QFMT == MOE_Q4_B32) {
-            const uint4 q = *reinterpret_cast<const uint4*>(hdq + (size_t)rr * 16);
-            // a sub-dword LDS load still fills one dword per lane (zero-extended)
-            const float s = moe_f16_to_f32(*reinterpret_cast<const uint16_t*>(hds + (size_t)rr * 4));
+            const float s = moe_f16_to_f32((uint16_t)ds[c]);
 #pragma unroll
             for (int i = 0; i < MT; ++i)
-              if (i < ntok) y[i] = s * pt_q4_dot(q, hhp + i * 16, hhc[i * 2].x);
+              if (i < ntok) y[i] = s * pt_q4_dot(dq[c], hhp + i * 16, hhc[i * 2].x);
           } else {
+            const uint32_t wv[2] = {dq[c].x, dq[c].y}, mv[2] = {dq[c].z, dq[c].w};
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
-              const uint32_t w = *reinterpret_cast<const uint32_t*>(hdq + (size_t)b * H * 4 + (size_t)rr * 4);
-              const uint32_t mw = *reinterpret_cast<const uint32_t*>(hds + (size_t)b * H * 4 + (size_t)rr * 4);
-              const float s = moe_f16_to_f32((uint16_t)(mw & 0xffff)), mm = moe_f16_to_f32((uint16_t)(mw >> 16));
+              const float s = moe_f16_to_f32((uint16_t)(mv[b] & 0xffff)), mm = moe_f16_to_f32((uint16_t)(mv[b] >> 16));
 #pragma unroll
               for (int i = 0; i < MT; ++i)
-                if (i < ntok) y[i] += pt_q2_dot(w, s, mm, hhp + i * 16 + 8 * b, hhc[i * 2 + b]);
+                if (i < ntok) y[i] += pt_q2_dot(wv[b], s, mm, hhp + i * 16 + 8 * b, hhc[i * 2 + b]);
             }
           }
 #pragma unroll
@@ -790,7 +812,7 @@ static PtLayout pt_layout(int T, int k, int E, int H, int F, int qfmt, int G) {
   P.lbuf = P.xbuf + moe_ws_up((size_t)T * H * 8);
   P.pbuf = P.lbuf + moe_ws_up((size_t)T * E * 8);
   P.total = P.pbuf + moe_ws_up((size_t)U1max * P.nfs * T * H * 8);
-  P.lds = pt_lds(T, k, E, H, P.nfs, P.prep_bytes).total;
+  P.lds = pt_lds(qfmt, T, k, E, H, P.nfs, P.prep_bytes).total;
   return P;
 }
 
@@ -798,12 +820,26 @@ size_t moe_ws_stack_persistent(int T, int k, int E, int H, int F, int qfmt) {
   return pt_layout(T, k, E, H, F, qfmt, 1).total;  // independent of G
 }
 
+// LDS one workgroup may reserve (the device's opt-in limit; 64 KB if unknown)
+static size_t pt_lds_limit() {
+  static size_t lim = 0;
+  if (!lim) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeSharedMemPerBlockOptin, dev) == hipSuccess && v > 0)
+      lim = (size_t)v;
+    else
+      lim = 64 * 1024;
+  }
+  return lim;
+}
+
 bool moe_persistent_supported(int T, int k, int E, int H, int F, int qfmt) {
   if (T < 1 || T > 4 || k > MOE_MAX_K) return false;
   const PtLayout P = pt_layout(T, k, E, H, F, qfmt, 1);
-  // down rows per thread (H / 256) and router chunks (H / 512) are unrolled
-  // up to 8 and 4: H <= 2048
-  return P.lds <= 128 * 1024 && H <= 2048 && H % 256 == 0;
+  // x words per thread (T * H / 512) and router chunks (H / 512) are unrolled
+  // up to 4 * MT and 4: H <= 2048
+  return P.lds <= pt_lds_limit() && H <= 2048 && H % 256 == 0;
 }
 
 int moe_launch_decode_persistent(const float* x_in, int T, int H, int F, int E, int k, int L,

@@ -333,7 +333,7 @@ def _check_stack(li, x, xo, idx_o, w_o, hist, layers):
 
 @pytest.mark.parametrize("path", ["chain", "persistent"])
 @pytest.mark.parametrize("qfmt", [0, 1])
-@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
 def test_decode_stack_tiny(moe, qfmt, T, path):
     L = 6
     li = C.layer_case(5, T, 256, 16, 2, 128, qfmt=qfmt, bias=True, L=L, gap=False, device="cuda")
@@ -346,18 +346,28 @@ def test_decode_stack_tiny(moe, qfmt, T, path):
 @pytest.mark.parametrize("qfmt", [0, 1])
 @pytest.mark.parametrize("T", [1, 4])
 def test_decode_stack_full_shape_persistent(moe, qfmt, T):
-    """4 layers of the full shape (512 experts top-10, H=2048, F=768), the
-    persistent kernel; layers 0 and 3 checked against the oracle, and the
-    chain path must agree within tolerance on every layer."""
+    """4 layers of the full shape (512 experts top-10, H=2048, F=768): the
+    persistent kernel and the kernel chain, each checked against the oracle on
+    every layer (the oracle fed that path's own layer inputs); the two paths
+    agree on layer 0, where their inputs are identical."""
     L = 4
     li = C.layer_case(6, T, 2048, 512, 10, 768, qfmt=qfmt, bias=True, L=L, gap=False, device="cuda")
     x = li.x.contiguous()
     ws = moe.workspace(moe.MOE_OP_DECODE_STACK, "cuda", T, 10, 512, 2048, 768, qfmt)
     xo, idx_o, w_o, hist = _stack_run(moe, li, x, "persistent", ws=ws)
-    _check_stack(li, x, xo, idx_o, w_o, hist, [0, 3])
+    excluded = _check_stack(li, x, xo, idx_o, w_o, hist, range(L))
     xc, idx_c, w_c, hist_c = _stack_run(moe, li, x, "chain")
-    assert torch.equal(idx_c, idx_o)
-    C.assert_close_moe(_np(xc), _np(xo), "chain vs persistent")
+    excluded += _check_stack(li, x, xc, idx_c, w_c, hist_c, range(L))
+    assert excluded <= 2 * T * L // 4
+    # Layer 0: the same input.  The paths sum the router dot products in
+    # different orders, so two nearly equal logits may come out in either
+    # order; such a swap leaves the weight at every position equal within
+    # W_ATOL.  Any other difference in the ids is an error.
+    same = (idx_c[0] == idx_o[0]).all(-1)
+    w_close = (w_c[0] - w_o[0]).abs().amax(-1) <= W_ATOL
+    assert bool((same | w_close).all()), "layer-0 expert ids differ beyond a near-tie swap"
+    keep = (idx_c[0].sort(-1).values == idx_o[0].sort(-1).values).all(-1)
+    C.assert_close_moe(_np((hist_c[1] - x)[keep]), _np((hist[1] - x)[keep]), "layer 0: chain vs persistent")
     # repeated calls on the same workspace: new tags each call, same result
     for rep in range(3):
         xo2, idx2, _, _ = _stack_run(moe, li, x, "persistent", ws=ws)
