@@ -56,7 +56,7 @@ extern "C" size_t moe_workspace_size(int op, int T, int k, int E, int H, int F, 
     case MOE_OP_ROUTE_TOPK: return moe_ws_route(T, E);
     case MOE_OP_PERMUTE: return moe_ws_permute(T, k, E);
     case MOE_OP_EXPERT_GEMV_Q: return moe_ws_gemv(T, k, H, F, qfmt);
-    case MOE_OP_GROUPED_GEMM_Q: return moe_ws_gemm(T, k, E, F);
+    case MOE_OP_GROUPED_GEMM_Q: return moe_ws_gemm(T, k, E, H, F);
     case MOE_OP_COMBINE: return 0;
     case MOE_OP_USAGE_UPDATE: return 0;
     case MOE_OP_DECODE_STACK: return moe_ws_decode_stack(T, k, E, H, F, qfmt);

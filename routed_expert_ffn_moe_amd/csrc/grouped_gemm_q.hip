@@ -7,32 +7,40 @@
 // the work is a dense contraction per expert and runs on the matrix cores.
 //
 // Per group g (expert g < E with rows offsets[g]..offsets[g+1], or the shared
-// expert g == E with rows 0..T-1), tiles of BM = 128 rows:
+// expert g == E with rows 0..T-1): its ceil(M/32) row tiles of 32 are split as
+// evenly as possible over ceil(M/128) workgroup tiles (at most 4 row tiles
+// each, so a 160-row expert runs as 64 + 96 rows, not 128 + 128):
 //   gate/up pass: G|U = X_rows . [Wg|Wu]^T, h = fp16(silu(G) * U)  -> ws
 //   down pass:    Y   = h_rows . Wd^T (fp32)                       -> y_perm / y_shared
 // MFMA v_mfma_f32_32x32x16_f16.  Weights are dequantised in registers to
 // fp16(s*q) (int4) or fp16(s*q+m) (int2), one rounding each; x (bf16) is
-// converted to fp16 exactly when staged into LDS; accumulation is fp32.
+// converted to fp16 (exact in fp16's normal range) once, into the workspace,
+// before the gate/up pass; accumulation is fp32.
 //
-// Workgroup: 4 waves, tile 128 rows x 256 weight rows; wave w owns weight
-// rows nbase..nbase+63 = two 32-wide MFMA column tiles and all four 32-row
-// MFMA row tiles (128 fp32 accumulators per lane).  For the gate/up pass the
+// Workgroup: 4 waves, tile of up to 128 rows x 256 weight rows; wave w owns
+// weight rows nbase..nbase+63 = two 32-wide MFMA column tiles and the tile's
+// (up to four) 32-row MFMA row tiles (128 fp32 accumulators per lane); the
+// MFMAs of absent row tiles are skipped.  For the gate/up pass the
 // record interleaves gate and up rows in runs of 32, so a wave's two column
 // tiles are gate and up of the same 32 f values and SiLU*mul happens in
-// registers.  K is walked 64 at a time with the next chunk's A tile and B
-// words prefetched into registers (LDS double buffer).
+// registers.  K is walked 128 at a time with the next chunk's A tile and B
+// words prefetched into registers (LDS double buffer); the chunk is long
+// enough that its MFMA work covers the prefetch's memory latency.
 //
 // Blocks are renumbered so that consecutive work items (the column tiles of
 // one row tile, then the row tiles of one expert) land on the same XCD
 // (hardware dispatch places block b on XCD b % 8): the x rows and weights a
 // tile shares stay in that XCD's L2.
+#include <algorithm>
+
 #include "moe_common.h"
 #include "moe_sizes.h"
 
 #define GEMM_BM MOE_GEMM_BM
 #define GEMM_BN 256
-#define GEMM_KC 64
-#define GEMM_LDS_STRIDE 72  // halves per staged row (64 + 8 pad)
+#define GEMM_KC 128
+#define GEMM_NB (GEMM_KC / 32)  // int4 blocks per K chunk
+#define GEMM_LDS_STRIDE 136     // halves per staged row (128 + 8 pad)
 
 __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __restrict__ offsets, int E, int T,
                                                              int32_t* __restrict__ tile_start) {
@@ -58,60 +66,87 @@ __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __re
   for (int g = threadIdx.x; g <= G; g += 1024) tile_start[g] = g == 0 ? 0 : s[g - 1];
 }
 
+// x (bf16) -> fp16, 8 values per thread (n8 = T * H / 8)
+__global__ __launch_bounds__(256) void x_to_f16_kernel(const uint4* __restrict__ x, size_t n8, uint4* __restrict__ y) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
+    const uint4 v = x[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      half2v h = {(_Float16)__uint_as_float(w[j] << 16), (_Float16)__uint_as_float(w[j] & 0xffff0000u)};
+      o[j] = moe_half2_as_u32(h);
+    }
+    y[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 template <int QFMT>
-struct BRegs;  // raw weight words of one K chunk (64) for one lane and two column tiles
+struct BRegs;  // raw weight words of one K chunk (128) for one lane and two column tiles
 
 template <>
 struct BRegs<MOE_Q4_B32> {
-  uint2 q[2][2];   // [sub][block in chunk]: dwords 2hh, 2hh+1 of the block
-  uint32_t s[2];   // [sub]: fp16 scales of the chunk's two blocks
+  uint2 q[2][GEMM_NB];   // [sub][block in chunk]: dwords 2hh, 2hh+1 of the block
+  uint32_t s[2][2];      // [sub][block pair]: fp16 scales of blocks 2p, 2p+1
 };
 template <>
 struct BRegs<MOE_Q2_B16> {
-  uint4 q[2];      // [sub]: q-unit (4 blocks)
-  uint4 m[2];      // [sub]: meta-unit
+  uint4 q[2][2];         // [sub][unit]: q-unit (4 blocks)
+  uint4 m[2][2];         // [sub][unit]: meta-unit
 };
 
 __device__ __forceinline__ void load_b(BRegs<MOE_Q4_B32>& b, const uint8_t* rec, const MoePlanes& pl, int rows,
                                        int row0, int hh, int c, bool gu) {
-  const int64_t q_off = gu ? pl.gu_q : pl.d_q, s_off = gu ? pl.gu_s : pl.d_s;
+  // rec is wave-uniform and a record is < 4 GiB: 32-bit offsets
+  const uint32_t q_off = (uint32_t)(gu ? pl.gu_q : pl.d_q), s_off = (uint32_t)(gu ? pl.gu_s : pl.d_s);
+  const uint32_t R = (uint32_t)rows;
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
-    const int r = row0 + 32 * sub;
+    const uint32_t r = (uint32_t)(row0 + 32 * sub);
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi) {
-      const int kb = 2 * c + bi;
-      b.q[sub][bi] = *reinterpret_cast<const uint2*>(rec + q_off + 16 * ((int64_t)kb * rows + r) + 8 * hh);
+    for (int bi = 0; bi < GEMM_NB; ++bi) {
+      const uint32_t kb = (uint32_t)(GEMM_NB * c + bi);
+      b.q[sub][bi] = *reinterpret_cast<const uint2*>(rec + (q_off + 16u * (kb * R + r) + 8u * (uint32_t)hh));
     }
-    const int kb = 2 * c;
-    if (gu) {  // 4-block groups: kb even -> both scales in one 4-byte word
-      b.s[sub] = *reinterpret_cast<const uint32_t*>(rec + s_off + 2 * ((int64_t)(kb >> 2) * rows * 4 + 4 * r + (kb & 3)));
+    const uint32_t kb = (uint32_t)(GEMM_NB * c);  // a multiple of 4
+    if (gu) {  // 4-block groups: the chunk's 4 scales in one 8-byte word
+      const uint2 w = *reinterpret_cast<const uint2*>(rec + (s_off + 2u * ((kb >> 2) * R * 4u + 4u * r)));
+      b.s[sub][0] = w.x;
+      b.s[sub][1] = w.y;
     } else {   // per block [kb][row]
-      const uint32_t s0 = *reinterpret_cast<const uint16_t*>(rec + s_off + 2 * ((int64_t)kb * rows + r));
-      const uint32_t s1 = *reinterpret_cast<const uint16_t*>(rec + s_off + 2 * ((int64_t)(kb + 1) * rows + r));
-      b.s[sub] = s0 | (s1 << 16);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const uint32_t s0 = *reinterpret_cast<const uint16_t*>(rec + (s_off + 2u * ((kb + 2 * p) * R + r)));
+        const uint32_t s1 = *reinterpret_cast<const uint16_t*>(rec + (s_off + 2u * ((kb + 2 * p + 1) * R + r)));
+        b.s[sub][p] = s0 | (s1 << 16);
+      }
     }
   }
 }
 
 __device__ __forceinline__ void load_b(BRegs<MOE_Q2_B16>& b, const uint8_t* rec, const MoePlanes& pl, int rows,
                                        int row0, int hh, int c, bool gu) {
-  const int64_t q_off = gu ? pl.gu_q : pl.d_q, m_off = gu ? pl.gu_s : pl.d_s;
+  const uint32_t q_off = (uint32_t)(gu ? pl.gu_q : pl.d_q), m_off = (uint32_t)(gu ? pl.gu_s : pl.d_s);
+  const uint32_t R = (uint32_t)rows;
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
-    const int r = row0 + 32 * sub;
-    if (gu) {  // 4-block units
-      b.q[sub] = *reinterpret_cast<const uint4*>(rec + q_off + 16 * ((int64_t)c * rows + r));
-      b.m[sub] = *reinterpret_cast<const uint4*>(rec + m_off + 16 * ((int64_t)c * rows + r));
-    } else {   // per block [b][row]
-      uint32_t qw[4], mw[4];
+    const uint32_t r = (uint32_t)(row0 + 32 * sub);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        qw[j] = *reinterpret_cast<const uint32_t*>(rec + q_off + 4 * ((int64_t)(4 * c + j) * rows + r));
-        mw[j] = *reinterpret_cast<const uint32_t*>(rec + m_off + 4 * ((int64_t)(4 * c + j) * rows + r));
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t un = (uint32_t)(2 * c + u);  // 4-block unit (64 values of K)
+      if (gu) {
+        b.q[sub][u] = *reinterpret_cast<const uint4*>(rec + (q_off + 16u * (un * R + r)));
+        b.m[sub][u] = *reinterpret_cast<const uint4*>(rec + (m_off + 16u * (un * R + r)));
+      } else {   // per block [b][row]
+        uint32_t qw[4], mw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          qw[j] = *reinterpret_cast<const uint32_t*>(rec + (q_off + 4u * ((4u * un + j) * R + r)));
+          mw[j] = *reinterpret_cast<const uint32_t*>(rec + (m_off + 4u * ((4u * un + j) * R + r)));
+        }
+        b.q[sub][u] = make_uint4(qw[0], qw[1], qw[2], qw[3]);
+        b.m[sub][u] = make_uint4(mw[0], mw[1], mw[2], mw[3]);
       }
-      b.q[sub] = make_uint4(qw[0], qw[1], qw[2], qw[3]);
-      b.m[sub] = make_uint4(mw[0], mw[1], mw[2], mw[3]);
     }
   }
   (void)hh;
@@ -170,9 +205,12 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
     else hi = mid - 1;
   }
   const int g = lo;
-  const int m0 = (tile - tile_start[g]) * GEMM_BM;
   const int Mg = g < E ? offsets[g + 1] - offsets[g] : T;
-  const int mv = min(GEMM_BM, Mg - m0);
+  // this tile's share of the group's 32-row tiles (ntile = ceil(M / 128))
+  const int nrt_g = (Mg + 31) / 32, ntile = tile_start[g + 1] - tile_start[g], lt = tile - tile_start[g];
+  const int rt0 = lt * nrt_g / ntile, nrt = (lt + 1) * nrt_g / ntile - rt0;  // nrt <= 4
+  const int m0 = 32 * rt0;
+  const int mv = min(32 * nrt, Mg - m0);
   const int gbase = g < E ? offsets[g] : T * k;  // first h row of the group
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -195,38 +233,28 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
   const MoePlanes pl = moe_planes(QFMT, H, F);
   __syncthreads();
 
-  // A staging: thread -> (row st_r, 32 values at st_c)
-  const int st_r = tid >> 1, st_c = 32 * (tid & 1);
+  // A staging (fp16 rows): thread -> (row st_r, 32 values at st_c)
+  const int st_r = tid >> 1, st_c = (GEMM_KC / 2) * (tid & 1);
   const int my_arow = arow[st_r];
-  uint4 areg[4];
+  constexpr int NA = GEMM_KC / 16;  // uint4 (8 halves) per staging thread
+  uint4 areg[NA];
+  const bool st_on = st_r < 32 * nrt;  // wave-uniform: wave w stages row tile w
   auto load_a = [&](int c) {
+    if (!st_on) return;
     if (my_arow >= 0) {
       const uint4* p = reinterpret_cast<const uint4*>(a_src + (size_t)my_arow * K + c * GEMM_KC + st_c);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) areg[i] = p[i];
+      for (int i = 0; i < NA; ++i) areg[i] = p[i];
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) areg[i] = make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < NA; ++i) areg[i] = make_uint4(0, 0, 0, 0);
     }
   };
   auto store_a = [&](int stage) {
+    if (!st_on) return;
     uint4* d = reinterpret_cast<uint4*>(&As[stage][st_r * GEMM_LDS_STRIDE + st_c]);
-    if constexpr (GU) {  // bf16 -> fp16
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w[4] = {areg[i].x, areg[i].y, areg[i].z, areg[i].w};
-        uint32_t o[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          half2v h = {(_Float16)__uint_as_float(w[j] << 16), (_Float16)__uint_as_float(w[j] & 0xffff0000u)};
-          o[j] = moe_half2_as_u32(h);
-        }
-        d[i] = make_uint4(o[0], o[1], o[2], o[3]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) d[i] = areg[i];
-    }
+    for (int i = 0; i < NA; ++i) d[i] = areg[i];
   };
 
   float16v acc[4][2];
@@ -255,19 +283,20 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
       if constexpr (QFMT == MOE_Q4_B32) {
         const BRegs<MOE_Q4_B32>& B = bcur;
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi) {
+        for (int bi = 0; bi < GEMM_NB; ++bi) {
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
             half8v bf[2];
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub) {
-              const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(B.s[sub] >> (16 * bi)));
+              const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(B.s[sub][bi >> 1] >> (16 * (bi & 1))));
               const half2v s2 = {sc, sc};
               bf[sub] = deq_q4(s == 0 ? B.q[sub][bi].x : B.q[sub][bi].y, s2);
             }
             const int kk = 32 * bi + 16 * hh + 8 * s;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
+              if (i >= nrt) break;
               const half8v af = *reinterpret_cast<const half8v*>(&Ab[(32 * i + ln) * GEMM_LDS_STRIDE + kk]);
 #pragma unroll
               for (int sub = 0; sub < 2; ++sub)
@@ -278,20 +307,23 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
       } else {
         const BRegs<MOE_Q2_B16>& B = bcur;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int jj = 0; jj < 8; ++jj) {
+          const int u = jj >> 2, j = jj & 3;
           half8v bf[2];
 #pragma unroll
           for (int sub = 0; sub < 2; ++sub) {
-            const uint32_t qw = j == 0 ? B.q[sub].x : j == 1 ? B.q[sub].y : j == 2 ? B.q[sub].z : B.q[sub].w;
-            const uint32_t mw = j == 0 ? B.m[sub].x : j == 1 ? B.m[sub].y : j == 2 ? B.m[sub].z : B.m[sub].w;
+            const uint4 Q = B.q[sub][u], Mm = B.m[sub][u];
+            const uint32_t qw = j == 0 ? Q.x : j == 1 ? Q.y : j == 2 ? Q.z : Q.w;
+            const uint32_t mw = j == 0 ? Mm.x : j == 1 ? Mm.y : j == 2 ? Mm.z : Mm.w;
             const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(mw & 0xffff));
             const _Float16 mn = __builtin_bit_cast(_Float16, (uint16_t)(mw >> 16));
             const half2v s2 = {sc, sc}, m2 = {mn, mn};
             bf[sub] = deq_q2(qw, hh, s2, m2);
           }
-          const int kk = 16 * j + 8 * hh;
+          const int kk = 16 * jj + 8 * hh;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
+            if (i >= nrt) break;
             const half8v af = *reinterpret_cast<const half8v*>(&Ab[(32 * i + ln) * GEMM_LDS_STRIDE + kk]);
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub)
@@ -309,30 +341,31 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
   // epilogue: lane holds column ln, rows 8*(v/4) + 4*hh + v%4 of each 32-row tile
   if constexpr (GU) {
     const int f = 32 * (nbase / 64) + ln;
+    _Float16* hb = h_out + (size_t)(gbase + m0) * F + f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      if (i >= nrt) break;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
         if (r < mv) {
           const float gv = acc[i][0][v], uv = acc[i][1][v];
-          h_out[(size_t)(gbase + m0 + r) * F + f] = (_Float16)(moe_silu(gv) * uv);
+          hb[(uint32_t)(r * F)] = (_Float16)(moe_silu_fast(gv) * uv);
         }
       }
     }
   } else {
+    float* yb = g < E ? y_perm + (size_t)(gbase + m0) * H : y_shared + (size_t)m0 * H;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int col = nbase + 32 * sub + ln;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        if (i >= nrt) break;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (r < mv) {
-            if (g < E) y_perm[(size_t)(gbase + m0 + r) * H + col] = acc[i][sub][v];
-            else y_shared[(size_t)(m0 + r) * H + col] = acc[i][sub][v];
-          }
+          if (r < mv) yb[(uint32_t)(r * H + col)] = acc[i][sub][v];
         }
       }
     }
@@ -345,12 +378,18 @@ static int launch_gemm_t(const uint16_t* x, int T, int H, int F, const int32_t* 
                          float* y_perm, float* y_shared, void* ws, hipStream_t st) {
   int32_t* tile_start = (int32_t*)ws;
   _Float16* h = (_Float16*)((uint8_t*)ws + moe_gemm_h_offset(E));
+  uint16_t* x16 = (uint16_t*)((uint8_t*)ws + moe_gemm_x16_offset(T, k, E, F));
   gemm_schedule_kernel<<<1, 1024, 0, st>>>(offsets, E, T, tile_start);
+  {
+    const size_t n8 = (size_t)T * H / 8;
+    const int grid = (int)std::min<size_t>((n8 + 255) / 256, 4096);
+    x_to_f16_kernel<<<grid, 256, 0, st>>>((const uint4*)x, n8, (uint4*)x16);
+  }
   const int max_tiles = moe_gemm_max_tiles(T, k, E);
   {
     const int nnt = (2 * F + GEMM_BN - 1) / GEMM_BN;
     const int total = (max_tiles * nnt + 7) / 8 * 8;
-    gemm_kernel<QFMT, true><<<total, 256, 0, st>>>(x, T, H, F, k, E, row_src, offsets, tile_start, slot_table, layer,
+    gemm_kernel<QFMT, true><<<total, 256, 0, st>>>(x16, T, H, F, k, E, row_src, offsets, tile_start, slot_table, layer,
                                                    (const uint8_t*)pool, record_bytes, h, y_perm, y_shared, nnt,
                                                    total);
   }
@@ -377,7 +416,7 @@ extern "C" int moe_grouped_gemm_q(const uint16_t* x, int T, int H, int F, const 
   MOE_REQUIRE(x && row_src && offsets && y_perm && y_shared, MOE_EINVAL,
               "x, row_src, offsets, y_perm and y_shared are required");
   MOE_REQUIRE(moe_aligned(x, 16), MOE_EALIGN, "x must be 16-byte aligned");
-  const size_t need = moe_ws_gemm(T, k, E, F);
+  const size_t need = moe_ws_gemm(T, k, E, H, F);
   MOE_REQUIRE(ws && ws_bytes >= need && moe_aligned(ws, 256), MOE_EWORKSPACE,
               "ws needs %zu bytes, 256-byte aligned", need);
   hipStream_t st = moe_stream(stream);

@@ -51,6 +51,11 @@ __device__ __forceinline__ float moe_dot2(half2v a, half2v b, float c) {
 }
 
 __device__ __forceinline__ float moe_silu(float z) { return z / (1.0f + expf(-z)); }
+// SiLU with the hardware exp and reciprocal (about 1 ulp in fp32), for values
+// that are rounded to fp16 right after; z -> -inf gives -0, z -> +inf gives z.
+__device__ __forceinline__ float moe_silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // Order-preserving map of a (non-NaN) fp32 to uint32; -0 and +0 map alike.
 __device__ __forceinline__ uint32_t moe_f32_order_key(float f) {
