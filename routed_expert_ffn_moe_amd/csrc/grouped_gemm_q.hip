@@ -193,11 +193,16 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
   __shared__ __attribute__((aligned(16))) _Float16 As[2][GEMM_BM * GEMM_LDS_STRIDE];
   __shared__ int arow[GEMM_BM];
 
-  // XCD-aware renumbering (total_wg is a multiple of 8)
+  // XCD-aware renumbering: block b runs on XCD b % 8; the real work count
+  // (known only here) is cut into 8 consecutive ranges, one per XCD.  The
+  // grid (total_wg, a multiple of 8) is an upper bound; surplus blocks exit.
   const int bid = blockIdx.x;
-  const int work = (bid & 7) * (total_wg >> 3) + (bid >> 3);
+  const int nwork = tile_start[E + 1] * n_ntiles;
+  const int per_xcd = (nwork + 7) >> 3;
+  const int idx = bid >> 3;
+  const int work = (bid & 7) * per_xcd + idx;
+  if (idx >= per_xcd || work >= nwork) return;
   const int tile = work / n_ntiles, nt = work % n_ntiles;
-  if (tile >= tile_start[E + 1]) return;
   int lo = 0, hi = E;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
