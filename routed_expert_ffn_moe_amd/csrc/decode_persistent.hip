@@ -109,6 +109,27 @@ __device__ __forceinline__ float pt_q2_dot(uint32_t w, float s, float m, const u
   return fmaf(s, d - c.x, m * c.y);
 }
 
+// dot of one int4 word (8 values) with its prepared activations xp[4]
+__device__ __forceinline__ float pt_q4_word(uint32_t w, const uint32_t* xp, float c) {
+  const uint32_t w8 = w >> 8;
+  float d = 0.f;
+  d = moe_dot2(moe_u32_as_half2((w & 0x000F000Fu) | MOE_F16_1024X2), moe_u32_as_half2(xp[0]), d);
+  d = moe_dot2(moe_u32_as_half2((w & 0x00F000F0u) | MOE_F16_1024X2), moe_u32_as_half2(xp[1]), d);
+  d = moe_dot2(moe_u32_as_half2((w8 & 0x000F000Fu) | MOE_F16_1024X2), moe_u32_as_half2(xp[2]), d);
+  d = moe_dot2(moe_u32_as_half2((w8 & 0x00F000F0u) | MOE_F16_1024X2), moe_u32_as_half2(xp[3]), d);
+  return d - c;
+}
+// 8 values of an int2 block word (the low or high byte of each half, w
+// already shifted): s * (dot - c0) + m * sum(x)
+__device__ __forceinline__ float pt_q2_word(uint32_t w, float s, float m, const uint32_t* xp, float2 c) {
+  float d = 0.f;
+  d = moe_dot2(moe_u32_as_half2((w & 0x00030003u) | MOE_F16_1024X2), moe_u32_as_half2(xp[0]), d);
+  d = moe_dot2(moe_u32_as_half2((w & 0x000C000Cu) | MOE_F16_1024X2), moe_u32_as_half2(xp[1]), d);
+  d = moe_dot2(moe_u32_as_half2((w & 0x00300030u) | MOE_F16_1024X2), moe_u32_as_half2(xp[2]), d);
+  d = moe_dot2(moe_u32_as_half2((w & 0x00C000C0u) | MOE_F16_1024X2), moe_u32_as_half2(xp[3]), d);
+  return fmaf(s, d - c.x, m * c.y);
+}
+
 // Prepared block writers (same arithmetic as the standalone decode path).
 template <int QFMT>
 __device__ void pt_prep_block(const float* b, float scale, uint32_t* p, float2* corr) {
@@ -229,12 +250,12 @@ __device__ __forceinline__ void pt_topk(const float* lg, int E, int k, int* ids,
 }
 
 // Work plan of one layer from the T * k chosen experts (one wave): the
-// distinct experts in order of first occurrence (token-major), each with its
-// tokens and their top-k positions, then the shared expert with every token.
-// uslot[t * (k + 1) + j] = u * 4 + c names the unit u and token slot c that
-// produce token t's j-th expert output.  n = T * k <= 64.
-__device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, int* p_exp, int* p_ntok, int* p_tok,
-                                        int* p_j, int* uslot, int* p_misc) {
+// distinct experts ("units") in order of first occurrence (token-major), each
+// with its tokens p_tok[4u + c] and their top-k positions p_j[4u + c] (k for
+// the shared expert), then the shared expert with every token; p_roff[u] is
+// the byte offset of the unit's record in the pool.  n = T * k <= 64.
+__device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, const int32_t* slots, int64_t rbytes,
+                                        int* p_exp, int* p_ntok, int* p_tok, int* p_j, int64_t* p_roff, int* p_misc) {
   const int lane = threadIdx.x & 63, n = T * k;
   const int e = lane < n ? topi[lane] : -1 - lane;  // distinct negatives for idle lanes
   int first = lane, before = 0, total = 0;           // first lane with this expert; count before; count
@@ -255,19 +276,19 @@ __device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, in
     if (first == lane) {
       p_exp[u] = e;
       p_ntok[u] = total;
+      p_roff[u] = (int64_t)slots[e] * rbytes;
     }
     p_tok[u * 4 + before] = t;
     p_j[u * 4 + before] = j;
-    uslot[t * (k + 1) + j] = u * 4 + before;
   }
   if (lane < T) {
     p_tok[U * 4 + lane] = lane;
     p_j[U * 4 + lane] = k;
-    uslot[lane * (k + 1) + k] = U * 4 + lane;
   }
   if (lane == 0) {
     p_exp[U] = E;
     p_ntok[U] = T;
+    p_roff[U] = (int64_t)slots[E] * rbytes;
     p_misc[0] = U + 1;
   }
 }
@@ -321,12 +342,12 @@ __device__ __forceinline__ void pt_prep_word(const float* v, float scale, bool v
 
 // ---------------------------------------------------------------- LDS layout
 // Section offsets (bytes, 16-byte aligned) shared by the kernel and the host.
-// Per-half sections (red, hs, hp, hc) exist twice: the two halves of the
-// workgroup run two work units side by side.
 struct PtLds {
-  size_t xs, xprep, lg, topi, topw, p_exp, p_ntok, p_tok, p_j, p_misc, red, hp, hc, inv, hs, uslot, poff, total;
+  size_t xs, xprep, lg, topi, topw, p_exp, p_ntok, p_tok, p_j, p_roff, p_misc, red, hp, hc, inv, slots, total;
 };
-__host__ __device__ inline PtLds pt_lds(int qfmt, int T, int k, int E, int H, int nfs, size_t prep_bytes) {
+#define PT_PB_MAX 5    // pieces per batch (at most)
+#define PT_SLOTS 128   // gate/up row slots per batch (16 per piece)
+__host__ __device__ inline PtLds pt_lds(int qfmt, int T, int k, int E, int H, size_t prep_bytes) {
   PtLds o;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -335,6 +356,7 @@ __host__ __device__ inline PtLds pt_lds(int qfmt, int T, int k, int E, int H, in
     return at;
   };
   const size_t U1max = (size_t)T * k + 1;
+  (void)qfmt;
   o.xs = take((size_t)T * H * 4);
   o.xprep = take((size_t)T * prep_bytes);
   o.lg = take((size_t)T * E * 4);
@@ -344,14 +366,13 @@ __host__ __device__ inline PtLds pt_lds(int qfmt, int T, int k, int E, int H, in
   o.p_ntok = take(U1max * 4);
   o.p_tok = take(U1max * 16);
   o.p_j = take(U1max * 16);
+  o.p_roff = take(U1max * 8);
   o.p_misc = take(16);
-  o.red = take((size_t)2 * 4 * 4 * 64 * 4);  // [half][wave][token][64]
-  o.hp = take(2 * 4 * 16 * 4);                // [half][token][16]
-  o.hc = take(2 * 4 * 2 * 8);                 // [half][token][2]
+  o.red = take((size_t)PT_WAVES * PT_SLOTS * 4 * 4);  // [wave][slot][token slot] partial gate/up dots
+  o.hp = take((size_t)PT_PB_MAX * 4 * 4 * 4);         // [piece][token slot][4] prepared h words
+  o.hc = take((size_t)PT_PB_MAX * 4 * 8);             // [piece][token slot] corrections
   o.inv = take(4 * 4);
-  o.hs = take(2 * 4 * 32 * 4);                // [half][token][32]
-  o.uslot = take((size_t)T * (k + 1) * 4);
-  o.poff = take((size_t)T * (k + 1) * nfs * 4);
+  o.slots = take((size_t)(E + 1) * 4);
   o.total = off;
   return o;
 }
@@ -363,12 +384,11 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
   const int T = a.T, H = a.H, F = a.F, E = a.E, k = a.k, L = a.L, G = a.G;
   const int tid = threadIdx.x, lane = tid & 63, g = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int half = wave >> 2, hw = wave & 3, htid = tid & 255;  // two 4-wave halves
   const int blk = QFMT == MOE_Q4_B32 ? 32 : 16;
   const MoePlanes pl = moe_planes(QFMT, H, F);  // a record is < 4 GiB: 32-bit plane offsets
   const uint32_t o_guq = (uint32_t)pl.gu_q, o_gus = (uint32_t)pl.gu_s, o_dq = (uint32_t)pl.d_q, o_ds = (uint32_t)pl.d_s;
 
-  const PtLds o = pt_lds(QFMT, T, k, E, H, a.nfs, a.prep_bytes);
+  const PtLds o = pt_lds(QFMT, T, k, E, H, a.prep_bytes);
   float* xs = (float*)(smem + o.xs);          // [T][H]
   uint8_t* xprep = smem + o.xprep;            // [T][prep_bytes]
   float* lg = (float*)(smem + o.lg);          // [T][E]
@@ -378,25 +398,29 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
   int* p_ntok = (int*)(smem + o.p_ntok);      // [U1max]
   int* p_tok = (int*)(smem + o.p_tok);        // [U1max][4]
   int* p_j = (int*)(smem + o.p_j);            // [U1max][4]
+  int64_t* p_roff = (int64_t*)(smem + o.p_roff); // [U1max] record byte offsets
   int* p_misc = (int*)(smem + o.p_misc);      // [0] = U1
-  float* red = (float*)(smem + o.red);        // [2][4][4][64]
-  uint32_t* hp = (uint32_t*)(smem + o.hp);    // [2][4][16]
-  float2* hc = (float2*)(smem + o.hc);        // [2][4][2]
+  float* red = (float*)(smem + o.red);        // [wave][slot][MT]
+  uint32_t* hp = (uint32_t*)(smem + o.hp);    // [piece][MT][4]
+  float2* hc = (float2*)(smem + o.hc);        // [piece][MT]
   float* inv = (float*)(smem + o.inv);        // [4]
-  float* hs = (float*)(smem + o.hs);          // [2][4][32]
-  int* uslot = (int*)(smem + o.uslot);        // [T][k+1] -> u * 4 + i
-  uint32_t* poff = (uint32_t*)(smem + o.poff); // [T][(k+1) * nfs]
+  int* lslots = (int*)(smem + o.slots);        // [E+1] this layer's slot-table row
 
   const uint32_t call = __hip_atomic_load(a.hdr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   bool ok = true;
   const int nrch = (H + 511) / 512;  // router chunks of 512 columns per row (<= 4)
-  const int nparts = (k + 1) * a.nfs;  // partial vectors summed into one output row
 
   for (int l = 0; l < L && ok; ++l) {
     const uint32_t tag = pt_tag(call, L, l);
     // ------------------------------------------------------------ phase A
     // this wave's router row (if any) is requested before waiting for x_l
     // (indices are clamped into range so that every load is unconditional)
+    // this layer's slot-table row (E + 1 <= 1025 entries, <= 3 per thread),
+    // requested now and kept in LDS for the plan
+    int srow[3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+      srow[c] = a.slot_table[(size_t)l * (E + 1) + min(tid + PT_THREADS * c, E)];
     const uint16_t* wr = a.w_router + (size_t)l * E * H;  // wave-uniform; 32-bit offsets below
     const int e_row = g + G * wave;
     uint4 rw[4];
@@ -513,6 +537,9 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
       __builtin_amdgcn_s_sleep(2);
     }
     if (!ok) break;
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+      if (tid + PT_THREADS * c <= E) lslots[tid + PT_THREADS * c] = srow[c];
     __syncthreads();
     if (wave < T) pt_topk<SLOTS>(lg + (size_t)wave * E, E, k, topi + wave * k, topw + wave * k);
     __syncthreads();
@@ -520,197 +547,301 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
       if (a.topk_idx_out) a.topk_idx_out[(size_t)l * T * k + tid] = topi[tid];
       if (a.topk_w_out) a.topk_w_out[(size_t)l * T * k + tid] = topw[tid];
     }
-    // plan (wave 0), then the partial-offset table
+    // plan (wave 0)
+    if (wave == 0)
+      pt_plan(topi, T, k, E, lslots, a.record_bytes, p_exp, p_ntok, p_tok, p_j, p_roff, p_misc);
+    __syncthreads();
+    // ------------------------------------------------------------ work pieces
+    // The layer's expert work is cut into pieces of 8 f values: (unit u, piece
+    // p) for the units u < U1 (distinct experts, then the shared expert) and
+    // p < F/8.  Piece (u, p) = the gate and up rows of f = 8p..8p+7 over all
+    // of K, then those 8 columns of the down matrix (int4: word p%4 of the
+    // blocks in column p/4; int2: half p%2 of the words of block p/2).
+    // With one token, piece q = u * F/8 + p (a workgroup's pieces are
+    // neighbours in one expert's record); with more, q = p * U1 + u (the units
+    // interleaved, so that every workgroup gets the same mix of experts and
+    // token counts, the shared expert's included).  Workgroup g takes q in
+    // [g*Q/G, (g+1)*Q/G): every CU streams the same share of the layer's
+    // weights, in batches of PB pieces.  Row slot s
+    // of a batch (lane s % 64, s / 64-th row of the lane) is gate/up row s%16
+    // of piece s/16, its K range split over the 8 waves; the down rows of
+    // thread tid are tid + 512 c.
     {
-      if (wave == 0) pt_plan(topi, T, k, E, p_exp, p_ntok, p_tok, p_j, uslot, p_misc);
-      __syncthreads();
-      // word offset in pbuf (without the row) of partial pi = j * nfs + fs of
-      // token t: unit v = u * nfs + fs, token slot i, both from uslot
-      for (int q = tid; q < T * nparts; q += PT_THREADS) {
-        const int t = q / nparts, pi = q % nparts, j = pi / a.nfs, fs = pi % a.nfs;
-        const int us = uslot[t * (k + 1) + j];
-        poff[q] = (uint32_t)((((us >> 2) * a.nfs + fs) * T + (us & 3)) * H);
-      }
-      __syncthreads();
-    }
-    const int nunits = p_misc[0] * a.nfs;
-    // work units: half h of workgroup g takes unit base + h * G + g
-    float* hred = red + half * 4 * 4 * 64;
-    float* hhs = hs + half * 4 * 32;
-    uint32_t* hhp = hp + half * 4 * 16;
-    float2* hhc = hc + half * 4 * 2;
-    for (int base = 0; base < nunits; base += 2 * G) {
-      const int v = base + half * G + g;
-      const bool act = v < nunits;
-      const int u = act ? v / a.nfs : 0, fs = act ? v % a.nfs : 0;
-      const int ntok = __builtin_amdgcn_readfirstlane(act ? p_ntok[u] : 0);
-      const int e = __builtin_amdgcn_readfirstlane(p_exp[u]);
-      const int slot = __builtin_amdgcn_readfirstlane(a.slot_table[(size_t)l * (E + 1) + e]);
-      const uint8_t* rec = a.pool + (int64_t)slot * a.record_bytes;  // wave-uniform base; 32-bit offsets below
-      const uint8_t* xpt[MT];
+      const int U1 = p_misc[0], NP = F / 8, Q = U1 * NP;
+      const bool ilv = T > 1;  // interleaved piece order
+      auto unit_of = [&](int q) { return ilv ? q % U1 : q / NP; };
+      auto piece_of = [&](int q) { return ilv ? q / U1 : q % NP; };
+      const int q0 = (int)((int64_t)g * Q / G), q1 = (int)((int64_t)(g + 1) * Q / G);
+      constexpr int PB = MT == 1 ? 5 : 4;  // one token: one batch per layer; more: one row slot per lane
+      constexpr int NRD = 4;                   // down rows per thread (H <= 2048)
+      const int NKU = H / 128;                 // K units of 128 values
+      const int ku0 = wave * NKU / 8, ku1 = (wave + 1) * NKU / 8;  // <= 2 per wave
+      float y[NRD][MT];
 #pragma unroll
-      for (int i = 0; i < MT; ++i) xpt[i] = xprep + (size_t)p_tok[u * 4 + (i < ntok ? i : 0)] * a.prep_bytes;
-      float acc[MT];
+      for (int c = 0; c < NRD; ++c)
 #pragma unroll
-      for (int i = 0; i < MT; ++i) acc[i] = 0.f;
-      // the down block column: thread htid holds rows htid + 256 * c (the
-      // rows it multiplies later).  With one token per unit the loads are
-      // issued right after the gate/up loads (which are needed first); with
-      // more tokens after the gate/up dot products, to bound live registers.
-      // A fixed count of 8 rows (H <= 2048); rows past H repeat the last row.
-      constexpr bool down_early = MT == 1;
-      uint4 dq[8];     // int4: the row's block; int2: two words, two metas
-      uint32_t ds[8];  // int4: the row's scale
-      auto issue_down = [&]() {
+        for (int t = 0; t < MT; ++t) y[c][t] = 0.f;
+      for (int qb = q0; qb < q1; qb += PB) {
+        const int nb = min(PB, q1 - qb);
+        // ---- gate/up loads.  Row slot A of lane l: row l (all K units of the
+        // wave).  With 5 pieces, row slot B: row 64 + l % 16 over a quarter of
+        // the wave's K range (lane group l / 16), so that the 16 extra rows
+        // take few registers.  Indices are clamped: every load is unconditional.
+        const int slA = min(lane, 16 * nb - 1);
+        const int slB = min(64 + (lane & 15), 16 * nb - 1);
+        auto row_of = [&](int sl, const uint8_t*& rec, uint32_t& row, int& unit) {
+          const int q = qb + (sl >> 4), u = unit_of(q), pp = piece_of(q), i = sl & 15;
+          unit = u;
+          rec = a.pool + p_roff[u];
+          row = (uint32_t)(64 * (pp >> 2) + 8 * (pp & 3) + (i & 7) + (i >= 8 ? 32 : 0));
+        };
+        const uint8_t* recA; uint32_t rowA; int unitA;
+        row_of(slA, recA, rowA, unitA);
+        const uint8_t* recB; uint32_t rowB; int unitB;
+        row_of(slB, recB, rowB, unitB);
+        uint4 gq[2][4];  // slot A: [K unit][block (int4) or q/meta unit (int2)]
+        uint2 gs[2];     // slot A, int4: the 4 scales of each K unit
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const uint32_t rr = (uint32_t)(htid + 256 * min(c, H / 256 - 1));
+        for (int c = 0; c < 2; ++c) {
+          const uint32_t ku = (uint32_t)min(ku0 + c, NKU - 1);
           if (QFMT == MOE_Q4_B32) {
-            dq[c] = *reinterpret_cast<const uint4*>(rec + (o_dq + 16u * ((uint32_t)fs * (uint32_t)H + rr)));
-            ds[c] = *reinterpret_cast<const uint16_t*>(rec + (o_ds + 2u * ((uint32_t)fs * (uint32_t)H + rr)));
-          } else {
-            const uint32_t w0 = (2u * fs) * (uint32_t)H + rr, w1 = w0 + (uint32_t)H;
-            dq[c].x = *reinterpret_cast<const uint32_t*>(rec + (o_dq + 4u * w0));
-            dq[c].y = *reinterpret_cast<const uint32_t*>(rec + (o_dq + 4u * w1));
-            dq[c].z = *reinterpret_cast<const uint32_t*>(rec + (o_ds + 4u * w0));
-            dq[c].w = *reinterpret_cast<const uint32_t*>(rec + (o_ds + 4u * w1));
-          }
-        }
-      };
-      if (act) {
-        const int r = 64 * fs + lane;  // gate/up row
-        // wave hw takes a quarter of the K blocks, in groups of 4 blocks (the
-        // unit of the scale planes); indices are clamped so that every load
-        // is unconditional and all of them are in flight together
-        if (QFMT == MOE_Q4_B32) {
-          const int NG = H / 128, g0 = hw * NG / 4, g1 = (hw + 1) * NG / 4;  // <= 4 groups
-          uint4 q[16];
-          uint2 sc[4];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const uint32_t gg = (uint32_t)min(g0 + c, NG - 1);
-            sc[c] = *reinterpret_cast<const uint2*>(rec + (o_gus + 16u * (gg * (uint32_t)F) + 8u * (uint32_t)r));
+            gs[c] = *reinterpret_cast<const uint2*>(recA + (o_gus + 16u * ku * (uint32_t)F + 8u * rowA));
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-              q[4 * c + b] = *reinterpret_cast<const uint4*>(rec + (o_guq + 16u * ((4u * gg + b) * 2u * (uint32_t)F + (uint32_t)r)));
-          }
-          if (down_early) issue_down();
-          // with one token every use is unconditional (a group past g1 gets
-          // scale 0), so the loads stay together ahead of the first dot
-          // product and the down loads behind them stay in flight
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int gg = min(g0 + c, NG - 1);
-            const bool gv = g0 + c < g1;
-            if (MT > 1 && !gv) continue;
-            const uint32_t sw[2] = {sc[c].x, sc[c].y};
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              const int kb = 4 * gg + b;
-              const float s = gv ? moe_f16_to_f32((uint16_t)(sw[b >> 1] >> (16 * (b & 1)))) : 0.f;
-#pragma unroll
-              for (int i = 0; i < MT; ++i) {
-                if ((MT == 1 && i == 0) || i < ntok) {
-                  const float cc = ((const float2*)(xpt[i] + 2 * (size_t)H))[kb].x;
-                  acc[i] = fmaf(s, pt_q4_dot(q[4 * c + b], (const uint32_t*)xpt[i] + 16 * kb, cc), acc[i]);
-                }
-              }
-            }
-          }
-        } else {
-          const int U4 = H / 64, u0 = hw * U4 / 4, u1 = (hw + 1) * U4 / 4;  // <= 8 units
-          uint4 q[8], m[8];
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const uint32_t uu = (uint32_t)min(u0 + c, U4 - 1);
-            q[c] = *reinterpret_cast<const uint4*>(rec + (o_guq + 16u * (uu * 2u * (uint32_t)F + (uint32_t)r)));
-            m[c] = *reinterpret_cast<const uint4*>(rec + (o_gus + 16u * (uu * 2u * (uint32_t)F + (uint32_t)r)));
-          }
-          if (down_early) issue_down();
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const int uu = min(u0 + c, U4 - 1);
-            const bool uv = u0 + c < u1;  // past u1: scale and min 0
-            if (MT > 1 && !uv) continue;
-            const uint32_t qw[4] = {q[c].x, q[c].y, q[c].z, q[c].w}, mw[4] = {m[c].x, m[c].y, m[c].z, m[c].w};
-#pragma unroll
-            for (int jb = 0; jb < 4; ++jb) {
-              const int b = 4 * uu + jb;
-              const float s = uv ? moe_f16_to_f32((uint16_t)(mw[jb] & 0xffff)) : 0.f;
-              const float mm = uv ? moe_f16_to_f32((uint16_t)(mw[jb] >> 16)) : 0.f;
-#pragma unroll
-              for (int i = 0; i < MT; ++i) {
-                if ((MT == 1 && i == 0) || i < ntok) {
-                  const float2 cc = ((const float2*)(xpt[i] + 2 * (size_t)H))[b];
-                  acc[i] += pt_q2_dot(qw[jb], s, mm, (const uint32_t*)xpt[i] + 8 * b, cc);
-                }
-              }
-            }
-          }
-        }
-      }
-      if (!down_early && act) issue_down();
-#pragma unroll
-      for (int i = 0; i < MT; ++i) hred[(hw * 4 + i) * 64 + lane] = acc[i];
-      __syncthreads();
-      if (act && hw == 0) {
-        for (int i = 0; i < ntok; ++i) {
-          const float sg = ((hred[(0 * 4 + i) * 64 + lane] + hred[(1 * 4 + i) * 64 + lane]) +
-                            hred[(2 * 4 + i) * 64 + lane]) + hred[(3 * 4 + i) * 64 + lane];
-          const float up = __shfl(sg, (lane + 32) & 63, 64);
-          if (lane < 32) hhs[i * 32 + lane] = moe_silu(sg) * up;
-        }
-      }
-      __syncthreads();
-      if (act && htid < ntok * (QFMT == MOE_Q4_B32 ? 1 : 2)) {
-        const int i = QFMT == MOE_Q4_B32 ? htid : htid >> 1, b = QFMT == MOE_Q4_B32 ? 0 : htid & 1;
-        pt_prep_block<QFMT>(hhs + i * 32 + 16 * b, 1.0f, hhp + i * 16 + 8 * b, hhc + i * 2 + b);
-      }
-      __syncthreads();
-      if (act) {
-        float wgt[MT];
-#pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          wgt[i] = 1.f;
-          if (i < ntok) {
-            const int t = p_tok[u * 4 + i], j = p_j[u * 4 + i];
-            if (j < k) wgt[i] = topw[t * k + j];
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          if (c >= H / 256) break;
-          const int rr = htid + 256 * c;
-          float y[MT];
-#pragma unroll
-          for (int i = 0; i < MT; ++i) y[i] = 0.f;
-          if (QFMT == MOE_Q4_B32) {
-            const float s = moe_f16_to_f32((uint16_t)ds[c]);
-#pragma unroll
-            for (int i = 0; i < MT; ++i)
-              if (i < ntok) y[i] = s * pt_q4_dot(dq[c], hhp + i * 16, hhc[i * 2].x);
+              gq[c][b] = *reinterpret_cast<const uint4*>(recA + (o_guq + 16u * ((4u * ku + b) * 2u * (uint32_t)F + rowA)));
           } else {
-            const uint32_t wv[2] = {dq[c].x, dq[c].y}, mv[2] = {dq[c].z, dq[c].w};
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
-              const float s = moe_f16_to_f32((uint16_t)(mv[b] & 0xffff)), mm = moe_f16_to_f32((uint16_t)(mv[b] >> 16));
-#pragma unroll
-              for (int i = 0; i < MT; ++i)
-                if (i < ntok) y[i] += pt_q2_dot(wv[b], s, mm, hhp + i * 16 + 8 * b, hhc[i * 2 + b]);
+              const uint32_t un = 2u * ku + b;  // 4-block unit of 64 values
+              gq[c][b] = *reinterpret_cast<const uint4*>(recA + (o_guq + 16u * (un * 2u * (uint32_t)F + rowA)));
+              gq[c][2 + b] = *reinterpret_cast<const uint4*>(recA + (o_gus + 16u * (un * 2u * (uint32_t)F + rowA)));
             }
           }
+        }
+        // slot B: K unit ku0 + (lq >> 1), half (lq & 1) of it; int4: 2 blocks
+        // and their scales (one word), int2: one q-unit and its meta-unit
+        const int lq = lane >> 4;
+        const int kuB = min(ku0 + (lq >> 1), NKU - 1);
+        const bool kvB = PB == 5 && ku0 + (lq >> 1) < ku1;
+        uint4 gqB[2];
+        uint32_t gsB = 0u;
+        if (PB == 5) {
+          if (QFMT == MOE_Q4_B32) {
+            const uint32_t kb0 = 4u * kuB + 2u * (lq & 1);
+            gsB = *reinterpret_cast<const uint32_t*>(recB + (o_gus + 16u * (uint32_t)kuB * (uint32_t)F + 8u * rowB + 4u * (lq & 1)));
 #pragma unroll
-          for (int i = 0; i < MT; ++i)
-            if (i < ntok) pt_put(pt_at(a.pbuf, (uint32_t)((v * T + i) * H + rr)), tag, y[i] * wgt[i]);
+            for (int b = 0; b < 2; ++b)
+              gqB[b] = *reinterpret_cast<const uint4*>(recB + (o_guq + 16u * ((kb0 + b) * 2u * (uint32_t)F + rowB)));
+          } else {
+            const uint32_t un = 2u * kuB + (lq & 1);
+            gqB[0] = *reinterpret_cast<const uint4*>(recB + (o_guq + 16u * (un * 2u * (uint32_t)F + rowB)));
+            gqB[1] = *reinterpret_cast<const uint4*>(recB + (o_gus + 16u * (un * 2u * (uint32_t)F + rowB)));
+          }
+        }
+        // ---- down loads (one token per unit: right behind the gate/up loads)
+        uint32_t dw[NRD][PB], dm[NRD][PB];  // word (int4) or block word (int2); scale (int4) or meta (int2)
+        auto load_down = [&]() {
+#pragma unroll
+          for (int pi = 0; pi < PB; ++pi) {
+            const int q = qb + min(pi, nb - 1), u = unit_of(q), pp = piece_of(q);
+            const uint8_t* rec = a.pool + p_roff[u];  // uniform over the workgroup
+#pragma unroll
+            for (int c = 0; c < NRD; ++c) {
+              const uint32_t r = (uint32_t)min(tid + 512 * c, H - 1);
+              if (QFMT == MOE_Q4_B32) {
+                const uint32_t bc = (uint32_t)(pp >> 2);
+                dw[c][pi] = *reinterpret_cast<const uint32_t*>(rec + (o_dq + 16u * (bc * (uint32_t)H + r) + 4u * (pp & 3)));
+                dm[c][pi] = *reinterpret_cast<const uint16_t*>(rec + (o_ds + 2u * (bc * (uint32_t)H + r)));
+              } else {
+                const uint32_t b2 = (uint32_t)(pp >> 1);
+                dw[c][pi] = *reinterpret_cast<const uint32_t*>(rec + (o_dq + 4u * (b2 * (uint32_t)H + r)));
+                dm[c][pi] = *reinterpret_cast<const uint32_t*>(rec + (o_ds + 4u * (b2 * (uint32_t)H + r)));
+              }
+            }
+          }
+        };
+        if (MT == 1) load_down();
+        __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any dot product
+        // ---- gate/up partial dots over this wave's K units
+        auto xp_of = [&](int u, int t) -> const uint8_t* {
+          return xprep + (size_t)(MT == 1 ? 0 : p_tok[u * 4 + t]) * a.prep_bytes;
+        };
+        {
+          const int ntok = MT == 1 ? 1 : p_ntok[unitA];
+          float acc[MT];
+#pragma unroll
+          for (int t = 0; t < MT; ++t) acc[t] = 0.f;
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int kuc = min(ku0 + c, NKU - 1);
+            const bool kv = ku0 + c < ku1;
+            if (QFMT == MOE_Q4_B32) {
+              const uint32_t sw[2] = {gs[c].x, gs[c].y};
+#pragma unroll
+              for (int b = 0; b < 4; ++b) {
+                const int kb = 4 * kuc + b;
+                const float sc = kv ? moe_f16_to_f32((uint16_t)(sw[b >> 1] >> (16 * (b & 1)))) : 0.f;
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                  if (MT == 1 || t < ntok) {
+                    const uint8_t* xp = xp_of(unitA, t);
+                    const float cc = ((const float2*)(xp + 2 * (size_t)H))[kb].x;
+                    acc[t] = fmaf(sc, pt_q4_dot(gq[c][b], (const uint32_t*)xp + 16 * kb, cc), acc[t]);
+                  }
+                }
+              }
+            } else {
+#pragma unroll
+              for (int b = 0; b < 2; ++b) {
+                const uint4 Qw = gq[c][b], Mw = gq[c][2 + b];
+                const uint32_t qw[4] = {Qw.x, Qw.y, Qw.z, Qw.w}, mw[4] = {Mw.x, Mw.y, Mw.z, Mw.w};
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) {
+                  const int bl = 4 * (2 * kuc + b) + jb;  // block of 16 values
+                  const float sc = kv ? moe_f16_to_f32((uint16_t)(mw[jb] & 0xffff)) : 0.f;
+                  const float mn = kv ? moe_f16_to_f32((uint16_t)(mw[jb] >> 16)) : 0.f;
+#pragma unroll
+                  for (int t = 0; t < MT; ++t) {
+                    if (MT == 1 || t < ntok) {
+                      const uint8_t* xp = xp_of(unitA, t);
+                      const float2 cc = ((const float2*)(xp + 2 * (size_t)H))[bl];
+                      acc[t] += pt_q2_dot(qw[jb], sc, mn, (const uint32_t*)xp + 8 * bl, cc);
+                    }
+                  }
+                }
+              }
+            }
+          }
+          // written by every lane (slots past 16 * nb are never read): a
+          // conditional use would let the compiler sink the loads behind it
+#pragma unroll
+          for (int t = 0; t < MT; ++t) red[(wave * PT_SLOTS + lane) * MT + t] = acc[t];
+        }
+        if (PB == 5) {  // slot B (one token per unit): 4 lane groups, summed with shuffles
+          float accB = 0.f;
+          if (QFMT == MOE_Q4_B32) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+              const int kb = 4 * kuB + 2 * (lq & 1) + b;
+              const float sc = kvB ? moe_f16_to_f32((uint16_t)(gsB >> (16 * b))) : 0.f;
+              const uint8_t* xp = xp_of(unitB, 0);
+              const float cc = ((const float2*)(xp + 2 * (size_t)H))[kb].x;
+              accB = fmaf(sc, pt_q4_dot(gqB[b], (const uint32_t*)xp + 16 * kb, cc), accB);
+            }
+          } else {
+            const uint32_t qw[4] = {gqB[0].x, gqB[0].y, gqB[0].z, gqB[0].w};
+            const uint32_t mw[4] = {gqB[1].x, gqB[1].y, gqB[1].z, gqB[1].w};
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+              const int bl = 4 * (2 * kuB + (lq & 1)) + jb;
+              const float sc = kvB ? moe_f16_to_f32((uint16_t)(mw[jb] & 0xffff)) : 0.f;
+              const float mn = kvB ? moe_f16_to_f32((uint16_t)(mw[jb] >> 16)) : 0.f;
+              const uint8_t* xp = xp_of(unitB, 0);
+              const float2 cc = ((const float2*)(xp + 2 * (size_t)H))[bl];
+              accB += pt_q2_dot(qw[jb], sc, mn, (const uint32_t*)xp + 8 * bl, cc);
+            }
+          }
+          accB += __shfl_xor(accB, 16, 64);
+          accB += __shfl_xor(accB, 32, 64);
+          red[(wave * PT_SLOTS + 64 + (lane & 15)) * MT] = accB;  // the 4 lane groups hold the same sum
+        }
+        if (MT > 1) load_down();
+        __syncthreads();
+        // ---- h = silu(gate) * up, 8 threads per (piece, token slot), then the
+        // prepared word of the 8 h values for the down dots
+        {
+          const int item = tid >> 3, fi = tid & 7;  // item = pi * MT + t
+          const int pi = item / MT, t = item % MT;
+          const bool iv = pi < nb;
+          float hv = 0.f;
+          if (iv) {
+            float sg = 0.f, su = 0.f;
+#pragma unroll
+            for (int w = 0; w < PT_WAVES; ++w) {
+              sg += red[(w * PT_SLOTS + 16 * pi + fi) * MT + t];
+              su += red[(w * PT_SLOTS + 16 * pi + 8 + fi) * MT + t];
+            }
+            hv = moe_silu(sg) * su;
+          }
+          const float hn = __shfl_xor(hv, 1, 64);  // partner value of the pair
+          const int pk = fi >> 1;                   // pair index within the word
+          float c0 = 0.f, c1 = 0.f;
+          uint32_t pw = 0u;
+          if ((fi & 1) == 0) {
+            if (QFMT == MOE_Q4_B32) {
+              const float mul = (pk & 1) ? 0.0625f : 1.f;
+              const half2v a2 = {(_Float16)(hv * mul), (_Float16)(hn * mul)};
+              const half2v kk = {(_Float16)((pk & 1) ? 1152.f : 1032.f), (_Float16)((pk & 1) ? 1152.f : 1032.f)};
+              pw = moe_half2_as_u32(a2);
+              c0 = moe_dot2(a2, kk, 0.f);
+            } else {
+              const float mul = pk == 0 ? 1.f : pk == 1 ? 0.25f : pk == 2 ? 0.0625f : 0.015625f;
+              const half2v a2 = {(_Float16)(hv * mul), (_Float16)(hn * mul)};
+              const half2v k1024 = {(_Float16)1024.f, (_Float16)1024.f};
+              const half2v kc = {(_Float16)(1.f / mul), (_Float16)(1.f / mul)};
+              pw = moe_half2_as_u32(a2);
+              c0 = moe_dot2(a2, k1024, 0.f);
+              c1 = moe_dot2(a2, kc, 0.f);
+            }
+          }
+          // corrections summed over the 4 pairs (lanes fi = 0, 2, 4, 6 of the item)
+          c0 += __shfl_xor(c0, 2, 64);
+          c0 += __shfl_xor(c0, 4, 64);
+          c1 += __shfl_xor(c1, 2, 64);
+          c1 += __shfl_xor(c1, 4, 64);
+          if (iv && item < PB * MT) {
+            if ((fi & 1) == 0) hp[item * 4 + pk] = pw;
+            if (fi == 0) hc[item] = make_float2(c0, c1);
+          }
+        }
+        __syncthreads();
+        // ---- down dots: rows tid + 512 c, every piece of the batch
+#pragma unroll
+        for (int pi = 0; pi < PB; ++pi) {
+          if (pi >= nb) break;
+          const int q = qb + pi, u = unit_of(q), pp = piece_of(q);
+          const int ntok = MT == 1 ? 1 : p_ntok[u];
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            if (MT > 1 && t >= ntok) break;
+            const int tk = MT == 1 ? 0 : p_tok[u * 4 + t], jj = p_j[u * 4 + t];
+            const float wgt = jj < k ? topw[tk * k + jj] : 1.f;
+            const uint32_t* hw4 = hp + (pi * MT + t) * 4;
+            const float2 cc = hc[pi * MT + t];
+#pragma unroll
+            for (int c = 0; c < NRD; ++c) {
+              float v;
+              if (QFMT == MOE_Q4_B32) {
+                v = moe_f16_to_f32((uint16_t)dm[c][pi]) * pt_q4_word(dw[c][pi], hw4, cc.x);
+              } else {
+                const uint32_t w = dw[c][pi] >> (8 * (pp & 1));
+                v = pt_q2_word(w, moe_f16_to_f32((uint16_t)(dm[c][pi] & 0xffff)),
+                               moe_f16_to_f32((uint16_t)(dm[c][pi] >> 16)), hw4, cc);
+              }
+#pragma unroll
+              for (int tt = 0; tt < MT; ++tt)
+                if (tt == tk) y[c][tt] = fmaf(wgt, v, y[c][tt]);
+            }
+          }
+        }
+        __syncthreads();  // red, hp, hc are reused by the next batch
+      }
+      // this workgroup's partial output, one vector per token
+#pragma unroll
+      for (int c = 0; c < NRD; ++c) {
+        const int r = tid + 512 * c;
+        if (r < H) {
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+            if (t < T) pt_put(pt_at(a.pbuf, (uint32_t)((g * T + t) * H + r)), tag, y[c][t]);
         }
       }
-      __syncthreads();
     }
     // ------------------------------------------------------------ phase C
     {
       // outputs (t, r) for r in this workgroup's rows; TPO threads per output,
-      // thread `sub` summing partials sub, sub + TPO, ... in order, then a
-      // butterfly over the TPO lanes (a fixed order for a given T)
+      // thread `sub` summing the partials of workgroups sub, sub + TPO, ... in
+      // order, then a butterfly over the TPO lanes (a fixed order for a given T)
       const int r0 = g * a.rpw;
       const int nout = T * a.rpw;
       const int tpo = a.tpo;
@@ -719,19 +850,19 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         const int oo = ob + tid / tpo, sub = tid % tpo;
         const bool act = oo < nout;
         const int t = act ? oo / a.rpw : 0, rr = act ? r0 + oo % a.rpw : r0;
-        const uint32_t* po = poff + t * nparts;
         float sum = 0.f;
         for (int it = 0;; ++it) {
           bool mine = true;
           float sacc = 0.f;
-          for (int p0 = sub; p0 < nparts; p0 += tpo * NQ) {
+          for (int p0 = sub; p0 < G; p0 += tpo * NQ) {
             u64 w[NQ];
 #pragma unroll
-            for (int q = 0; q < NQ; ++q) w[q] = pt_load(a.pbuf, po[min(p0 + tpo * q, nparts - 1)] + (uint32_t)rr);
+            for (int qq = 0; qq < NQ; ++qq)
+              w[qq] = pt_load(a.pbuf, (uint32_t)((min(p0 + tpo * qq, G - 1) * T + t) * H + rr));
 #pragma unroll
-            for (int q = 0; q < NQ; ++q) {
-              if (p0 + tpo * q < nparts) {
-                if ((uint32_t)(w[q] >> 32) == tag) sacc += __uint_as_float((uint32_t)w[q]);
+            for (int qq = 0; qq < NQ; ++qq) {
+              if (p0 + tpo * qq < G) {
+                if ((uint32_t)(w[qq] >> 32) == tag) sacc += __uint_as_float((uint32_t)w[qq]);
                 else mine = false;
               }
             }
@@ -811,13 +942,13 @@ static PtLayout pt_layout(int T, int k, int E, int H, int F, int qfmt, int G) {
   P.xbuf = 256;
   P.lbuf = P.xbuf + moe_ws_up((size_t)T * H * 8);
   P.pbuf = P.lbuf + moe_ws_up((size_t)T * E * 8);
-  P.total = P.pbuf + moe_ws_up((size_t)U1max * P.nfs * T * H * 8);
-  P.lds = pt_lds(qfmt, T, k, E, H, P.nfs, P.prep_bytes).total;
+  P.total = P.pbuf + moe_ws_up((size_t)G * T * H * 8);  // one partial vector per (workgroup, token)
+  P.lds = pt_lds(qfmt, T, k, E, H, P.prep_bytes).total;
   return P;
 }
 
 size_t moe_ws_stack_persistent(int T, int k, int E, int H, int F, int qfmt) {
-  return pt_layout(T, k, E, H, F, qfmt, 1).total;  // independent of G
+  return pt_layout(T, k, E, H, F, qfmt, pt_grid(H, E)).total;
 }
 
 // LDS one workgroup may reserve (the device's opt-in limit; 64 KB if unknown)
@@ -836,10 +967,11 @@ static size_t pt_lds_limit() {
 
 bool moe_persistent_supported(int T, int k, int E, int H, int F, int qfmt) {
   if (T < 1 || T > 4 || k > MOE_MAX_K) return false;
-  const PtLayout P = pt_layout(T, k, E, H, F, qfmt, 1);
-  // x words per thread (T * H / 512) and router chunks (H / 512) are unrolled
-  // up to 4 * MT and 4: H <= 2048
-  return P.lds <= pt_lds_limit() && H <= 2048 && H % 256 == 0;
+  const PtLayout P = pt_layout(T, k, E, H, F, qfmt, pt_grid(H, E));
+  // x words per thread (T * H / 512), router chunks (H / 512) and down rows
+  // per thread (H / 512) are unrolled up to 4 * MT, 4 and 4; gate/up K units
+  // of 128 per wave up to 2: 256 <= H <= 2048
+  return P.lds <= pt_lds_limit() && H <= 2048 && H % 256 == 0 && T * k <= 64;
 }
 
 int moe_launch_decode_persistent(const float* x_in, int T, int H, int F, int E, int k, int L,
