@@ -231,6 +231,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the verify and prefill measurements")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--copy-ref-mb", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (the reference kernel that scales "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -244,6 +247,16 @@ def main():
     M.load(build_if_missing=True)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.copy_ref_mb > 0:
+        n = args.copy_ref_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy reference: {args.copy_ref_mb} MiB read, {args.copy_ref_mb} MiB written")
+        del src, dst
 
     L, E, H, F, k = 48, 512, 2048, 768, 10
     t0 = time.perf_counter()

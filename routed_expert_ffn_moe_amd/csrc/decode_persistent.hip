@@ -75,6 +75,21 @@ __device__ __forceinline__ u64* pt_at(u64* base, uint32_t i) {
 __device__ __forceinline__ u64 pt_load(u64* base, uint32_t i) {
   return __hip_atomic_load(pt_at(base, i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Waits until word base[first + g * stride] carries `tag` for every g < n
+// (one word per producing workgroup), polling 4 bytes of tag per producer
+// instead of all of its data.  The data itself is read and every tag checked
+// afterwards, so this only shortens the busy polling.  Returns false on
+// timeout.  Called by the whole workgroup.
+__device__ bool pt_wait_sentinels(u64* base, uint32_t first, uint32_t stride, int n, uint32_t tag, int spin_max) {
+  for (int it = 0;; ++it) {
+    bool mine = true;
+    for (int i = threadIdx.x; i < n; i += blockDim.x)
+      mine &= (uint32_t)(pt_load(base, first + (uint32_t)i * stride) >> 32) == tag;
+    if (__syncthreads_and(mine)) return true;
+    if (it > spin_max) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
 __device__ __forceinline__ uint32_t pt_tag(uint32_t call, int L, int l) {
   return (uint32_t)(((uint64_t)call * (uint64_t)L + (uint64_t)l) % 0xFFFFFFFFull) + 1u;
 }
@@ -437,6 +452,10 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     } else {
       const uint32_t ptag = pt_tag(call, L, l - 1);
       const int last = T * H - 1;
+      if (!pt_wait_sentinels(a.xbuf, (uint32_t)((T - 1) * H + a.rpw - 1), (uint32_t)a.rpw, G, ptag, PT_SPIN_MAX)) {
+        ok = false;
+        break;
+      }
       for (int it = 0;; ++it) {
         u64 w[NX];
 #pragma unroll
@@ -846,6 +865,11 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
       const int nout = T * a.rpw;
       const int tpo = a.tpo;
       constexpr int NQ = MT == 1 ? 8 : MT == 2 ? 12 : 24;
+      if (!pt_wait_sentinels(a.pbuf, (uint32_t)((T - 1) * H + r0 + a.rpw - 1), (uint32_t)(T * H), G, tag,
+                             PT_SPIN_MAX)) {
+        ok = false;
+        break;
+      }
       for (int ob = 0; ob < nout && ok; ob += PT_THREADS / tpo) {
         const int oo = ob + tid / tpo, sub = tid % tpo;
         const bool act = oo < nout;
