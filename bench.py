@@ -286,7 +286,7 @@ def main():
                    "launch": "hip-graph replay per step" if not args.no_graph else "eager"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "whole decode step (router + top-k + expert GEMV + combine, 48 layers)",
+                     "kernel": "decode_persistent_kernel: one launch = one 48-layer step (router, top-k, experts, sum)",
                      "algorithmic_bytes_per_step": round(bytes_per_step)},
     }
     if not args.no_extra:
