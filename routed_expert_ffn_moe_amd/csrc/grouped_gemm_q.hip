@@ -42,8 +42,12 @@
 #define GEMM_NB (GEMM_KC / 32)  // int4 blocks per K chunk
 #define GEMM_LDS_STRIDE 136     // halves per staged row (128 + 8 pad)
 
+// tile_start[g] = first tile of group g (exclusive scan of ceil(M_g / BM));
+// tile_info[t] = {group, first row m0, rows, first h row of the group}: the
+// group's 32-row tiles split as evenly as possible over its BM-row tiles.
 __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __restrict__ offsets, int E, int T,
-                                                             int32_t* __restrict__ tile_start) {
+                                                             int k, int32_t* __restrict__ tile_start,
+                                                             int4* __restrict__ tile_info) {
   __shared__ int s[2048];
   const int G = E + 1;
   for (int g = threadIdx.x; g < 2048; g += 1024) {
@@ -64,6 +68,17 @@ __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __re
     __syncthreads();
   }
   for (int g = threadIdx.x; g <= G; g += 1024) tile_start[g] = g == 0 ? 0 : s[g - 1];
+  for (int g = threadIdx.x; g < G; g += 1024) {
+    const int t0 = g == 0 ? 0 : s[g - 1], n = s[g] - t0;
+    const int Mg = g < E ? offsets[g + 1] - offsets[g] : T;
+    const int gbase = g < E ? offsets[g] : T * k;
+    const int nrt_g = (Mg + 31) / 32;
+    for (int lt = 0; lt < n; ++lt) {
+      const int rt0 = lt * nrt_g / n, nrt = (lt + 1) * nrt_g / n - rt0;
+      const int m0 = 32 * rt0;
+      tile_info[t0 + lt] = make_int4(g, m0, min(32 * nrt, Mg - m0), gbase);
+    }
+  }
 }
 
 // x (bf16) -> fp16, 8 values per thread (n8 = T * H / 8)
@@ -186,6 +201,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
                                                       int E, const int32_t* __restrict__ row_src,
                                                       const int32_t* __restrict__ offsets,
                                                       const int32_t* __restrict__ tile_start,
+                                                      const int4* __restrict__ tile_info,
                                                       const int32_t* __restrict__ slot_table, int layer,
                                                       const uint8_t* __restrict__ pool, int64_t record_bytes,
                                                       _Float16* __restrict__ h_out, float* __restrict__ y_perm,
@@ -203,20 +219,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
   const int work = (bid & 7) * per_xcd + idx;
   if (idx >= per_xcd || work >= nwork) return;
   const int tile = work / n_ntiles, nt = work % n_ntiles;
-  int lo = 0, hi = E;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tile_start[mid] <= tile) lo = mid;
-    else hi = mid - 1;
-  }
-  const int g = lo;
-  const int Mg = g < E ? offsets[g + 1] - offsets[g] : T;
-  // this tile's share of the group's 32-row tiles (ntile = ceil(M / 128))
-  const int nrt_g = (Mg + 31) / 32, ntile = tile_start[g + 1] - tile_start[g], lt = tile - tile_start[g];
-  const int rt0 = lt * nrt_g / ntile, nrt = (lt + 1) * nrt_g / ntile - rt0;  // nrt <= 4
-  const int m0 = 32 * rt0;
-  const int mv = min(32 * nrt, Mg - m0);
-  const int gbase = g < E ? offsets[g] : T * k;  // first h row of the group
+  const int4 ti = tile_info[tile];
+  const int g = ti.x, m0 = ti.y, mv = ti.z, gbase = ti.w;  // gbase: first h row of the group
+  const int nrt = (mv + 31) / 32;                           // row tiles present (<= 4)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, ln = lane & 31;
@@ -382,9 +387,10 @@ static int launch_gemm_t(const uint16_t* x, int T, int H, int F, const int32_t* 
                          int k, int E, const int32_t* slot_table, int layer, const void* pool, int64_t record_bytes,
                          float* y_perm, float* y_shared, void* ws, hipStream_t st) {
   int32_t* tile_start = (int32_t*)ws;
-  _Float16* h = (_Float16*)((uint8_t*)ws + moe_gemm_h_offset(E));
+  int4* tile_info = (int4*)((uint8_t*)ws + moe_gemm_info_offset(E));
+  _Float16* h = (_Float16*)((uint8_t*)ws + moe_gemm_h_offset(T, k, E));
   uint16_t* x16 = (uint16_t*)((uint8_t*)ws + moe_gemm_x16_offset(T, k, E, F));
-  gemm_schedule_kernel<<<1, 1024, 0, st>>>(offsets, E, T, tile_start);
+  gemm_schedule_kernel<<<1, 1024, 0, st>>>(offsets, E, T, k, tile_start, tile_info);
   {
     const size_t n8 = (size_t)T * H / 8;
     const int grid = (int)std::min<size_t>((n8 + 255) / 256, 4096);
@@ -394,7 +400,7 @@ static int launch_gemm_t(const uint16_t* x, int T, int H, int F, const int32_t* 
   {
     const int nnt = (2 * F + GEMM_BN - 1) / GEMM_BN;
     const int total = (max_tiles * nnt + 7) / 8 * 8;
-    gemm_kernel<QFMT, true><<<total, 256, 0, st>>>(x16, T, H, F, k, E, row_src, offsets, tile_start, slot_table, layer,
+    gemm_kernel<QFMT, true><<<total, 256, 0, st>>>(x16, T, H, F, k, E, row_src, offsets, tile_start, tile_info, slot_table, layer,
                                                    (const uint8_t*)pool, record_bytes, h, y_perm, y_shared, nnt,
                                                    total);
   }
@@ -402,7 +408,7 @@ static int launch_gemm_t(const uint16_t* x, int T, int H, int F, const int32_t* 
     const int nnt = (H + GEMM_BN - 1) / GEMM_BN;
     const int total = (max_tiles * nnt + 7) / 8 * 8;
     gemm_kernel<QFMT, false><<<total, 256, 0, st>>>((const uint16_t*)h, T, H, F, k, E, row_src, offsets, tile_start,
-                                                    slot_table, layer, (const uint8_t*)pool, record_bytes, h, y_perm,
+                                                    tile_info, slot_table, layer, (const uint8_t*)pool, record_bytes, h, y_perm,
                                                     y_shared, nnt, total);
   }
   return moe_check_launch("grouped gemm");

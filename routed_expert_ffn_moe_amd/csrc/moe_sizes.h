@@ -59,10 +59,14 @@ static inline size_t moe_ws_gemv(int T, int k, int H, int F, int qfmt) {
 static inline int moe_gemm_max_tiles(int T, int k, int E) {
   return (int)(((int64_t)T * k) / MOE_GEMM_BM + E + ((int64_t)T + MOE_GEMM_BM - 1) / MOE_GEMM_BM + 1);
 }
-static inline size_t moe_gemm_h_offset(int E) { return moe_ws_up((size_t)(E + 2) * 4); }
+// grouped GEMM workspace: tile_start [E+2] int32, tile_info [max_tiles] int4,
+static inline size_t moe_gemm_info_offset(int E) { return moe_ws_up((size_t)(E + 2) * 4); }
+static inline size_t moe_gemm_h_offset(int T, int k, int E) {
+  return moe_gemm_info_offset(E) + moe_ws_up((size_t)moe_gemm_max_tiles(T, k, E) * 16);
+}
 // then h (fp16) [T*k + T][F], then x converted to fp16 [T][H]
 static inline size_t moe_gemm_x16_offset(int T, int k, int E, int F) {
-  return moe_gemm_h_offset(E) + moe_ws_up(((size_t)T * k + T) * F * 2);
+  return moe_gemm_h_offset(T, k, E) + moe_ws_up(((size_t)T * k + T) * F * 2);
 }
 static inline size_t moe_ws_gemm(int T, int k, int E, int H, int F) {
   return moe_gemm_x16_offset(T, k, E, F) + moe_ws_up((size_t)T * H * 2);
