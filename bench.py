@@ -35,23 +35,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash():
+# the sources that make up the persistent decode kernel
+DECODE_SOURCES = ("decode_persistent.hip", "moe_common.h", "moe_kernels.h")
+
+
+def source_hash(files=DECODE_SOURCES):
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "routed_expert_ffn_moe_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
+    for name in files:
+        with open(os.path.join(ROOT, "routed_expert_ffn_moe_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel_tag, per_launch_units):
     """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
-    taken on the current kernel sources; else None."""
+    taken on the current sources of that kernel; else None."""
     p = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         d = json.load(f)
-    if d.get("source_hash") != source_hash():
+    if d.get("source_hash") != source_hash(tuple(d.get("source_files", DECODE_SOURCES))):
         return None
     return d.get("bytes_per_" + per_launch_units)
 

@@ -255,6 +255,30 @@ def test_grouped_gemm_full_size_sampled(moe):
     C.assert_close_moe(rows, rparts[:, :k], "routed rows (sampled)")
 
 
+def test_grouped_gemm_int2_16k_chunk_sampled(moe):
+    """16,384-token chunk through one int2 layer (blocks of 16 with fp16 scale
+    and min) under the Zipf routing bias, so expert loads are skewed (about
+    320 rows each on average, some far more, possibly none): routing and
+    permutation exact on every token, outputs checked on sampled tokens."""
+    T, H, E, k, F = 16384, 2048, 512, 10, 768
+    li = C.layer_case(4, T, H, E, k, F, qfmt=1, bias=True, x_bf16=True, device="cuda")
+    idx, w, counts, inv_row, y_perm, y_sh, y = _prefill_layer(moe, li, li.x)
+    xf = C.x_as_f64(li.x)
+    b = li.bias[0].cpu().double().numpy()
+    ref_i, ref_w = O.topk_select(O.router_logits(xf, C.router_f64(li.Wr[0]), b), k)
+    _check_routing(idx, w, ref_i, ref_w)
+    rc, ro, rs, ri = O.permute(ref_i, E)
+    assert np.array_equal(_np(counts), rc) and np.array_equal(_np(inv_row), ri)
+    assert rc.max() > 2 * rc.mean()  # the bias skews the groups
+    sample = np.random.default_rng(1).choice(T, size=12, replace=False)
+    sample = np.concatenate([[0, T - 1], sample])
+    ry, ri2, rw2, rparts, _ = C.oracle_layer(li, tokens=sample)
+    C.assert_close_moe(_np(y)[sample], ry, "y (sampled)")
+    rows = _np(y_perm)[_np(inv_row).reshape(T, k)[sample]]
+    C.assert_close_moe(rows, rparts[:, :k], "routed rows (sampled)")
+    C.assert_close_moe(_np(y_sh)[sample], rparts[:, k], "shared (sampled)")
+
+
 # ---------------------------------------------------------------- usage
 
 def test_usage_update_steps(moe):
@@ -324,7 +348,8 @@ def _check_stack(li, x, xo, idx_o, w_o, hist, layers):
         ok = O.gap_ok(rl, li.k, C.MIN_GAP)
         excluded += int((~ok).sum())
         assert np.array_equal(_np(idx_o[l])[ok], ri[ok])
-        assert np.max(np.abs(_np(w_o[l])[ok] - rw[ok])) <= W_ATOL
+        if ok.any():
+            assert np.max(np.abs(_np(w_o[l])[ok] - rw[ok])) <= W_ATOL
         nxt = hist[l + 1] if l + 1 < L else xo
         if ok.all():
             C.assert_close_moe(_np(nxt - hist[l]), ry, f"layer {l}")
@@ -372,6 +397,19 @@ def test_decode_stack_full_shape_persistent(moe, qfmt, T):
     for rep in range(3):
         xo2, idx2, _, _ = _stack_run(moe, li, x, "persistent", ws=ws)
         assert torch.equal(xo2, xo) and torch.equal(idx2, idx_o)
+
+
+def test_decode_stack_48_layers(moe):
+    """The whole 48-layer int4 stack (65 GB pool, Zipf routing bias), one
+    token, the persistent kernel: every layer input finite, and layers 0, 16,
+    32 and 47 checked against the oracle on the kernel's own layer inputs."""
+    L = 48
+    li = C.layer_case(2, 1, 2048, 512, 10, 768, qfmt=0, bias=True, L=L, device="cuda")
+    x = li.x.contiguous()
+    xo, idx_o, w_o, hist = _stack_run(moe, li, x, "persistent")
+    assert bool(torch.isfinite(hist).all()) and bool(torch.isfinite(xo).all())
+    excluded = _check_stack(li, x, xo, idx_o, w_o, hist, [0, 16, 32, 47])
+    assert excluded <= 2  # layer 0 is gap-filtered; later layers may hold a near tie
 
 
 # ---------------------------------------------------------------- generator
