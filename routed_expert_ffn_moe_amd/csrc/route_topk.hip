@@ -57,6 +57,92 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const XT* __restrict__
 }
 
 // ---------------------------------------------------------------- logits, many tokens
+// ---------------------------------------------------------------- logits, bf16 chunks
+// x (bf16) . Wr^T (bf16) on the matrix cores (v_mfma_f32_32x32x16_bf16): the
+// bf16 x bf16 products are exact and accumulate in fp32, like the VALU path
+// (only the summation order differs).  Workgroup tile 128 tokens x 128
+// experts, wave (wm, wn) owns tokens 64wm.. and experts 64wn.. (2 x 2 MFMA
+// tiles).  Both operands go straight from global memory into registers: an
+// MFMA sums over K, so A and B only have to agree on the K order, and within
+// each 32 of K lane group hh = lane / 32 holds K values 16hh + 8s + i in step
+// s (i < 8) -- 32 contiguous bytes of its row.  K is walked 64 at a time with
+// the next chunk prefetched.  Rows past T and experts past E are clamped on
+// load and not stored.  Needs H % 64 == 0.
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+__global__ __launch_bounds__(256, 2) void router_mfma_kernel(const uint16_t* __restrict__ x, int T, int H,
+                                                             const uint16_t* __restrict__ wr,
+                                                             const float* __restrict__ bias, int E,
+                                                             float* __restrict__ logits) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1, ln = lane & 31, hh = lane >> 5;
+  const int t0 = blockIdx.x * 128 + 64 * wm, e0 = blockIdx.y * 128 + 64 * wn;
+  const uint16_t* ap[2];
+  const uint16_t* bp[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    ap[i] = x + (size_t)min(t0 + 32 * i + ln, T - 1) * H + 16 * hh;
+    bp[i] = wr + (size_t)min(e0 + 32 * i + ln, E - 1) * H + 16 * hh;
+  }
+  float16v acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  // chunk of 64: 2 sub-chunks of 32, 2 uint4 (steps) each
+  uint4 a[2][4], b[2][4], an[2][4], bn[2][4];
+  auto load = [&](uint4 (&A)[2][4], uint4 (&B)[2][4], int c) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint4* pa = reinterpret_cast<const uint4*>(ap[i] + c * 64 + 32 * q);
+        const uint4* pb = reinterpret_cast<const uint4*>(bp[i] + c * 64 + 32 * q);
+        A[i][2 * q] = pa[0];
+        A[i][2 * q + 1] = pa[1];
+        B[i][2 * q] = pb[0];
+        B[i][2 * q + 1] = pb[1];
+      }
+  };
+  const int nc = H / 64;
+  load(a, b, 0);
+  for (int c = 0; c < nc; ++c) {
+    if (c + 1 < nc) load(an, bn, c + 1);
+#pragma unroll
+    for (int s8 = 0; s8 < 4; ++s8)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, a[i][s8]),
+                                                             __builtin_bit_cast(bf16x8v, b[j][s8]), acc[i][j], 0, 0, 0);
+    if (c + 1 < nc) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          a[i][q] = an[i][q];
+          b[i][q] = bn[i][q];
+        }
+    }
+  }
+  // lane holds expert column ln, tokens 8*(v/4) + 4*hh + v%4 of each 32 x 32 tile
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = e0 + 32 * j + ln;
+    if (e >= E) continue;
+    const float be = bias ? bias[e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = t0 + 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (t < T) logits[(size_t)t * E + e] = acc[i][j][v] + be;
+      }
+  }
+}
+
 // 64 tokens x 64 experts per workgroup, K staged through LDS 32 at a time;
 // each thread owns 4 tokens x 4 experts.
 template <typename XT>
@@ -176,6 +262,9 @@ int moe_launch_route(const void* x, int x_dtype, int T, int H, const uint16_t* w
       router_gemv_kernel<float, MOE_MAX_DECODE_T><<<grid, 256, 0, st>>>((const float*)x, T, H, w_router, bias, E, logits);
     else
       router_gemv_kernel<uint16_t, MOE_MAX_DECODE_T><<<grid, 256, 0, st>>>((const uint16_t*)x, T, H, w_router, bias, E, logits);
+  } else if (x_dtype == MOE_BF16 && H % 64 == 0) {
+    dim3 grid((T + 127) / 128, (E + 127) / 128);
+    router_mfma_kernel<<<grid, 256, 0, st>>>((const uint16_t*)x, T, H, w_router, bias, E, logits);
   } else {
     dim3 grid((T + 63) / 64, (E + 63) / 64);
     if (x_dtype == MOE_F32)
