@@ -184,33 +184,28 @@ __device__ void pt_prep_block(const float* b, float scale, uint32_t* p, float2* 
   }
 }
 
-// wave-wide max of uint32 through DPP row operations and row read-out
+// wave-wide max of uint32 entirely in DPP (row_bcast15 / row_bcast31 carry the
+// row maxima upwards), read from lane 63
 __device__ __forceinline__ uint32_t pt_wave_max(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false)); // row_half_mirror
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false)); // row_mirror
-  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-  return max(max(r0, r1), max(r2, r3));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast31
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
-// Top-k of one token's E logits (LDS) by one wave.  Lane l holds the keys of
-// experts l + 64 * i (i < SLOTS): the order-preserving logit bits, and on
-// equal bits the lower expert first.  Each lane sorts its keys; every round
-// takes the wave-wide maximum of the lane heads and the lane holding it pops
-// its head.  Lane j < k ends with the j-th expert and its softmax weight over
-// the k chosen logits (ids[j], wts[j]).
+// Top-k by repeated extraction (the general case of pt_topk below): each lane
+// sorts its keys; every round takes the wave-wide maximum of the lane heads
+// and the lane holding it pops its head.  Lane j < k ends with the j-th key
+// and expert.
 template <int SLOTS>
-__device__ __forceinline__ void pt_topk(const float* lg, int E, int k, int* ids, float* wts) {
+__device__ __forceinline__ void pt_topk_rounds(uint32_t (&hi)[SLOTS], int k, uint32_t& my_key, uint32_t& my_e) {
   const int lane = threadIdx.x & 63;
-  uint32_t hi[SLOTS], ex[SLOTS];
+  uint32_t ex[SLOTS];
 #pragma unroll
-  for (int i = 0; i < SLOTS; ++i) {
-    const int e = lane + 64 * i;
-    hi[i] = e < E ? moe_f32_order_key(lg[e < E ? e : 0]) : 0u;  // every real key has hi > 0
-    ex[i] = (uint32_t)e;
-  }
+  for (int i = 0; i < SLOTS; ++i) ex[i] = (uint32_t)(lane + 64 * i);
   // descending sort of the lane's keys (odd-even transposition network); the
   // experts of one lane ascend with i, so equal keys keep the lower expert first
 #pragma unroll
@@ -225,29 +220,100 @@ __device__ __forceinline__ void pt_topk(const float* lg, int E, int k, int* ids,
       ex[i + 1] = sw ? e0 : ex[i + 1];
     }
   }
-  uint32_t my_key = 0u, my_e = 0u;
+  int pos = 0;  // the lane's head is entry `pos` of its sorted keys (past the end: key 0)
+  uint32_t head = hi[0], head_e = ex[0];
   for (int j = 0; j < k; ++j) {
-    const uint32_t M = pt_wave_max(hi[0]);
-    const uint64_t cand = __ballot(hi[0] == M);
+    const uint32_t M = pt_wave_max(head);
+    const uint64_t cand = __ballot(head == M);
     int wl = __ffsll((long long)cand) - 1;
     if (__popcll(cand) > 1) {  // equal logits in several lanes: the lowest expert
-      const uint32_t ce = hi[0] == M ? ex[0] : 0xFFFFFFFFu;
+      const uint32_t ce = head == M ? head_e : 0xFFFFFFFFu;
       const uint32_t emin = ~pt_wave_max(~ce);
       wl = (int)(emin & 63);
     }
-    const uint32_t ew = __builtin_amdgcn_readlane(ex[0], wl);
-    if (lane == j) {
-      my_key = M;
-      my_e = ew;
-    }
-    if (lane == wl) {  // pop the head
+    const uint32_t ew = __builtin_amdgcn_readlane(head_e, wl);
+    my_key = lane == j ? M : my_key;
+    my_e = lane == j ? ew : my_e;
+    pos += lane == wl;
+    uint32_t nh = 0u, ne = 0u;
 #pragma unroll
-      for (int i = 0; i + 1 < SLOTS; ++i) {
-        hi[i] = hi[i + 1];
-        ex[i] = ex[i + 1];
-      }
-      hi[SLOTS - 1] = 0u;
+    for (int i = 0; i < SLOTS; ++i) {
+      nh = pos == i ? hi[i] : nh;
+      ne = pos == i ? ex[i] : ne;
     }
+    head = nh;
+    head_e = ne;
+  }
+}
+
+// Top-k of one token's E logits (LDS) by one wave.  Lane l holds the keys of
+// experts l + 64 * i (i < SLOTS): the order-preserving bits of the logit; the
+// order is by key, and on equal keys the lower expert first.
+//  1. tau = the k-th largest lane maximum, its top 20 bits found with ballots
+//     (the rest left 0): at least k keys are >= tau, so every chosen
+//     expert's key is >= tau.
+//  2. The keys >= tau (usually a few more than k) are packed into `cand` as
+//     key << 32 | ~expert, which orders them exactly as the rule above.
+//  3. Each candidate's rank = the number of larger candidates; rank j < k is
+//     the j-th choice.
+// More than 64 candidates (many equal logits) take the extraction rounds.
+// Lane j < k ends with the j-th expert and its softmax weight over the k
+// chosen logits (ids[j], wts[j]).  `cand`: 64 words of LDS for this wave.
+template <int SLOTS>
+__device__ __forceinline__ void pt_topk(const float* lg, int E, int k, int* ids, float* wts, u64* cand) {
+  const int lane = threadIdx.x & 63;
+  uint32_t hi[SLOTS];
+  uint32_t head = 0u;
+  float v[SLOTS];  // every load is issued before the first use
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) v[i] = lg[min(lane + 64 * i, E - 1)];
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) {
+    const uint32_t key = moe_f32_order_key(v[i]);
+    hi[i] = lane + 64 * i < E ? key : 0u;  // every real key is > 0
+    head = max(head, hi[i]);
+  }
+  // two bits per step, from bits 31..30 down to 13..12; the low 12 bits stay
+  // 0, which only lowers tau (a few more candidates at most)
+  uint32_t tau = 0u;
+#pragma unroll
+  for (int b = 30; b >= 12; b -= 2) {
+    const uint32_t c1 = tau | (1u << b), c2 = tau | (2u << b), c3 = tau | (3u << b);
+    const int n1 = __popcll(__ballot(head >= c1)), n2 = __popcll(__ballot(head >= c2));
+    const int n3 = __popcll(__ballot(head >= c3));
+    tau = n3 >= k ? c3 : n2 >= k ? c2 : n1 >= k ? c1 : tau;
+  }
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) {
+    const bool t = hi[i] >= tau && lane + 64 * i < E;
+    const uint64_t m = __ballot(t);
+    const int p = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (t && p < 64) cand[p] = ((u64)hi[i] << 32) | (uint32_t)~(uint32_t)(lane + 64 * i);
+    n += __popcll(m);
+  }
+  uint32_t my_key = 0u, my_e = 0u;
+  if (n <= 64) {
+    const int n8 = (n + 7) & ~7;
+    if (lane >= n && lane < n8) cand[lane] = 0ull;  // pads: below every candidate
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const u64 me = cand[lane];
+    int rank = 0;
+    for (int m = 0; m < n8; m += 8) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) rank += cand[m + q] > me;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (lane < n && rank < k) cand[rank] = me;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const u64 w = cand[lane < k ? lane : 0];
+    my_key = lane < k ? (uint32_t)(w >> 32) : 0u;
+    my_e = lane < k ? ~(uint32_t)w : 0u;
+  } else {
+    pt_topk_rounds<SLOTS>(hi, k, my_key, my_e);
   }
   // softmax over the chosen logits, lane j holding logit j (max is lane 0's)
   const float m0 = moe_order_key_f32(__builtin_amdgcn_readfirstlane(my_key));
@@ -266,12 +332,35 @@ __device__ __forceinline__ void pt_topk(const float* lg, int E, int k, int* ids,
 
 // Work plan of one layer from the T * k chosen experts (one wave): the
 // distinct experts ("units") in order of first occurrence (token-major), each
-// with its tokens p_tok[4u + c] and their top-k positions p_j[4u + c] (k for
-// the shared expert), then the shared expert with every token; p_roff[u] is
-// the byte offset of the unit's record in the pool.  n = T * k <= 64.
+// with its tokens p_tok[4u + c] and their top-k positions p_j[4u + c];
+// then, if with_shared, the shared expert with every token (top-k position
+// k); p_roff[u] is the byte offset of the unit's record in the pool;
+// p_misc[0] = the number of units.  n = T * k <= 64.
 __device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, const int32_t* slots, int64_t rbytes,
-                                        int* p_exp, int* p_ntok, int* p_tok, int* p_j, int64_t* p_roff, int* p_misc) {
+                                        bool with_shared, int* p_exp, int* p_ntok, int* p_tok, int* p_j,
+                                        int64_t* p_roff, int* p_misc) {
   const int lane = threadIdx.x & 63, n = T * k;
+  if (T == 1) {  // one token: its k experts are distinct, in top-k order
+    if (lane < k) {
+      const int e1 = topi[lane];
+      p_exp[lane] = e1;
+      p_ntok[lane] = 1;
+      p_roff[lane] = (int64_t)slots[e1] * rbytes;
+      p_tok[lane * 4] = 0;
+      p_j[lane * 4] = lane;
+    }
+    if (lane == 0) {
+      if (with_shared) {
+        p_exp[k] = E;
+        p_ntok[k] = 1;
+        p_roff[k] = (int64_t)slots[E] * rbytes;
+        p_tok[k * 4] = 0;
+        p_j[k * 4] = k;
+      }
+      p_misc[0] = with_shared ? k + 1 : k;
+    }
+    return;
+  }
   const int e = lane < n ? topi[lane] : -1 - lane;  // distinct negatives for idle lanes
   int first = lane, before = 0, total = 0;           // first lane with this expert; count before; count
   for (int q = 0; q < n; ++q) {
@@ -296,16 +385,18 @@ __device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, co
     p_tok[u * 4 + before] = t;
     p_j[u * 4 + before] = j;
   }
-  if (lane < T) {
-    p_tok[U * 4 + lane] = lane;
-    p_j[U * 4 + lane] = k;
+  if (with_shared) {
+    if (lane < T) {
+      p_tok[U * 4 + lane] = lane;
+      p_j[U * 4 + lane] = k;
+    }
+    if (lane == 0) {
+      p_exp[U] = E;
+      p_ntok[U] = T;
+      p_roff[U] = (int64_t)slots[E] * rbytes;
+    }
   }
-  if (lane == 0) {
-    p_exp[U] = E;
-    p_ntok[U] = T;
-    p_roff[U] = (int64_t)slots[E] * rbytes;
-    p_misc[0] = U + 1;
-  }
+  if (lane == 0) p_misc[0] = with_shared ? U + 1 : U;
 }
 
 // Prepared activations, one 8-value word of a quantisation block per thread.
@@ -360,8 +451,8 @@ __device__ __forceinline__ void pt_prep_word(const float* v, float scale, bool v
 struct PtLds {
   size_t xs, xprep, lg, topi, topw, p_exp, p_ntok, p_tok, p_j, p_roff, p_misc, red, hp, hc, inv, slots, total;
 };
-#define PT_PB_MAX 5    // pieces per batch (at most)
-#define PT_SLOTS 128   // gate/up row slots per batch (16 per piece)
+#define PT_PB_MAX 5    // pieces per batch: 4 of row slot A, 1 of row slot B
+#define PT_SLOTS 80    // gate/up row slots per batch (16 per piece)
 __host__ __device__ inline PtLds pt_lds(int qfmt, int T, int k, int E, int H, size_t prep_bytes) {
   PtLds o;
   size_t off = 0;
@@ -397,8 +488,9 @@ template <int QFMT, int MT, int SLOTS>
 __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int T = a.T, H = a.H, F = a.F, E = a.E, k = a.k, L = a.L, G = a.G;
-  const int tid = threadIdx.x, lane = tid & 63, g = blockIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  int tid = threadIdx.x, lane = tid & 63;
   const int blk = QFMT == MOE_Q4_B32 ? 32 : 16;
   const MoePlanes pl = moe_planes(QFMT, H, F);  // a record is < 4 GiB: 32-bit plane offsets
   const uint32_t o_guq = (uint32_t)pl.gu_q, o_gus = (uint32_t)pl.gu_s, o_dq = (uint32_t)pl.d_q, o_ds = (uint32_t)pl.d_s;
@@ -426,6 +518,11 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
   const int nrch = (H + 511) / 512;  // router chunks of 512 columns per row (<= 4)
 
   for (int l = 0; l < L && ok; ++l) {
+    // the thread index is made opaque once per layer, so that the compiler
+    // derives per-thread offsets where they are used instead of keeping them
+    // live across the whole layer loop
+    asm volatile("" : "+v"(tid));
+    lane = tid & 63;
     const uint32_t tag = pt_tag(call, L, l);
     // ------------------------------------------------------------ phase A
     // this wave's router row (if any) is requested before waiting for x_l
@@ -444,6 +541,61 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
       for (int c = 0; c < 4; ++c) {
         const uint32_t h0 = 512 * c + 8 * lane;
         rw[c] = *reinterpret_cast<const uint4*>(wr + (uint32_t)e_row * (uint32_t)H + (h0 < (uint32_t)H ? h0 : 0u));
+      }
+    }
+    // One token: the shared expert is kept out of the plan when its F/8 pieces
+    // fit one per workgroup.  They go first to the workgroups whose routed
+    // share is the smaller one (counted for k distinct experts).  The piece's
+    // gate/up rows and down words are requested here, before x_l and the
+    // logits are exchanged, and used as row slot B (piece 4) of the first
+    // batch.  Row slot B: gate/up row l % 16 of the piece over a quarter of
+    // the wave's K range (lane group l / 16).
+    const int NP = F / 8;
+    const int NKU = H / 128;                                     // K units of 128 values
+    const int ku0 = wave * NKU / 8, ku1 = (wave + 1) * NKU / 8;  // <= 2 per wave
+    const int lq = lane >> 4;
+    const int kuB = min(ku0 + (lq >> 1), NKU - 1);
+    const bool kvB = ku0 + (lq >> 1) < ku1;
+    const bool sep = MT == 1 && NP <= G;  // shared expert in slot B
+    int sp = -1;                          // this workgroup's shared piece
+    if (sep) {
+      const int64_t QR = (int64_t)k * NP;
+      const int64_t clo = QR / G, nhi = QR % G;  // nhi workgroups take clo + 1
+      const int64_t hi_before = (int64_t)g * QR / G - (int64_t)g * clo;
+      const bool small = (int64_t)(g + 1) * QR / G - (int64_t)g * QR / G == clo;
+      const int gr = (int)(small ? g - hi_before : (G - nhi) + hi_before);
+      sp = gr < NP ? gr : -1;
+    }
+    uint4 gqS[2] = {};
+    uint32_t gsS = 0u;
+    uint32_t dwS[4] = {0u, 0u, 0u, 0u}, dmS[4] = {0u, 0u, 0u, 0u};
+    if (sp >= 0) {  // uniform over the workgroup
+      const uint8_t* recS = a.pool + (int64_t)a.slot_table[(size_t)l * (E + 1) + E] * a.record_bytes;
+      const int i = lane & 15;
+      const uint32_t rowS = (uint32_t)(64 * (sp >> 2) + 8 * (sp & 3) + (i & 7) + (i >= 8 ? 32 : 0));
+      if (QFMT == MOE_Q4_B32) {
+        const uint32_t kb0 = 4u * kuB + 2u * (lq & 1);
+        gsS = *reinterpret_cast<const uint32_t*>(recS + (o_gus + 16u * (uint32_t)kuB * (uint32_t)F + 8u * rowS + 4u * (lq & 1)));
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          gqS[b] = *reinterpret_cast<const uint4*>(recS + (o_guq + 16u * ((kb0 + b) * 2u * (uint32_t)F + rowS)));
+      } else {
+        const uint32_t un = 2u * kuB + (lq & 1);
+        gqS[0] = *reinterpret_cast<const uint4*>(recS + (o_guq + 16u * (un * 2u * (uint32_t)F + rowS)));
+        gqS[1] = *reinterpret_cast<const uint4*>(recS + (o_gus + 16u * (un * 2u * (uint32_t)F + rowS)));
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t r = (uint32_t)min(tid + 512 * c, H - 1);
+        if (QFMT == MOE_Q4_B32) {
+          const uint32_t bc = (uint32_t)(sp >> 2);
+          dwS[c] = *reinterpret_cast<const uint32_t*>(recS + (o_dq + 16u * (bc * (uint32_t)H + r) + 4u * (sp & 3)));
+          dmS[c] = *reinterpret_cast<const uint16_t*>(recS + (o_ds + 2u * (bc * (uint32_t)H + r)));
+        } else {
+          const uint32_t b2 = (uint32_t)(sp >> 1);
+          dwS[c] = *reinterpret_cast<const uint32_t*>(recS + (o_dq + 4u * (b2 * (uint32_t)H + r)));
+          dmS[c] = *reinterpret_cast<const uint32_t*>(recS + (o_ds + 4u * (b2 * (uint32_t)H + r)));
+        }
       }
     }
     constexpr int NX = 4 * MT;  // words of x per thread: T * H <= 512 * NX
@@ -560,7 +712,8 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     for (int c = 0; c < 3; ++c)
       if (tid + PT_THREADS * c <= E) lslots[tid + PT_THREADS * c] = srow[c];
     __syncthreads();
-    if (wave < T) pt_topk<SLOTS>(lg + (size_t)wave * E, E, k, topi + wave * k, topw + wave * k);
+    if (wave < T)  // `red` is free until the work pieces: 64 candidate words per token
+      pt_topk<SLOTS>(lg + (size_t)wave * E, E, k, topi + wave * k, topw + wave * k, (u64*)red + 64 * wave);
     __syncthreads();
     if (g == 0 && tid < T * k) {
       if (a.topk_idx_out) a.topk_idx_out[(size_t)l * T * k + tid] = topi[tid];
@@ -568,58 +721,48 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     }
     // plan (wave 0)
     if (wave == 0)
-      pt_plan(topi, T, k, E, lslots, a.record_bytes, p_exp, p_ntok, p_tok, p_j, p_roff, p_misc);
+      pt_plan(topi, T, k, E, lslots, a.record_bytes, !sep, p_exp, p_ntok, p_tok, p_j, p_roff, p_misc);
     __syncthreads();
     // ------------------------------------------------------------ work pieces
     // The layer's expert work is cut into pieces of 8 f values: (unit u, piece
-    // p) for the units u < U1 (distinct experts, then the shared expert) and
-    // p < F/8.  Piece (u, p) = the gate and up rows of f = 8p..8p+7 over all
-    // of K, then those 8 columns of the down matrix (int4: word p%4 of the
-    // blocks in column p/4; int2: half p%2 of the words of block p/2).
-    // With one token, piece q = u * F/8 + p (a workgroup's pieces are
-    // neighbours in one expert's record); with more, q = p * U1 + u (the units
-    // interleaved, so that every workgroup gets the same mix of experts and
-    // token counts, the shared expert's included).  Workgroup g takes q in
-    // [g*Q/G, (g+1)*Q/G): every CU streams the same share of the layer's
-    // weights, in batches of PB pieces.  Row slot s
-    // of a batch (lane s % 64, s / 64-th row of the lane) is gate/up row s%16
-    // of piece s/16, its K range split over the 8 waves; the down rows of
-    // thread tid are tid + 512 c.
+    // p) for the units u < U1 of the plan and p < F/8.  Piece (u, p) = the
+    // gate and up rows of f = 8p..8p+7 over all of K, then those 8 columns of
+    // the down matrix (int4: word p%4 of the blocks in column p/4; int2: half
+    // p%2 of the words of block p/2).  With one token, piece q = u * F/8 + p
+    // (a workgroup's pieces are neighbours in one expert's record); with more,
+    // q = p * U1 + u (the units interleaved, so that every workgroup gets the
+    // same mix of experts and token counts, the shared expert's included).
+    // Workgroup g takes q in [g*Q/G, (g+1)*Q/G): every CU streams the same
+    // share of the layer's weights, in batches of 4 pieces (row slot A: row
+    // slot s = lane s % 64 is gate/up row s%16 of piece s/16, its K range
+    // split over the 8 waves).  The first batch also takes the shared piece of
+    // row slot B, if any (piece 4).  The down rows of thread tid are
+    // tid + 512 c.
     {
-      const int U1 = p_misc[0], NP = F / 8, Q = U1 * NP;
+      const int U1 = p_misc[0], Q = U1 * NP;
       const bool ilv = T > 1;  // interleaved piece order
       auto unit_of = [&](int q) { return ilv ? q % U1 : q / NP; };
       auto piece_of = [&](int q) { return ilv ? q / U1 : q % NP; };
       const int q0 = (int)((int64_t)g * Q / G), q1 = (int)((int64_t)(g + 1) * Q / G);
-      constexpr int PB = MT == 1 ? 5 : 4;  // one token: one batch per layer; more: one row slot per lane
-      constexpr int NRD = 4;                   // down rows per thread (H <= 2048)
-      const int NKU = H / 128;                 // K units of 128 values
-      const int ku0 = wave * NKU / 8, ku1 = (wave + 1) * NKU / 8;  // <= 2 per wave
+      constexpr int PA = 4;                   // pieces of row slot A per batch
+      constexpr int NRD = 4;                  // down rows per thread (H <= 2048)
       float y[NRD][MT];
 #pragma unroll
       for (int c = 0; c < NRD; ++c)
 #pragma unroll
         for (int t = 0; t < MT; ++t) y[c][t] = 0.f;
-      for (int qb = q0; qb < q1; qb += PB) {
-        const int nb = min(PB, q1 - qb);
-        // ---- gate/up loads.  Row slot A of lane l: row l (all K units of the
-        // wave).  With 5 pieces, row slot B: row 64 + l % 16 over a quarter of
-        // the wave's K range (lane group l / 16), so that the 16 extra rows
-        // take few registers.  Indices are clamped: every load is unconditional.
-        const int slA = min(lane, 16 * nb - 1);
-        const int slB = min(64 + (lane & 15), 16 * nb - 1);
-        auto row_of = [&](int sl, const uint8_t*& rec, uint32_t& row, int& unit) {
-          const int q = qb + (sl >> 4), u = unit_of(q), pp = piece_of(q), i = sl & 15;
-          unit = u;
-          rec = a.pool + p_roff[u];
-          row = (uint32_t)(64 * (pp >> 2) + 8 * (pp & 3) + (i & 7) + (i >= 8 ? 32 : 0));
-        };
-        const uint8_t* recA; uint32_t rowA; int unitA;
-        row_of(slA, recA, rowA, unitA);
-        const uint8_t* recB; uint32_t rowB; int unitB;
-        row_of(slB, recB, rowB, unitB);
-        uint4 gq[2][4];  // slot A: [K unit][block (int4) or q/meta unit (int2)]
-        uint2 gs[2];     // slot A, int4: the 4 scales of each K unit
+      for (int qb = q0; qb < q1 || (qb == q0 && sp >= 0); qb += PA) {
+        const int nb = max(0, min(PA, q1 - qb));  // routed pieces in this batch
+        const bool withS = qb == q0 && sp >= 0;     // shared piece in this batch
+        // ---- gate/up loads of row slot A (lane l: row l, all K units of the
+        // wave).  Indices are clamped (to a real piece even when nb == 0):
+        // every load is unconditional.
+        const int slA = max(0, min(lane, 16 * nb - 1));
+        const int qA = min(qb + (slA >> 4), Q - 1), unitA = unit_of(qA), ppA = piece_of(qA), iA = slA & 15;
+        const uint8_t* recA = a.pool + p_roff[unitA];
+        const uint32_t rowA = (uint32_t)(64 * (ppA >> 2) + 8 * (ppA & 3) + (iA & 7) + (iA >= 8 ? 32 : 0));
+        uint4 gq[2][4];  // [K unit][block (int4) or q/meta unit (int2)]
+        uint2 gs[2];     // int4: the 4 scales of each K unit
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const uint32_t ku = (uint32_t)min(ku0 + c, NKU - 1);
@@ -637,32 +780,12 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
             }
           }
         }
-        // slot B: K unit ku0 + (lq >> 1), half (lq & 1) of it; int4: 2 blocks
-        // and their scales (one word), int2: one q-unit and its meta-unit
-        const int lq = lane >> 4;
-        const int kuB = min(ku0 + (lq >> 1), NKU - 1);
-        const bool kvB = PB == 5 && ku0 + (lq >> 1) < ku1;
-        uint4 gqB[2];
-        uint32_t gsB = 0u;
-        if (PB == 5) {
-          if (QFMT == MOE_Q4_B32) {
-            const uint32_t kb0 = 4u * kuB + 2u * (lq & 1);
-            gsB = *reinterpret_cast<const uint32_t*>(recB + (o_gus + 16u * (uint32_t)kuB * (uint32_t)F + 8u * rowB + 4u * (lq & 1)));
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-              gqB[b] = *reinterpret_cast<const uint4*>(recB + (o_guq + 16u * ((kb0 + b) * 2u * (uint32_t)F + rowB)));
-          } else {
-            const uint32_t un = 2u * kuB + (lq & 1);
-            gqB[0] = *reinterpret_cast<const uint4*>(recB + (o_guq + 16u * (un * 2u * (uint32_t)F + rowB)));
-            gqB[1] = *reinterpret_cast<const uint4*>(recB + (o_gus + 16u * (un * 2u * (uint32_t)F + rowB)));
-          }
-        }
         // ---- down loads (one token per unit: right behind the gate/up loads)
-        uint32_t dw[NRD][PB], dm[NRD][PB];  // word (int4) or block word (int2); scale (int4) or meta (int2)
+        uint32_t dw[NRD][PA], dm[NRD][PA];  // word (int4) or block word (int2); scale (int4) or meta (int2)
         auto load_down = [&]() {
 #pragma unroll
-          for (int pi = 0; pi < PB; ++pi) {
-            const int q = qb + min(pi, nb - 1), u = unit_of(q), pp = piece_of(q);
+          for (int pi = 0; pi < PA; ++pi) {
+            const int q = min(qb + min(pi, max(nb - 1, 0)), Q - 1), u = unit_of(q), pp = piece_of(q);
             const uint8_t* rec = a.pool + p_roff[u];  // uniform over the workgroup
 #pragma unroll
             for (int c = 0; c < NRD; ++c) {
@@ -736,26 +859,25 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
 #pragma unroll
           for (int t = 0; t < MT; ++t) red[(wave * PT_SLOTS + lane) * MT + t] = acc[t];
         }
-        if (PB == 5) {  // slot B (one token per unit): 4 lane groups, summed with shuffles
+        if (MT == 1) {  // row slot B: the shared piece, 4 lane groups summed with shuffles
           float accB = 0.f;
+          const uint8_t* xp = xprep;
           if (QFMT == MOE_Q4_B32) {
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
               const int kb = 4 * kuB + 2 * (lq & 1) + b;
-              const float sc = kvB ? moe_f16_to_f32((uint16_t)(gsB >> (16 * b))) : 0.f;
-              const uint8_t* xp = xp_of(unitB, 0);
+              const float sc = kvB ? moe_f16_to_f32((uint16_t)(gsS >> (16 * b))) : 0.f;
               const float cc = ((const float2*)(xp + 2 * (size_t)H))[kb].x;
-              accB = fmaf(sc, pt_q4_dot(gqB[b], (const uint32_t*)xp + 16 * kb, cc), accB);
+              accB = fmaf(sc, pt_q4_dot(gqS[b], (const uint32_t*)xp + 16 * kb, cc), accB);
             }
           } else {
-            const uint32_t qw[4] = {gqB[0].x, gqB[0].y, gqB[0].z, gqB[0].w};
-            const uint32_t mw[4] = {gqB[1].x, gqB[1].y, gqB[1].z, gqB[1].w};
+            const uint32_t qw[4] = {gqS[0].x, gqS[0].y, gqS[0].z, gqS[0].w};
+            const uint32_t mw[4] = {gqS[1].x, gqS[1].y, gqS[1].z, gqS[1].w};
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) {
               const int bl = 4 * (2 * kuB + (lq & 1)) + jb;
               const float sc = kvB ? moe_f16_to_f32((uint16_t)(mw[jb] & 0xffff)) : 0.f;
               const float mn = kvB ? moe_f16_to_f32((uint16_t)(mw[jb] >> 16)) : 0.f;
-              const uint8_t* xp = xp_of(unitB, 0);
               const float2 cc = ((const float2*)(xp + 2 * (size_t)H))[bl];
               accB += pt_q2_dot(qw[jb], sc, mn, (const uint32_t*)xp + 8 * bl, cc);
             }
@@ -771,7 +893,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         {
           const int item = tid >> 3, fi = tid & 7;  // item = pi * MT + t
           const int pi = item / MT, t = item % MT;
-          const bool iv = pi < nb;
+          const bool iv = pi < nb || (pi == PA && withS);
           float hv = 0.f;
           if (iv) {
             float sg = 0.f, su = 0.f;
@@ -808,7 +930,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
           c0 += __shfl_xor(c0, 4, 64);
           c1 += __shfl_xor(c1, 2, 64);
           c1 += __shfl_xor(c1, 4, 64);
-          if (iv && item < PB * MT) {
+          if (iv && item < PT_PB_MAX * MT) {
             if ((fi & 1) == 0) hp[item * 4 + pk] = pw;
             if (fi == 0) hc[item] = make_float2(c0, c1);
           }
@@ -816,7 +938,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         __syncthreads();
         // ---- down dots: rows tid + 512 c, every piece of the batch
 #pragma unroll
-        for (int pi = 0; pi < PB; ++pi) {
+        for (int pi = 0; pi < PA; ++pi) {
           if (pi >= nb) break;
           const int q = qb + pi, u = unit_of(q), pp = piece_of(q);
           const int ntok = MT == 1 ? 1 : p_ntok[u];
@@ -843,12 +965,32 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
             }
           }
         }
+        if (MT == 1 && withS) {  // the shared piece: weight 1
+          const uint32_t* hw4 = hp + PA * 4;
+          const float2 cc = hc[PA];
+#pragma unroll
+          for (int c = 0; c < NRD; ++c) {
+            float v;
+            if (QFMT == MOE_Q4_B32) {
+              v = moe_f16_to_f32((uint16_t)dmS[c]) * pt_q4_word(dwS[c], hw4, cc.x);
+            } else {
+              const uint32_t w = dwS[c] >> (8 * (sp & 1));
+              v = pt_q2_word(w, moe_f16_to_f32((uint16_t)(dmS[c] & 0xffff)), moe_f16_to_f32((uint16_t)(dmS[c] >> 16)),
+                             hw4, cc);
+            }
+            y[c][0] += v;
+          }
+        }
         __syncthreads();  // red, hp, hc are reused by the next batch
       }
-      // this workgroup's partial output, one vector per token
+      // this workgroup's partial output, one vector per token (the thread
+      // index is made opaque here so that the compiler computes the NRD * MT
+      // offsets now instead of keeping them live across the layer loop)
+      int tid_o = tid;
+      asm volatile("" : "+v"(tid_o));
 #pragma unroll
       for (int c = 0; c < NRD; ++c) {
-        const int r = tid + 512 * c;
+        const int r = tid_o + 512 * c;
         if (r < H) {
 #pragma unroll
           for (int t = 0; t < MT; ++t)
@@ -961,7 +1103,6 @@ static PtLayout pt_layout(int T, int k, int E, int H, int F, int qfmt, int G) {
   P.nfs = F / 32;
   P.rpw = H / G;
   P.prep_bytes = moe_prep_bytes(H, qfmt);
-  const int U1max = T * k + 1;
   P.hdr = 0;
   P.xbuf = 256;
   P.lbuf = P.xbuf + moe_ws_up((size_t)T * H * 8);

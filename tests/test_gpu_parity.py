@@ -412,6 +412,37 @@ def test_decode_stack_48_layers(moe):
     assert excluded <= 2  # layer 0 is gap-filtered; later layers may hold a near tie
 
 
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_stack_router_ties(moe, T):
+    """A zero router makes every logit equal its bias, so the persistent
+    kernel's top-k sees exact ties: all 512 logits equal (more candidates than
+    one wave ranks at once), runs of 8 equal values, 64 distinct values each
+    held by 8 experts in scattered positions, and 40 values drawn with many
+    repeats.  The ids follow the lower-index rule exactly; the weights and
+    each layer's output match the oracle."""
+    L, E, k = 4, 512, 10
+    li = C.layer_case(8, T, 2048, E, k, 768, qfmt=0, bias=True, L=L, gap=False, device="cuda")
+    li.Wr = torch.zeros_like(li.Wr)
+    rng = np.random.default_rng(3)
+    b = np.zeros((L, E), np.float32)
+    b[0] = 0.5
+    b[1] = -(np.arange(E) // 8) * 0.25
+    b[2] = (np.arange(E) * 37 % 64) * 0.125
+    b[3] = rng.integers(0, 40, E) * 0.0625
+    li.bias = torch.from_numpy(b).cuda()
+    x = li.x.contiguous()
+    xo, idx_o, w_o, hist = _stack_run(moe, li, x, "persistent")
+    assert bool(torch.isfinite(xo).all())
+    for l in range(L):
+        ri, rw = O.topk_select(np.repeat(b[l][None].astype(np.float64), T, 0), k)
+        assert np.array_equal(_np(idx_o[l]), ri), f"layer {l}"
+        assert np.max(np.abs(_np(w_o[l]) - rw)) <= W_ATOL
+        xl = torch.from_numpy(O.rms_normalize(C.x_as_f64(hist[l])))
+        ry = C.oracle_layer(li, layer=l, x=xl)[0]
+        nxt = hist[l + 1] if l + 1 < L else xo
+        C.assert_close_moe(_np(nxt - hist[l]), ry, f"layer {l}")
+
+
 # ---------------------------------------------------------------- generator
 
 @pytest.mark.parametrize("qfmt", [0, 1])
