@@ -543,28 +543,27 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         rw[c] = *reinterpret_cast<const uint4*>(wr + (uint32_t)e_row * (uint32_t)H + (h0 < (uint32_t)H ? h0 : 0u));
       }
     }
-    // One token: the shared expert is kept out of the plan when its F/8 pieces
-    // fit one per workgroup.  They go first to the workgroups whose routed
-    // share is the smaller one (counted for k distinct experts).  The piece's
-    // gate/up rows and down words are requested here, before x_l and the
-    // logits are exchanged, and used as row slot B (piece 4) of the first
-    // batch.  Row slot B: gate/up row l % 16 of the piece over a quarter of
-    // the wave's K range (lane group l / 16).
+    // Work is handed out in groups of 4 pieces (see "work pieces" below).  One
+    // token: when the units' groups outnumber the workgroups by at most G/4,
+    // every workgroup takes one group and the remaining groups (the last ones
+    // of the shared expert) are split into single pieces, one per workgroup at
+    // most.  Such a piece's gate/up rows and down words are requested here,
+    // before x_l and the logits are exchanged, and used as row slot B (piece
+    // 4) of the batch.  Row slot B: gate/up row l % 16 of the piece over a
+    // quarter of the wave's K range (lane group l / 16).
     const int NP = F / 8;
     const int NKU = H / 128;                                     // K units of 128 values
     const int ku0 = wave * NKU / 8, ku1 = (wave + 1) * NKU / 8;  // <= 2 per wave
     const int lq = lane >> 4;
     const int kuB = min(ku0 + (lq >> 1), NKU - 1);
     const bool kvB = ku0 + (lq >> 1) < ku1;
-    const bool sep = MT == 1 && NP <= G;  // shared expert in slot B
-    int sp = -1;                          // this workgroup's shared piece
-    if (sep) {
-      const int64_t QR = (int64_t)k * NP;
-      const int64_t clo = QR / G, nhi = QR % G;  // nhi workgroups take clo + 1
-      const int64_t hi_before = (int64_t)g * QR / G - (int64_t)g * clo;
-      const bool small = (int64_t)(g + 1) * QR / G - (int64_t)g * QR / G == clo;
-      const int gr = (int)(small ? g - hi_before : (G - nhi) + hi_before);
-      sp = gr < NP ? gr : -1;
+    const int TG1 = (k + 1) * (NP / 4);  // groups with one token: k experts and the shared one
+    const int nL = 4 * (TG1 - G);        // single pieces left over
+    const bool sepB = MT == 1 && nL > 0 && nL <= NP && nL <= G;
+    int sp = -1;  // this workgroup's single shared piece
+    if (sepB) {
+      const int j0 = (int)((int64_t)g * nL / G), j1 = (int)((int64_t)(g + 1) * nL / G);
+      sp = j1 > j0 ? NP - nL + j0 : -1;
     }
     uint4 gqS[2] = {};
     uint32_t gsS = 0u;
@@ -721,95 +720,93 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     }
     // plan (wave 0)
     if (wave == 0)
-      pt_plan(topi, T, k, E, lslots, a.record_bytes, !sep, p_exp, p_ntok, p_tok, p_j, p_roff, p_misc);
+      pt_plan(topi, T, k, E, lslots, a.record_bytes, true, p_exp, p_ntok, p_tok, p_j, p_roff, p_misc);
     __syncthreads();
     // ------------------------------------------------------------ work pieces
     // The layer's expert work is cut into pieces of 8 f values: (unit u, piece
-    // p) for the units u < U1 of the plan and p < F/8.  Piece (u, p) = the
-    // gate and up rows of f = 8p..8p+7 over all of K, then those 8 columns of
-    // the down matrix (int4: word p%4 of the blocks in column p/4; int2: half
-    // p%2 of the words of block p/2).  With one token, piece q = u * F/8 + p
-    // (a workgroup's pieces are neighbours in one expert's record); with more,
-    // q = p * U1 + u (the units interleaved, so that every workgroup gets the
-    // same mix of experts and token counts, the shared expert's included).
-    // Workgroup g takes q in [g*Q/G, (g+1)*Q/G): every CU streams the same
-    // share of the layer's weights, in batches of 4 pieces (row slot A: row
-    // slot s = lane s % 64 is gate/up row s%16 of piece s/16, its K range
-    // split over the 8 waves).  The first batch also takes the shared piece of
-    // row slot B, if any (piece 4).  The down rows of thread tid are
-    // tid + 512 c.
+    // p) for the units u < U1 of the plan (the shared expert last) and p <
+    // F/8.  Piece (u, p) = the gate and up rows of f = 8p..8p+7 over all of K,
+    // then those 8 columns of the down matrix.  A group is the 4 pieces of one
+    // unit whose down values share a down block column (int4: the 4 words of
+    // the 16-byte blocks of column p/4; int2: the two words of blocks p/2), so
+    // that one group's gate/up rows are 64 consecutive rows of its record and
+    // its down values are 16 bytes (int4) or two words (int2) per row.  With
+    // one token, group i = u * F/32 + b (a workgroup's work is one expert's
+    // rows); with more, i = b * U1 + u (the units interleaved, so that every
+    // workgroup gets the same mix of experts and token counts).  Workgroup g
+    // takes the groups [g*NG/G, (g+1)*NG/G) (with a single shared piece:
+    // group g and that piece), one batch per group: row slot s = lane s of
+    // the batch is gate/up row s%16 of piece s/16, its K range split over the
+    // 8 waves; the down rows of thread tid are tid + 512 c.
     {
-      const int U1 = p_misc[0], Q = U1 * NP;
-      const bool ilv = T > 1;  // interleaved piece order
-      auto unit_of = [&](int q) { return ilv ? q % U1 : q / NP; };
-      auto piece_of = [&](int q) { return ilv ? q / U1 : q % NP; };
-      const int q0 = (int)((int64_t)g * Q / G), q1 = (int)((int64_t)(g + 1) * Q / G);
-      constexpr int PA = 4;                   // pieces of row slot A per batch
-      constexpr int NRD = 4;                  // down rows per thread (H <= 2048)
+      const int U1 = p_misc[0], NB4 = NP / 4, NG = U1 * NB4;
+      const bool ilv = T > 1;  // interleaved group order
+      int gi0 = (int)((int64_t)g * NG / G), gi1 = (int)((int64_t)(g + 1) * NG / G);
+      if (sepB) {
+        gi0 = g;
+        gi1 = g + 1;
+      }
+      constexpr int NRD = 4;  // down rows per thread (H <= 2048)
       float y[NRD][MT];
 #pragma unroll
       for (int c = 0; c < NRD; ++c)
 #pragma unroll
         for (int t = 0; t < MT; ++t) y[c][t] = 0.f;
-      for (int qb = q0; qb < q1 || (qb == q0 && sp >= 0); qb += PA) {
-        const int nb = max(0, min(PA, q1 - qb));  // routed pieces in this batch
-        const bool withS = qb == q0 && sp >= 0;     // shared piece in this batch
-        // ---- gate/up loads of row slot A (lane l: row l, all K units of the
-        // wave).  Indices are clamped (to a real piece even when nb == 0):
-        // every load is unconditional.
-        const int slA = max(0, min(lane, 16 * nb - 1));
-        const int qA = min(qb + (slA >> 4), Q - 1), unitA = unit_of(qA), ppA = piece_of(qA), iA = slA & 15;
-        const uint8_t* recA = a.pool + p_roff[unitA];
-        const uint32_t rowA = (uint32_t)(64 * (ppA >> 2) + 8 * (ppA & 3) + (iA & 7) + (iA >= 8 ? 32 : 0));
+      for (int gi = gi0; gi < gi1; ++gi) {
+        const bool withS = gi == gi0 && sp >= 0;  // the single shared piece rides along
+        const int u = ilv ? gi % U1 : gi / NB4, bq = ilv ? gi / U1 : gi % NB4;
+        const int ntok = MT == 1 ? 1 : p_ntok[u];
+        const uint8_t* rec = a.pool + p_roff[u];  // uniform over the workgroup
+        // ---- gate/up loads: lane l holds row 64 bq + 8 (l / 16) + l % 8 (+ 32
+        // for the up half, l % 16 >= 8), all K units of the wave
+        const uint32_t row = (uint32_t)(64 * bq + 8 * (lane >> 4) + (lane & 7) + ((lane & 8) ? 32 : 0));
         uint4 gq[2][4];  // [K unit][block (int4) or q/meta unit (int2)]
         uint2 gs[2];     // int4: the 4 scales of each K unit
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const uint32_t ku = (uint32_t)min(ku0 + c, NKU - 1);
           if (QFMT == MOE_Q4_B32) {
-            gs[c] = *reinterpret_cast<const uint2*>(recA + (o_gus + 16u * ku * (uint32_t)F + 8u * rowA));
+            gs[c] = *reinterpret_cast<const uint2*>(rec + (o_gus + 16u * ku * (uint32_t)F + 8u * row));
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-              gq[c][b] = *reinterpret_cast<const uint4*>(recA + (o_guq + 16u * ((4u * ku + b) * 2u * (uint32_t)F + rowA)));
+              gq[c][b] = *reinterpret_cast<const uint4*>(rec + (o_guq + 16u * ((4u * ku + b) * 2u * (uint32_t)F + row)));
           } else {
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
               const uint32_t un = 2u * ku + b;  // 4-block unit of 64 values
-              gq[c][b] = *reinterpret_cast<const uint4*>(recA + (o_guq + 16u * (un * 2u * (uint32_t)F + rowA)));
-              gq[c][2 + b] = *reinterpret_cast<const uint4*>(recA + (o_gus + 16u * (un * 2u * (uint32_t)F + rowA)));
+              gq[c][b] = *reinterpret_cast<const uint4*>(rec + (o_guq + 16u * (un * 2u * (uint32_t)F + row)));
+              gq[c][2 + b] = *reinterpret_cast<const uint4*>(rec + (o_gus + 16u * (un * 2u * (uint32_t)F + row)));
             }
           }
         }
-        // ---- down loads (one token per unit: right behind the gate/up loads)
-        uint32_t dw[NRD][PA], dm[NRD][PA];  // word (int4) or block word (int2); scale (int4) or meta (int2)
+        // ---- down loads of the group: int4: the 16-byte block and its scale;
+        // int2: the two block words and their two meta words
+        uint4 dq[NRD];
+        uint32_t dsc[NRD];
         auto load_down = [&]() {
 #pragma unroll
-          for (int pi = 0; pi < PA; ++pi) {
-            const int q = min(qb + min(pi, max(nb - 1, 0)), Q - 1), u = unit_of(q), pp = piece_of(q);
-            const uint8_t* rec = a.pool + p_roff[u];  // uniform over the workgroup
-#pragma unroll
-            for (int c = 0; c < NRD; ++c) {
-              const uint32_t r = (uint32_t)min(tid + 512 * c, H - 1);
-              if (QFMT == MOE_Q4_B32) {
-                const uint32_t bc = (uint32_t)(pp >> 2);
-                dw[c][pi] = *reinterpret_cast<const uint32_t*>(rec + (o_dq + 16u * (bc * (uint32_t)H + r) + 4u * (pp & 3)));
-                dm[c][pi] = *reinterpret_cast<const uint16_t*>(rec + (o_ds + 2u * (bc * (uint32_t)H + r)));
-              } else {
-                const uint32_t b2 = (uint32_t)(pp >> 1);
-                dw[c][pi] = *reinterpret_cast<const uint32_t*>(rec + (o_dq + 4u * (b2 * (uint32_t)H + r)));
-                dm[c][pi] = *reinterpret_cast<const uint32_t*>(rec + (o_ds + 4u * (b2 * (uint32_t)H + r)));
-              }
+          for (int c = 0; c < NRD; ++c) {
+            const uint32_t r = (uint32_t)min(tid + 512 * c, H - 1);
+            if (QFMT == MOE_Q4_B32) {
+              dq[c] = *reinterpret_cast<const uint4*>(rec + (o_dq + 16u * ((uint32_t)bq * (uint32_t)H + r)));
+              dsc[c] = *reinterpret_cast<const uint16_t*>(rec + (o_ds + 2u * ((uint32_t)bq * (uint32_t)H + r)));
+            } else {
+              const uint32_t b0 = 2u * (uint32_t)bq;
+              dq[c].x = *reinterpret_cast<const uint32_t*>(rec + (o_dq + 4u * (b0 * (uint32_t)H + r)));
+              dq[c].y = *reinterpret_cast<const uint32_t*>(rec + (o_dq + 4u * ((b0 + 1u) * (uint32_t)H + r)));
+              dq[c].z = *reinterpret_cast<const uint32_t*>(rec + (o_ds + 4u * (b0 * (uint32_t)H + r)));
+              dq[c].w = *reinterpret_cast<const uint32_t*>(rec + (o_ds + 4u * ((b0 + 1u) * (uint32_t)H + r)));
+              dsc[c] = 0u;
             }
           }
         };
         if (MT == 1) load_down();
         __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any dot product
         // ---- gate/up partial dots over this wave's K units
-        auto xp_of = [&](int u, int t) -> const uint8_t* {
+        auto xp_of = [&](int t) -> const uint8_t* {
           return xprep + (size_t)(MT == 1 ? 0 : p_tok[u * 4 + t]) * a.prep_bytes;
         };
         {
-          const int ntok = MT == 1 ? 1 : p_ntok[unitA];
           float acc[MT];
 #pragma unroll
           for (int t = 0; t < MT; ++t) acc[t] = 0.f;
@@ -826,7 +823,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {
                   if (MT == 1 || t < ntok) {
-                    const uint8_t* xp = xp_of(unitA, t);
+                    const uint8_t* xp = xp_of(t);
                     const float cc = ((const float2*)(xp + 2 * (size_t)H))[kb].x;
                     acc[t] = fmaf(sc, pt_q4_dot(gq[c][b], (const uint32_t*)xp + 16 * kb, cc), acc[t]);
                   }
@@ -845,7 +842,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
 #pragma unroll
                   for (int t = 0; t < MT; ++t) {
                     if (MT == 1 || t < ntok) {
-                      const uint8_t* xp = xp_of(unitA, t);
+                      const uint8_t* xp = xp_of(t);
                       const float2 cc = ((const float2*)(xp + 2 * (size_t)H))[bl];
                       acc[t] += pt_q2_dot(qw[jb], sc, mn, (const uint32_t*)xp + 8 * bl, cc);
                     }
@@ -854,12 +851,10 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
               }
             }
           }
-          // written by every lane (slots past 16 * nb are never read): a
-          // conditional use would let the compiler sink the loads behind it
 #pragma unroll
           for (int t = 0; t < MT; ++t) red[(wave * PT_SLOTS + lane) * MT + t] = acc[t];
         }
-        if (MT == 1) {  // row slot B: the shared piece, 4 lane groups summed with shuffles
+        if (MT == 1) {  // row slot B: the single shared piece, 4 lane groups summed with shuffles
           float accB = 0.f;
           const uint8_t* xp = xprep;
           if (QFMT == MOE_Q4_B32) {
@@ -893,7 +888,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         {
           const int item = tid >> 3, fi = tid & 7;  // item = pi * MT + t
           const int pi = item / MT, t = item % MT;
-          const bool iv = pi < nb || (pi == PA && withS);
+          const bool iv = pi < 4 || (pi == 4 && withS);
           float hv = 0.f;
           if (iv) {
             float sg = 0.f, su = 0.f;
@@ -936,28 +931,26 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
           }
         }
         __syncthreads();
-        // ---- down dots: rows tid + 512 c, every piece of the batch
+        // ---- down dots: rows tid + 512 c, the group's 4 pieces
 #pragma unroll
-        for (int pi = 0; pi < PA; ++pi) {
-          if (pi >= nb) break;
-          const int q = qb + pi, u = unit_of(q), pp = piece_of(q);
-          const int ntok = MT == 1 ? 1 : p_ntok[u];
+        for (int t = 0; t < MT; ++t) {
+          if (MT > 1 && t >= ntok) break;
+          const int tk = MT == 1 ? 0 : p_tok[u * 4 + t], jj = p_j[u * 4 + t];
+          const float wgt = jj < k ? topw[tk * k + jj] : 1.f;
 #pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            if (MT > 1 && t >= ntok) break;
-            const int tk = MT == 1 ? 0 : p_tok[u * 4 + t], jj = p_j[u * 4 + t];
-            const float wgt = jj < k ? topw[tk * k + jj] : 1.f;
+          for (int pi = 0; pi < 4; ++pi) {
             const uint32_t* hw4 = hp + (pi * MT + t) * 4;
             const float2 cc = hc[pi * MT + t];
 #pragma unroll
             for (int c = 0; c < NRD; ++c) {
               float v;
               if (QFMT == MOE_Q4_B32) {
-                v = moe_f16_to_f32((uint16_t)dm[c][pi]) * pt_q4_word(dw[c][pi], hw4, cc.x);
+                const uint32_t w = pi == 0 ? dq[c].x : pi == 1 ? dq[c].y : pi == 2 ? dq[c].z : dq[c].w;
+                v = moe_f16_to_f32((uint16_t)dsc[c]) * pt_q4_word(w, hw4, cc.x);
               } else {
-                const uint32_t w = dw[c][pi] >> (8 * (pp & 1));
-                v = pt_q2_word(w, moe_f16_to_f32((uint16_t)(dm[c][pi] & 0xffff)),
-                               moe_f16_to_f32((uint16_t)(dm[c][pi] >> 16)), hw4, cc);
+                const uint32_t w = (pi < 2 ? dq[c].x : dq[c].y) >> (8 * (pi & 1));
+                const uint32_t m = pi < 2 ? dq[c].z : dq[c].w;
+                v = pt_q2_word(w, moe_f16_to_f32((uint16_t)(m & 0xffff)), moe_f16_to_f32((uint16_t)(m >> 16)), hw4, cc);
               }
 #pragma unroll
               for (int tt = 0; tt < MT; ++tt)
@@ -965,9 +958,9 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
             }
           }
         }
-        if (MT == 1 && withS) {  // the shared piece: weight 1
-          const uint32_t* hw4 = hp + PA * 4;
-          const float2 cc = hc[PA];
+        if (MT == 1 && withS) {  // the single shared piece: weight 1
+          const uint32_t* hw4 = hp + 4 * 4;
+          const float2 cc = hc[4];
 #pragma unroll
           for (int c = 0; c < NRD; ++c) {
             float v;
