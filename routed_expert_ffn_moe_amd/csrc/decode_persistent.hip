@@ -257,10 +257,10 @@ __device__ __forceinline__ void pt_topk_rounds(uint32_t (&hi)[SLOTS], int k, uin
 //  3. Each candidate's rank = the number of larger candidates; rank j < k is
 //     the j-th choice.
 // More than 64 candidates (many equal logits) take the extraction rounds.
-// Lane j < k ends with the j-th expert and its softmax weight over the k
-// chosen logits (ids[j], wts[j]).  `cand`: 64 words of LDS for this wave.
+// Lane j < k writes the j-th expert to ids[j] and returns its key (the
+// weights follow in pt_topk_weights).  `cand`: 64 words of LDS for this wave.
 template <int SLOTS>
-__device__ __forceinline__ void pt_topk(const float* lg, int E, int k, int* ids, float* wts, u64* cand) {
+__device__ __forceinline__ uint32_t pt_topk_select(const float* lg, int E, int k, int* ids, u64* cand) {
   const int lane = threadIdx.x & 63;
   uint32_t hi[SLOTS];
   uint32_t head = 0u;
@@ -315,7 +315,14 @@ __device__ __forceinline__ void pt_topk(const float* lg, int E, int k, int* ids,
   } else {
     pt_topk_rounds<SLOTS>(hi, k, my_key, my_e);
   }
-  // softmax over the chosen logits, lane j holding logit j (max is lane 0's)
+  if (lane < k) ids[lane] = (int)my_e;
+  return my_key;
+}
+
+// Softmax weights of the chosen logits, lane j < k holding the key of the
+// j-th (the largest in lane 0): wts[j].  One wave.
+__device__ __forceinline__ void pt_topk_weights(uint32_t my_key, int k, float* wts) {
+  const int lane = threadIdx.x & 63;
   const float m0 = moe_order_key_f32(__builtin_amdgcn_readfirstlane(my_key));
   const float z = lane < k ? expf(moe_order_key_f32(my_key) - m0) : 0.f;
   float sum = z;  // sum in lane order: lanes 0..k-1 are added left to right
@@ -324,10 +331,7 @@ __device__ __forceinline__ void pt_topk(const float* lg, int E, int k, int* ids,
     for (int j = 0; j < k; ++j) acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), j));
     sum = acc;
   }
-  if (lane < k) {
-    ids[lane] = (int)my_e;
-    wts[lane] = z / sum;
-  }
+  if (lane < k) wts[lane] = z / sum;
 }
 
 // Work plan of one layer from the T * k chosen experts (one wave): the
@@ -449,7 +453,7 @@ __device__ __forceinline__ void pt_prep_word(const float* v, float scale, bool v
 // ---------------------------------------------------------------- LDS layout
 // Section offsets (bytes, 16-byte aligned) shared by the kernel and the host.
 struct PtLds {
-  size_t xs, xprep, lg, topi, topw, p_exp, p_ntok, p_tok, p_j, p_roff, p_misc, red, hp, hc, inv, slots, total;
+  size_t xs, xprep, lg, topi, topw, p_exp, p_ntok, p_tok, p_j, p_roff, p_misc, red, hp, hc, slots, total;
 };
 #define PT_PB_MAX 5    // pieces per batch: 4 of row slot A, 1 of row slot B
 #define PT_SLOTS 80    // gate/up row slots per batch (16 per piece)
@@ -477,7 +481,6 @@ __host__ __device__ inline PtLds pt_lds(int qfmt, int T, int k, int E, int H, si
   o.red = take((size_t)PT_WAVES * PT_SLOTS * 4 * 4);  // [wave][slot][token slot] partial gate/up dots
   o.hp = take((size_t)PT_PB_MAX * 4 * 4 * 4);         // [piece][token slot][4] prepared h words
   o.hc = take((size_t)PT_PB_MAX * 4 * 8);             // [piece][token slot] corrections
-  o.inv = take(4 * 4);
   o.slots = take((size_t)(E + 1) * 4);
   o.total = off;
   return o;
@@ -510,7 +513,6 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
   float* red = (float*)(smem + o.red);        // [wave][slot][MT]
   uint32_t* hp = (uint32_t*)(smem + o.hp);    // [piece][MT][4]
   float2* hc = (float2*)(smem + o.hc);        // [piece][MT]
-  float* inv = (float*)(smem + o.inv);        // [4]
   int* lslots = (int*)(smem + o.slots);        // [E+1] this layer's slot-table row
 
   const uint32_t call = __hip_atomic_load(a.hdr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -626,16 +628,29 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
       if (!ok) break;
     }
     __syncthreads();
-    // mean square of token t by wave t: lane sums in column order, then the wave
-    if (wave < T) {
+    // 1 / rms of every token, taken by every wave for itself (no barrier): lane
+    // l sums the squares of its 8-value chunks 512 c + 8 l, then the wave sums
+    float invr[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
       float ss = 0.f;
-      for (int h = lane; h < H; h += 64) ss = fmaf(xs[wave * H + h], xs[wave * H + h], ss);
+      if (t < T) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int h0 = 512 * c + 8 * lane;
+          if (h0 < H) {
+            const float4 v0 = *reinterpret_cast<const float4*>(xs + t * H + h0);
+            const float4 v1 = *reinterpret_cast<const float4*>(xs + t * H + h0 + 4);
+            ss = fmaf(v0.x, v0.x, ss); ss = fmaf(v0.y, v0.y, ss); ss = fmaf(v0.z, v0.z, ss); ss = fmaf(v0.w, v0.w, ss);
+            ss = fmaf(v1.x, v1.x, ss); ss = fmaf(v1.y, v1.y, ss); ss = fmaf(v1.z, v1.z, ss); ss = fmaf(v1.w, v1.w, ss);
+          }
+        }
+      }
       ss = moe_wave_sum(ss);
-      if (lane == 0) inv[wave] = 1.0f / sqrtf(ss / (float)H + PT_EPS);
+      invr[t] = 1.0f / sqrtf(ss / (float)H + PT_EPS);
     }
     if (a.x_hist && g == 0)
       for (int i = tid; i < T * H; i += PT_THREADS) a.x_hist[(size_t)l * T * H + i] = xs[i];
-    __syncthreads();
     // router rows: the prefetched one, then any further rows of this wave
     for (int e = e_row; e < E; e += G * PT_WAVES) {
       if (e != e_row) {
@@ -670,7 +685,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
       for (int t = 0; t < MT; ++t) {
         if (t < T) {
           const float s = moe_wave_sum(acc[t]);
-          if (lane == t) pt_put(pt_at(a.lbuf, (uint32_t)(t * E + e)), tag, s * inv[t] + b);
+          if (lane == t) pt_put(pt_at(a.lbuf, (uint32_t)(t * E + e)), tag, s * invr[t] + b);
         }
       }
     }
@@ -683,7 +698,8 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         const int t = valid ? wi / (H / 8) : 0, wh = valid ? wi % (H / 8) : 0;  // word within the token
         const int b = wh / (blk / 8), sub = wh % (blk / 8);
         uint8_t* out = xprep + (size_t)t * a.prep_bytes;
-        pt_prep_word<QFMT>(xs + (size_t)t * H + 8 * wh, inv[t], valid, (uint32_t*)out + (blk / 2) * b + 4 * sub,
+        const float it = t == 0 ? invr[0] : t == 1 ? invr[MT > 1 ? 1 : 0] : t == 2 ? invr[MT > 2 ? 2 : 0] : invr[MT > 3 ? 3 : 0];
+        pt_prep_word<QFMT>(xs + (size_t)t * H + 8 * wh, it, valid, (uint32_t*)out + (blk / 2) * b + 4 * sub,
                            (float2*)(out + 2 * (size_t)H) + b, sub);
       }
     }
@@ -711,17 +727,27 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     for (int c = 0; c < 3; ++c)
       if (tid + PT_THREADS * c <= E) lslots[tid + PT_THREADS * c] = srow[c];
     __syncthreads();
-    if (wave < T)  // `red` is free until the work pieces: 64 candidate words per token
-      pt_topk<SLOTS>(lg + (size_t)wave * E, E, k, topi + wave * k, topw + wave * k, (u64*)red + 64 * wave);
-    __syncthreads();
-    if (g == 0 && tid < T * k) {
-      if (a.topk_idx_out) a.topk_idx_out[(size_t)l * T * k + tid] = topi[tid];
-      if (a.topk_w_out) a.topk_w_out[(size_t)l * T * k + tid] = topw[tid];
+    uint32_t my_key = 0u;  // wave t < T: the key of top-k position `lane` of token t
+    if (wave < T) {  // `red` is free until the work pieces: 64 candidate words per token
+      my_key = pt_topk_select<SLOTS>(lg + (size_t)wave * E, E, k, topi + wave * k, (u64*)red + 64 * wave);
+      if (MT > 1) pt_topk_weights(my_key, k, topw + wave * k);
     }
-    // plan (wave 0)
-    if (wave == 0)
-      pt_plan(topi, T, k, E, lslots, a.record_bytes, true, p_exp, p_ntok, p_tok, p_j, p_roff, p_misc);
     __syncthreads();
+    // With one token, unit u < k is top-k choice u and unit k the shared
+    // expert: no plan, and the weights are taken once this workgroup's weight
+    // loads are in flight (below).  With more tokens: the plan (wave 0).
+    auto emit_topk = [&]() {
+      if (g == 0 && tid < T * k) {
+        if (a.topk_idx_out) a.topk_idx_out[(size_t)l * T * k + tid] = topi[tid];
+        if (a.topk_w_out) a.topk_w_out[(size_t)l * T * k + tid] = topw[tid];
+      }
+    };
+    if (MT > 1) {
+      emit_topk();
+      if (wave == 0)
+        pt_plan(topi, T, k, E, lslots, a.record_bytes, true, p_exp, p_ntok, p_tok, p_j, p_roff, p_misc);
+      __syncthreads();
+    }
     // ------------------------------------------------------------ work pieces
     // The layer's expert work is cut into pieces of 8 f values: (unit u, piece
     // p) for the units u < U1 of the plan (the shared expert last) and p <
@@ -739,7 +765,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     // the batch is gate/up row s%16 of piece s/16, its K range split over the
     // 8 waves; the down rows of thread tid are tid + 512 c.
     {
-      const int U1 = p_misc[0], NB4 = NP / 4, NG = U1 * NB4;
+      const int U1 = MT == 1 ? k + 1 : p_misc[0], NB4 = NP / 4, NG = U1 * NB4;
       const bool ilv = T > 1;  // interleaved group order
       int gi0 = (int)((int64_t)g * NG / G), gi1 = (int)((int64_t)(g + 1) * NG / G);
       if (sepB) {
@@ -756,7 +782,8 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         const bool withS = gi == gi0 && sp >= 0;  // the single shared piece rides along
         const int u = ilv ? gi % U1 : gi / NB4, bq = ilv ? gi / U1 : gi % NB4;
         const int ntok = MT == 1 ? 1 : p_ntok[u];
-        const uint8_t* rec = a.pool + p_roff[u];  // uniform over the workgroup
+        const int64_t roff = MT == 1 ? (int64_t)lslots[u < k ? topi[u] : E] * a.record_bytes : p_roff[u];
+        const uint8_t* rec = a.pool + roff;  // uniform over the workgroup
         // ---- gate/up loads: lane l holds row 64 bq + 8 (l / 16) + l % 8 (+ 32
         // for the up half, l % 16 >= 8), all K units of the wave
         const uint32_t row = (uint32_t)(64 * bq + 8 * (lane >> 4) + (lane & 7) + ((lane & 8) ? 32 : 0));
@@ -802,6 +829,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         };
         if (MT == 1) load_down();
         __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any dot product
+        if (MT == 1 && gi == gi0 && wave == 0) pt_topk_weights(my_key, k, topw);  // read after the next barrier
         // ---- gate/up partial dots over this wave's K units
         auto xp_of = [&](int t) -> const uint8_t* {
           return xprep + (size_t)(MT == 1 ? 0 : p_tok[u * 4 + t]) * a.prep_bytes;
@@ -935,7 +963,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
           if (MT > 1 && t >= ntok) break;
-          const int tk = MT == 1 ? 0 : p_tok[u * 4 + t], jj = p_j[u * 4 + t];
+          const int tk = MT == 1 ? 0 : p_tok[u * 4 + t], jj = MT == 1 ? u : p_j[u * 4 + t];
           const float wgt = jj < k ? topw[tk * k + jj] : 1.f;
 #pragma unroll
           for (int pi = 0; pi < 4; ++pi) {
@@ -975,6 +1003,10 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
           }
         }
         __syncthreads();  // red, hp, hc are reused by the next batch
+      }
+      if (MT == 1) {
+        if (gi0 == gi1 && wave == 0) pt_topk_weights(my_key, k, topw);
+        emit_topk();  // topw was written before a barrier above (or by this thread's wave, lanes < k)
       }
       // this workgroup's partial output, one vector per token (the thread
       // index is made opaque here so that the compiler computes the NRD * MT
