@@ -34,6 +34,7 @@
 #define PT_THREADS 512
 #define PT_WAVES 8
 #define PT_SPIN_MAX (1 << 18)
+#define PT_GROUP_BASE 4  // cost of a group's loads, in units of one token's dot passes
 #define PT_MAGIC 0x4d6f4531u
 #define PT_EPS 1e-6f
 
@@ -342,7 +343,7 @@ __device__ __forceinline__ void pt_topk_weights(uint32_t my_key, int k, float* w
 // p_misc[0] = the number of units.  n = T * k <= 64.
 __device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, const int32_t* slots, int64_t rbytes,
                                         bool with_shared, int* p_exp, int* p_ntok, int* p_tok, int* p_j,
-                                        int64_t* p_roff, int* p_misc) {
+                                        int64_t* p_roff, int* p_cum, int* p_misc) {
   const int lane = threadIdx.x & 63, n = T * k;
   if (T == 1) {  // one token: its k experts are distinct, in top-k order
     if (lane < k) {
@@ -400,7 +401,24 @@ __device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, co
       p_roff[U] = (int64_t)slots[E] * rbytes;
     }
   }
-  if (lane == 0) p_misc[0] = with_shared ? U + 1 : U;
+  // p_cum[u] = the summed costs of units < u, a group of unit u costing
+  // PT_GROUP_BASE + (its token count); p_cum[U1] = all of them
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const int c = lane < U ? PT_GROUP_BASE + p_ntok[lane] : 0;
+  int incl = c;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    incl += lane >= d ? v : 0;
+  }
+  if (lane < U) p_cum[lane] = incl - c;
+  const int sum_r = U > 0 ? __builtin_amdgcn_readlane(incl, U - 1) : 0;
+  if (lane == 0) {
+    p_cum[U] = sum_r;
+    if (with_shared) p_cum[U + 1] = sum_r + PT_GROUP_BASE + T;
+    p_misc[0] = with_shared ? U + 1 : U;
+  }
 }
 
 // Prepared activations, one 8-value word of a quantisation block per thread.
@@ -453,7 +471,7 @@ __device__ __forceinline__ void pt_prep_word(const float* v, float scale, bool v
 // ---------------------------------------------------------------- LDS layout
 // Section offsets (bytes, 16-byte aligned) shared by the kernel and the host.
 struct PtLds {
-  size_t xs, xprep, lg, topi, topw, p_exp, p_ntok, p_tok, p_j, p_roff, p_misc, red, hp, hc, slots, total;
+  size_t xs, xprep, lg, topi, topw, p_exp, p_ntok, p_tok, p_j, p_roff, p_cum, p_misc, red, hp, hc, slots, total;
 };
 #define PT_PB_MAX 5    // pieces per batch: 4 of row slot A, 1 of row slot B
 #define PT_SLOTS 80    // gate/up row slots per batch (16 per piece)
@@ -477,6 +495,7 @@ __host__ __device__ inline PtLds pt_lds(int qfmt, int T, int k, int E, int H, si
   o.p_tok = take(U1max * 16);
   o.p_j = take(U1max * 16);
   o.p_roff = take(U1max * 8);
+  o.p_cum = take((U1max + 1) * 4);
   o.p_misc = take(16);
   o.red = take((size_t)PT_WAVES * PT_SLOTS * 4 * 4);  // [wave][slot][token slot] partial gate/up dots
   o.hp = take((size_t)PT_PB_MAX * 4 * 4 * 4);         // [piece][token slot][4] prepared h words
@@ -509,6 +528,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
   int* p_tok = (int*)(smem + o.p_tok);        // [U1max][4]
   int* p_j = (int*)(smem + o.p_j);            // [U1max][4]
   int64_t* p_roff = (int64_t*)(smem + o.p_roff); // [U1max] record byte offsets
+  int* p_cum = (int*)(smem + o.p_cum);        // [U1max + 1] group cost prefix per unit
   int* p_misc = (int*)(smem + o.p_misc);      // [0] = U1
   float* red = (float*)(smem + o.red);        // [wave][slot][MT]
   uint32_t* hp = (uint32_t*)(smem + o.hp);    // [piece][MT][4]
@@ -745,7 +765,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     if (MT > 1) {
       emit_topk();
       if (wave == 0)
-        pt_plan(topi, T, k, E, lslots, a.record_bytes, true, p_exp, p_ntok, p_tok, p_j, p_roff, p_misc);
+        pt_plan(topi, T, k, E, lslots, a.record_bytes, true, p_exp, p_ntok, p_tok, p_j, p_roff, p_cum, p_misc);
       __syncthreads();
     }
     // ------------------------------------------------------------ work pieces
@@ -772,40 +792,67 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         gi0 = g;
         gi1 = g + 1;
       }
+      if (MT > 1) {
+        // balanced by cost: group i = b * U1 + u starts at cost b * Crow +
+        // p_cum[u]; workgroup g takes the groups starting in [g C/G, (g+1) C/G)
+        const int Crow = p_cum[U1];
+        const int64_t C = (int64_t)NB4 * Crow;
+        auto first_at = [&](int64_t target) -> int {
+          if (target >= C) return NG;
+          const int b = (int)(target / Crow), rem = (int)(target - (int64_t)b * Crow);
+          const uint64_t m = __ballot(lane < U1 && p_cum[lane < U1 ? lane : 0] >= rem);
+          int u = m ? __ffsll((long long)m) - 1 : min(U1, 64);
+          if (!m)  // units past the wave's 64 lanes (U1 = 65)
+            while (u < U1 && p_cum[u] < rem) ++u;
+          return b * U1 + u;
+        };
+        gi0 = first_at((int64_t)g * C / G);
+        gi1 = first_at((int64_t)(g + 1) * C / G);
+      }
       constexpr int NRD = 4;  // down rows per thread (H <= 2048)
       float y[NRD][MT];
 #pragma unroll
       for (int c = 0; c < NRD; ++c)
 #pragma unroll
         for (int t = 0; t < MT; ++t) y[c][t] = 0.f;
-      for (int gi = gi0; gi < gi1; ++gi) {
-        const bool withS = gi == gi0 && sp >= 0;  // the single shared piece rides along
-        const int u = ilv ? gi % U1 : gi / NB4, bq = ilv ? gi / U1 : gi % NB4;
-        const int ntok = MT == 1 ? 1 : p_ntok[u];
-        const int64_t roff = MT == 1 ? (int64_t)lslots[u < k ? topi[u] : E] * a.record_bytes : p_roff[u];
-        const uint8_t* rec = a.pool + roff;  // uniform over the workgroup
-        // ---- gate/up loads: lane l holds row 64 bq + 8 (l / 16) + l % 8 (+ 32
-        // for the up half, l % 16 >= 8), all K units of the wave
-        const uint32_t row = (uint32_t)(64 * bq + 8 * (lane >> 4) + (lane & 7) + ((lane & 8) ? 32 : 0));
-        uint4 gq[2][4];  // [K unit][block (int4) or q/meta unit (int2)]
-        uint2 gs[2];     // int4: the 4 scales of each K unit
+      auto unit_of = [&](int gi) { return ilv ? gi % U1 : gi / NB4; };
+      auto block_of = [&](int gi) { return ilv ? gi / U1 : gi % NB4; };
+      auto rec_of = [&](int u) -> const uint8_t* {  // uniform over the workgroup
+        return a.pool + (MT == 1 ? (int64_t)lslots[u < k ? topi[u] : E] * a.record_bytes : p_roff[u]);
+      };
+      // ---- gate/up loads of group gi: lane l holds row 64 b + 8 (l / 16) +
+      // l % 8 (+ 32 for the up half, l % 16 >= 8), all K units of the wave
+      auto load_gu = [&](int gi, uint4 (&q)[2][4], uint2 (&sc)[2]) {
+        const uint8_t* rg = rec_of(unit_of(gi));
+        const uint32_t row = (uint32_t)(64 * block_of(gi) + 8 * (lane >> 4) + (lane & 7) + ((lane & 8) ? 32 : 0));
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const uint32_t ku = (uint32_t)min(ku0 + c, NKU - 1);
           if (QFMT == MOE_Q4_B32) {
-            gs[c] = *reinterpret_cast<const uint2*>(rec + (o_gus + 16u * ku * (uint32_t)F + 8u * row));
+            sc[c] = *reinterpret_cast<const uint2*>(rg + (o_gus + 16u * ku * (uint32_t)F + 8u * row));
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-              gq[c][b] = *reinterpret_cast<const uint4*>(rec + (o_guq + 16u * ((4u * ku + b) * 2u * (uint32_t)F + row)));
+              q[c][b] = *reinterpret_cast<const uint4*>(rg + (o_guq + 16u * ((4u * ku + b) * 2u * (uint32_t)F + row)));
           } else {
+            sc[c] = make_uint2(0u, 0u);
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
               const uint32_t un = 2u * ku + b;  // 4-block unit of 64 values
-              gq[c][b] = *reinterpret_cast<const uint4*>(rec + (o_guq + 16u * (un * 2u * (uint32_t)F + row)));
-              gq[c][2 + b] = *reinterpret_cast<const uint4*>(rec + (o_gus + 16u * (un * 2u * (uint32_t)F + row)));
+              q[c][b] = *reinterpret_cast<const uint4*>(rg + (o_guq + 16u * (un * 2u * (uint32_t)F + row)));
+              q[c][2 + b] = *reinterpret_cast<const uint4*>(rg + (o_gus + 16u * (un * 2u * (uint32_t)F + row)));
             }
           }
         }
+      };
+      uint4 gq[2][4];  // [K unit][block (int4) or q/meta unit (int2)]
+      uint2 gs[2];     // int4: the 4 scales of each K unit
+      if (MT > 1) load_gu(min(gi0, NG - 1), gq, gs);  // clamped: every load is unconditional
+      for (int gi = gi0; gi < gi1; ++gi) {
+        const bool withS = gi == gi0 && sp >= 0;  // the single shared piece rides along
+        const int u = unit_of(gi), bq = block_of(gi);
+        const int ntok = MT == 1 ? 1 : p_ntok[u];
+        const uint8_t* rec = rec_of(u);
+        if (MT == 1) load_gu(gi, gq, gs);
         // ---- down loads of the group: int4: the 16-byte block and its scale;
         // int2: the two block words and their two meta words
         uint4 dq[NRD];
@@ -827,7 +874,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
             }
           }
         };
-        if (MT == 1) load_down();
+        load_down();
         __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any dot product
         if (MT == 1 && gi == gi0 && wave == 0) pt_topk_weights(my_key, k, topw);  // read after the next barrier
         // ---- gate/up partial dots over this wave's K units
@@ -909,7 +956,12 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
           accB += __shfl_xor(accB, 32, 64);
           red[(wave * PT_SLOTS + 64 + (lane & 15)) * MT] = accB;  // the 4 lane groups hold the same sum
         }
-        if (MT > 1) load_down();
+        // several tokens: the next group's gate/up rows are requested now (after
+        // this group's down words, so that the down dots need not wait for
+        // them) and land while this group's SiLU and down dots run
+        uint4 gqN[2][4];
+        uint2 gsN[2];
+        if (MT > 1) load_gu(min(gi + 1, gi1 - 1), gqN, gsN);
         __syncthreads();
         // ---- h = silu(gate) * up, 8 threads per (piece, token slot), then the
         // prepared word of the 8 h values for the down dots
@@ -1003,6 +1055,14 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
           }
         }
         __syncthreads();  // red, hp, hc are reused by the next batch
+        if (MT > 1) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            gs[c] = gsN[c];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) gq[c][b] = gqN[c][b];
+          }
+        }
       }
       if (MT == 1) {
         if (gi0 == gi1 && wave == 0) pt_topk_weights(my_key, k, topw);
