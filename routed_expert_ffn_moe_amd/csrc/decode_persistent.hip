@@ -76,6 +76,16 @@ __device__ __forceinline__ u64* pt_at(u64* base, uint32_t i) {
 __device__ __forceinline__ u64 pt_load(u64* base, uint32_t i) {
   return __hip_atomic_load(pt_at(base, i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// The thread index and lane, made opaque at each call: values derived from
+// them inside the layer loop are then computed where used instead of being
+// hoisted out of the loop and kept live (or spilled) for the whole kernel.
+__device__ __forceinline__ int pt_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+__device__ __forceinline__ int pt_lane() { return pt_tid() & 63; }
+
 // Waits until word base[first + g * stride] carries `tag` for every g < n
 // (one word per producing workgroup), polling 4 bytes of tag per producer
 // instead of all of its data.  The data itself is read and every tag checked
@@ -84,7 +94,7 @@ __device__ __forceinline__ u64 pt_load(u64* base, uint32_t i) {
 __device__ bool pt_wait_sentinels(u64* base, uint32_t first, uint32_t stride, int n, uint32_t tag, int spin_max) {
   for (int it = 0;; ++it) {
     bool mine = true;
-    for (int i = threadIdx.x; i < n; i += blockDim.x)
+    for (int i = pt_tid(); i < n; i += blockDim.x)
       mine &= (uint32_t)(pt_load(base, first + (uint32_t)i * stride) >> 32) == tag;
     if (__syncthreads_and(mine)) return true;
     if (it > spin_max) return false;
@@ -203,7 +213,7 @@ __device__ __forceinline__ uint32_t pt_wave_max(uint32_t v) {
 // and expert.
 template <int SLOTS>
 __device__ __forceinline__ void pt_topk_rounds(uint32_t (&hi)[SLOTS], int k, uint32_t& my_key, uint32_t& my_e) {
-  const int lane = threadIdx.x & 63;
+  const int lane = pt_lane();
   uint32_t ex[SLOTS];
 #pragma unroll
   for (int i = 0; i < SLOTS; ++i) ex[i] = (uint32_t)(lane + 64 * i);
@@ -262,7 +272,7 @@ __device__ __forceinline__ void pt_topk_rounds(uint32_t (&hi)[SLOTS], int k, uin
 // weights follow in pt_topk_weights).  `cand`: 64 words of LDS for this wave.
 template <int SLOTS>
 __device__ __forceinline__ uint32_t pt_topk_select(const float* lg, int E, int k, int* ids, u64* cand) {
-  const int lane = threadIdx.x & 63;
+  const int lane = pt_lane();
   uint32_t hi[SLOTS];
   uint32_t head = 0u;
   float v[SLOTS];  // every load is issued before the first use
@@ -323,7 +333,7 @@ __device__ __forceinline__ uint32_t pt_topk_select(const float* lg, int E, int k
 // Softmax weights of the chosen logits, lane j < k holding the key of the
 // j-th (the largest in lane 0): wts[j].  One wave.
 __device__ __forceinline__ void pt_topk_weights(uint32_t my_key, int k, float* wts) {
-  const int lane = threadIdx.x & 63;
+  const int lane = pt_lane();
   const float m0 = moe_order_key_f32(__builtin_amdgcn_readfirstlane(my_key));
   const float z = lane < k ? expf(moe_order_key_f32(my_key) - m0) : 0.f;
   float sum = z;  // sum in lane order: lanes 0..k-1 are added left to right
@@ -344,7 +354,7 @@ __device__ __forceinline__ void pt_topk_weights(uint32_t my_key, int k, float* w
 __device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, const int32_t* slots, int64_t rbytes,
                                         bool with_shared, int* p_exp, int* p_ntok, int* p_tok, int* p_j,
                                         int64_t* p_roff, int* p_cum, int* p_misc) {
-  const int lane = threadIdx.x & 63, n = T * k;
+  const int lane = pt_lane(), n = T * k;
   if (T == 1) {  // one token: its k experts are distinct, in top-k order
     if (lane < k) {
       const int e1 = topi[lane];
@@ -820,32 +830,69 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
       auto rec_of = [&](int u) -> const uint8_t* {  // uniform over the workgroup
         return a.pool + (MT == 1 ? (int64_t)lslots[u < k ? topi[u] : E] * a.record_bytes : p_roff[u]);
       };
-      // ---- gate/up loads of group gi: lane l holds row 64 b + 8 (l / 16) +
-      // l % 8 (+ 32 for the up half, l % 16 >= 8), all K units of the wave
-      auto load_gu = [&](int gi, uint4 (&q)[2][4], uint2 (&sc)[2]) {
+      // ---- gate/up loads of group gi (its 64 consecutive rows 64 b + rho),
+      // 8 16-byte words q and 4 words sc per lane.
+      // One token: lane l holds slot l, row rho = 8 (l / 16) + l % 8 (+ 32
+      // for the up half, l % 16 >= 8), over all of the wave's K range: q[2c +
+      // b/2][b%2] = block b of K unit c (int4) or its q-unit b / meta unit b-2
+      // (int2), sc[2c..2c+1] = the 4 scales of K unit c; the activations are
+      // read from LDS as the dots need them.
+      // More tokens: lane l = (p = l % 16, quarter q = l / 16) holds rows rho
+      // = p + 16 j (j < 4) over quarter q of the wave's K range, 64 values
+      // (int4: blocks 2q, 2q+1 of the wave's 8; int2: q-unit q of its 4):
+      // q[j][0..1] = the two blocks (int4) or the q-unit and its meta unit
+      // (int2), sc[j] = the two scales (int4).  Each quarter's activations are
+      // read once per token and used for 4 rows; the quarters are summed with
+      // shuffles.
+      const int lp = lane & 15;
+      const int kuq = min(ku0 + (lq >> 1), NKU - 1);  // K unit of the lane's quarter
+      const bool kvq = ku0 + (lq >> 1) < ku1;
+      auto load_gu = [&](int gi, uint4 (&q)[4][2], uint32_t (&sc)[4]) {
         const uint8_t* rg = rec_of(unit_of(gi));
-        const uint32_t row = (uint32_t)(64 * block_of(gi) + 8 * (lane >> 4) + (lane & 7) + ((lane & 8) ? 32 : 0));
+        if (MT == 1) {
+          const uint32_t row = (uint32_t)(64 * block_of(gi) + 8 * (lane >> 4) + (lane & 7) + ((lane & 8) ? 32 : 0));
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const uint32_t ku = (uint32_t)min(ku0 + c, NKU - 1);
-          if (QFMT == MOE_Q4_B32) {
-            sc[c] = *reinterpret_cast<const uint2*>(rg + (o_gus + 16u * ku * (uint32_t)F + 8u * row));
+          for (int c = 0; c < 2; ++c) {
+            const uint32_t ku = (uint32_t)min(ku0 + c, NKU - 1);
+            if (QFMT == MOE_Q4_B32) {
+              const uint2 s2 = *reinterpret_cast<const uint2*>(rg + (o_gus + 16u * ku * (uint32_t)F + 8u * row));
+              sc[2 * c] = s2.x;
+              sc[2 * c + 1] = s2.y;
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
-              q[c][b] = *reinterpret_cast<const uint4*>(rg + (o_guq + 16u * ((4u * ku + b) * 2u * (uint32_t)F + row)));
-          } else {
-            sc[c] = make_uint2(0u, 0u);
+              for (int b = 0; b < 4; ++b)
+                q[2 * c + b / 2][b % 2] =
+                    *reinterpret_cast<const uint4*>(rg + (o_guq + 16u * ((4u * ku + b) * 2u * (uint32_t)F + row)));
+            } else {
+              sc[2 * c] = sc[2 * c + 1] = 0u;
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              const uint32_t un = 2u * ku + b;  // 4-block unit of 64 values
-              q[c][b] = *reinterpret_cast<const uint4*>(rg + (o_guq + 16u * (un * 2u * (uint32_t)F + row)));
-              q[c][2 + b] = *reinterpret_cast<const uint4*>(rg + (o_gus + 16u * (un * 2u * (uint32_t)F + row)));
+              for (int b = 0; b < 2; ++b) {
+                const uint32_t un = 2u * ku + b;  // 4-block unit of 64 values
+                q[2 * c][b] = *reinterpret_cast<const uint4*>(rg + (o_guq + 16u * (un * 2u * (uint32_t)F + row)));
+                q[2 * c + 1][b] = *reinterpret_cast<const uint4*>(rg + (o_gus + 16u * (un * 2u * (uint32_t)F + row)));
+              }
             }
+          }
+          return;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t row = (uint32_t)(64 * block_of(gi) + lp + 16 * j);
+          if (QFMT == MOE_Q4_B32) {
+            const uint32_t kb0 = 4u * (uint32_t)kuq + 2u * (lq & 1);
+            sc[j] = *reinterpret_cast<const uint32_t*>(rg + (o_gus + 16u * (uint32_t)kuq * (uint32_t)F + 8u * row + 4u * (lq & 1)));
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+              q[j][bb] = *reinterpret_cast<const uint4*>(rg + (o_guq + 16u * ((kb0 + bb) * 2u * (uint32_t)F + row)));
+          } else {
+            const uint32_t un = 2u * (uint32_t)kuq + (lq & 1);  // q-unit of 64 values
+            sc[j] = 0u;
+            q[j][0] = *reinterpret_cast<const uint4*>(rg + (o_guq + 16u * (un * 2u * (uint32_t)F + row)));
+            q[j][1] = *reinterpret_cast<const uint4*>(rg + (o_gus + 16u * (un * 2u * (uint32_t)F + row)));
           }
         }
       };
-      uint4 gq[2][4];  // [K unit][block (int4) or q/meta unit (int2)]
-      uint2 gs[2];     // int4: the 4 scales of each K unit
+      uint4 gq[4][2];
+      uint32_t gs[4];
       if (MT > 1) load_gu(min(gi0, NG - 1), gq, gs);  // clamped: every load is unconditional
       for (int gi = gi0; gi < gi1; ++gi) {
         const bool withS = gi == gi0 && sp >= 0;  // the single shared piece rides along
@@ -877,57 +924,99 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         load_down();
         __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any dot product
         if (MT == 1 && gi == gi0 && wave == 0) pt_topk_weights(my_key, k, topw);  // read after the next barrier
-        // ---- gate/up partial dots over this wave's K units
+        // ---- gate/up partial dots
         auto xp_of = [&](int t) -> const uint8_t* {
           return xprep + (size_t)(MT == 1 ? 0 : p_tok[u * 4 + t]) * a.prep_bytes;
         };
-        {
-          float acc[MT];
-#pragma unroll
-          for (int t = 0; t < MT; ++t) acc[t] = 0.f;
+        if (MT == 1) {  // one token: row slot `lane`, all of the wave's K units
+          const float2* corr = (const float2*)(xprep + 2 * (size_t)H);
+          float acc = 0.f;
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             const int kuc = min(ku0 + c, NKU - 1);
             const bool kv = ku0 + c < ku1;
             if (QFMT == MOE_Q4_B32) {
-              const uint32_t sw[2] = {gs[c].x, gs[c].y};
 #pragma unroll
               for (int b = 0; b < 4; ++b) {
                 const int kb = 4 * kuc + b;
-                const float sc = kv ? moe_f16_to_f32((uint16_t)(sw[b >> 1] >> (16 * (b & 1)))) : 0.f;
-#pragma unroll
-                for (int t = 0; t < MT; ++t) {
-                  if (MT == 1 || t < ntok) {
-                    const uint8_t* xp = xp_of(t);
-                    const float cc = ((const float2*)(xp + 2 * (size_t)H))[kb].x;
-                    acc[t] = fmaf(sc, pt_q4_dot(gq[c][b], (const uint32_t*)xp + 16 * kb, cc), acc[t]);
-                  }
-                }
+                const float sc = kv ? moe_f16_to_f32((uint16_t)(gs[2 * c + b / 2] >> (16 * (b & 1)))) : 0.f;
+                acc = fmaf(sc, pt_q4_dot(gq[2 * c + b / 2][b % 2], (const uint32_t*)xprep + 16 * kb, corr[kb].x), acc);
               }
             } else {
 #pragma unroll
               for (int b = 0; b < 2; ++b) {
-                const uint4 Qw = gq[c][b], Mw = gq[c][2 + b];
+                const uint4 Qw = gq[2 * c][b], Mw = gq[2 * c + 1][b];
                 const uint32_t qw[4] = {Qw.x, Qw.y, Qw.z, Qw.w}, mw[4] = {Mw.x, Mw.y, Mw.z, Mw.w};
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb) {
                   const int bl = 4 * (2 * kuc + b) + jb;  // block of 16 values
                   const float sc = kv ? moe_f16_to_f32((uint16_t)(mw[jb] & 0xffff)) : 0.f;
                   const float mn = kv ? moe_f16_to_f32((uint16_t)(mw[jb] >> 16)) : 0.f;
-#pragma unroll
-                  for (int t = 0; t < MT; ++t) {
-                    if (MT == 1 || t < ntok) {
-                      const uint8_t* xp = xp_of(t);
-                      const float2 cc = ((const float2*)(xp + 2 * (size_t)H))[bl];
-                      acc[t] += pt_q2_dot(qw[jb], sc, mn, (const uint32_t*)xp + 8 * bl, cc);
-                    }
-                  }
+                  acc += pt_q2_dot(qw[jb], sc, mn, (const uint32_t*)xprep + 8 * bl, corr[bl]);
                 }
               }
             }
           }
+          // written by every lane (slots past the pieces are never read): a
+          // conditional use would let the compiler sink the loads behind it
+          red[wave * PT_SLOTS + lane] = acc;
+        } else {  // more tokens: the quarter mapping, one token and one block of x at a time
+          const int rho = lp + 16 * lq;
+          const int slot = 16 * ((rho & 31) >> 3) + (rho & 7) + 8 * (rho >> 5);
+#pragma unroll 1
+          for (int t = 0; t < ntok; ++t) {
+            const uint8_t* xp = xp_of(t);
+            const float2* corr = (const float2*)(xp + 2 * (size_t)H);
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            if (QFMT == MOE_Q4_B32) {
+              const int kb0 = 4 * kuq + 2 * (lq & 1);
 #pragma unroll
-          for (int t = 0; t < MT; ++t) red[(wave * PT_SLOTS + lane) * MT + t] = acc[t];
+              for (int bb = 0; bb < 2; ++bb) {
+                uint32_t xw[16];  // the prepared x of block kb0 + bb
+#pragma unroll
+                for (int w4 = 0; w4 < 4; ++w4) {
+                  const uint4 v = *reinterpret_cast<const uint4*>((const uint32_t*)xp + 16 * (kb0 + bb) + 4 * w4);
+                  xw[4 * w4] = v.x; xw[4 * w4 + 1] = v.y; xw[4 * w4 + 2] = v.z; xw[4 * w4 + 3] = v.w;
+                }
+                const float cb = corr[kb0 + bb].x;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  const float sj = kvq ? moe_f16_to_f32((uint16_t)(gs[j] >> (16 * bb))) : 0.f;
+                  acc[j] = fmaf(sj, pt_q4_dot(gq[j][bb], xw, cb), acc[j]);
+                }
+              }
+            } else {
+              const int un = 2 * kuq + (lq & 1);
+#pragma unroll
+              for (int jb = 0; jb < 4; ++jb) {
+                uint32_t xw[8];  // the prepared x of block 4 un + jb
+#pragma unroll
+                for (int w4 = 0; w4 < 2; ++w4) {
+                  const uint4 v = *reinterpret_cast<const uint4*>((const uint32_t*)xp + 32 * un + 8 * jb + 4 * w4);
+                  xw[4 * w4] = v.x; xw[4 * w4 + 1] = v.y; xw[4 * w4 + 2] = v.z; xw[4 * w4 + 3] = v.w;
+                }
+                const float2 cb = corr[4 * un + jb];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  const uint32_t qw = jb == 0 ? gq[j][0].x : jb == 1 ? gq[j][0].y : jb == 2 ? gq[j][0].z : gq[j][0].w;
+                  const uint32_t mw = jb == 0 ? gq[j][1].x : jb == 1 ? gq[j][1].y : jb == 2 ? gq[j][1].z : gq[j][1].w;
+                  const float sc = kvq ? moe_f16_to_f32((uint16_t)(mw & 0xffff)) : 0.f;
+                  const float mn = kvq ? moe_f16_to_f32((uint16_t)(mw >> 16)) : 0.f;
+                  acc[j] += pt_q2_dot(qw, sc, mn, xw, cb);
+                }
+              }
+            }
+            // sum over the quarters (lanes l, l ^ 16, l ^ 32, l ^ 48)
+            float mine = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              float v = acc[j];
+              v += __shfl_xor(v, 16, 64);
+              v += __shfl_xor(v, 32, 64);
+              mine = lq == j ? v : mine;
+            }
+            red[(wave * PT_SLOTS + slot) * MT + t] = mine;
+          }
         }
         if (MT == 1) {  // row slot B: the single shared piece, 4 lane groups summed with shuffles
           float accB = 0.f;
@@ -959,8 +1048,8 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         // several tokens: the next group's gate/up rows are requested now (after
         // this group's down words, so that the down dots need not wait for
         // them) and land while this group's SiLU and down dots run
-        uint4 gqN[2][4];
-        uint2 gsN[2];
+        uint4 gqN[4][2];
+        uint32_t gsN[4];
         if (MT > 1) load_gu(min(gi + 1, gi1 - 1), gqN, gsN);
         __syncthreads();
         // ---- h = silu(gate) * up, 8 threads per (piece, token slot), then the
@@ -1057,10 +1146,10 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         __syncthreads();  // red, hp, hc are reused by the next batch
         if (MT > 1) {
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            gs[c] = gsN[c];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) gq[c][b] = gqN[c][b];
+          for (int j = 0; j < 4; ++j) {
+            gs[j] = gsN[j];
+            gq[j][0] = gqN[j][0];
+            gq[j][1] = gqN[j][1];
           }
         }
       }
