@@ -369,7 +369,7 @@ def test_decode_stack_tiny(moe, qfmt, T, path):
 
 
 @pytest.mark.parametrize("qfmt", [0, 1])
-@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
 def test_decode_stack_full_shape_persistent(moe, qfmt, T):
     """4 layers of the full shape (512 experts top-10, H=2048, F=768): the
     persistent kernel and the kernel chain, each checked against the oracle on
@@ -399,12 +399,14 @@ def test_decode_stack_full_shape_persistent(moe, qfmt, T):
         assert torch.equal(xo2, xo) and torch.equal(idx2, idx_o)
 
 
-def test_decode_stack_48_layers(moe):
-    """The whole 48-layer int4 stack (65 GB pool, Zipf routing bias), one
-    token, the persistent kernel: every layer input finite, and layers 0, 16,
-    32 and 47 checked against the oracle on the kernel's own layer inputs."""
+@pytest.mark.parametrize("qfmt", [0, 1])
+def test_decode_stack_48_layers(moe, qfmt):
+    """The whole 48-layer stack (int4: 65 GB pool; int2: 58 GB; Zipf routing
+    bias), one token, the persistent kernel: every layer input finite, and
+    layers 0, 16, 32 and 47 checked against the oracle on the kernel's own
+    layer inputs."""
     L = 48
-    li = C.layer_case(2, 1, 2048, 512, 10, 768, qfmt=0, bias=True, L=L, device="cuda")
+    li = C.layer_case(2, 1, 2048, 512, 10, 768, qfmt=qfmt, bias=True, L=L, device="cuda")
     x = li.x.contiguous()
     xo, idx_o, w_o, hist = _stack_run(moe, li, x, "persistent")
     assert bool(torch.isfinite(hist).all()) and bool(torch.isfinite(xo).all())
