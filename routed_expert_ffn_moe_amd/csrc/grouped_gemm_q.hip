@@ -32,6 +32,8 @@
 // (hardware dispatch places block b on XCD b % 8): the x rows and weights a
 // tile shares stay in that XCD's L2.
 #include <algorithm>
+#include <cstdlib>
+#include <cstring>
 
 #include "moe_common.h"
 #include "moe_sizes.h"
@@ -42,18 +44,19 @@
 #define GEMM_NB (GEMM_KC / 32)  // int4 blocks per K chunk
 #define GEMM_LDS_STRIDE 136     // halves per staged row (128 + 8 pad)
 
-// tile_start[g] = first tile of group g (exclusive scan of ceil(M_g / BM));
+// tile_start[g] = first tile of group g (exclusive scan of ceil(M_g / BM), BM a
+// multiple of 32);
 // tile_info[t] = {group, first row m0, rows, first h row of the group}: the
 // group's 32-row tiles split as evenly as possible over its BM-row tiles.
 __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __restrict__ offsets, int E, int T,
-                                                             int k, int32_t* __restrict__ tile_start,
+                                                             int k, int BM, int32_t* __restrict__ tile_start,
                                                              int4* __restrict__ tile_info) {
   __shared__ int s[2048];
   const int G = E + 1;
   for (int g = threadIdx.x; g < 2048; g += 1024) {
     int n = 0;
-    if (g < E) n = (offsets[g + 1] - offsets[g] + GEMM_BM - 1) / GEMM_BM;
-    else if (g == E) n = (T + GEMM_BM - 1) / GEMM_BM;
+    if (g < E) n = (offsets[g + 1] - offsets[g] + BM - 1) / BM;
+    else if (g == E) n = (T + BM - 1) / BM;
     s[g] = n;
   }
   __syncthreads();
@@ -382,6 +385,275 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
   }
 }
 
+// ---------------------------------------------------------------- gemm2
+// The same contraction with tiles of up to 160 rows (5 MFMA row tiles) x 256
+// weight rows and K chunks of 64.  Wave w owns two 32-wide column tiles (for
+// gate/up: the gate and the up columns of the same 32 f values, which the
+// record interleaves in runs of 32, so SiLU*mul happens in registers); each
+// dequantised B operand feeds up to 5 MFMAs (a 160-row expert is one tile,
+// not 64 + 96 rows) and each A operand read from LDS feeds 2.
+#define G2_BM 160
+#define G2_BN 256
+#define G2_KC 64
+#define G2_NB (G2_KC / 32)  // int4 blocks per K chunk
+#define G2_STRIDE 72        // halves per staged row (64 + 8 pad)
+#define G2_RT (G2_BM / 32)  // MFMA row tiles per workgroup tile
+#define G2_NA ((G2_BM * G2_KC / 8 + 255) / 256)  // 16-byte A words per staging thread
+
+template <int QFMT>
+struct B2Regs;  // raw weight words of one K chunk (64) for one lane and one column tile
+template <>
+struct B2Regs<MOE_Q4_B32> {
+  uint2 q[G2_NB];  // [block in chunk]: dwords 2hh, 2hh+1 of the block
+  uint32_t s;      // fp16 scales of the chunk's two blocks
+};
+template <>
+struct B2Regs<MOE_Q2_B16> {
+  uint4 q;  // the chunk's q-unit (4 blocks of 16)
+  uint4 m;  // its meta unit
+};
+// for a wave's two column tiles
+template <int QFMT>
+struct B2Pair {
+  B2Regs<QFMT> t[2];
+};
+
+__device__ __forceinline__ void load_b2(B2Regs<MOE_Q4_B32>& b, const uint8_t* rec, const MoePlanes& pl, int rows,
+                                        int r, int hh, int c, bool gu) {
+  const uint32_t q_off = (uint32_t)(gu ? pl.gu_q : pl.d_q), s_off = (uint32_t)(gu ? pl.gu_s : pl.d_s);
+  const uint32_t R = (uint32_t)rows, ur = (uint32_t)r;
+#pragma unroll
+  for (int bi = 0; bi < G2_NB; ++bi) {
+    const uint32_t kb = (uint32_t)(G2_NB * c + bi);
+    b.q[bi] = *reinterpret_cast<const uint2*>(rec + (q_off + 16u * (kb * R + ur) + 8u * (uint32_t)hh));
+  }
+  const uint32_t kb0 = (uint32_t)(G2_NB * c);  // even
+  if (gu)  // 4-block groups [kb/4][row][4]: the two scales are half of the group's word
+    b.s = *reinterpret_cast<const uint32_t*>(rec + (s_off + 2u * ((kb0 >> 2) * R * 4u + 4u * ur + (kb0 & 3u))));
+  else {   // per block [kb][row]
+    const uint32_t s0 = *reinterpret_cast<const uint16_t*>(rec + (s_off + 2u * (kb0 * R + ur)));
+    const uint32_t s1 = *reinterpret_cast<const uint16_t*>(rec + (s_off + 2u * ((kb0 + 1u) * R + ur)));
+    b.s = s0 | (s1 << 16);
+  }
+}
+
+__device__ __forceinline__ void load_b2(B2Regs<MOE_Q2_B16>& b, const uint8_t* rec, const MoePlanes& pl, int rows,
+                                        int r, int hh, int c, bool gu) {
+  const uint32_t q_off = (uint32_t)(gu ? pl.gu_q : pl.d_q), m_off = (uint32_t)(gu ? pl.gu_s : pl.d_s);
+  const uint32_t R = (uint32_t)rows, ur = (uint32_t)r, un = (uint32_t)c;  // one 4-block unit per chunk
+  if (gu) {
+    b.q = *reinterpret_cast<const uint4*>(rec + (q_off + 16u * (un * R + ur)));
+    b.m = *reinterpret_cast<const uint4*>(rec + (m_off + 16u * (un * R + ur)));
+  } else {  // per block [b][row]
+    uint32_t qw[4], mw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      qw[j] = *reinterpret_cast<const uint32_t*>(rec + (q_off + 4u * ((4u * un + j) * R + ur)));
+      mw[j] = *reinterpret_cast<const uint32_t*>(rec + (m_off + 4u * ((4u * un + j) * R + ur)));
+    }
+    b.q = make_uint4(qw[0], qw[1], qw[2], qw[3]);
+    b.m = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+  }
+  (void)hh;
+}
+
+// The K loop of gemm2 for NRT row tiles: A chunks staged through registers
+// into a double-buffered LDS tile (the next chunk's A and B words are
+// requested before the current chunk's MFMAs), B dequantised in registers.
+template <int QFMT, bool GU, int NRT>
+__device__ __forceinline__ void gemm2_k_loop(const uint16_t* __restrict__ a_src, int K, int rows, const uint8_t* rec,
+                                             const MoePlanes& pl, int nbase, const int* arow,
+                                             _Float16 (*As)[G2_BM * G2_STRIDE], float16v (&acc)[G2_RT][2]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int hh = lane >> 5, ln = lane & 31;
+  constexpr int NW = NRT * 32 * G2_KC / 8;     // 16-byte A words of a chunk
+  constexpr int NA = (NW + 255) / 256;         // per thread
+  int src[NA];     // source row (clamped) of each staged word
+  bool live[NA];   // the row has a source (else the word is zero)
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    const int i = min(tid + 256 * j, NW - 1);
+    const int r = arow[i >> 3];
+    live[j] = r >= 0;
+    src[j] = r >= 0 ? r : 0;
+  }
+  uint4 areg[NA];
+  auto load_a = [&](int c) {
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int i = min(tid + 256 * j, NW - 1);
+      const uint4 v = *reinterpret_cast<const uint4*>(a_src + (size_t)src[j] * K + c * G2_KC + 8 * (i & 7));
+      areg[j] = live[j] ? v : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_a = [&](int stage) {
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int i = tid + 256 * j;
+      if (i < NW) *reinterpret_cast<uint4*>(&As[stage][(i >> 3) * G2_STRIDE + 8 * (i & 7)]) = areg[j];
+    }
+  };
+  const int brow0 = min(nbase + ln, rows - 1), brow1 = min(nbase + 32 + ln, rows - 1);
+  const int nc = K / G2_KC;
+  B2Pair<QFMT> bcur, bnext;
+  load_a(0);
+  load_b2(bcur.t[0], rec, pl, rows, brow0, hh, 0, GU);
+  load_b2(bcur.t[1], rec, pl, rows, brow1, hh, 0, GU);
+  store_a(0);
+  __syncthreads();
+  for (int c = 0; c < nc; ++c) {
+    const int stage = c & 1;
+    const int cn = min(c + 1, nc - 1);  // the last chunk requests itself again (unused)
+    load_a(cn);
+    load_b2(bnext.t[0], rec, pl, rows, brow0, hh, cn, GU);
+    load_b2(bnext.t[1], rec, pl, rows, brow1, hh, cn, GU);
+    const _Float16* Ab = &As[stage][0];
+    if constexpr (QFMT == MOE_Q4_B32) {
+#pragma unroll
+      for (int bi = 0; bi < G2_NB; ++bi) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int kk = 32 * bi + 16 * hh + 8 * s;
+          half8v af[NRT];
+#pragma unroll
+          for (int i = 0; i < NRT; ++i) af[i] = *reinterpret_cast<const half8v*>(&Ab[(32 * i + ln) * G2_STRIDE + kk]);
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub) {
+            const B2Regs<QFMT>& B = bcur.t[sub];
+            const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(B.s >> (16 * bi)));
+            const half2v s2 = {sc, sc};
+            const half8v bf = deq_q4(s == 0 ? B.q[bi].x : B.q[bi].y, s2);
+#pragma unroll
+            for (int i = 0; i < NRT; ++i)
+              acc[i][sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf, acc[i][sub], 0, 0, 0);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int kk = 16 * jj + 8 * hh;
+        half8v af[NRT];
+#pragma unroll
+        for (int i = 0; i < NRT; ++i) af[i] = *reinterpret_cast<const half8v*>(&Ab[(32 * i + ln) * G2_STRIDE + kk]);
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const B2Regs<QFMT>& B = bcur.t[sub];
+          const uint32_t qw = jj == 0 ? B.q.x : jj == 1 ? B.q.y : jj == 2 ? B.q.z : B.q.w;
+          const uint32_t mw = jj == 0 ? B.m.x : jj == 1 ? B.m.y : jj == 2 ? B.m.z : B.m.w;
+          const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(mw & 0xffff));
+          const _Float16 mn = __builtin_bit_cast(_Float16, (uint16_t)(mw >> 16));
+          const half2v s2 = {sc, sc}, m2 = {mn, mn};
+          const half8v bf = deq_q2(qw, hh, s2, m2);
+#pragma unroll
+          for (int i = 0; i < NRT; ++i)
+            acc[i][sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf, acc[i][sub], 0, 0, 0);
+        }
+      }
+    }
+    store_a(stage ^ 1);  // (after the last chunk: a harmless rewrite of the free stage)
+    __syncthreads();
+    bcur = bnext;
+  }
+}
+
+template <int QFMT, bool GU>
+__global__ __launch_bounds__(256, 2) void gemm2_kernel(const uint16_t* __restrict__ a_src, int T, int H, int F, int k,
+                                                       int E, const int32_t* __restrict__ row_src,
+                                                       const int32_t* __restrict__ tile_start,
+                                                       const int4* __restrict__ tile_info,
+                                                       const int32_t* __restrict__ slot_table, int layer,
+                                                       const uint8_t* __restrict__ pool, int64_t record_bytes,
+                                                       _Float16* __restrict__ h_out, float* __restrict__ y_perm,
+                                                       float* __restrict__ y_shared, int n_ntiles) {
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][G2_BM * G2_STRIDE];
+  __shared__ int arow[G2_BM];
+
+  // XCD-aware renumbering (block b runs on XCD b % 8): the work count is cut
+  // into 8 consecutive ranges, one per XCD, so that the column tiles of one
+  // row tile and the row tiles of one expert share an XCD's L2
+  const int bid = blockIdx.x;
+  const int nwork = tile_start[E + 1] * n_ntiles;
+  const int per_xcd = (nwork + 7) >> 3;
+  const int idx = bid >> 3;
+  const int work = (bid & 7) * per_xcd + idx;
+  if (idx >= per_xcd || work >= nwork) return;
+  const int tile = work / n_ntiles, nt = work % n_ntiles;
+  const int4 ti = tile_info[tile];
+  const int g = ti.x, m0 = ti.y, mv = ti.z, gbase = ti.w;
+  const int nrt = (mv + 31) / 32;  // row tiles present (<= 5)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, ln = lane & 31;
+  const int K = GU ? H : F;
+  const int rows = GU ? 2 * F : H;
+  const int nbase = nt * G2_BN + 64 * wave;  // this wave's 64 weight rows
+  const bool active = nbase < rows;
+
+  if (tid < G2_BM) {
+    int r = -1;
+    if (tid < mv) {
+      if (GU) r = g < E ? row_src[gbase + m0 + tid] / k : m0 + tid;
+      else r = gbase + m0 + tid;
+    }
+    arow[tid] = r;
+  }
+  const int64_t slot = slot_table[(size_t)layer * (E + 1) + g];
+  const uint8_t* rec = pool + slot * record_bytes;
+  const MoePlanes pl = moe_planes(QFMT, H, F);
+  __syncthreads();
+
+  float16v acc[G2_RT][2];
+#pragma unroll
+  for (int i = 0; i < G2_RT; ++i)
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][sub][v] = 0.f;
+  // The K loop, specialised on the row-tile count (uniform per workgroup),
+  // so that it has no branches: its loads are unconditional (indices clamped
+  // into range; rows without a source are zeroed after the load) and the
+  // waits the compiler places count only the loads a step really needs.
+  switch (nrt) {
+    case 1: gemm2_k_loop<QFMT, GU, 1>(a_src, K, rows, rec, pl, nbase, arow, As, acc); break;
+    case 2: gemm2_k_loop<QFMT, GU, 2>(a_src, K, rows, rec, pl, nbase, arow, As, acc); break;
+    case 3: gemm2_k_loop<QFMT, GU, 3>(a_src, K, rows, rec, pl, nbase, arow, As, acc); break;
+    case 4: gemm2_k_loop<QFMT, GU, 4>(a_src, K, rows, rec, pl, nbase, arow, As, acc); break;
+    default: gemm2_k_loop<QFMT, GU, 5>(a_src, K, rows, rec, pl, nbase, arow, As, acc); break;
+  }
+
+  // epilogue: lane holds column ln, rows 8*(v/4) + 4*hh + v%4 of each 32-row tile
+  if (!active) return;
+  if constexpr (GU) {
+    const int f = 32 * (nbase / 64) + ln;
+    _Float16* hb = h_out + (size_t)(gbase + m0) * F + f;
+#pragma unroll
+    for (int i = 0; i < G2_RT; ++i) {
+      if (i >= nrt) break;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (r < mv) hb[(uint32_t)(r * F)] = (_Float16)(moe_silu_fast(acc[i][0][v]) * acc[i][1][v]);
+      }
+    }
+  } else {
+    float* yb = g < E ? y_perm + (size_t)(gbase + m0) * H : y_shared + (size_t)m0 * H;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int col = nbase + 32 * sub + ln;
+#pragma unroll
+      for (int i = 0; i < G2_RT; ++i) {
+        if (i >= nrt) break;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (r < mv) yb[(uint32_t)(r * H + col)] = acc[i][sub][v];
+        }
+      }
+    }
+  }
+}
+
 template <int QFMT>
 static int launch_gemm_t(const uint16_t* x, int T, int H, int F, const int32_t* row_src, const int32_t* offsets,
                          int k, int E, const int32_t* slot_table, int layer, const void* pool, int64_t record_bytes,
@@ -390,13 +662,26 @@ static int launch_gemm_t(const uint16_t* x, int T, int H, int F, const int32_t* 
   int4* tile_info = (int4*)((uint8_t*)ws + moe_gemm_info_offset(E));
   _Float16* h = (_Float16*)((uint8_t*)ws + moe_gemm_h_offset(T, k, E));
   uint16_t* x16 = (uint16_t*)((uint8_t*)ws + moe_gemm_x16_offset(T, k, E, F));
-  gemm_schedule_kernel<<<1, 1024, 0, st>>>(offsets, E, T, k, tile_start, tile_info);
+  const char* kv = getenv("MOE_GEMM_KERNEL");
+  const bool v2 = !(kv && strcmp(kv, "v1") == 0);
+  gemm_schedule_kernel<<<1, 1024, 0, st>>>(offsets, E, T, k, v2 ? G2_BM : GEMM_BM, tile_start, tile_info);
   {
     const size_t n8 = (size_t)T * H / 8;
     const int grid = (int)std::min<size_t>((n8 + 255) / 256, 4096);
     x_to_f16_kernel<<<grid, 256, 0, st>>>((const uint4*)x, n8, (uint4*)x16);
   }
-  const int max_tiles = moe_gemm_max_tiles(T, k, E);
+  const int max_tiles = moe_gemm_max_tiles(T, k, E);  // bounds the tile count for BM >= 128
+  if (v2) {
+    const int nnt_gu = (2 * F + G2_BN - 1) / G2_BN, nnt_d = (H + G2_BN - 1) / G2_BN;
+    const int tot_gu = (max_tiles * nnt_gu + 7) / 8 * 8, tot_d = (max_tiles * nnt_d + 7) / 8 * 8;
+    gemm2_kernel<QFMT, true><<<tot_gu, 256, 0, st>>>(x16, T, H, F, k, E, row_src, tile_start, tile_info, slot_table,
+                                                     layer, (const uint8_t*)pool, record_bytes, h, y_perm, y_shared,
+                                                     nnt_gu);
+    gemm2_kernel<QFMT, false><<<tot_d, 256, 0, st>>>((const uint16_t*)h, T, H, F, k, E, row_src, tile_start, tile_info,
+                                                      slot_table, layer, (const uint8_t*)pool, record_bytes, h, y_perm,
+                                                      y_shared, nnt_d);
+    return moe_check_launch("grouped gemm");
+  }
   {
     const int nnt = (2 * F + GEMM_BN - 1) / GEMM_BN;
     const int total = (max_tiles * nnt + 7) / 8 * 8;
