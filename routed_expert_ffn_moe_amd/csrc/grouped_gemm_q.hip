@@ -8,8 +8,7 @@
 //
 // Per group g (expert g < E with rows offsets[g]..offsets[g+1], or the shared
 // expert g == E with rows 0..T-1): its ceil(M/32) row tiles of 32 are split as
-// evenly as possible over ceil(M/128) workgroup tiles (at most 4 row tiles
-// each, so a 160-row expert runs as 64 + 96 rows, not 128 + 128):
+// evenly as possible over ceil(M/BM) workgroup tiles:
 //   gate/up pass: G|U = X_rows . [Wg|Wu]^T, h = fp16(silu(G) * U)  -> ws
 //   down pass:    Y   = h_rows . Wd^T (fp32)                       -> y_perm / y_shared
 // MFMA v_mfma_f32_32x32x16_f16.  Weights are dequantised in registers to
@@ -17,15 +16,21 @@
 // converted to fp16 (exact in fp16's normal range) once, into the workspace,
 // before the gate/up pass; accumulation is fp32.
 //
-// Workgroup: 4 waves, tile of up to 128 rows x 256 weight rows; wave w owns
-// weight rows nbase..nbase+63 = two 32-wide MFMA column tiles and the tile's
-// (up to four) 32-row MFMA row tiles (128 fp32 accumulators per lane); the
-// MFMAs of absent row tiles are skipped.  For the gate/up pass the
-// record interleaves gate and up rows in runs of 32, so a wave's two column
-// tiles are gate and up of the same 32 f values and SiLU*mul happens in
-// registers.  K is walked 128 at a time with the next chunk's A tile and B
-// words prefetched into registers (LDS double buffer); the chunk is long
-// enough that its MFMA work covers the prefetch's memory latency.
+// Two kernels compute it (gemm2_kernel is the one used; gemm_kernel, the
+// first version, is kept behind MOE_GEMM_KERNEL=v1 for comparison).  Both
+// use workgroups of 4 waves where wave w owns weight rows nbase..nbase+63 =
+// two 32-wide MFMA column tiles over the tile's 32-row MFMA row tiles; for
+// the gate/up pass the record interleaves gate and up rows in runs of 32, so
+// a wave's two column tiles are gate and up of the same 32 f values and
+// SiLU*mul happens in registers.  The next K chunk's A tile and B words are
+// requested before the current chunk's MFMAs (A through registers into a
+// double-buffered LDS tile).
+//   gemm_kernel:  BM = 128 (a 160-row expert runs as 64 + 96 rows), K chunks
+//                 of 128, the MFMAs of absent row tiles skipped by branches.
+//   gemm2_kernel: BM = 160 (a typical expert is one tile, each dequantised
+//                 weight operand feeds up to 5 MFMAs), K chunks of 64, and a
+//                 K loop specialised on the row-tile count: no branches, so
+//                 the compiler's waits count only the loads a step needs.
 //
 // Blocks are renumbered so that consecutive work items (the column tiles of
 // one row tile, then the row tiles of one expert) land on the same XCD
