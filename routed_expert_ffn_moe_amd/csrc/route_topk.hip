@@ -105,27 +105,29 @@ __global__ __launch_bounds__(256, 2) void router_mfma_kernel(const uint16_t* __r
         B[i][2 * q + 1] = pb[1];
       }
   };
-  const int nc = H / 64;
-  load(a, b, 0);
-  for (int c = 0; c < nc; ++c) {
-    if (c + 1 < nc) load(an, bn, c + 1);
+  const int nc = H / 64;  // even: H is a multiple of 128
+  auto mfmas = [&](const uint4 (&A)[2][4], const uint4 (&B)[2][4]) {
 #pragma unroll
     for (int s8 = 0; s8 < 4; ++s8)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, a[i][s8]),
-                                                             __builtin_bit_cast(bf16x8v, b[j][s8]), acc[i][j], 0, 0, 0);
-    if (c + 1 < nc) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          a[i][q] = an[i][q];
-          b[i][q] = bn[i][q];
-        }
-    }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, A[i][s8]),
+                                                             __builtin_bit_cast(bf16x8v, B[j][s8]), acc[i][j], 0, 0, 0);
+  };
+  // two register buffers in turn (no copy between them, which would make
+  // the compiler wait for the prefetch at the end of every chunk); every
+  // prefetch is unconditional (the last chunks request themselves again)
+  // and issued before the MFMAs of the chunk in hand
+  load(a, b, 0);
+  for (int c = 0; c < nc; c += 2) {
+    load(an, bn, min(c + 1, nc - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(a, b);
+    load(a, b, min(c + 2, nc - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(an, bn);
   }
   // lane holds expert column ln, tokens 8*(v/4) + 4*hh + v%4 of each 32 x 32 tile
 #pragma unroll
