@@ -86,6 +86,10 @@ __device__ __forceinline__ int pt_tid() {
 }
 __device__ __forceinline__ int pt_lane() { return pt_tid() & 63; }
 
+// Polling loops here do not sleep between rounds: each round is a memory
+// round trip and a workgroup barrier already, and a sleep only delayed the
+// detection (measured: 1.2% of a decode step).
+//
 // Waits until word base[first + g * stride] carries `tag` for every g < n
 // (one word per producing workgroup), polling 4 bytes of tag per producer
 // instead of all of its data.  The data itself is read and every tag checked
@@ -98,7 +102,6 @@ __device__ bool pt_wait_sentinels(u64* base, uint32_t first, uint32_t stride, in
       mine &= (uint32_t)(pt_load(base, first + (uint32_t)i * stride) >> 32) == tag;
     if (__syncthreads_and(mine)) return true;
     if (it > spin_max) return false;
-    __builtin_amdgcn_s_sleep(2);
   }
 }
 __device__ __forceinline__ uint32_t pt_tag(uint32_t call, int L, int l) {
@@ -653,7 +656,6 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
           break;
         }
         if (it > PT_SPIN_MAX) { ok = false; break; }
-        __builtin_amdgcn_s_sleep(2);
       }
       if (!ok) break;
     }
@@ -750,7 +752,6 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         break;
       }
       if (it > PT_SPIN_MAX) { ok = false; break; }
-      __builtin_amdgcn_s_sleep(2);
     }
     if (!ok) break;
 #pragma unroll
@@ -1210,7 +1211,6 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
           sum = sacc;
           if (__syncthreads_and(mine || !act)) break;
           if (it > PT_SPIN_MAX) { ok = false; break; }
-          __builtin_amdgcn_s_sleep(2);
         }
         if (!ok) break;
 #pragma unroll
