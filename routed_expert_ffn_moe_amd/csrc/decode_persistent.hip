@@ -263,7 +263,7 @@ __device__ __forceinline__ void pt_topk_rounds(uint32_t (&hi)[SLOTS], int k, uin
 // Top-k of one token's E logits (LDS) by one wave.  Lane l holds the keys of
 // experts l + 64 * i (i < SLOTS): the order-preserving bits of the logit; the
 // order is by key, and on equal keys the lower expert first.
-//  1. tau = the k-th largest lane maximum, its top 20 bits found with ballots
+//  1. tau = the k-th largest lane maximum, its top 16 bits found with ballots
 //     (the rest left 0): at least k keys are >= tau, so every chosen
 //     expert's key is >= tau.
 //  2. The keys >= tau (usually a few more than k) are packed into `cand` as
@@ -287,15 +287,13 @@ __device__ __forceinline__ uint32_t pt_topk_select(const float* lg, int E, int k
     hi[i] = lane + 64 * i < E ? key : 0u;  // every real key is > 0
     head = max(head, hi[i]);
   }
-  // two bits per step, from bits 31..30 down to 13..12; the low 12 bits stay
-  // 0, which only lowers tau (a few more candidates at most)
+  // one bit per step, bits 31..16; the low 16 bits stay 0, which only lowers
+  // tau (keys within about 1% of the k-th lane maximum join the candidates)
   uint32_t tau = 0u;
 #pragma unroll
-  for (int b = 30; b >= 12; b -= 2) {
-    const uint32_t c1 = tau | (1u << b), c2 = tau | (2u << b), c3 = tau | (3u << b);
-    const int n1 = __popcll(__ballot(head >= c1)), n2 = __popcll(__ballot(head >= c2));
-    const int n3 = __popcll(__ballot(head >= c3));
-    tau = n3 >= k ? c3 : n2 >= k ? c2 : n1 >= k ? c1 : tau;
+  for (int b = 31; b >= 16; --b) {
+    const uint32_t c = tau | (1u << b);
+    tau = __popcll(__ballot(head >= c)) >= k ? c : tau;
   }
   int n = 0;
 #pragma unroll
@@ -638,10 +636,8 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     } else {
       const uint32_t ptag = pt_tag(call, L, l - 1);
       const int last = T * H - 1;
-      if (!pt_wait_sentinels(a.xbuf, (uint32_t)((T - 1) * H + a.rpw - 1), (uint32_t)a.rpw, G, ptag, PT_SPIN_MAX)) {
-        ok = false;
-        break;
-      }
+      // x is polled word by word (every word carries its tag): one round trip
+      // less than waiting for per-producer sentinels first
       for (int it = 0;; ++it) {
         u64 w[NX];
 #pragma unroll
