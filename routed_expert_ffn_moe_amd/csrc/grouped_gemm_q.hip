@@ -175,13 +175,22 @@ __device__ __forceinline__ void load_b(BRegs<MOE_Q2_B16>& b, const uint8_t* rec,
   (void)hh;
 }
 
-// fp16(s*q) for 8 consecutive int4 values of one dword (natural order).
-__device__ __forceinline__ half8v deq_q4(uint32_t w, half2v s2) {
+// The nibble mask held in a register: (x & mask) | magic is then one
+// v_and_or_b32 (with both operands literal constants it takes two
+// instructions, the VOP3 encoding taking no literal here).
+__device__ __forceinline__ uint32_t moe_vgpr_const(uint32_t c) {
+  asm volatile("" : "+v"(c));
+  return c;
+}
+
+// fp16(s*q) for 8 consecutive int4 values of one dword (natural order);
+// m4 = 0x000F000F (in a register).
+__device__ __forceinline__ half8v deq_q4(uint32_t w, half2v s2, uint32_t m4) {
   const half2v k1032 = {(_Float16)1032.f, (_Float16)1032.f};
   half8v r;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    half2v q = moe_u32_as_half2(((w >> (4 * p)) & 0x000F000Fu) | MOE_F16_1024X2) - k1032;
+    half2v q = moe_u32_as_half2(((w >> (4 * p)) & m4) | MOE_F16_1024X2) - k1032;
     half2v v = q * s2;
     r[2 * p] = v[0];
     r[2 * p + 1] = v[1];
@@ -189,14 +198,15 @@ __device__ __forceinline__ half8v deq_q4(uint32_t w, half2v s2) {
   return r;
 }
 
-// fp16(s*q+m) for values 8hh..8hh+7 of one int2 block word.
-__device__ __forceinline__ half8v deq_q2(uint32_t w, int hh, half2v s2, half2v m2) {
+// fp16(s*q+m) for values 8hh..8hh+7 of one int2 block word; m2b = 0x00030003
+// (in a register).
+__device__ __forceinline__ half8v deq_q2(uint32_t w, int hh, half2v s2, half2v m2, uint32_t m2b) {
   const half2v k1024 = {(_Float16)1024.f, (_Float16)1024.f};
   const uint32_t x = w >> (8 * hh);
   half8v r;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    half2v q = moe_u32_as_half2(((x >> (2 * p)) & 0x00030003u) | MOE_F16_1024X2) - k1024;
+    half2v q = moe_u32_as_half2(((x >> (2 * p)) & m2b) | MOE_F16_1024X2) - k1024;
     half2v v = __builtin_elementwise_fma(q, s2, m2);
     r[2 * p] = v[0];
     r[2 * p + 1] = v[1];
@@ -284,6 +294,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
       for (int v = 0; v < 16; ++v) acc[i][s][v] = 0.f;
 
   const int nc = K / GEMM_KC;
+  const uint32_t m4 = moe_vgpr_const(0x000F000Fu), m2b = moe_vgpr_const(0x00030003u);
   BRegs<QFMT> bcur, bnext;
   load_a(0);
   if (active) load_b(bcur, rec, pl, rows, nbase + ln, hh, 0, GU);
@@ -309,7 +320,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
             for (int sub = 0; sub < 2; ++sub) {
               const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(B.s[sub][bi >> 1] >> (16 * (bi & 1))));
               const half2v s2 = {sc, sc};
-              bf[sub] = deq_q4(s == 0 ? B.q[sub][bi].x : B.q[sub][bi].y, s2);
+              bf[sub] = deq_q4(s == 0 ? B.q[sub][bi].x : B.q[sub][bi].y, s2, m4);
             }
             const int kk = 32 * bi + 16 * hh + 8 * s;
 #pragma unroll
@@ -336,7 +347,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
             const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(mw & 0xffff));
             const _Float16 mn = __builtin_bit_cast(_Float16, (uint16_t)(mw >> 16));
             const half2v s2 = {sc, sc}, m2 = {mn, mn};
-            bf[sub] = deq_q2(qw, hh, s2, m2);
+            bf[sub] = deq_q2(qw, hh, s2, m2, m2b);
           }
           const int kk = 16 * jj + 8 * hh;
 #pragma unroll
@@ -500,6 +511,7 @@ __device__ __forceinline__ void gemm2_k_loop(const uint16_t* __restrict__ a_src,
   };
   const int brow0 = min(nbase + ln, rows - 1), brow1 = min(nbase + 32 + ln, rows - 1);
   const int nc = K / G2_KC;
+  const uint32_t m4 = moe_vgpr_const(0x000F000Fu), m2b = moe_vgpr_const(0x00030003u);
   B2Pair<QFMT> bcur, bnext;
   load_a(0);
   load_b2(bcur.t[0], rec, pl, rows, brow0, hh, 0, GU);
@@ -527,7 +539,7 @@ __device__ __forceinline__ void gemm2_k_loop(const uint16_t* __restrict__ a_src,
             const B2Regs<QFMT>& B = bcur.t[sub];
             const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(B.s >> (16 * bi)));
             const half2v s2 = {sc, sc};
-            const half8v bf = deq_q4(s == 0 ? B.q[bi].x : B.q[bi].y, s2);
+            const half8v bf = deq_q4(s == 0 ? B.q[bi].x : B.q[bi].y, s2, m4);
 #pragma unroll
             for (int i = 0; i < NRT; ++i)
               acc[i][sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf, acc[i][sub], 0, 0, 0);
@@ -549,7 +561,7 @@ __device__ __forceinline__ void gemm2_k_loop(const uint16_t* __restrict__ a_src,
           const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(mw & 0xffff));
           const _Float16 mn = __builtin_bit_cast(_Float16, (uint16_t)(mw >> 16));
           const half2v s2 = {sc, sc}, m2 = {mn, mn};
-          const half8v bf = deq_q2(qw, hh, s2, m2);
+          const half8v bf = deq_q2(qw, hh, s2, m2, m2b);
 #pragma unroll
           for (int i = 0; i < NRT; ++i)
             acc[i][sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf, acc[i][sub], 0, 0, 0);
