@@ -109,53 +109,71 @@ __device__ __forceinline__ uint32_t pt_tag(uint32_t call, int L, int l) {
 }
 
 // ---------------------------------------------------------------- small helpers
+// The nibble / crumb masks of the dots, held in registers (made opaque once
+// per layer): (x & mask) | magic is then one v_and_or_b32; with both
+// operands literal constants it takes two instructions, as the VOP3
+// encoding takes no literal here.  int4: q = 0x000F000F, r = 0x00F000F0;
+// int2: q, r, s, t = 0x00030003 << 2i.
+struct PtMask {
+  uint32_t q, r, s, t;
+};
+__device__ __forceinline__ PtMask pt_masks(int qfmt) {
+  PtMask m;
+  if (qfmt == MOE_Q4_B32) {
+    m.q = 0x000F000Fu; m.r = 0x00F000F0u; m.s = 0u; m.t = 0u;
+  } else {
+    m.q = 0x00030003u; m.r = 0x000C000Cu; m.s = 0x00300030u; m.t = 0x00C000C0u;
+  }
+  asm volatile("" : "+v"(m.q), "+v"(m.r), "+v"(m.s), "+v"(m.t));
+  return m;
+}
 // dot of one int4 block (16 bytes) with a prepared activation block
-__device__ __forceinline__ float pt_q4_dot(uint4 q, const uint32_t* xp, float c) {
+__device__ __forceinline__ float pt_q4_dot(uint4 q, const uint32_t* xp, float c, const PtMask& mk) {
   const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
   float d = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint32_t w = qw[j], w8 = qw[j] >> 8;
-    d = moe_dot2(moe_u32_as_half2((w & 0x000F000Fu) | MOE_F16_1024X2), moe_u32_as_half2(xp[4 * j + 0]), d);
-    d = moe_dot2(moe_u32_as_half2((w & 0x00F000F0u) | MOE_F16_1024X2), moe_u32_as_half2(xp[4 * j + 1]), d);
-    d = moe_dot2(moe_u32_as_half2((w8 & 0x000F000Fu) | MOE_F16_1024X2), moe_u32_as_half2(xp[4 * j + 2]), d);
-    d = moe_dot2(moe_u32_as_half2((w8 & 0x00F000F0u) | MOE_F16_1024X2), moe_u32_as_half2(xp[4 * j + 3]), d);
+    d = moe_dot2(moe_u32_as_half2((w & mk.q) | MOE_F16_1024X2), moe_u32_as_half2(xp[4 * j + 0]), d);
+    d = moe_dot2(moe_u32_as_half2((w & mk.r) | MOE_F16_1024X2), moe_u32_as_half2(xp[4 * j + 1]), d);
+    d = moe_dot2(moe_u32_as_half2((w8 & mk.q) | MOE_F16_1024X2), moe_u32_as_half2(xp[4 * j + 2]), d);
+    d = moe_dot2(moe_u32_as_half2((w8 & mk.r) | MOE_F16_1024X2), moe_u32_as_half2(xp[4 * j + 3]), d);
   }
   return d - c;
 }
 // one int2 block (one word) with a prepared block: s * (dot - c0) + m * sum(x)
-__device__ __forceinline__ float pt_q2_dot(uint32_t w, float s, float m, const uint32_t* xp, float2 c) {
+__device__ __forceinline__ float pt_q2_dot(uint32_t w, float s, float m, const uint32_t* xp, float2 c, const PtMask& mk) {
   const uint32_t w8 = w >> 8;
   float d = 0.f;
-  d = moe_dot2(moe_u32_as_half2((w & 0x00030003u) | MOE_F16_1024X2), moe_u32_as_half2(xp[0]), d);
-  d = moe_dot2(moe_u32_as_half2((w & 0x000C000Cu) | MOE_F16_1024X2), moe_u32_as_half2(xp[1]), d);
-  d = moe_dot2(moe_u32_as_half2((w & 0x00300030u) | MOE_F16_1024X2), moe_u32_as_half2(xp[2]), d);
-  d = moe_dot2(moe_u32_as_half2((w & 0x00C000C0u) | MOE_F16_1024X2), moe_u32_as_half2(xp[3]), d);
-  d = moe_dot2(moe_u32_as_half2((w8 & 0x00030003u) | MOE_F16_1024X2), moe_u32_as_half2(xp[4]), d);
-  d = moe_dot2(moe_u32_as_half2((w8 & 0x000C000Cu) | MOE_F16_1024X2), moe_u32_as_half2(xp[5]), d);
-  d = moe_dot2(moe_u32_as_half2((w8 & 0x00300030u) | MOE_F16_1024X2), moe_u32_as_half2(xp[6]), d);
-  d = moe_dot2(moe_u32_as_half2((w8 & 0x00C000C0u) | MOE_F16_1024X2), moe_u32_as_half2(xp[7]), d);
+  d = moe_dot2(moe_u32_as_half2((w & mk.q) | MOE_F16_1024X2), moe_u32_as_half2(xp[0]), d);
+  d = moe_dot2(moe_u32_as_half2((w & mk.r) | MOE_F16_1024X2), moe_u32_as_half2(xp[1]), d);
+  d = moe_dot2(moe_u32_as_half2((w & mk.s) | MOE_F16_1024X2), moe_u32_as_half2(xp[2]), d);
+  d = moe_dot2(moe_u32_as_half2((w & mk.t) | MOE_F16_1024X2), moe_u32_as_half2(xp[3]), d);
+  d = moe_dot2(moe_u32_as_half2((w8 & mk.q) | MOE_F16_1024X2), moe_u32_as_half2(xp[4]), d);
+  d = moe_dot2(moe_u32_as_half2((w8 & mk.r) | MOE_F16_1024X2), moe_u32_as_half2(xp[5]), d);
+  d = moe_dot2(moe_u32_as_half2((w8 & mk.s) | MOE_F16_1024X2), moe_u32_as_half2(xp[6]), d);
+  d = moe_dot2(moe_u32_as_half2((w8 & mk.t) | MOE_F16_1024X2), moe_u32_as_half2(xp[7]), d);
   return fmaf(s, d - c.x, m * c.y);
 }
 
 // dot of one int4 word (8 values) with its prepared activations xp[4]
-__device__ __forceinline__ float pt_q4_word(uint32_t w, const uint32_t* xp, float c) {
+__device__ __forceinline__ float pt_q4_word(uint32_t w, const uint32_t* xp, float c, const PtMask& mk) {
   const uint32_t w8 = w >> 8;
   float d = 0.f;
-  d = moe_dot2(moe_u32_as_half2((w & 0x000F000Fu) | MOE_F16_1024X2), moe_u32_as_half2(xp[0]), d);
-  d = moe_dot2(moe_u32_as_half2((w & 0x00F000F0u) | MOE_F16_1024X2), moe_u32_as_half2(xp[1]), d);
-  d = moe_dot2(moe_u32_as_half2((w8 & 0x000F000Fu) | MOE_F16_1024X2), moe_u32_as_half2(xp[2]), d);
-  d = moe_dot2(moe_u32_as_half2((w8 & 0x00F000F0u) | MOE_F16_1024X2), moe_u32_as_half2(xp[3]), d);
+  d = moe_dot2(moe_u32_as_half2((w & mk.q) | MOE_F16_1024X2), moe_u32_as_half2(xp[0]), d);
+  d = moe_dot2(moe_u32_as_half2((w & mk.r) | MOE_F16_1024X2), moe_u32_as_half2(xp[1]), d);
+  d = moe_dot2(moe_u32_as_half2((w8 & mk.q) | MOE_F16_1024X2), moe_u32_as_half2(xp[2]), d);
+  d = moe_dot2(moe_u32_as_half2((w8 & mk.r) | MOE_F16_1024X2), moe_u32_as_half2(xp[3]), d);
   return d - c;
 }
 // 8 values of an int2 block word (the low or high byte of each half, w
 // already shifted): s * (dot - c0) + m * sum(x)
-__device__ __forceinline__ float pt_q2_word(uint32_t w, float s, float m, const uint32_t* xp, float2 c) {
+__device__ __forceinline__ float pt_q2_word(uint32_t w, float s, float m, const uint32_t* xp, float2 c, const PtMask& mk) {
   float d = 0.f;
-  d = moe_dot2(moe_u32_as_half2((w & 0x00030003u) | MOE_F16_1024X2), moe_u32_as_half2(xp[0]), d);
-  d = moe_dot2(moe_u32_as_half2((w & 0x000C000Cu) | MOE_F16_1024X2), moe_u32_as_half2(xp[1]), d);
-  d = moe_dot2(moe_u32_as_half2((w & 0x00300030u) | MOE_F16_1024X2), moe_u32_as_half2(xp[2]), d);
-  d = moe_dot2(moe_u32_as_half2((w & 0x00C000C0u) | MOE_F16_1024X2), moe_u32_as_half2(xp[3]), d);
+  d = moe_dot2(moe_u32_as_half2((w & mk.q) | MOE_F16_1024X2), moe_u32_as_half2(xp[0]), d);
+  d = moe_dot2(moe_u32_as_half2((w & mk.r) | MOE_F16_1024X2), moe_u32_as_half2(xp[1]), d);
+  d = moe_dot2(moe_u32_as_half2((w & mk.s) | MOE_F16_1024X2), moe_u32_as_half2(xp[2]), d);
+  d = moe_dot2(moe_u32_as_half2((w & mk.t) | MOE_F16_1024X2), moe_u32_as_half2(xp[3]), d);
   return fmaf(s, d - c.x, m * c.y);
 }
 
@@ -793,6 +811,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     // 8 waves; the down rows of thread tid are tid + 512 c.
     {
       const int U1 = MT == 1 ? k + 1 : p_misc[0], NB4 = NP / 4, NG = U1 * NB4;
+      const PtMask mk = pt_masks(QFMT);
       const bool ilv = T > 1;  // interleaved group order
       int gi0 = (int)((int64_t)g * NG / G), gi1 = (int)((int64_t)(g + 1) * NG / G);
       if (sepB) {
@@ -937,7 +956,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
               for (int b = 0; b < 4; ++b) {
                 const int kb = 4 * kuc + b;
                 const float sc = kv ? moe_f16_to_f32((uint16_t)(gs[2 * c + b / 2] >> (16 * (b & 1)))) : 0.f;
-                acc = fmaf(sc, pt_q4_dot(gq[2 * c + b / 2][b % 2], (const uint32_t*)xprep + 16 * kb, corr[kb].x), acc);
+                acc = fmaf(sc, pt_q4_dot(gq[2 * c + b / 2][b % 2], (const uint32_t*)xprep + 16 * kb, corr[kb].x, mk), acc);
               }
             } else {
 #pragma unroll
@@ -949,7 +968,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
                   const int bl = 4 * (2 * kuc + b) + jb;  // block of 16 values
                   const float sc = kv ? moe_f16_to_f32((uint16_t)(mw[jb] & 0xffff)) : 0.f;
                   const float mn = kv ? moe_f16_to_f32((uint16_t)(mw[jb] >> 16)) : 0.f;
-                  acc += pt_q2_dot(qw[jb], sc, mn, (const uint32_t*)xprep + 8 * bl, corr[bl]);
+                  acc += pt_q2_dot(qw[jb], sc, mn, (const uint32_t*)xprep + 8 * bl, corr[bl], mk);
                 }
               }
             }
@@ -979,7 +998,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                   const float sj = kvq ? moe_f16_to_f32((uint16_t)(gs[j] >> (16 * bb))) : 0.f;
-                  acc[j] = fmaf(sj, pt_q4_dot(gq[j][bb], xw, cb), acc[j]);
+                  acc[j] = fmaf(sj, pt_q4_dot(gq[j][bb], xw, cb, mk), acc[j]);
                 }
               }
             } else {
@@ -999,7 +1018,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
                   const uint32_t mw = jb == 0 ? gq[j][1].x : jb == 1 ? gq[j][1].y : jb == 2 ? gq[j][1].z : gq[j][1].w;
                   const float sc = kvq ? moe_f16_to_f32((uint16_t)(mw & 0xffff)) : 0.f;
                   const float mn = kvq ? moe_f16_to_f32((uint16_t)(mw >> 16)) : 0.f;
-                  acc[j] += pt_q2_dot(qw, sc, mn, xw, cb);
+                  acc[j] += pt_q2_dot(qw, sc, mn, xw, cb, mk);
                 }
               }
             }
@@ -1024,7 +1043,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
               const int kb = 4 * kuB + 2 * (lq & 1) + b;
               const float sc = kvB ? moe_f16_to_f32((uint16_t)(gsS >> (16 * b))) : 0.f;
               const float cc = ((const float2*)(xp + 2 * (size_t)H))[kb].x;
-              accB = fmaf(sc, pt_q4_dot(gqS[b], (const uint32_t*)xp + 16 * kb, cc), accB);
+              accB = fmaf(sc, pt_q4_dot(gqS[b], (const uint32_t*)xp + 16 * kb, cc, mk), accB);
             }
           } else {
             const uint32_t qw[4] = {gqS[0].x, gqS[0].y, gqS[0].z, gqS[0].w};
@@ -1035,7 +1054,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
               const float sc = kvB ? moe_f16_to_f32((uint16_t)(mw[jb] & 0xffff)) : 0.f;
               const float mn = kvB ? moe_f16_to_f32((uint16_t)(mw[jb] >> 16)) : 0.f;
               const float2 cc = ((const float2*)(xp + 2 * (size_t)H))[bl];
-              accB += pt_q2_dot(qw[jb], sc, mn, (const uint32_t*)xp + 8 * bl, cc);
+              accB += pt_q2_dot(qw[jb], sc, mn, (const uint32_t*)xp + 8 * bl, cc, mk);
             }
           }
           accB += __shfl_xor(accB, 16, 64);
@@ -1112,11 +1131,11 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
               float v;
               if (QFMT == MOE_Q4_B32) {
                 const uint32_t w = pi == 0 ? dq[c].x : pi == 1 ? dq[c].y : pi == 2 ? dq[c].z : dq[c].w;
-                v = moe_f16_to_f32((uint16_t)dsc[c]) * pt_q4_word(w, hw4, cc.x);
+                v = moe_f16_to_f32((uint16_t)dsc[c]) * pt_q4_word(w, hw4, cc.x, mk);
               } else {
                 const uint32_t w = (pi < 2 ? dq[c].x : dq[c].y) >> (8 * (pi & 1));
                 const uint32_t m = pi < 2 ? dq[c].z : dq[c].w;
-                v = pt_q2_word(w, moe_f16_to_f32((uint16_t)(m & 0xffff)), moe_f16_to_f32((uint16_t)(m >> 16)), hw4, cc);
+                v = pt_q2_word(w, moe_f16_to_f32((uint16_t)(m & 0xffff)), moe_f16_to_f32((uint16_t)(m >> 16)), hw4, cc, mk);
               }
 #pragma unroll
               for (int tt = 0; tt < MT; ++tt)
@@ -1131,11 +1150,11 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
           for (int c = 0; c < NRD; ++c) {
             float v;
             if (QFMT == MOE_Q4_B32) {
-              v = moe_f16_to_f32((uint16_t)dmS[c]) * pt_q4_word(dwS[c], hw4, cc.x);
+              v = moe_f16_to_f32((uint16_t)dmS[c]) * pt_q4_word(dwS[c], hw4, cc.x, mk);
             } else {
               const uint32_t w = dwS[c] >> (8 * (sp & 1));
               v = pt_q2_word(w, moe_f16_to_f32((uint16_t)(dmS[c] & 0xffff)), moe_f16_to_f32((uint16_t)(dmS[c] >> 16)),
-                             hw4, cc);
+                             hw4, cc, mk);
             }
             y[c][0] += v;
           }
