@@ -847,49 +847,19 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         return a.pool + (MT == 1 ? (int64_t)lslots[u < k ? topi[u] : E] * a.record_bytes : p_roff[u]);
       };
       // ---- gate/up loads of group gi (its 64 consecutive rows 64 b + rho),
-      // 8 16-byte words q and 4 words sc per lane.
-      // One token: lane l holds slot l, row rho = 8 (l / 16) + l % 8 (+ 32
-      // for the up half, l % 16 >= 8), over all of the wave's K range: q[2c +
-      // b/2][b%2] = block b of K unit c (int4) or its q-unit b / meta unit b-2
-      // (int2), sc[2c..2c+1] = the 4 scales of K unit c; the activations are
-      // read from LDS as the dots need them.
-      // More tokens: lane l = (p = l % 16, quarter q = l / 16) holds rows rho
-      // = p + 16 j (j < 4) over quarter q of the wave's K range, 64 values
-      // (int4: blocks 2q, 2q+1 of the wave's 8; int2: q-unit q of its 4):
-      // q[j][0..1] = the two blocks (int4) or the q-unit and its meta unit
-      // (int2), sc[j] = the two scales (int4).  Each quarter's activations are
-      // read once per token and used for 4 rows; the quarters are summed with
-      // shuffles.
+      // 8 16-byte words q and 4 words sc per lane.  Lane l = (p = l % 16,
+      // quarter q = l / 16) holds rows rho = p + 16 j (j < 4) over quarter q of
+      // the wave's K range, 64 values (int4: blocks 2q, 2q+1 of the wave's 8;
+      // int2: q-unit q of its 4): q[j][0..1] = the two blocks (int4) or the
+      // q-unit and its meta unit (int2), sc[j] = the two scales (int4).  Each
+      // quarter's activations are read from LDS once per token and used for 4
+      // rows (a quarter of the LDS traffic of one row per lane); the quarters
+      // are summed with shuffles.
       const int lp = lane & 15;
       const int kuq = min(ku0 + (lq >> 1), NKU - 1);  // K unit of the lane's quarter
       const bool kvq = ku0 + (lq >> 1) < ku1;
       auto load_gu = [&](int gi, uint4 (&q)[4][2], uint32_t (&sc)[4]) {
         const uint8_t* rg = rec_of(unit_of(gi));
-        if (MT == 1) {
-          const uint32_t row = (uint32_t)(64 * block_of(gi) + 8 * (lane >> 4) + (lane & 7) + ((lane & 8) ? 32 : 0));
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const uint32_t ku = (uint32_t)min(ku0 + c, NKU - 1);
-            if (QFMT == MOE_Q4_B32) {
-              const uint2 s2 = *reinterpret_cast<const uint2*>(rg + (o_gus + 16u * ku * (uint32_t)F + 8u * row));
-              sc[2 * c] = s2.x;
-              sc[2 * c + 1] = s2.y;
-#pragma unroll
-              for (int b = 0; b < 4; ++b)
-                q[2 * c + b / 2][b % 2] =
-                    *reinterpret_cast<const uint4*>(rg + (o_guq + 16u * ((4u * ku + b) * 2u * (uint32_t)F + row)));
-            } else {
-              sc[2 * c] = sc[2 * c + 1] = 0u;
-#pragma unroll
-              for (int b = 0; b < 2; ++b) {
-                const uint32_t un = 2u * ku + b;  // 4-block unit of 64 values
-                q[2 * c][b] = *reinterpret_cast<const uint4*>(rg + (o_guq + 16u * (un * 2u * (uint32_t)F + row)));
-                q[2 * c + 1][b] = *reinterpret_cast<const uint4*>(rg + (o_gus + 16u * (un * 2u * (uint32_t)F + row)));
-              }
-            }
-          }
-          return;
-        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint32_t row = (uint32_t)(64 * block_of(gi) + lp + 16 * j);
@@ -944,39 +914,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         auto xp_of = [&](int t) -> const uint8_t* {
           return xprep + (size_t)(MT == 1 ? 0 : p_tok[u * 4 + t]) * a.prep_bytes;
         };
-        if (MT == 1) {  // one token: row slot `lane`, all of the wave's K units
-          const float2* corr = (const float2*)(xprep + 2 * (size_t)H);
-          float acc = 0.f;
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int kuc = min(ku0 + c, NKU - 1);
-            const bool kv = ku0 + c < ku1;
-            if (QFMT == MOE_Q4_B32) {
-#pragma unroll
-              for (int b = 0; b < 4; ++b) {
-                const int kb = 4 * kuc + b;
-                const float sc = kv ? moe_f16_to_f32((uint16_t)(gs[2 * c + b / 2] >> (16 * (b & 1)))) : 0.f;
-                acc = fmaf(sc, pt_q4_dot(gq[2 * c + b / 2][b % 2], (const uint32_t*)xprep + 16 * kb, corr[kb].x, mk), acc);
-              }
-            } else {
-#pragma unroll
-              for (int b = 0; b < 2; ++b) {
-                const uint4 Qw = gq[2 * c][b], Mw = gq[2 * c + 1][b];
-                const uint32_t qw[4] = {Qw.x, Qw.y, Qw.z, Qw.w}, mw[4] = {Mw.x, Mw.y, Mw.z, Mw.w};
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) {
-                  const int bl = 4 * (2 * kuc + b) + jb;  // block of 16 values
-                  const float sc = kv ? moe_f16_to_f32((uint16_t)(mw[jb] & 0xffff)) : 0.f;
-                  const float mn = kv ? moe_f16_to_f32((uint16_t)(mw[jb] >> 16)) : 0.f;
-                  acc += pt_q2_dot(qw[jb], sc, mn, (const uint32_t*)xprep + 8 * bl, corr[bl], mk);
-                }
-              }
-            }
-          }
-          // written by every lane (slots past the pieces are never read): a
-          // conditional use would let the compiler sink the loads behind it
-          red[wave * PT_SLOTS + lane] = acc;
-        } else {  // more tokens: the quarter mapping, one token and one block of x at a time
+        {  // the quarter mapping, one token and one block of x at a time
           const int rho = lp + 16 * lq;
           const int slot = 16 * ((rho & 31) >> 3) + (rho & 7) + 8 * (rho >> 5);
 #pragma unroll 1
