@@ -586,6 +586,9 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
       srow[c] = a.slot_table[(size_t)l * (E + 1) + min(tid + PT_THREADS * c, E)];
     const uint16_t* wr = a.w_router + (size_t)l * E * H;  // wave-uniform; 32-bit offsets below
     const int e_row = g + G * wave;
+    // its routing bias too (a load issued only after the dot product would
+    // put a memory round trip between x's arrival and the published logit)
+    const float b_row = a.bias ? a.bias[(size_t)l * E + min(e_row, E - 1)] : 0.f;
     uint4 rw[4];
     if (e_row < E) {  // wave-uniform
 #pragma unroll
@@ -726,7 +729,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
           }
         }
       }
-      const float b = a.bias ? a.bias[(size_t)l * E + e] : 0.f;
+      const float b = e == e_row ? b_row : a.bias ? a.bias[(size_t)l * E + e] : 0.f;
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         if (t < T) {
