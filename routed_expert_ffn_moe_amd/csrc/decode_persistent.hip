@@ -11,18 +11,19 @@
 //   * a consumer polls exactly the words it needs until every tag matches
 //     the current (call, layer) tag.  No counters, so nothing serialises.
 // Per layer l (tag t_l), workgroup g:
-//   A  read x_l (tagged, or x_in for l = 0); mean square -> inv rms;
-//      router rows e = g (mod G): logits of xn = x * inv, tagged.
-//      Prepare xn for the expert dot products (fp16 pairs) in LDS.
-//   B  read all logits; top-k + softmax per token (one wave per token); the
-//      plan of distinct experts (computed identically by every workgroup).
-//      Work units (distinct expert u, f-slice fs of 32): gate/up rows of fs
-//      (all of K) -> h = silu(g) * up for the slice -> the slice's column
-//      block of the down matrix times h -> a weighted partial output vector
-//      of H rows per token, tagged.  A unit reads its gate/up rows and its
-//      down block column at once: one weight stream per layer.
-//   C  rows r of workgroup g: x_{l+1}[r] = x_l[r] + sum over the token's
-//      k+1 experts and all f-slices of the partials, in a fixed order.
+//   A  read x_l (tagged, or x_in for l = 0); 1/rms per token in every wave;
+//      router rows e = g (mod G): logits of xn = x * inv, tagged.  Prepare
+//      xn for the expert dot products (fp16 pairs) in LDS.
+//   B  read all logits; top-k per token (one wave per token: a ballot
+//      threshold, then exact ranking of the candidates); with several
+//      tokens, the plan of distinct experts (computed identically by every
+//      workgroup).  The experts' work is cut into groups of 4 pieces of 8 f
+//      values (64 gate/up rows and one down block column each; see "work
+//      pieces"), handed out to the workgroups; a group's gate/up dots, SiLU
+//      and down dots give a weighted partial output vector of H rows per
+//      token, tagged.
+//   C  rows r of workgroup g: x_{l+1}[r] = x_l[r] + the G partials, summed
+//      in a fixed order.
 // Every workgroup produces router rows in A and output rows in C, so no
 // workgroup can fall a layer behind the data it still has to read.
 // Every wait is bounded; on timeout the error word is set, x_out is filled
@@ -808,10 +809,13 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     // one token, group i = u * F/32 + b (a workgroup's work is one expert's
     // rows); with more, i = b * U1 + u (the units interleaved, so that every
     // workgroup gets the same mix of experts and token counts).  Workgroup g
-    // takes the groups [g*NG/G, (g+1)*NG/G) (with a single shared piece:
-    // group g and that piece), one batch per group: row slot s = lane s of
-    // the batch is gate/up row s%16 of piece s/16, its K range split over the
-    // 8 waves; the down rows of thread tid are tid + 512 c.
+    // takes the groups [g*NG/G, (g+1)*NG/G) (with single shared pieces: group
+    // g and that piece; with more tokens: a range balanced by cost), one
+    // batch per group.  In a batch the gate/up rows are split over the 8
+    // waves by K and over the lanes as described at load_gu; row slot s
+    // (s < 64) of the batch is gate/up row s%16 of piece s/16, slots 64..79
+    // the single shared piece (row slot B); the down rows of thread tid are
+    // tid + 512 c.
     {
       const int U1 = MT == 1 ? k + 1 : p_misc[0], NB4 = NP / 4, NG = U1 * NB4;
       const PtMask mk = pt_masks(QFMT);
