@@ -94,12 +94,14 @@ def cpu_baseline(li, x_tok, budget_s):
                       f"{wall:.1f} s, scaled to {li.L} layers"}, np
 
 
-def decode_bench(M, li, T, steps, warmup, use_graph, seed_tag):
-    """Times `steps` decode steps of T tokens.  Returns a dict of results."""
+def decode_bench(M, li, T, steps, warmup, use_graph, seed_tag, k=None):
+    """Times `steps` decode steps of T tokens (top-k, li.k by default).
+    Returns a dict of results."""
     import torch
     import gen as G
     dev = li.pool.device
-    L, E, H, F, k = li.L, li.E, li.H, li.F, li.k
+    L, E, H, F = li.L, li.E, li.H, li.F
+    k = li.k if k is None else k
     xs = G.draw_x(2, (steps + warmup) * T, H, dev, tag=seed_tag).view(steps + warmup, T, H)
     x_in = torch.empty((T, H), dtype=torch.float32, device=dev)
     x_out = torch.empty_like(x_in)
@@ -155,6 +157,24 @@ def decode_bench(M, li, T, steps, warmup, use_graph, seed_tag):
         ids = idx_out.cpu()
         uniq.append([len(set(ids[l].reshape(-1).tolist())) for l in range(L)])
     return {"ms": ms, "uniq": uniq, "steps": steps, "T": T}
+
+
+def decode_sweep(M, li, steps, warmup, use_graph):
+    """Verify windows of 1..8 token positions at top-10, and T = 1, 4, 6 at
+    top-6: ms per step, token positions per second, distinct experts per
+    layer and the HBM rate of the algorithmic bytes."""
+    rows = []
+    for T, k in [(1, 10), (2, 10), (3, 10), (4, 10), (5, 10), (6, 10), (8, 10), (1, 6), (4, 6), (6, 6)]:
+        d = decode_bench(M, li, T, steps, warmup, use_graph, f"sweep-x{T}-{k}", k=k)
+        ms = d["ms"] / steps
+        b = sum(decode_bytes(li, u, T) for u in d["uniq"]) / len(d["uniq"])
+        u = sum(sum(x) for x in d["uniq"]) / (len(d["uniq"]) * li.L)
+        row = {"T": T, "k": k, "ms_per_step": round(ms, 4), "token_positions_per_s": round(T / (ms / 1e3), 1),
+               "mean_distinct_experts_per_layer": round(u, 2), "gbs": round(b / (ms / 1e3) / 1e9, 1),
+               "path": "persistent" if T <= 4 else "kernel chain"}
+        log(f"sweep: {json.dumps(row)}")
+        rows.append(row)
+    return rows
 
 
 def decode_bytes(li, uniq_step, T):
@@ -234,6 +254,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch the step eagerly instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the verify and prefill measurements")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time verify windows T = 1..8 at top-10 and T = 1, 4, 6 at top-6")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-ref-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (the reference kernel that scales "
@@ -307,6 +329,9 @@ def main():
             "prefill_c4": pf,
         }
         log(f"verify T=4: {ms4:.4f} ms/step; prefill: {json.dumps(pf)}")
+    if args.sweep:
+        out.setdefault("extra", {})["decode_sweep"] = decode_sweep(M, li, min(args.steps, 32), args.warmup,
+                                                                   not args.no_graph)
     if not args.no_cpu_baseline:
         xs = G.draw_x(2, 1, H, dev, tag="bench-x")
         cb, _ = cpu_baseline(li, xs, args.cpu_budget)

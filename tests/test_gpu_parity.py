@@ -369,16 +369,17 @@ def test_decode_stack_tiny(moe, qfmt, T, path):
 
 
 @pytest.mark.parametrize("qfmt", [0, 1])
-@pytest.mark.parametrize("T", [1, 2, 3, 4])
-def test_decode_stack_full_shape_persistent(moe, qfmt, T):
-    """4 layers of the full shape (512 experts top-10, H=2048, F=768): the
-    persistent kernel and the kernel chain, each checked against the oracle on
-    every layer (the oracle fed that path's own layer inputs); the two paths
-    agree on layer 0, where their inputs are identical."""
+@pytest.mark.parametrize("T,k", [(1, 10), (2, 10), (3, 10), (4, 10), (1, 6), (4, 6), (3, 5)])
+def test_decode_stack_full_shape_persistent(moe, qfmt, T, k):
+    """4 layers of the full shape (512 experts, H=2048, F=768; top-10, and the
+    smaller k of a faster routing mode): the persistent kernel and the kernel
+    chain, each checked against the oracle on every layer (the oracle fed that
+    path's own layer inputs); the two paths agree on layer 0, where their
+    inputs are identical."""
     L = 4
-    li = C.layer_case(6, T, 2048, 512, 10, 768, qfmt=qfmt, bias=True, L=L, gap=False, device="cuda")
+    li = C.layer_case(6, T, 2048, 512, k, 768, qfmt=qfmt, bias=True, L=L, gap=False, device="cuda")
     x = li.x.contiguous()
-    ws = moe.workspace(moe.MOE_OP_DECODE_STACK, "cuda", T, 10, 512, 2048, 768, qfmt)
+    ws = moe.workspace(moe.MOE_OP_DECODE_STACK, "cuda", T, k, 512, 2048, 768, qfmt)
     xo, idx_o, w_o, hist = _stack_run(moe, li, x, "persistent", ws=ws)
     excluded = _check_stack(li, x, xo, idx_o, w_o, hist, range(L))
     xc, idx_c, w_c, hist_c = _stack_run(moe, li, x, "chain")
@@ -397,6 +398,22 @@ def test_decode_stack_full_shape_persistent(moe, qfmt, T):
     for rep in range(3):
         xo2, idx2, _, _ = _stack_run(moe, li, x, "persistent", ws=ws)
         assert torch.equal(xo2, xo) and torch.equal(idx2, idx_o)
+
+
+@pytest.mark.parametrize("T,k", [(5, 10), (6, 10), (8, 10), (6, 6)])
+def test_decode_stack_wide_verify(moe, T, k):
+    """Verify windows wider than the persistent kernel takes (5, 6 and 8
+    token positions: the per-layer kernel chain), 4 layers of the full shape,
+    each layer checked against the oracle on the path's own layer inputs, and
+    the same step repeated bit for bit."""
+    L = 4
+    li = C.layer_case(9, T, 2048, 512, k, 768, qfmt=0, bias=True, L=L, gap=False, device="cuda")
+    x = li.x.contiguous()
+    xo, idx_o, w_o, hist = _stack_run(moe, li, x, "auto")
+    excluded = _check_stack(li, x, xo, idx_o, w_o, hist, range(L))
+    assert excluded <= T * L // 4
+    xo2, idx2, _, _ = _stack_run(moe, li, x, "auto")
+    assert torch.equal(xo2, xo) and torch.equal(idx2, idx_o)
 
 
 @pytest.mark.parametrize("qfmt", [0, 1])
