@@ -278,9 +278,10 @@ int moe_usage_update(const int32_t* topk_idx, int T, int k, int layer, int L,
  *   x_{l+1} = x_l + MoE_l(xn_l)
  * where MoE_l(xn_l) is exactly what moe_route_topk + moe_expert_gemv_q +
  * moe_combine compute on xn_l with layer l's router, bias and slots.
- * Execution: for 1 <= T <= 4 (and shapes whose working set fits in LDS) the
- * step runs as ONE persistent kernel whose workgroups pass data through
- * tagged words in ws (no host synchronisation, no grid barrier); otherwise,
+ * Execution: for 1 <= T <= 8 with T * k <= 64 (and shapes whose working set
+ * fits in LDS) the step runs as ONE persistent kernel whose workgroups pass
+ * data through tagged words in ws (no host synchronisation, no grid
+ * barrier); otherwise,
  * or when the environment variable MOE_DECODE_PATH=chain is set, as a chain
  * of kernels per layer.  The persistent path keeps a call counter and tagged
  * buffers in ws across calls: pass the same ws to every call of a stack and

@@ -367,12 +367,13 @@ __device__ __forceinline__ void pt_topk_weights(uint32_t my_key, int k, float* w
 
 // Work plan of one layer from the T * k chosen experts (one wave): the
 // distinct experts ("units") in order of first occurrence (token-major), each
-// with its tokens p_tok[4u + c] and their top-k positions p_j[4u + c];
+// with its tokens p_tok[ts u + c] and their top-k positions p_j[ts u + c]
+// (ts >= T: a unit holds each token at most once);
 // then, if with_shared, the shared expert with every token (top-k position
 // k); p_roff[u] is the byte offset of the unit's record in the pool;
 // p_misc[0] = the number of units.  n = T * k <= 64.
 __device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, const int32_t* slots, int64_t rbytes,
-                                        bool with_shared, int* p_exp, int* p_ntok, int* p_tok, int* p_j,
+                                        bool with_shared, int ts, int* p_exp, int* p_ntok, int* p_tok, int* p_j,
                                         int64_t* p_roff, int* p_cum, int* p_misc) {
   const int lane = pt_lane(), n = T * k;
   if (T == 1) {  // one token: its k experts are distinct, in top-k order
@@ -381,16 +382,16 @@ __device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, co
       p_exp[lane] = e1;
       p_ntok[lane] = 1;
       p_roff[lane] = (int64_t)slots[e1] * rbytes;
-      p_tok[lane * 4] = 0;
-      p_j[lane * 4] = lane;
+      p_tok[lane * ts] = 0;
+      p_j[lane * ts] = lane;
     }
     if (lane == 0) {
       if (with_shared) {
         p_exp[k] = E;
         p_ntok[k] = 1;
         p_roff[k] = (int64_t)slots[E] * rbytes;
-        p_tok[k * 4] = 0;
-        p_j[k * 4] = k;
+        p_tok[k * ts] = 0;
+        p_j[k * ts] = k;
       }
       p_misc[0] = with_shared ? k + 1 : k;
     }
@@ -417,13 +418,13 @@ __device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, co
       p_ntok[u] = total;
       p_roff[u] = (int64_t)slots[e] * rbytes;
     }
-    p_tok[u * 4 + before] = t;
-    p_j[u * 4 + before] = j;
+    p_tok[u * ts + before] = t;
+    p_j[u * ts + before] = j;
   }
   if (with_shared) {
     if (lane < T) {
-      p_tok[U * 4 + lane] = lane;
-      p_j[U * 4 + lane] = k;
+      p_tok[U * ts + lane] = lane;
+      p_j[U * ts + lane] = k;
     }
     if (lane == 0) {
       p_exp[U] = E;
@@ -505,6 +506,10 @@ struct PtLds {
 };
 #define PT_PB_MAX 5    // pieces per batch: 4 of row slot A, 1 of row slot B
 #define PT_SLOTS 80    // gate/up row slots per batch (16 per piece)
+// Token slots of the kernel instance that runs T tokens (its MT; 4 for one
+// token too, whose instance uses a single slot of the same layout), and the
+// per-unit token stride of the plan.
+__host__ __device__ inline int pt_token_slots(int T) { return T <= 4 ? 4 : 8; }
 __host__ __device__ inline PtLds pt_lds(int qfmt, int T, int k, int E, int H, size_t prep_bytes) {
   PtLds o;
   size_t off = 0;
@@ -514,6 +519,7 @@ __host__ __device__ inline PtLds pt_lds(int qfmt, int T, int k, int E, int H, si
     return at;
   };
   const size_t U1max = (size_t)T * k + 1;
+  const size_t ts = (size_t)pt_token_slots(T);
   (void)qfmt;
   o.xs = take((size_t)T * H * 4);
   o.xprep = take((size_t)T * prep_bytes);
@@ -522,14 +528,14 @@ __host__ __device__ inline PtLds pt_lds(int qfmt, int T, int k, int E, int H, si
   o.topw = take((size_t)T * k * 4);
   o.p_exp = take(U1max * 4);
   o.p_ntok = take(U1max * 4);
-  o.p_tok = take(U1max * 16);
-  o.p_j = take(U1max * 16);
+  o.p_tok = take(U1max * ts * 4);
+  o.p_j = take(U1max * ts * 4);
   o.p_roff = take(U1max * 8);
   o.p_cum = take((U1max + 1) * 4);
   o.p_misc = take(16);
-  o.red = take((size_t)PT_WAVES * PT_SLOTS * 4 * 4);  // [wave][slot][token slot] partial gate/up dots
-  o.hp = take((size_t)PT_PB_MAX * 4 * 4 * 4);         // [piece][token slot][4] prepared h words
-  o.hc = take((size_t)PT_PB_MAX * 4 * 8);             // [piece][token slot] corrections
+  o.red = take((size_t)PT_WAVES * PT_SLOTS * ts * 4);  // [wave][slot][token slot] partial gate/up dots
+  o.hp = take((size_t)PT_PB_MAX * ts * 4 * 4);         // [piece][token slot][4] prepared h words
+  o.hc = take((size_t)PT_PB_MAX * ts * 8);             // [piece][token slot] corrections
   o.slots = take((size_t)(E + 1) * 4);
   o.total = off;
   return o;
@@ -555,8 +561,9 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
   float* topw = (float*)(smem + o.topw);      // [T][k]
   int* p_exp = (int*)(smem + o.p_exp);        // [U1max]
   int* p_ntok = (int*)(smem + o.p_ntok);      // [U1max]
-  int* p_tok = (int*)(smem + o.p_tok);        // [U1max][4]
-  int* p_j = (int*)(smem + o.p_j);            // [U1max][4]
+  constexpr int TS = MT > 4 ? 8 : 4;          // per-unit token stride of the plan
+  int* p_tok = (int*)(smem + o.p_tok);        // [U1max][TS]
+  int* p_j = (int*)(smem + o.p_j);            // [U1max][TS]
   int64_t* p_roff = (int64_t*)(smem + o.p_roff); // [U1max] record byte offsets
   int* p_cum = (int*)(smem + o.p_cum);        // [U1max + 1] group cost prefix per unit
   int* p_misc = (int*)(smem + o.p_misc);      // [0] = U1
@@ -748,7 +755,9 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         const int t = valid ? wi / (H / 8) : 0, wh = valid ? wi % (H / 8) : 0;  // word within the token
         const int b = wh / (blk / 8), sub = wh % (blk / 8);
         uint8_t* out = xprep + (size_t)t * a.prep_bytes;
-        const float it = t == 0 ? invr[0] : t == 1 ? invr[MT > 1 ? 1 : 0] : t == 2 ? invr[MT > 2 ? 2 : 0] : invr[MT > 3 ? 3 : 0];
+        float it = invr[0];
+#pragma unroll
+        for (int q = 1; q < MT; ++q) it = t == q ? invr[q] : it;
         pt_prep_word<QFMT>(xs + (size_t)t * H + 8 * wh, it, valid, (uint32_t*)out + (blk / 2) * b + 4 * sub,
                            (float2*)(out + 2 * (size_t)H) + b, sub);
       }
@@ -794,7 +803,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     if (MT > 1) {
       emit_topk();
       if (wave == 0)
-        pt_plan(topi, T, k, E, lslots, a.record_bytes, true, p_exp, p_ntok, p_tok, p_j, p_roff, p_cum, p_misc);
+        pt_plan(topi, T, k, E, lslots, a.record_bytes, true, TS, p_exp, p_ntok, p_tok, p_j, p_roff, p_cum, p_misc);
       __syncthreads();
     }
     // ------------------------------------------------------------ work pieces
@@ -919,7 +928,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         if (MT == 1 && gi == gi0 && wave == 0) pt_topk_weights(my_key, k, topw);  // read after the next barrier
         // ---- gate/up partial dots
         auto xp_of = [&](int t) -> const uint8_t* {
-          return xprep + (size_t)(MT == 1 ? 0 : p_tok[u * 4 + t]) * a.prep_bytes;
+          return xprep + (size_t)(MT == 1 ? 0 : p_tok[u * TS + t]) * a.prep_bytes;
         };
         {  // the quarter mapping, one token and one block of x at a time
           const int rho = lp + 16 * lq;
@@ -1065,7 +1074,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
           if (MT > 1 && t >= ntok) break;
-          const int tk = MT == 1 ? 0 : p_tok[u * 4 + t], jj = MT == 1 ? u : p_j[u * 4 + t];
+          const int tk = MT == 1 ? 0 : p_tok[u * TS + t], jj = MT == 1 ? u : p_j[u * TS + t];
           const float wgt = jj < k ? topw[tk * k + jj] : 1.f;
 #pragma unroll
           for (int pi = 0; pi < 4; ++pi) {
@@ -1141,7 +1150,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
       const int r0 = g * a.rpw;
       const int nout = T * a.rpw;
       const int tpo = a.tpo;
-      constexpr int NQ = MT == 1 ? 8 : MT == 2 ? 12 : 24;
+      constexpr int NQ = MT == 1 ? 8 : MT == 2 ? 12 : MT == 4 ? 24 : 32;
       if (!pt_wait_sentinels(a.pbuf, (uint32_t)((T - 1) * H + r0 + a.rpw - 1), (uint32_t)(T * H), G, tag,
                              PT_SPIN_MAX)) {
         ok = false;
@@ -1265,7 +1274,7 @@ static size_t pt_lds_limit() {
 }
 
 bool moe_persistent_supported(int T, int k, int E, int H, int F, int qfmt) {
-  if (T < 1 || T > 4 || k > MOE_MAX_K) return false;
+  if (T < 1 || T > 8 || k > MOE_MAX_K) return false;
   const PtLayout P = pt_layout(T, k, E, H, F, qfmt, pt_grid(H, E));
   // x words per thread (T * H / 512), router chunks (H / 512) and down rows
   // per thread (H / 512) are unrolled up to 4 * MT, 4 and 4; gate/up K units
@@ -1297,14 +1306,14 @@ int moe_launch_decode_persistent(const float* x_in, int T, int H, int F, int E, 
   const size_t nwords = (P.total - P.xbuf) / 8;
   decode_persistent_init_kernel<<<256, 256, 0, st>>>(a.hdr, a.xbuf, nwords);
   decode_persistent_mark_kernel<<<1, 64, 0, st>>>(a.hdr);
-  const int mt = T == 1 ? 1 : T == 2 ? 2 : 4;
+  const int mt = T == 1 ? 1 : T == 2 ? 2 : T <= 4 ? 4 : 8;
   const int slots = E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : 16;
   const void* fn = nullptr;
 #define PT_PICK(Q, M, S) \
   if (qfmt == Q && mt == M && slots == S) fn = (const void*)decode_persistent_kernel<Q, M, S>;
 #define PT_PICK_S(Q, M) PT_PICK(Q, M, 1) PT_PICK(Q, M, 2) PT_PICK(Q, M, 4) PT_PICK(Q, M, 8) PT_PICK(Q, M, 16)
-  PT_PICK_S(MOE_Q4_B32, 1) PT_PICK_S(MOE_Q4_B32, 2) PT_PICK_S(MOE_Q4_B32, 4)
-  PT_PICK_S(MOE_Q2_B16, 1) PT_PICK_S(MOE_Q2_B16, 2) PT_PICK_S(MOE_Q2_B16, 4)
+  PT_PICK_S(MOE_Q4_B32, 1) PT_PICK_S(MOE_Q4_B32, 2) PT_PICK_S(MOE_Q4_B32, 4) PT_PICK_S(MOE_Q4_B32, 8)
+  PT_PICK_S(MOE_Q2_B16, 1) PT_PICK_S(MOE_Q2_B16, 2) PT_PICK_S(MOE_Q2_B16, 4) PT_PICK_S(MOE_Q2_B16, 8)
 #undef PT_PICK_S
 #undef PT_PICK
   if (!fn) return moe_fail(MOE_EUNSUPPORTED, "decode persistent: no kernel for this shape");

@@ -358,7 +358,7 @@ def _check_stack(li, x, xo, idx_o, w_o, hist, layers):
 
 @pytest.mark.parametrize("path", ["chain", "persistent"])
 @pytest.mark.parametrize("qfmt", [0, 1])
-@pytest.mark.parametrize("T", [1, 2, 3, 4])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 8])
 def test_decode_stack_tiny(moe, qfmt, T, path):
     L = 6
     li = C.layer_case(5, T, 256, 16, 2, 128, qfmt=qfmt, bias=True, L=L, gap=False, device="cuda")
@@ -400,20 +400,26 @@ def test_decode_stack_full_shape_persistent(moe, qfmt, T, k):
         assert torch.equal(xo2, xo) and torch.equal(idx2, idx_o)
 
 
-@pytest.mark.parametrize("T,k", [(5, 10), (6, 10), (8, 10), (6, 6)])
-def test_decode_stack_wide_verify(moe, T, k):
-    """Verify windows wider than the persistent kernel takes (5, 6 and 8
-    token positions: the per-layer kernel chain), 4 layers of the full shape,
-    each layer checked against the oracle on the path's own layer inputs, and
-    the same step repeated bit for bit."""
+@pytest.mark.parametrize("qfmt", [0, 1])
+@pytest.mark.parametrize("T,k", [(5, 10), (6, 10), (8, 10), (6, 6), (8, 8)])
+def test_decode_stack_wide_verify(moe, qfmt, T, k):
+    """Verify windows of 5, 6 and 8 token positions, 4 layers of the full
+    shape: the default path (the persistent kernel while T * k <= 64, else
+    the per-layer kernel chain) and the chain, each layer checked against the
+    oracle on the path's own layer inputs, and the same step repeated bit for
+    bit on the same workspace."""
     L = 4
-    li = C.layer_case(9, T, 2048, 512, k, 768, qfmt=0, bias=True, L=L, gap=False, device="cuda")
+    li = C.layer_case(9, T, 2048, 512, k, 768, qfmt=qfmt, bias=True, L=L, gap=False, device="cuda")
     x = li.x.contiguous()
-    xo, idx_o, w_o, hist = _stack_run(moe, li, x, "auto")
+    ws = moe.workspace(moe.MOE_OP_DECODE_STACK, "cuda", T, k, 512, 2048, 768, qfmt)
+    xo, idx_o, w_o, hist = _stack_run(moe, li, x, "auto", ws=ws)
     excluded = _check_stack(li, x, xo, idx_o, w_o, hist, range(L))
-    assert excluded <= T * L // 4
-    xo2, idx2, _, _ = _stack_run(moe, li, x, "auto")
-    assert torch.equal(xo2, xo) and torch.equal(idx2, idx_o)
+    xc, idx_c, w_c, hist_c = _stack_run(moe, li, x, "chain")
+    excluded += _check_stack(li, x, xc, idx_c, w_c, hist_c, range(L))
+    assert excluded <= 2 * T * L // 4
+    for rep in range(2):
+        xo2, idx2, _, _ = _stack_run(moe, li, x, "auto", ws=ws)
+        assert torch.equal(xo2, xo) and torch.equal(idx2, idx_o)
 
 
 @pytest.mark.parametrize("qfmt", [0, 1])
