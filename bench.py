@@ -36,7 +36,7 @@ def log(*a):
 
 
 # the sources that make up the persistent decode kernel
-DECODE_SOURCES = ("decode_persistent.hip", "moe_common.h", "moe_kernels.h")
+DECODE_SOURCES = ("decode_persistent_kernel.h", "decode_persistent.hip", "moe_common.h", "moe_kernels.h")
 
 
 def source_hash(files=DECODE_SOURCES):

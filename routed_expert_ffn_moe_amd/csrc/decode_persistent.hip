@@ -1,1207 +1,7 @@
-// One decode / verify step through L layers as ONE persistent kernel.
-//
-// Batch-1 decode is a strict dependency chain (router -> top-k -> experts ->
-// sum -> next layer; "为什么 Strata 在小显存显卡上这么快", section "一个 token，
-// 三路工人"), so per-layer kernel boundaries dominate the step.  Here G
-// workgroups (at most one per CU) stay resident for the whole step and hand
-// data to each other through tagged words instead of kernel boundaries or
-// grid barriers:
-//   * a producer writes 64-bit words (tag << 32 | payload) with relaxed
-//     agent-scope atomic stores (coherent across XCDs, single-copy atomic);
-//   * a consumer polls exactly the words it needs until every tag matches
-//     the current (call, layer) tag.  No counters, so nothing serialises.
-// Per layer l (tag t_l), workgroup g:
-//   A  read x_l (tagged, or x_in for l = 0); 1/rms per token in every wave;
-//      router rows e = g (mod G): logits of xn = x * inv, tagged.  Prepare
-//      xn for the expert dot products (fp16 pairs) in LDS.
-//   B  read all logits; top-k per token (one wave per token: a ballot
-//      threshold, then exact ranking of the candidates); with several
-//      tokens, the plan of distinct experts (computed identically by every
-//      workgroup).  The experts' work is cut into groups of 4 pieces of 8 f
-//      values (64 gate/up rows and one down block column each; see "work
-//      pieces"), handed out to the workgroups; a group's gate/up dots, SiLU
-//      and down dots give a weighted partial output vector of H rows per
-//      token, tagged.
-//   C  rows r of workgroup g: x_{l+1}[r] = x_l[r] + the G partials, summed
-//      in a fixed order.
-// Every workgroup produces router rows in A and output rows in C, so no
-// workgroup can fall a layer behind the data it still has to read.
-// Every wait is bounded; on timeout the error word is set, x_out is filled
-// with NaN and the kernel ends.
-#include "moe_common.h"
-#include "moe_sizes.h"
-#include "moe_kernels.h"
-
-#define PT_THREADS 512
-#define PT_WAVES 8
-#define PT_SPIN_MAX (1 << 18)
-#define PT_GROUP_BASE 4  // cost of a group's loads, in units of one token's dot passes
-#define PT_MAGIC 0x4d6f4531u
-#define PT_EPS 1e-6f
-
-typedef unsigned long long u64;
-
-struct PtArgs {
-  const float* x_in;
-  int T, H, F, E, k, L, qfmt;
-  const uint16_t* w_router;
-  const float* bias;
-  const int32_t* slot_table;
-  const uint8_t* pool;
-  int64_t record_bytes;
-  float* x_out;
-  int32_t* topk_idx_out;
-  float* topk_w_out;
-  float* x_hist;
-  uint32_t* hdr;  // [0] magic, [1] call counter, [2] error
-  u64* xbuf;      // [T][H]
-  u64* lbuf;      // [T][E]
-  u64* pbuf;      // [(unit * T + i)][H]
-  int G, nfs, rpw, tpo;
-  size_t prep_bytes;
-};
-
-__device__ __forceinline__ void pt_put(u64* p, uint32_t tag, float v) {
-  __hip_atomic_store(p, ((u64)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ bool pt_get(const u64* p, uint32_t tag, float& v) {
-  const u64 w = __hip_atomic_load(const_cast<u64*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  v = __uint_as_float((uint32_t)w);
-  return (uint32_t)(w >> 32) == tag;
-}
-// word `i` of a tagged buffer through a 32-bit byte offset (buffers < 4 GiB),
-// so that the address is a uniform base plus a 32-bit lane offset
-__device__ __forceinline__ u64* pt_at(u64* base, uint32_t i) {
-  return (u64*)((uint8_t*)base + (i << 3));
-}
-__device__ __forceinline__ u64 pt_load(u64* base, uint32_t i) {
-  return __hip_atomic_load(pt_at(base, i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// The thread index and lane, made opaque at each call: values derived from
-// them inside the layer loop are then computed where used instead of being
-// hoisted out of the loop and kept live (or spilled) for the whole kernel.
-__device__ __forceinline__ int pt_tid() {
-  int t = threadIdx.x;
-  asm volatile("" : "+v"(t));
-  return t;
-}
-__device__ __forceinline__ int pt_lane() { return pt_tid() & 63; }
-
-// Polling loops here do not sleep between rounds: each round is a memory
-// round trip and a workgroup barrier already, and a sleep only delayed the
-// detection (measured: 1.2% of a decode step).
-//
-// Waits until word base[first + g * stride] carries `tag` for every g < n
-// (one word per producing workgroup), polling 4 bytes of tag per producer
-// instead of all of its data.  The data itself is read and every tag checked
-// afterwards, so this only shortens the busy polling.  Returns false on
-// timeout.  Called by the whole workgroup.
-__device__ bool pt_wait_sentinels(u64* base, uint32_t first, uint32_t stride, int n, uint32_t tag, int spin_max) {
-  for (int it = 0;; ++it) {
-    bool mine = true;
-    for (int i = pt_tid(); i < n; i += blockDim.x)
-      mine &= (uint32_t)(pt_load(base, first + (uint32_t)i * stride) >> 32) == tag;
-    if (__syncthreads_and(mine)) return true;
-    if (it > spin_max) return false;
-  }
-}
-__device__ __forceinline__ uint32_t pt_tag(uint32_t call, int L, int l) {
-  return (uint32_t)(((uint64_t)call * (uint64_t)L + (uint64_t)l) % 0xFFFFFFFFull) + 1u;
-}
-
-// ---------------------------------------------------------------- small helpers
-// The nibble / crumb masks of the dots, held in registers (made opaque once
-// per layer): (x & mask) | magic is then one v_and_or_b32; with both
-// operands literal constants it takes two instructions, as the VOP3
-// encoding takes no literal here.  int4: q = 0x000F000F, r = 0x00F000F0;
-// int2: q, r, s, t = 0x00030003 << 2i.
-struct PtMask {
-  uint32_t q, r, s, t;
-};
-__device__ __forceinline__ PtMask pt_masks(int qfmt) {
-  PtMask m;
-  if (qfmt == MOE_Q4_B32) {
-    m.q = 0x000F000Fu; m.r = 0x00F000F0u; m.s = 0u; m.t = 0u;
-  } else {
-    m.q = 0x00030003u; m.r = 0x000C000Cu; m.s = 0x00300030u; m.t = 0x00C000C0u;
-  }
-  asm volatile("" : "+v"(m.q), "+v"(m.r), "+v"(m.s), "+v"(m.t));
-  return m;
-}
-// dot of one int4 block (16 bytes) with a prepared activation block
-__device__ __forceinline__ float pt_q4_dot(uint4 q, const uint32_t* xp, float c, const PtMask& mk) {
-  const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
-  float d = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t w = qw[j], w8 = qw[j] >> 8;
-    d = moe_dot2(moe_u32_as_half2((w & mk.q) | MOE_F16_1024X2), moe_u32_as_half2(xp[4 * j + 0]), d);
-    d = moe_dot2(moe_u32_as_half2((w & mk.r) | MOE_F16_1024X2), moe_u32_as_half2(xp[4 * j + 1]), d);
-    d = moe_dot2(moe_u32_as_half2((w8 & mk.q) | MOE_F16_1024X2), moe_u32_as_half2(xp[4 * j + 2]), d);
-    d = moe_dot2(moe_u32_as_half2((w8 & mk.r) | MOE_F16_1024X2), moe_u32_as_half2(xp[4 * j + 3]), d);
-  }
-  return d - c;
-}
-// one int2 block (one word) with a prepared block: s * (dot - c0) + m * sum(x)
-__device__ __forceinline__ float pt_q2_dot(uint32_t w, float s, float m, const uint32_t* xp, float2 c, const PtMask& mk) {
-  const uint32_t w8 = w >> 8;
-  float d = 0.f;
-  d = moe_dot2(moe_u32_as_half2((w & mk.q) | MOE_F16_1024X2), moe_u32_as_half2(xp[0]), d);
-  d = moe_dot2(moe_u32_as_half2((w & mk.r) | MOE_F16_1024X2), moe_u32_as_half2(xp[1]), d);
-  d = moe_dot2(moe_u32_as_half2((w & mk.s) | MOE_F16_1024X2), moe_u32_as_half2(xp[2]), d);
-  d = moe_dot2(moe_u32_as_half2((w & mk.t) | MOE_F16_1024X2), moe_u32_as_half2(xp[3]), d);
-  d = moe_dot2(moe_u32_as_half2((w8 & mk.q) | MOE_F16_1024X2), moe_u32_as_half2(xp[4]), d);
-  d = moe_dot2(moe_u32_as_half2((w8 & mk.r) | MOE_F16_1024X2), moe_u32_as_half2(xp[5]), d);
-  d = moe_dot2(moe_u32_as_half2((w8 & mk.s) | MOE_F16_1024X2), moe_u32_as_half2(xp[6]), d);
-  d = moe_dot2(moe_u32_as_half2((w8 & mk.t) | MOE_F16_1024X2), moe_u32_as_half2(xp[7]), d);
-  return fmaf(s, d - c.x, m * c.y);
-}
-
-// dot of one int4 word (8 values) with its prepared activations xp[4]
-__device__ __forceinline__ float pt_q4_word(uint32_t w, const uint32_t* xp, float c, const PtMask& mk) {
-  const uint32_t w8 = w >> 8;
-  float d = 0.f;
-  d = moe_dot2(moe_u32_as_half2((w & mk.q) | MOE_F16_1024X2), moe_u32_as_half2(xp[0]), d);
-  d = moe_dot2(moe_u32_as_half2((w & mk.r) | MOE_F16_1024X2), moe_u32_as_half2(xp[1]), d);
-  d = moe_dot2(moe_u32_as_half2((w8 & mk.q) | MOE_F16_1024X2), moe_u32_as_half2(xp[2]), d);
-  d = moe_dot2(moe_u32_as_half2((w8 & mk.r) | MOE_F16_1024X2), moe_u32_as_half2(xp[3]), d);
-  return d - c;
-}
-// 8 values of an int2 block word (the low or high byte of each half, w
-// already shifted): s * (dot - c0) + m * sum(x)
-__device__ __forceinline__ float pt_q2_word(uint32_t w, float s, float m, const uint32_t* xp, float2 c, const PtMask& mk) {
-  float d = 0.f;
-  d = moe_dot2(moe_u32_as_half2((w & mk.q) | MOE_F16_1024X2), moe_u32_as_half2(xp[0]), d);
-  d = moe_dot2(moe_u32_as_half2((w & mk.r) | MOE_F16_1024X2), moe_u32_as_half2(xp[1]), d);
-  d = moe_dot2(moe_u32_as_half2((w & mk.s) | MOE_F16_1024X2), moe_u32_as_half2(xp[2]), d);
-  d = moe_dot2(moe_u32_as_half2((w & mk.t) | MOE_F16_1024X2), moe_u32_as_half2(xp[3]), d);
-  return fmaf(s, d - c.x, m * c.y);
-}
-
-// Prepared block writers (same arithmetic as the standalone decode path).
-template <int QFMT>
-__device__ void pt_prep_block(const float* b, float scale, uint32_t* p, float2* corr) {
-  if (QFMT == MOE_Q4_B32) {
-    const half2v k0 = {(_Float16)1032.f, (_Float16)1032.f};
-    const half2v k1 = {(_Float16)1152.f, (_Float16)1152.f};
-    float c = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      half2v a0 = {(_Float16)(b[8 * j + 0] * scale), (_Float16)(b[8 * j + 1] * scale)};
-      half2v a1 = {(_Float16)(b[8 * j + 2] * scale * 0.0625f), (_Float16)(b[8 * j + 3] * scale * 0.0625f)};
-      half2v a2 = {(_Float16)(b[8 * j + 4] * scale), (_Float16)(b[8 * j + 5] * scale)};
-      half2v a3 = {(_Float16)(b[8 * j + 6] * scale * 0.0625f), (_Float16)(b[8 * j + 7] * scale * 0.0625f)};
-      p[4 * j + 0] = moe_half2_as_u32(a0);
-      p[4 * j + 1] = moe_half2_as_u32(a1);
-      p[4 * j + 2] = moe_half2_as_u32(a2);
-      p[4 * j + 3] = moe_half2_as_u32(a3);
-      c = moe_dot2(a0, k0, c);
-      c = moe_dot2(a1, k1, c);
-      c = moe_dot2(a2, k0, c);
-      c = moe_dot2(a3, k1, c);
-    }
-    *corr = make_float2(c, 0.f);
-  } else {
-    const half2v k1024 = {(_Float16)1024.f, (_Float16)1024.f};
-    float c0 = 0.f, sx = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float mul = (i & 3) == 0 ? 1.f : (i & 3) == 1 ? 0.25f : (i & 3) == 2 ? 0.0625f : 0.015625f;
-      half2v a = {(_Float16)(b[2 * i] * scale * mul), (_Float16)(b[2 * i + 1] * scale * mul)};
-      p[i] = moe_half2_as_u32(a);
-      const half2v kc = {(_Float16)(1.f / mul), (_Float16)(1.f / mul)};
-      c0 = moe_dot2(a, k1024, c0);
-      sx = moe_dot2(a, kc, sx);
-    }
-    *corr = make_float2(c0, sx);
-  }
-}
-
-// wave-wide max of uint32 entirely in DPP (row_bcast15 / row_bcast31 carry the
-// row maxima upwards), read from lane 63
-__device__ __forceinline__ uint32_t pt_wave_max(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast15
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast31
-  return __builtin_amdgcn_readlane(v, 63);
-}
-
-// Top-k by repeated extraction (the general case of pt_topk below): each lane
-// sorts its keys; every round takes the wave-wide maximum of the lane heads
-// and the lane holding it pops its head.  Lane j < k ends with the j-th key
-// and expert.
-template <int SLOTS>
-__device__ __forceinline__ void pt_topk_rounds(uint32_t (&hi)[SLOTS], int k, uint32_t& my_key, uint32_t& my_e) {
-  const int lane = pt_lane();
-  uint32_t ex[SLOTS];
-#pragma unroll
-  for (int i = 0; i < SLOTS; ++i) ex[i] = (uint32_t)(lane + 64 * i);
-  // descending sort of the lane's keys (odd-even transposition network); the
-  // experts of one lane ascend with i, so equal keys keep the lower expert first
-#pragma unroll
-  for (int r = 0; r < SLOTS; ++r) {
-#pragma unroll
-    for (int i = r & 1; i + 1 < SLOTS; i += 2) {
-      const bool sw = hi[i] < hi[i + 1] || (hi[i] == hi[i + 1] && ex[i] > ex[i + 1]);
-      const uint32_t h0 = hi[i], e0 = ex[i];
-      hi[i] = sw ? hi[i + 1] : hi[i];
-      ex[i] = sw ? ex[i + 1] : ex[i];
-      hi[i + 1] = sw ? h0 : hi[i + 1];
-      ex[i + 1] = sw ? e0 : ex[i + 1];
-    }
-  }
-  int pos = 0;  // the lane's head is entry `pos` of its sorted keys (past the end: key 0)
-  uint32_t head = hi[0], head_e = ex[0];
-  for (int j = 0; j < k; ++j) {
-    const uint32_t M = pt_wave_max(head);
-    const uint64_t cand = __ballot(head == M);
-    int wl = __ffsll((long long)cand) - 1;
-    if (__popcll(cand) > 1) {  // equal logits in several lanes: the lowest expert
-      const uint32_t ce = head == M ? head_e : 0xFFFFFFFFu;
-      const uint32_t emin = ~pt_wave_max(~ce);
-      wl = (int)(emin & 63);
-    }
-    const uint32_t ew = __builtin_amdgcn_readlane(head_e, wl);
-    my_key = lane == j ? M : my_key;
-    my_e = lane == j ? ew : my_e;
-    pos += lane == wl;
-    uint32_t nh = 0u, ne = 0u;
-#pragma unroll
-    for (int i = 0; i < SLOTS; ++i) {
-      nh = pos == i ? hi[i] : nh;
-      ne = pos == i ? ex[i] : ne;
-    }
-    head = nh;
-    head_e = ne;
-  }
-}
-
-// Top-k of one token's E logits (LDS) by one wave.  Lane l holds the keys of
-// experts l + 64 * i (i < SLOTS): the order-preserving bits of the logit; the
-// order is by key, and on equal keys the lower expert first.
-//  1. tau = the k-th largest lane maximum, its top 16 bits found with ballots
-//     (the rest left 0): at least k keys are >= tau, so every chosen
-//     expert's key is >= tau.
-//  2. The keys >= tau (usually a few more than k) are packed into `cand` as
-//     key << 32 | ~expert, which orders them exactly as the rule above.
-//  3. Each candidate's rank = the number of larger candidates; rank j < k is
-//     the j-th choice.
-// More than 64 candidates (many equal logits) take the extraction rounds.
-// Lane j < k writes the j-th expert to ids[j] and returns its key (the
-// weights follow in pt_topk_weights).  `cand`: 64 words of LDS for this wave.
-template <int SLOTS>
-__device__ __forceinline__ uint32_t pt_topk_select(const float* lg, int E, int k, int* ids, u64* cand) {
-  const int lane = pt_lane();
-  uint32_t hi[SLOTS];
-  uint32_t head = 0u;
-  float v[SLOTS];  // every load is issued before the first use
-#pragma unroll
-  for (int i = 0; i < SLOTS; ++i) v[i] = lg[min(lane + 64 * i, E - 1)];
-#pragma unroll
-  for (int i = 0; i < SLOTS; ++i) {
-    const uint32_t key = moe_f32_order_key(v[i]);
-    hi[i] = lane + 64 * i < E ? key : 0u;  // every real key is > 0
-    head = max(head, hi[i]);
-  }
-  // one bit per step, bits 31..16; the low 16 bits stay 0, which only lowers
-  // tau (keys within about 1% of the k-th lane maximum join the candidates)
-  uint32_t tau = 0u;
-#pragma unroll
-  for (int b = 31; b >= 16; --b) {
-    const uint32_t c = tau | (1u << b);
-    tau = __popcll(__ballot(head >= c)) >= k ? c : tau;
-  }
-  int n = 0;
-#pragma unroll
-  for (int i = 0; i < SLOTS; ++i) {
-    const bool t = hi[i] >= tau && lane + 64 * i < E;
-    const uint64_t m = __ballot(t);
-    const int p = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-    if (t && p < 64) cand[p] = ((u64)hi[i] << 32) | (uint32_t)~(uint32_t)(lane + 64 * i);
-    n += __popcll(m);
-  }
-  uint32_t my_key = 0u, my_e = 0u;
-  if (n <= 64) {
-    const int n8 = (n + 7) & ~7;
-    if (lane >= n && lane < n8) cand[lane] = 0ull;  // pads: below every candidate
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    const u64 me = cand[lane];
-    int rank = 0;
-    for (int m = 0; m < n8; m += 8) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) rank += cand[m + q] > me;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    if (lane < n && rank < k) cand[rank] = me;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    const u64 w = cand[lane < k ? lane : 0];
-    my_key = lane < k ? (uint32_t)(w >> 32) : 0u;
-    my_e = lane < k ? ~(uint32_t)w : 0u;
-  } else {
-    pt_topk_rounds<SLOTS>(hi, k, my_key, my_e);
-  }
-  if (lane < k) ids[lane] = (int)my_e;
-  return my_key;
-}
-
-// Softmax weights of the chosen logits, lane j < k holding the key of the
-// j-th (the largest in lane 0): wts[j].  One wave.
-__device__ __forceinline__ void pt_topk_weights(uint32_t my_key, int k, float* wts) {
-  const int lane = pt_lane();
-  const float m0 = moe_order_key_f32(__builtin_amdgcn_readfirstlane(my_key));
-  const float z = lane < k ? expf(moe_order_key_f32(my_key) - m0) : 0.f;
-  float sum = z;  // sum in lane order: lanes 0..k-1 are added left to right
-  {
-    float acc = 0.f;
-    for (int j = 0; j < k; ++j) acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), j));
-    sum = acc;
-  }
-  if (lane < k) wts[lane] = z / sum;
-}
-
-// Work plan of one layer from the T * k chosen experts (one wave): the
-// distinct experts ("units") in order of first occurrence (token-major), each
-// with its tokens p_tok[ts u + c] and their top-k positions p_j[ts u + c]
-// (ts >= T: a unit holds each token at most once);
-// then, if with_shared, the shared expert with every token (top-k position
-// k); p_roff[u] is the byte offset of the unit's record in the pool;
-// p_misc[0] = the number of units.  n = T * k <= 64.
-__device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, const int32_t* slots, int64_t rbytes,
-                                        bool with_shared, int ts, int* p_exp, int* p_ntok, int* p_tok, int* p_j,
-                                        int64_t* p_roff, int* p_cum, int* p_misc) {
-  const int lane = pt_lane(), n = T * k;
-  if (T == 1) {  // one token: its k experts are distinct, in top-k order
-    if (lane < k) {
-      const int e1 = topi[lane];
-      p_exp[lane] = e1;
-      p_ntok[lane] = 1;
-      p_roff[lane] = (int64_t)slots[e1] * rbytes;
-      p_tok[lane * ts] = 0;
-      p_j[lane * ts] = lane;
-    }
-    if (lane == 0) {
-      if (with_shared) {
-        p_exp[k] = E;
-        p_ntok[k] = 1;
-        p_roff[k] = (int64_t)slots[E] * rbytes;
-        p_tok[k * ts] = 0;
-        p_j[k * ts] = k;
-      }
-      p_misc[0] = with_shared ? k + 1 : k;
-    }
-    return;
-  }
-  const int e = lane < n ? topi[lane] : -1 - lane;  // distinct negatives for idle lanes
-  int first = lane, before = 0, total = 0;           // first lane with this expert; count before; count
-  for (int q = 0; q < n; ++q) {
-    const int eq = __builtin_amdgcn_readlane(e, q);
-    if (eq == e) {
-      first = min(first, q);
-      before += q < lane;
-      ++total;
-    }
-  }
-  const uint64_t firsts = __ballot(lane < n && first == lane);
-  const int u_first = (int)__popcll(firsts & ((1ull << lane) - 1ull));  // rank among first occurrences
-  const int u = __shfl(u_first, first, 64);
-  const int U = (int)__popcll(firsts);
-  if (lane < n) {
-    const int t = lane / k, j = lane % k;
-    if (first == lane) {
-      p_exp[u] = e;
-      p_ntok[u] = total;
-      p_roff[u] = (int64_t)slots[e] * rbytes;
-    }
-    p_tok[u * ts + before] = t;
-    p_j[u * ts + before] = j;
-  }
-  if (with_shared) {
-    if (lane < T) {
-      p_tok[U * ts + lane] = lane;
-      p_j[U * ts + lane] = k;
-    }
-    if (lane == 0) {
-      p_exp[U] = E;
-      p_ntok[U] = T;
-      p_roff[U] = (int64_t)slots[E] * rbytes;
-    }
-  }
-  // p_cum[u] = the summed costs of units < u, a group of unit u costing
-  // PT_GROUP_BASE + (its token count); p_cum[U1] = all of them
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  const int c = lane < U ? PT_GROUP_BASE + p_ntok[lane] : 0;
-  int incl = c;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(incl, d, 64);
-    incl += lane >= d ? v : 0;
-  }
-  if (lane < U) p_cum[lane] = incl - c;
-  const int sum_r = U > 0 ? __builtin_amdgcn_readlane(incl, U - 1) : 0;
-  if (lane == 0) {
-    p_cum[U] = sum_r;
-    if (with_shared) p_cum[U + 1] = sum_r + PT_GROUP_BASE + T;
-    p_misc[0] = with_shared ? U + 1 : U;
-  }
-}
-
-// Prepared activations, one 8-value word of a quantisation block per thread.
-// int4: 4 threads per 32-value block; int2: 2 threads per 16-value block.
-// The block correction is summed over those lanes with shuffles (the lanes
-// of a block are consecutive and the shuffles are executed by the whole wave).
-template <int QFMT>
-__device__ __forceinline__ void pt_prep_word(const float* v, float scale, bool valid, uint32_t* p, float2* corr,
-                                             int sub) {
-  float c0 = 0.f, c1 = 0.f;
-  if (QFMT == MOE_Q4_B32) {
-    const half2v k0 = {(_Float16)1032.f, (_Float16)1032.f};
-    const half2v k1 = {(_Float16)1152.f, (_Float16)1152.f};
-    if (valid) {
-      half2v a0 = {(_Float16)(v[0] * scale), (_Float16)(v[1] * scale)};
-      half2v a1 = {(_Float16)(v[2] * scale * 0.0625f), (_Float16)(v[3] * scale * 0.0625f)};
-      half2v a2 = {(_Float16)(v[4] * scale), (_Float16)(v[5] * scale)};
-      half2v a3 = {(_Float16)(v[6] * scale * 0.0625f), (_Float16)(v[7] * scale * 0.0625f)};
-      p[0] = moe_half2_as_u32(a0);
-      p[1] = moe_half2_as_u32(a1);
-      p[2] = moe_half2_as_u32(a2);
-      p[3] = moe_half2_as_u32(a3);
-      c0 = moe_dot2(a0, k0, c0);
-      c0 = moe_dot2(a1, k1, c0);
-      c0 = moe_dot2(a2, k0, c0);
-      c0 = moe_dot2(a3, k1, c0);
-    }
-    c0 += __shfl_xor(c0, 1, 64);
-    c0 += __shfl_xor(c0, 2, 64);
-    if (valid && sub == 0) *corr = make_float2(c0, 0.f);
-  } else {
-    const half2v k1024 = {(_Float16)1024.f, (_Float16)1024.f};
-    if (valid) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {  // pairs 4*sub + i of the block: multiplier 4^i
-        const float mul = i == 0 ? 1.f : i == 1 ? 0.25f : i == 2 ? 0.0625f : 0.015625f;
-        half2v a = {(_Float16)(v[2 * i] * scale * mul), (_Float16)(v[2 * i + 1] * scale * mul)};
-        p[i] = moe_half2_as_u32(a);
-        const half2v kc = {(_Float16)(1.f / mul), (_Float16)(1.f / mul)};
-        c0 = moe_dot2(a, k1024, c0);
-        c1 = moe_dot2(a, kc, c1);
-      }
-    }
-    c0 += __shfl_xor(c0, 1, 64);
-    c1 += __shfl_xor(c1, 1, 64);
-    if (valid && sub == 0) *corr = make_float2(c0, c1);
-  }
-}
-
-// ---------------------------------------------------------------- LDS layout
-// Section offsets (bytes, 16-byte aligned) shared by the kernel and the host.
-struct PtLds {
-  size_t xs, xprep, lg, topi, topw, p_exp, p_ntok, p_tok, p_j, p_roff, p_cum, p_misc, red, hp, hc, slots, total;
-};
-#define PT_PB_MAX 5    // pieces per batch: 4 of row slot A, 1 of row slot B
-#define PT_SLOTS 80    // gate/up row slots per batch (16 per piece)
-// Token slots of the kernel instance that runs T tokens (its MT; 4 for one
-// token too, whose instance uses a single slot of the same layout), and the
-// per-unit token stride of the plan.
-__host__ __device__ inline int pt_token_slots(int T) { return T <= 4 ? 4 : 8; }
-__host__ __device__ inline PtLds pt_lds(int qfmt, int T, int k, int E, int H, size_t prep_bytes) {
-  PtLds o;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t at = off;
-    off = (off + bytes + 15) / 16 * 16;
-    return at;
-  };
-  const size_t U1max = (size_t)T * k + 1;
-  const size_t ts = (size_t)pt_token_slots(T);
-  (void)qfmt;
-  o.xs = take((size_t)T * H * 4);
-  o.xprep = take((size_t)T * prep_bytes);
-  o.lg = take((size_t)T * E * 4);
-  o.topi = take((size_t)T * k * 4);
-  o.topw = take((size_t)T * k * 4);
-  o.p_exp = take(U1max * 4);
-  o.p_ntok = take(U1max * 4);
-  o.p_tok = take(U1max * ts * 4);
-  o.p_j = take(U1max * ts * 4);
-  o.p_roff = take(U1max * 8);
-  o.p_cum = take((U1max + 1) * 4);
-  o.p_misc = take(16);
-  o.red = take((size_t)PT_WAVES * PT_SLOTS * ts * 4);  // [wave][slot][token slot] partial gate/up dots
-  o.hp = take((size_t)PT_PB_MAX * ts * 4 * 4);         // [piece][token slot][4] prepared h words
-  o.hc = take((size_t)PT_PB_MAX * ts * 8);             // [piece][token slot] corrections
-  o.slots = take((size_t)(E + 1) * 4);
-  o.total = off;
-  return o;
-}
-
-// ---------------------------------------------------------------- the kernel
-template <int QFMT, int MT, int SLOTS>
-__global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int T = a.T, H = a.H, F = a.F, E = a.E, k = a.k, L = a.L, G = a.G;
-  const int g = blockIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  int tid = threadIdx.x, lane = tid & 63;
-  const int blk = QFMT == MOE_Q4_B32 ? 32 : 16;
-  const MoePlanes pl = moe_planes(QFMT, H, F);  // a record is < 4 GiB: 32-bit plane offsets
-  const uint32_t o_guq = (uint32_t)pl.gu_q, o_gus = (uint32_t)pl.gu_s, o_dq = (uint32_t)pl.d_q, o_ds = (uint32_t)pl.d_s;
-
-  const PtLds o = pt_lds(QFMT, T, k, E, H, a.prep_bytes);
-  float* xs = (float*)(smem + o.xs);          // [T][H]
-  uint8_t* xprep = smem + o.xprep;            // [T][prep_bytes]
-  float* lg = (float*)(smem + o.lg);          // [T][E]
-  int* topi = (int*)(smem + o.topi);          // [T][k]
-  float* topw = (float*)(smem + o.topw);      // [T][k]
-  int* p_exp = (int*)(smem + o.p_exp);        // [U1max]
-  int* p_ntok = (int*)(smem + o.p_ntok);      // [U1max]
-  constexpr int TS = MT > 4 ? 8 : 4;          // per-unit token stride of the plan
-  int* p_tok = (int*)(smem + o.p_tok);        // [U1max][TS]
-  int* p_j = (int*)(smem + o.p_j);            // [U1max][TS]
-  int64_t* p_roff = (int64_t*)(smem + o.p_roff); // [U1max] record byte offsets
-  int* p_cum = (int*)(smem + o.p_cum);        // [U1max + 1] group cost prefix per unit
-  int* p_misc = (int*)(smem + o.p_misc);      // [0] = U1
-  float* red = (float*)(smem + o.red);        // [wave][slot][MT]
-  uint32_t* hp = (uint32_t*)(smem + o.hp);    // [piece][MT][4]
-  float2* hc = (float2*)(smem + o.hc);        // [piece][MT]
-  int* lslots = (int*)(smem + o.slots);        // [E+1] this layer's slot-table row
-
-  const uint32_t call = __hip_atomic_load(a.hdr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  bool ok = true;
-  const int nrch = (H + 511) / 512;  // router chunks of 512 columns per row (<= 4)
-
-  for (int l = 0; l < L && ok; ++l) {
-    // the thread index is made opaque once per layer, so that the compiler
-    // derives per-thread offsets where they are used instead of keeping them
-    // live across the whole layer loop
-    asm volatile("" : "+v"(tid));
-    lane = tid & 63;
-    const uint32_t tag = pt_tag(call, L, l);
-    // ------------------------------------------------------------ phase A
-    // this wave's router row (if any) is requested before waiting for x_l
-    // (indices are clamped into range so that every load is unconditional)
-    // this layer's slot-table row (E + 1 <= 1025 entries, <= 3 per thread),
-    // requested now and kept in LDS for the plan
-    int srow[3];
-#pragma unroll
-    for (int c = 0; c < 3; ++c)
-      srow[c] = a.slot_table[(size_t)l * (E + 1) + min(tid + PT_THREADS * c, E)];
-    const uint16_t* wr = a.w_router + (size_t)l * E * H;  // wave-uniform; 32-bit offsets below
-    const int e_row = g + G * wave;
-    // its routing bias too (a load issued only after the dot product would
-    // put a memory round trip between x's arrival and the published logit)
-    const float b_row = a.bias ? a.bias[(size_t)l * E + min(e_row, E - 1)] : 0.f;
-    uint4 rw[4];
-    if (e_row < E) {  // wave-uniform
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t h0 = 512 * c + 8 * lane;
-        rw[c] = *reinterpret_cast<const uint4*>(wr + (uint32_t)e_row * (uint32_t)H + (h0 < (uint32_t)H ? h0 : 0u));
-      }
-    }
-    // Work is handed out in groups of 4 pieces (see "work pieces" below).  One
-    // token: when the units' groups outnumber the workgroups by at most G/4,
-    // every workgroup takes one group and the remaining groups (the last ones
-    // of the shared expert) are split into single pieces, one per workgroup at
-    // most.  Such a piece's gate/up rows and down words are requested here,
-    // before x_l and the logits are exchanged, and used as row slot B (piece
-    // 4) of the batch.  Row slot B: gate/up row l % 16 of the piece over a
-    // quarter of the wave's K range (lane group l / 16).
-    const int NP = F / 8;
-    const int NKU = H / 128;                                     // K units of 128 values
-    const int ku0 = wave * NKU / 8, ku1 = (wave + 1) * NKU / 8;  // <= 2 per wave
-    const int lq = lane >> 4;
-    const int kuB = min(ku0 + (lq >> 1), NKU - 1);
-    const bool kvB = ku0 + (lq >> 1) < ku1;
-    const int TG1 = (k + 1) * (NP / 4);  // groups with one token: k experts and the shared one
-    const int nL = 4 * (TG1 - G);        // single pieces left over
-    const bool sepB = MT == 1 && nL > 0 && nL <= NP && nL <= G;
-    int sp = -1;  // this workgroup's single shared piece
-    if (sepB) {
-      const int j0 = (int)((int64_t)g * nL / G), j1 = (int)((int64_t)(g + 1) * nL / G);
-      sp = j1 > j0 ? NP - nL + j0 : -1;
-    }
-    uint4 gqS[2] = {};
-    uint32_t gsS = 0u;
-    uint32_t dwS[4] = {0u, 0u, 0u, 0u}, dmS[4] = {0u, 0u, 0u, 0u};
-    if (sp >= 0) {  // uniform over the workgroup
-      const uint8_t* recS = a.pool + (int64_t)a.slot_table[(size_t)l * (E + 1) + E] * a.record_bytes;
-      const int i = lane & 15;
-      const uint32_t rowS = (uint32_t)(64 * (sp >> 2) + 8 * (sp & 3) + (i & 7) + (i >= 8 ? 32 : 0));
-      if (QFMT == MOE_Q4_B32) {
-        const uint32_t kb0 = 4u * kuB + 2u * (lq & 1);
-        gsS = *reinterpret_cast<const uint32_t*>(recS + (o_gus + 16u * (uint32_t)kuB * (uint32_t)F + 8u * rowS + 4u * (lq & 1)));
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-          gqS[b] = *reinterpret_cast<const uint4*>(recS + (o_guq + 16u * ((kb0 + b) * 2u * (uint32_t)F + rowS)));
-      } else {
-        const uint32_t un = 2u * kuB + (lq & 1);
-        gqS[0] = *reinterpret_cast<const uint4*>(recS + (o_guq + 16u * (un * 2u * (uint32_t)F + rowS)));
-        gqS[1] = *reinterpret_cast<const uint4*>(recS + (o_gus + 16u * (un * 2u * (uint32_t)F + rowS)));
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t r = (uint32_t)min(tid + 512 * c, H - 1);
-        if (QFMT == MOE_Q4_B32) {
-          const uint32_t bc = (uint32_t)(sp >> 2);
-          dwS[c] = *reinterpret_cast<const uint32_t*>(recS + (o_dq + 16u * (bc * (uint32_t)H + r) + 4u * (sp & 3)));
-          dmS[c] = *reinterpret_cast<const uint16_t*>(recS + (o_ds + 2u * (bc * (uint32_t)H + r)));
-        } else {
-          const uint32_t b2 = (uint32_t)(sp >> 1);
-          dwS[c] = *reinterpret_cast<const uint32_t*>(recS + (o_dq + 4u * (b2 * (uint32_t)H + r)));
-          dmS[c] = *reinterpret_cast<const uint32_t*>(recS + (o_ds + 4u * (b2 * (uint32_t)H + r)));
-        }
-      }
-    }
-    constexpr int NX = 4 * MT;  // words of x per thread: T * H <= 512 * NX
-    if (l == 0) {
-      for (int i = tid; i < T * H; i += PT_THREADS) xs[i] = a.x_in[i];
-    } else {
-      const uint32_t ptag = pt_tag(call, L, l - 1);
-      const int last = T * H - 1;
-      // x is polled word by word (every word carries its tag): one round trip
-      // less than waiting for per-producer sentinels first
-      for (int it = 0;; ++it) {
-        u64 w[NX];
-#pragma unroll
-        for (int q = 0; q < NX; ++q) w[q] = pt_load(a.xbuf, (uint32_t)min(tid + q * PT_THREADS, last));
-        bool mine = true;
-#pragma unroll
-        for (int q = 0; q < NX; ++q) mine &= (uint32_t)(w[q] >> 32) == ptag;
-        if (__syncthreads_and(mine)) {
-#pragma unroll
-          for (int q = 0; q < NX; ++q)
-            if (tid + q * PT_THREADS <= last) xs[tid + q * PT_THREADS] = __uint_as_float((uint32_t)w[q]);
-          break;
-        }
-        if (it > PT_SPIN_MAX) { ok = false; break; }
-      }
-      if (!ok) break;
-    }
-    __syncthreads();
-    // 1 / rms of every token, taken by every wave for itself (no barrier): lane
-    // l sums the squares of its 8-value chunks 512 c + 8 l, then the wave sums
-    float invr[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      float ss = 0.f;
-      if (t < T) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int h0 = 512 * c + 8 * lane;
-          if (h0 < H) {
-            const float4 v0 = *reinterpret_cast<const float4*>(xs + t * H + h0);
-            const float4 v1 = *reinterpret_cast<const float4*>(xs + t * H + h0 + 4);
-            ss = fmaf(v0.x, v0.x, ss); ss = fmaf(v0.y, v0.y, ss); ss = fmaf(v0.z, v0.z, ss); ss = fmaf(v0.w, v0.w, ss);
-            ss = fmaf(v1.x, v1.x, ss); ss = fmaf(v1.y, v1.y, ss); ss = fmaf(v1.z, v1.z, ss); ss = fmaf(v1.w, v1.w, ss);
-          }
-        }
-      }
-      ss = moe_wave_sum(ss);
-      invr[t] = 1.0f / sqrtf(ss / (float)H + PT_EPS);
-    }
-    if (a.x_hist && g == 0)
-      for (int i = tid; i < T * H; i += PT_THREADS) a.x_hist[(size_t)l * T * H + i] = xs[i];
-    // router rows: the prefetched one, then any further rows of this wave
-    for (int e = e_row; e < E; e += G * PT_WAVES) {
-      if (e != e_row) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t h0 = 512 * c + 8 * lane;
-          rw[c] = *reinterpret_cast<const uint4*>(wr + (uint32_t)e * (uint32_t)H + (h0 < (uint32_t)H ? h0 : 0u));
-        }
-      }
-      float acc[MT];
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[t] = 0.f;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int h0 = 512 * c + 8 * lane;
-        if (c < nrch && h0 < H) {
-          const uint32_t ww[4] = {rw[c].x, rw[c].y, rw[c].z, rw[c].w};
-#pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            if (t < T) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {  // the 4 words (8 bf16) of the chunk
-                acc[t] = fmaf(xs[t * H + h0 + 2 * i], __uint_as_float(ww[i] << 16), acc[t]);
-                acc[t] = fmaf(xs[t * H + h0 + 2 * i + 1], __uint_as_float(ww[i] & 0xffff0000u), acc[t]);
-              }
-            }
-          }
-        }
-      }
-      const float b = e == e_row ? b_row : a.bias ? a.bias[(size_t)l * E + e] : 0.f;
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        if (t < T) {
-          const float s = moe_wave_sum(acc[t]);
-          if (lane == t) pt_put(pt_at(a.lbuf, (uint32_t)(t * E + e)), tag, s * invr[t] + b);
-        }
-      }
-    }
-    // prepared xn for the gate/up dot products: one 8-value word per thread
-    {
-      const int nwords = T * H / 8;
-      for (int w0 = 0; w0 < nwords; w0 += PT_THREADS) {
-        const int wi = w0 + tid;
-        const bool valid = wi < nwords;
-        const int t = valid ? wi / (H / 8) : 0, wh = valid ? wi % (H / 8) : 0;  // word within the token
-        const int b = wh / (blk / 8), sub = wh % (blk / 8);
-        uint8_t* out = xprep + (size_t)t * a.prep_bytes;
-        float it = invr[0];
-#pragma unroll
-        for (int q = 1; q < MT; ++q) it = t == q ? invr[q] : it;
-        pt_prep_word<QFMT>(xs + (size_t)t * H + 8 * wh, it, valid, (uint32_t*)out + (blk / 2) * b + 4 * sub,
-                           (float2*)(out + 2 * (size_t)H) + b, sub);
-      }
-    }
-    // ------------------------------------------------------------ phase B
-    for (int it = 0;; ++it) {
-      constexpr int NLG = MT * SLOTS / 8 > 0 ? MT * SLOTS / 8 : 1;  // T * E <= 512 * NLG
-      const int last = T * E - 1;
-      u64 w[NLG];
-#pragma unroll
-      for (int q = 0; q < NLG; ++q) w[q] = pt_load(a.lbuf, (uint32_t)min(tid + q * PT_THREADS, last));
-      bool mine = true;
-#pragma unroll
-      for (int q = 0; q < NLG; ++q) mine &= (uint32_t)(w[q] >> 32) == tag;
-      if (__syncthreads_and(mine)) {
-#pragma unroll
-        for (int q = 0; q < NLG; ++q)
-          if (tid + q * PT_THREADS <= last) lg[tid + q * PT_THREADS] = __uint_as_float((uint32_t)w[q]);
-        break;
-      }
-      if (it > PT_SPIN_MAX) { ok = false; break; }
-    }
-    if (!ok) break;
-#pragma unroll
-    for (int c = 0; c < 3; ++c)
-      if (tid + PT_THREADS * c <= E) lslots[tid + PT_THREADS * c] = srow[c];
-    __syncthreads();
-    uint32_t my_key = 0u;  // wave t < T: the key of top-k position `lane` of token t
-    if (wave < T) {  // `red` is free until the work pieces: 64 candidate words per token
-      my_key = pt_topk_select<SLOTS>(lg + (size_t)wave * E, E, k, topi + wave * k, (u64*)red + 64 * wave);
-      if (MT > 1) pt_topk_weights(my_key, k, topw + wave * k);
-    }
-    __syncthreads();
-    // With one token, unit u < k is top-k choice u and unit k the shared
-    // expert: no plan, and the weights are taken once this workgroup's weight
-    // loads are in flight (below).  With more tokens: the plan (wave 0).
-    auto emit_topk = [&]() {
-      if (g == 0 && tid < T * k) {
-        if (a.topk_idx_out) a.topk_idx_out[(size_t)l * T * k + tid] = topi[tid];
-        if (a.topk_w_out) a.topk_w_out[(size_t)l * T * k + tid] = topw[tid];
-      }
-    };
-    if (MT > 1) {
-      emit_topk();
-      if (wave == 0)
-        pt_plan(topi, T, k, E, lslots, a.record_bytes, true, TS, p_exp, p_ntok, p_tok, p_j, p_roff, p_cum, p_misc);
-      __syncthreads();
-    }
-    // ------------------------------------------------------------ work pieces
-    // The layer's expert work is cut into pieces of 8 f values: (unit u, piece
-    // p) for the units u < U1 of the plan (the shared expert last) and p <
-    // F/8.  Piece (u, p) = the gate and up rows of f = 8p..8p+7 over all of K,
-    // then those 8 columns of the down matrix.  A group is the 4 pieces of one
-    // unit whose down values share a down block column (int4: the 4 words of
-    // the 16-byte blocks of column p/4; int2: the two words of blocks p/2), so
-    // that one group's gate/up rows are 64 consecutive rows of its record and
-    // its down values are 16 bytes (int4) or two words (int2) per row.  With
-    // one token, group i = u * F/32 + b (a workgroup's work is one expert's
-    // rows); with more, i = b * U1 + u (the units interleaved, so that every
-    // workgroup gets the same mix of experts and token counts).  Workgroup g
-    // takes the groups [g*NG/G, (g+1)*NG/G) (with single shared pieces: group
-    // g and that piece; with more tokens: a range balanced by cost), one
-    // batch per group.  In a batch the gate/up rows are split over the 8
-    // waves by K and over the lanes as described at load_gu; row slot s
-    // (s < 64) of the batch is gate/up row s%16 of piece s/16, slots 64..79
-    // the single shared piece (row slot B); the down rows of thread tid are
-    // tid + 512 c.
-    {
-      const int U1 = MT == 1 ? k + 1 : p_misc[0], NB4 = NP / 4, NG = U1 * NB4;
-      const PtMask mk = pt_masks(QFMT);
-      const bool ilv = T > 1;  // interleaved group order
-      int gi0 = (int)((int64_t)g * NG / G), gi1 = (int)((int64_t)(g + 1) * NG / G);
-      if (sepB) {
-        gi0 = g;
-        gi1 = g + 1;
-      }
-      if (MT > 1) {
-        // balanced by cost: group i = b * U1 + u starts at cost b * Crow +
-        // p_cum[u]; workgroup g takes the groups starting in [g C/G, (g+1) C/G)
-        const int Crow = p_cum[U1];
-        const int64_t C = (int64_t)NB4 * Crow;
-        auto first_at = [&](int64_t target) -> int {
-          if (target >= C) return NG;
-          const int b = (int)(target / Crow), rem = (int)(target - (int64_t)b * Crow);
-          const uint64_t m = __ballot(lane < U1 && p_cum[lane < U1 ? lane : 0] >= rem);
-          int u = m ? __ffsll((long long)m) - 1 : min(U1, 64);
-          if (!m)  // units past the wave's 64 lanes (U1 = 65)
-            while (u < U1 && p_cum[u] < rem) ++u;
-          return b * U1 + u;
-        };
-        gi0 = first_at((int64_t)g * C / G);
-        gi1 = first_at((int64_t)(g + 1) * C / G);
-      }
-      constexpr int NRD = 4;  // down rows per thread (H <= 2048)
-      float y[NRD][MT];
-#pragma unroll
-      for (int c = 0; c < NRD; ++c)
-#pragma unroll
-        for (int t = 0; t < MT; ++t) y[c][t] = 0.f;
-      auto unit_of = [&](int gi) { return ilv ? gi % U1 : gi / NB4; };
-      auto block_of = [&](int gi) { return ilv ? gi / U1 : gi % NB4; };
-      auto rec_of = [&](int u) -> const uint8_t* {  // uniform over the workgroup
-        return a.pool + (MT == 1 ? (int64_t)lslots[u < k ? topi[u] : E] * a.record_bytes : p_roff[u]);
-      };
-      // ---- gate/up loads of group gi (its 64 consecutive rows 64 b + rho),
-      // 8 16-byte words q and 4 words sc per lane.  Lane l = (p = l % 16,
-      // quarter q = l / 16) holds rows rho = p + 16 j (j < 4) over quarter q of
-      // the wave's K range, 64 values (int4: blocks 2q, 2q+1 of the wave's 8;
-      // int2: q-unit q of its 4): q[j][0..1] = the two blocks (int4) or the
-      // q-unit and its meta unit (int2), sc[j] = the two scales (int4).  Each
-      // quarter's activations are read from LDS once per token and used for 4
-      // rows (a quarter of the LDS traffic of one row per lane); the quarters
-      // are summed with shuffles.
-      const int lp = lane & 15;
-      const int kuq = min(ku0 + (lq >> 1), NKU - 1);  // K unit of the lane's quarter
-      const bool kvq = ku0 + (lq >> 1) < ku1;
-      auto load_gu = [&](int gi, uint4 (&q)[4][2], uint32_t (&sc)[4]) {
-        const uint8_t* rg = rec_of(unit_of(gi));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t row = (uint32_t)(64 * block_of(gi) + lp + 16 * j);
-          if (QFMT == MOE_Q4_B32) {
-            const uint32_t kb0 = 4u * (uint32_t)kuq + 2u * (lq & 1);
-            sc[j] = *reinterpret_cast<const uint32_t*>(rg + (o_gus + 16u * (uint32_t)kuq * (uint32_t)F + 8u * row + 4u * (lq & 1)));
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
-              q[j][bb] = *reinterpret_cast<const uint4*>(rg + (o_guq + 16u * ((kb0 + bb) * 2u * (uint32_t)F + row)));
-          } else {
-            const uint32_t un = 2u * (uint32_t)kuq + (lq & 1);  // q-unit of 64 values
-            sc[j] = 0u;
-            q[j][0] = *reinterpret_cast<const uint4*>(rg + (o_guq + 16u * (un * 2u * (uint32_t)F + row)));
-            q[j][1] = *reinterpret_cast<const uint4*>(rg + (o_gus + 16u * (un * 2u * (uint32_t)F + row)));
-          }
-        }
-      };
-      uint4 gq[4][2];
-      uint32_t gs[4];
-      if (MT > 1) load_gu(min(gi0, NG - 1), gq, gs);  // clamped: every load is unconditional
-      for (int gi = gi0; gi < gi1; ++gi) {
-        const bool withS = gi == gi0 && sp >= 0;  // the single shared piece rides along
-        const int u = unit_of(gi), bq = block_of(gi);
-        const int ntok = MT == 1 ? 1 : p_ntok[u];
-        const uint8_t* rec = rec_of(u);
-        if (MT == 1) load_gu(gi, gq, gs);
-        // ---- down loads of the group: int4: the 16-byte block and its scale;
-        // int2: the two block words and their two meta words
-        uint4 dq[NRD];
-        uint32_t dsc[NRD];
-        auto load_down = [&]() {
-#pragma unroll
-          for (int c = 0; c < NRD; ++c) {
-            const uint32_t r = (uint32_t)min(tid + 512 * c, H - 1);
-            if (QFMT == MOE_Q4_B32) {
-              dq[c] = *reinterpret_cast<const uint4*>(rec + (o_dq + 16u * ((uint32_t)bq * (uint32_t)H + r)));
-              dsc[c] = *reinterpret_cast<const uint16_t*>(rec + (o_ds + 2u * ((uint32_t)bq * (uint32_t)H + r)));
-            } else {
-              const uint32_t b0 = 2u * (uint32_t)bq;
-              dq[c].x = *reinterpret_cast<const uint32_t*>(rec + (o_dq + 4u * (b0 * (uint32_t)H + r)));
-              dq[c].y = *reinterpret_cast<const uint32_t*>(rec + (o_dq + 4u * ((b0 + 1u) * (uint32_t)H + r)));
-              dq[c].z = *reinterpret_cast<const uint32_t*>(rec + (o_ds + 4u * (b0 * (uint32_t)H + r)));
-              dq[c].w = *reinterpret_cast<const uint32_t*>(rec + (o_ds + 4u * ((b0 + 1u) * (uint32_t)H + r)));
-              dsc[c] = 0u;
-            }
-          }
-        };
-        load_down();
-        __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any dot product
-        if (MT == 1 && gi == gi0 && wave == 0) pt_topk_weights(my_key, k, topw);  // read after the next barrier
-        // ---- gate/up partial dots
-        auto xp_of = [&](int t) -> const uint8_t* {
-          return xprep + (size_t)(MT == 1 ? 0 : p_tok[u * TS + t]) * a.prep_bytes;
-        };
-        {  // the quarter mapping, one token and one block of x at a time
-          const int rho = lp + 16 * lq;
-          const int slot = 16 * ((rho & 31) >> 3) + (rho & 7) + 8 * (rho >> 5);
-#pragma unroll 1
-          for (int t = 0; t < ntok; ++t) {
-            const uint8_t* xp = xp_of(t);
-            const float2* corr = (const float2*)(xp + 2 * (size_t)H);
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
-            if (QFMT == MOE_Q4_B32) {
-              const int kb0 = 4 * kuq + 2 * (lq & 1);
-#pragma unroll
-              for (int bb = 0; bb < 2; ++bb) {
-                uint32_t xw[16];  // the prepared x of block kb0 + bb
-#pragma unroll
-                for (int w4 = 0; w4 < 4; ++w4) {
-                  const uint4 v = *reinterpret_cast<const uint4*>((const uint32_t*)xp + 16 * (kb0 + bb) + 4 * w4);
-                  xw[4 * w4] = v.x; xw[4 * w4 + 1] = v.y; xw[4 * w4 + 2] = v.z; xw[4 * w4 + 3] = v.w;
-                }
-                const float cb = corr[kb0 + bb].x;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                  const float sj = kvq ? moe_f16_to_f32((uint16_t)(gs[j] >> (16 * bb))) : 0.f;
-                  acc[j] = fmaf(sj, pt_q4_dot(gq[j][bb], xw, cb, mk), acc[j]);
-                }
-              }
-            } else {
-              const int un = 2 * kuq + (lq & 1);
-#pragma unroll
-              for (int jb = 0; jb < 4; ++jb) {
-                uint32_t xw[8];  // the prepared x of block 4 un + jb
-#pragma unroll
-                for (int w4 = 0; w4 < 2; ++w4) {
-                  const uint4 v = *reinterpret_cast<const uint4*>((const uint32_t*)xp + 32 * un + 8 * jb + 4 * w4);
-                  xw[4 * w4] = v.x; xw[4 * w4 + 1] = v.y; xw[4 * w4 + 2] = v.z; xw[4 * w4 + 3] = v.w;
-                }
-                const float2 cb = corr[4 * un + jb];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                  const uint32_t qw = jb == 0 ? gq[j][0].x : jb == 1 ? gq[j][0].y : jb == 2 ? gq[j][0].z : gq[j][0].w;
-                  const uint32_t mw = jb == 0 ? gq[j][1].x : jb == 1 ? gq[j][1].y : jb == 2 ? gq[j][1].z : gq[j][1].w;
-                  const float sc = kvq ? moe_f16_to_f32((uint16_t)(mw & 0xffff)) : 0.f;
-                  const float mn = kvq ? moe_f16_to_f32((uint16_t)(mw >> 16)) : 0.f;
-                  acc[j] += pt_q2_dot(qw, sc, mn, xw, cb, mk);
-                }
-              }
-            }
-            // sum over the quarters (lanes l, l ^ 16, l ^ 32, l ^ 48)
-            float mine = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              float v = acc[j];
-              v += __shfl_xor(v, 16, 64);
-              v += __shfl_xor(v, 32, 64);
-              mine = lq == j ? v : mine;
-            }
-            red[(wave * PT_SLOTS + slot) * MT + t] = mine;
-          }
-        }
-        if (MT == 1) {  // row slot B: the single shared piece, 4 lane groups summed with shuffles
-          float accB = 0.f;
-          const uint8_t* xp = xprep;
-          if (QFMT == MOE_Q4_B32) {
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              const int kb = 4 * kuB + 2 * (lq & 1) + b;
-              const float sc = kvB ? moe_f16_to_f32((uint16_t)(gsS >> (16 * b))) : 0.f;
-              const float cc = ((const float2*)(xp + 2 * (size_t)H))[kb].x;
-              accB = fmaf(sc, pt_q4_dot(gqS[b], (const uint32_t*)xp + 16 * kb, cc, mk), accB);
-            }
-          } else {
-            const uint32_t qw[4] = {gqS[0].x, gqS[0].y, gqS[0].z, gqS[0].w};
-            const uint32_t mw[4] = {gqS[1].x, gqS[1].y, gqS[1].z, gqS[1].w};
-#pragma unroll
-            for (int jb = 0; jb < 4; ++jb) {
-              const int bl = 4 * (2 * kuB + (lq & 1)) + jb;
-              const float sc = kvB ? moe_f16_to_f32((uint16_t)(mw[jb] & 0xffff)) : 0.f;
-              const float mn = kvB ? moe_f16_to_f32((uint16_t)(mw[jb] >> 16)) : 0.f;
-              const float2 cc = ((const float2*)(xp + 2 * (size_t)H))[bl];
-              accB += pt_q2_dot(qw[jb], sc, mn, (const uint32_t*)xp + 8 * bl, cc, mk);
-            }
-          }
-          accB += __shfl_xor(accB, 16, 64);
-          accB += __shfl_xor(accB, 32, 64);
-          red[(wave * PT_SLOTS + 64 + (lane & 15)) * MT] = accB;  // the 4 lane groups hold the same sum
-        }
-        // several tokens: the next group's gate/up rows are requested now (after
-        // this group's down words, so that the down dots need not wait for
-        // them) and land while this group's SiLU and down dots run
-        uint4 gqN[4][2];
-        uint32_t gsN[4];
-        if (MT > 1) load_gu(min(gi + 1, gi1 - 1), gqN, gsN);
-        __syncthreads();
-        // ---- h = silu(gate) * up, 8 threads per (piece, token slot), then the
-        // prepared word of the 8 h values for the down dots
-        {
-          const int item = tid >> 3, fi = tid & 7;  // item = pi * MT + t
-          const int pi = item / MT, t = item % MT;
-          const bool iv = pi < 4 || (pi == 4 && withS);
-          float hv = 0.f;
-          if (iv) {
-            float sg = 0.f, su = 0.f;
-#pragma unroll
-            for (int w = 0; w < PT_WAVES; ++w) {
-              sg += red[(w * PT_SLOTS + 16 * pi + fi) * MT + t];
-              su += red[(w * PT_SLOTS + 16 * pi + 8 + fi) * MT + t];
-            }
-            hv = moe_silu(sg) * su;
-          }
-          const float hn = __shfl_xor(hv, 1, 64);  // partner value of the pair
-          const int pk = fi >> 1;                   // pair index within the word
-          float c0 = 0.f, c1 = 0.f;
-          uint32_t pw = 0u;
-          if ((fi & 1) == 0) {
-            if (QFMT == MOE_Q4_B32) {
-              const float mul = (pk & 1) ? 0.0625f : 1.f;
-              const half2v a2 = {(_Float16)(hv * mul), (_Float16)(hn * mul)};
-              const half2v kk = {(_Float16)((pk & 1) ? 1152.f : 1032.f), (_Float16)((pk & 1) ? 1152.f : 1032.f)};
-              pw = moe_half2_as_u32(a2);
-              c0 = moe_dot2(a2, kk, 0.f);
-            } else {
-              const float mul = pk == 0 ? 1.f : pk == 1 ? 0.25f : pk == 2 ? 0.0625f : 0.015625f;
-              const half2v a2 = {(_Float16)(hv * mul), (_Float16)(hn * mul)};
-              const half2v k1024 = {(_Float16)1024.f, (_Float16)1024.f};
-              const half2v kc = {(_Float16)(1.f / mul), (_Float16)(1.f / mul)};
-              pw = moe_half2_as_u32(a2);
-              c0 = moe_dot2(a2, k1024, 0.f);
-              c1 = moe_dot2(a2, kc, 0.f);
-            }
-          }
-          // corrections summed over the 4 pairs (lanes fi = 0, 2, 4, 6 of the item)
-          c0 += __shfl_xor(c0, 2, 64);
-          c0 += __shfl_xor(c0, 4, 64);
-          c1 += __shfl_xor(c1, 2, 64);
-          c1 += __shfl_xor(c1, 4, 64);
-          if (iv && item < PT_PB_MAX * MT) {
-            if ((fi & 1) == 0) hp[item * 4 + pk] = pw;
-            if (fi == 0) hc[item] = make_float2(c0, c1);
-          }
-        }
-        __syncthreads();
-        // ---- down dots: rows tid + 512 c, the group's 4 pieces
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          if (MT > 1 && t >= ntok) break;
-          const int tk = MT == 1 ? 0 : p_tok[u * TS + t], jj = MT == 1 ? u : p_j[u * TS + t];
-          const float wgt = jj < k ? topw[tk * k + jj] : 1.f;
-#pragma unroll
-          for (int pi = 0; pi < 4; ++pi) {
-            const uint32_t* hw4 = hp + (pi * MT + t) * 4;
-            const float2 cc = hc[pi * MT + t];
-#pragma unroll
-            for (int c = 0; c < NRD; ++c) {
-              float v;
-              if (QFMT == MOE_Q4_B32) {
-                const uint32_t w = pi == 0 ? dq[c].x : pi == 1 ? dq[c].y : pi == 2 ? dq[c].z : dq[c].w;
-                v = moe_f16_to_f32((uint16_t)dsc[c]) * pt_q4_word(w, hw4, cc.x, mk);
-              } else {
-                const uint32_t w = (pi < 2 ? dq[c].x : dq[c].y) >> (8 * (pi & 1));
-                const uint32_t m = pi < 2 ? dq[c].z : dq[c].w;
-                v = pt_q2_word(w, moe_f16_to_f32((uint16_t)(m & 0xffff)), moe_f16_to_f32((uint16_t)(m >> 16)), hw4, cc, mk);
-              }
-#pragma unroll
-              for (int tt = 0; tt < MT; ++tt)
-                if (tt == tk) y[c][tt] = fmaf(wgt, v, y[c][tt]);
-            }
-          }
-        }
-        if (MT == 1 && withS) {  // the single shared piece: weight 1
-          const uint32_t* hw4 = hp + 4 * 4;
-          const float2 cc = hc[4];
-#pragma unroll
-          for (int c = 0; c < NRD; ++c) {
-            float v;
-            if (QFMT == MOE_Q4_B32) {
-              v = moe_f16_to_f32((uint16_t)dmS[c]) * pt_q4_word(dwS[c], hw4, cc.x, mk);
-            } else {
-              const uint32_t w = dwS[c] >> (8 * (sp & 1));
-              v = pt_q2_word(w, moe_f16_to_f32((uint16_t)(dmS[c] & 0xffff)), moe_f16_to_f32((uint16_t)(dmS[c] >> 16)),
-                             hw4, cc, mk);
-            }
-            y[c][0] += v;
-          }
-        }
-        __syncthreads();  // red, hp, hc are reused by the next batch
-        if (MT > 1) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            gs[j] = gsN[j];
-            gq[j][0] = gqN[j][0];
-            gq[j][1] = gqN[j][1];
-          }
-        }
-      }
-      if (MT == 1) {
-        if (gi0 == gi1 && wave == 0) pt_topk_weights(my_key, k, topw);
-        emit_topk();  // topw was written before a barrier above (or by this thread's wave, lanes < k)
-      }
-      // this workgroup's partial output, one vector per token (the thread
-      // index is made opaque here so that the compiler computes the NRD * MT
-      // offsets now instead of keeping them live across the layer loop)
-      int tid_o = tid;
-      asm volatile("" : "+v"(tid_o));
-#pragma unroll
-      for (int c = 0; c < NRD; ++c) {
-        const int r = tid_o + 512 * c;
-        if (r < H) {
-#pragma unroll
-          for (int t = 0; t < MT; ++t)
-            if (t < T) pt_put(pt_at(a.pbuf, (uint32_t)((g * T + t) * H + r)), tag, y[c][t]);
-        }
-      }
-    }
-    // ------------------------------------------------------------ phase C
-    {
-      // outputs (t, r) for r in this workgroup's rows; TPO threads per output,
-      // thread `sub` summing the partials of workgroups sub, sub + TPO, ... in
-      // order, then a butterfly over the TPO lanes (a fixed order for a given T)
-      const int r0 = g * a.rpw;
-      const int nout = T * a.rpw;
-      const int tpo = a.tpo;
-      constexpr int NQ = MT == 1 ? 8 : MT == 2 ? 12 : MT == 4 ? 24 : 32;
-      if (!pt_wait_sentinels(a.pbuf, (uint32_t)((T - 1) * H + r0 + a.rpw - 1), (uint32_t)(T * H), G, tag,
-                             PT_SPIN_MAX)) {
-        ok = false;
-        break;
-      }
-      for (int ob = 0; ob < nout && ok; ob += PT_THREADS / tpo) {
-        const int oo = ob + tid / tpo, sub = tid % tpo;
-        const bool act = oo < nout;
-        const int t = act ? oo / a.rpw : 0, rr = act ? r0 + oo % a.rpw : r0;
-        float sum = 0.f;
-        for (int it = 0;; ++it) {
-          bool mine = true;
-          float sacc = 0.f;
-          for (int p0 = sub; p0 < G; p0 += tpo * NQ) {
-            u64 w[NQ];
-#pragma unroll
-            for (int qq = 0; qq < NQ; ++qq)
-              w[qq] = pt_load(a.pbuf, (uint32_t)((min(p0 + tpo * qq, G - 1) * T + t) * H + rr));
-#pragma unroll
-            for (int qq = 0; qq < NQ; ++qq) {
-              if (p0 + tpo * qq < G) {
-                if ((uint32_t)(w[qq] >> 32) == tag) sacc += __uint_as_float((uint32_t)w[qq]);
-                else mine = false;
-              }
-            }
-          }
-          sum = sacc;
-          if (__syncthreads_and(mine || !act)) break;
-          if (it > PT_SPIN_MAX) { ok = false; break; }
-        }
-        if (!ok) break;
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1)
-          if (m < tpo) sum += __shfl_xor(sum, m, 64);
-        if (act && sub == 0) {
-          const float xn = xs[t * H + rr] + sum;
-          if (l + 1 < L) pt_put(pt_at(a.xbuf, (uint32_t)(t * H + rr)), tag, xn);
-          else a.x_out[(size_t)t * H + rr] = xn;
-        }
-      }
-      if (!ok) break;
-    }
-    __syncthreads();
-  }
-  if (!ok) {
-    if (tid == 0) __hip_atomic_store(a.hdr + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int i = g * PT_THREADS + tid; i < T * H; i += G * PT_THREADS) a.x_out[i] = __builtin_nanf("");
-    return;
-  }
-  if (g == 0 && tid == 0) __hip_atomic_store(a.hdr + 1, call + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// One decode / verify step through L layers as ONE persistent kernel: the
+// buffer set-up kernels and the host launcher.  The kernel and its design are
+// in decode_persistent_kernel.h; its instances in decode_persistent_mt*.hip.
+#include "decode_persistent_kernel.h"
 
 // Zeroes the tagged buffers once per workspace (recognised by a magic word).
 __global__ void decode_persistent_init_kernel(uint32_t* hdr, u64* buf, size_t nwords) {
@@ -1306,16 +106,14 @@ int moe_launch_decode_persistent(const float* x_in, int T, int H, int F, int E, 
   const size_t nwords = (P.total - P.xbuf) / 8;
   decode_persistent_init_kernel<<<256, 256, 0, st>>>(a.hdr, a.xbuf, nwords);
   decode_persistent_mark_kernel<<<1, 64, 0, st>>>(a.hdr);
-  const int mt = T == 1 ? 1 : T == 2 ? 2 : T <= 4 ? 4 : 8;
+  // the instance with the fewest token slots >= T (unused slots cost registers
+  // and instructions: T=3 on 3 slots 2.21 -> 2.11 ms, T=5 and 6 on 6 slots instead
+  // of 8 3.84 -> 3.39 and 4.23 -> 3.71 ms per 48-layer step)
+  const int mt = T <= 4 ? T : T <= 6 ? 6 : 8;
   const int slots = E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : 16;
-  const void* fn = nullptr;
-#define PT_PICK(Q, M, S) \
-  if (qfmt == Q && mt == M && slots == S) fn = (const void*)decode_persistent_kernel<Q, M, S>;
-#define PT_PICK_S(Q, M) PT_PICK(Q, M, 1) PT_PICK(Q, M, 2) PT_PICK(Q, M, 4) PT_PICK(Q, M, 8) PT_PICK(Q, M, 16)
-  PT_PICK_S(MOE_Q4_B32, 1) PT_PICK_S(MOE_Q4_B32, 2) PT_PICK_S(MOE_Q4_B32, 4) PT_PICK_S(MOE_Q4_B32, 8)
-  PT_PICK_S(MOE_Q2_B16, 1) PT_PICK_S(MOE_Q2_B16, 2) PT_PICK_S(MOE_Q2_B16, 4) PT_PICK_S(MOE_Q2_B16, 8)
-#undef PT_PICK_S
-#undef PT_PICK
+  const void* fn = pt_kernel_mt12(qfmt, mt, slots);
+  if (!fn) fn = pt_kernel_mt34(qfmt, mt, slots);
+  if (!fn) fn = pt_kernel_mt68(qfmt, mt, slots);
   if (!fn) return moe_fail(MOE_EUNSUPPORTED, "decode persistent: no kernel for this shape");
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)P.lds) != hipSuccess)
     return moe_fail(MOE_EHIP, "decode persistent: cannot reserve %zu bytes of LDS", P.lds);
