@@ -13,6 +13,7 @@ import torch
 
 import gen as G
 import oracle as O
+from oracle import tier as T
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -293,6 +294,104 @@ def test_usage_topn_brute_force():
     flat = new.reshape(-1).tolist()
     brute = sorted(range(L * E), key=lambda i: (-flat[i], i))[:17]
     assert top.tolist() == brute
+
+
+# ---------------------------------------------------------------- hot tier
+
+def _tier_home(L, E, n_hot):
+    return np.array([[n_hot + l * (E + 1) + e for e in range(E + 1)] for l in range(L)], np.int32)
+
+
+def _tier_consistent(slot, owner, home, E):
+    """Every hot slot's expert points at that slot, every other expert at its
+    home record, no expert held twice, the shared column never touched."""
+    held = [int(f) for f in owner if f >= 0]
+    assert len(held) == len(set(held))
+    L = home.shape[0]
+    for f in range(L * E):
+        l, e = divmod(f, E)
+        want = [i for i, o in enumerate(owner) if o == f]
+        want = want[0] if want else None
+        if want is not None:
+            assert owner[want] == f and slot[l][e] == want
+        else:
+            assert slot[l][e] == home[l][e]
+    assert np.array_equal(np.asarray(slot)[:, E], home[:, E])
+
+
+def test_tier_worked_example():
+    g = json.load(open(os.path.join(GOLD, "tier_small.json")))
+    L, E, n = g["L"], g["E"], g["n_hot"]
+    home = _tier_home(L, E, n)
+    slot, owner, swaps = T.tier_fill(np.array(g["profile"], np.float32), n, home)
+    assert owner.tolist() == g["fill_owner"] and slot.tolist() == g["fill_slot_table"]
+    assert [sw[2] for sw in swaps] == [0, 1, 2] and all(sw[1] == -1 for sw in swaps)
+    start = home.copy()
+    for i, f in enumerate(g["owner"]):
+        start[f // E][f % E] = i
+    sc = np.array(g["scores"], np.float32)
+    slot, owner, swaps = T.tier_rebalance(sc, g["top_idx"], n, g["max_swaps"], home, start, g["owner"])
+    assert [list(sw) for sw in swaps] == g["swaps"] and owner.tolist() == g["rebalance_owner"]
+    _tier_consistent(slot, owner, home, E)
+    swaps3 = T.tier_rebalance(sc, g["top_idx"], n, 3, home, start, g["owner"])[2]
+    assert [list(sw) for sw in swaps3] == g["max_swaps_3_swaps"]
+    sc[0][0] = 2.0
+    swaps_tie = T.tier_rebalance(sc, g["top_idx"], n, 3, home, start, g["owner"])[2]
+    assert [list(sw) for sw in swaps_tie] == g["tie_swaps"]
+    # residents 1 and 2 scored alike: the higher index (2, in slot 1) goes first
+    sc2 = np.array(g["scores"], np.float32)
+    sc2[0][1] = sc2[0][2] = 1.0
+    assert T.tier_rebalance(sc2, [6], n, 1, home, start, g["owner"])[2] == [(6, 2, 1, 10)]
+    # empty slots are taken first, the lower slot first: owner [-1, 2, -1]
+    part = home.copy()
+    part[0][2] = 1
+    sw = T.tier_rebalance(np.array(g["scores"], np.float32), g["top_idx"], n, 3, home, part, [-1, 2, -1])[2]
+    assert [(c, v, d) for c, v, d, _ in sw] == [(6, -1, 0), (3, -1, 2), (0, 2, 1)]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tier_fill_and_rebalance_brute_force(seed):
+    """Random tiers (ties, empty slots, caps): the fill holds exactly the
+    brute-force top n_hot; after a rebalance no re-ranked expert left outside
+    scores strictly above any resident, unless the swap cap stopped it, and
+    the swapped-in experts are the first candidates in rank order."""
+    rng = np.random.default_rng(100 + seed)
+    L, E = int(rng.integers(1, 4)), int(rng.integers(3, 12))
+    N = L * E
+    n_hot = int(rng.integers(1, N + 1))
+    home = _tier_home(L, E, n_hot)
+    prof = rng.integers(0, 5, size=(L, E)).astype(np.float32)
+    slot, owner, _ = T.tier_fill(prof, n_hot, home)
+    key = lambda sc: (lambda i: (-float(sc.reshape(-1)[i]), i))
+    assert sorted(owner.tolist()) == sorted(sorted(range(N), key=key(prof))[:n_hot])
+    assert owner.tolist() == sorted(owner.tolist())
+    _tier_consistent(slot, owner, home, E)
+    # start from a random partial tier: some slots empty
+    owner = np.full(n_hot, -1, np.int32)
+    held = rng.choice(N, size=int(rng.integers(0, n_hot + 1)), replace=False)
+    pos = rng.choice(n_hot, size=held.size, replace=False)
+    owner[pos] = held
+    slot = home.copy()
+    for i, f in enumerate(owner):
+        if f >= 0:
+            slot[f // E][f % E] = i
+    scores = rng.integers(0, 6, size=(L, E)).astype(np.float32) * 0.5
+    flat = scores.reshape(-1)
+    n_top = int(rng.integers(1, N + 1))
+    top = sorted(range(N), key=key(scores))[:n_top]
+    cap = int(rng.integers(1, n_top + 2))
+    new_slot, new_owner, swaps = T.tier_rebalance(scores, top, n_hot, cap, home, slot, owner)
+    _tier_consistent(new_slot, new_owner, home, E)
+    cands = [f for f in top if f not in set(owner.tolist())]
+    assert [sw[0] for sw in swaps] == cands[:len(swaps)] and len(swaps) <= cap
+    empties_before = int((owner < 0).sum())
+    assert [sw[1] for sw in swaps[:empties_before]] == [-1] * min(empties_before, len(swaps))
+    residents = [int(f) for f in new_owner if f >= 0]
+    left_out = [f for f in top if f not in residents]
+    if len(swaps) < cap and residents and len(residents) == n_hot:
+        assert all(flat[f] <= min(flat[r] for r in residents) for f in left_out)
+    if len(swaps) < cap and len(residents) < n_hot:
+        assert not left_out  # free slots take every candidate
 
 
 # ---------------------------------------------------------------- stack
