@@ -259,6 +259,53 @@ int moe_usage_update(const int32_t* topk_idx, int T, int k, int layer, int L,
                      int32_t* top_out, void* stream);
 
 /* --------------------------------------------------------------------------
+ * Capacity-limited hot tier of expert records.  Pages: "为什么 Strata 在小显存
+ * 显卡上这么快", section "一台电脑就是一组水管" (a shipped usage profile ranks
+ * every expert and each card fills its expert slots in that order; an
+ * adaptive tier swaps in at most 96 experts every four rounds, towards the
+ * experts in actual use); "Strata：12GB 显卡跑 125B 模型，MoE 专家热缓存打破
+ * VRAM 限制", section "工作原理" (a decayed usage score decides eviction).
+ *
+ * Layout: pool holds n_hot hot slots (slots 0..n_hot-1) followed by every
+ * expert's record at its home slot, home_table int32 [L][E+1] (every home slot
+ * >= n_hot, distinct; column E, the shared expert, is never part of the
+ * tier).  slot_table int32 [L][E+1] is what the expert ops and
+ * moe_decode_stack read: a resident expert's entry is its hot slot, every
+ * other entry equals home_table.  hot_owner int32 [n_hot] holds the flat index
+ * l*E+e of the expert in each hot slot, or -1 (empty).  Records are copied on
+ * the device with 16-byte loads and stores; record_bytes is a multiple of 256
+ * and pool 256-byte aligned.  swaps int32 [max(n_hot, max_swaps)][4] receives
+ * one entry per copied record: (expert, evicted expert or -1, hot slot, home
+ * slot of the expert); n_swaps int32 [1] their count.  All device memory,
+ * owned by the caller; asynchronous on `stream`.  Requires L*E <= 65536,
+ * 1 <= n_hot <= L*E, finite scores.  A call that overlaps another tier call
+ * or a reader of the same slot table on another stream races.
+ *
+ * moe_tier_fill -- resets the tier from a profile: slot_table = home_table,
+ *   then the n_hot experts first in the order (scores desc, flat index asc)
+ *   become resident, hot slot i holding the i-th of them in flat-index order.
+ *   scores fp32 [L][E] (e.g. the scores of moe_usage_update).
+ *
+ * moe_tier_rebalance -- one adaptive step.  Candidates: the entries of top_idx
+ *   [n_top] (flat indices in rank order, as moe_usage_update's top_out) that
+ *   are not resident, in that order.  Victims: the hot slots, empty ones first
+ *   (lower slot first), then by the held expert's score ascending, equal
+ *   scores the higher flat index first.  Candidate i takes victim i's slot
+ *   while that slot is empty or the candidate's score is strictly higher
+ *   (equal scores never swap), at most max_swaps times; an evicted expert's
+ *   entry returns to its home slot.  0 <= n_top <= min(L*E, 1024),
+ *   0 <= max_swaps <= 1024. */
+int moe_tier_fill(const float* scores, int L, int E, int n_hot,
+                  const int32_t* home_table, int32_t* slot_table,
+                  int32_t* hot_owner, void* pool, int64_t record_bytes,
+                  int32_t* swaps, int32_t* n_swaps, void* stream);
+int moe_tier_rebalance(const float* scores, const int32_t* top_idx, int n_top,
+                       int L, int E, int n_hot, int max_swaps,
+                       const int32_t* home_table, int32_t* slot_table,
+                       int32_t* hot_owner, void* pool, int64_t record_bytes,
+                       int32_t* swaps, int32_t* n_swaps, void* stream);
+
+/* --------------------------------------------------------------------------
  * moe_decode_stack -- one decode / verify step through L chained layers
  * (1 <= T <= MOE_MAX_DECODE_T), the whole step enqueued on `stream` with no
  * host synchronisation (it may be captured into a HIP graph).  Pages: "为什么 Strata 在小显存显卡上这么快", section

@@ -10,6 +10,7 @@
 //   unique; an 8-pass MSB radix select finds the top_n-th largest key, the
 //   keys at or above it are gathered and bitonic-sorted (descending).
 #include "moe_common.h"
+#include "moe_select.h"
 
 __global__ __launch_bounds__(1024) void usage_decay_kernel(const int32_t* __restrict__ idx, int T, int k, int layer,
                                                            int E, float decay, int32_t* __restrict__ hits_ws,
@@ -42,61 +43,9 @@ __device__ __forceinline__ uint64_t usage_key(const float* s, int i) {
 
 __global__ __launch_bounds__(1024) void usage_rerank_kernel(const float* __restrict__ scores, int N, int top_n,
                                                             int32_t* __restrict__ top_out) {
-  __shared__ unsigned hist[256];
   __shared__ uint64_t sel[1024];
-  __shared__ uint64_t prefix_s;
-  __shared__ int need_s, cnt_s;
-  const int tid = threadIdx.x;
-  uint64_t prefix = 0;
-  int need = top_n;
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
-    const uint64_t hi_mask = pass == 0 ? 0ull : (~0ull << (shift + 8));
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < N; i += 1024) {
-      const uint64_t key = usage_key(scores, i);
-      if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1u);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int above = 0, d = 255;
-      for (; d > 0; --d) {
-        if (above + (int)hist[d] >= need) break;
-        above += hist[d];
-      }
-      prefix_s = prefix | ((uint64_t)d << shift);
-      need_s = need - above;
-    }
-    __syncthreads();
-    prefix = prefix_s;
-    need = need_s;
-    __syncthreads();
-  }
-  if (tid == 0) cnt_s = 0;
-  __syncthreads();
-  for (int i = tid; i < N; i += 1024) {
-    const uint64_t key = usage_key(scores, i);
-    if (key >= prefix) sel[atomicAdd(&cnt_s, 1)] = key;
-  }
-  __syncthreads();
-  if (tid >= cnt_s) sel[tid] = 0ull;
-  __syncthreads();
-  for (int size = 2; size <= 1024; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const int j = tid ^ stride;
-      if (j > tid) {
-        const bool desc = (tid & size) == 0;
-        const uint64_t a = sel[tid], b = sel[j];
-        if (desc ? (a < b) : (a > b)) {
-          sel[tid] = b;
-          sel[j] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  if (tid < top_n) top_out[tid] = (int32_t)(0xFFFFFFFFu - (uint32_t)sel[tid]);
+  moe_top_keys_sorted([&](int i) { return usage_key(scores, i); }, N, top_n, sel);
+  if (threadIdx.x < top_n) top_out[threadIdx.x] = (int32_t)(0xFFFFFFFFu - (uint32_t)sel[threadIdx.x]);
 }
 
 extern "C" int moe_usage_update(const int32_t* topk_idx, int T, int k, int layer, int L, int E, float decay,

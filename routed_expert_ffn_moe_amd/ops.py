@@ -17,6 +17,7 @@ from ._lib import (MOE_BF16, MOE_F32, MOE_OP_DECODE_STACK, MOE_OP_EXPERT_GEMV_Q,
 __all__ = [
     "moe_abi_version", "moe_record_bytes", "moe_workspace_size", "workspace", "moe_route_topk", "moe_permute",
     "moe_expert_gemv_q", "moe_grouped_gemm_q", "moe_combine", "moe_usage_update", "moe_decode_stack",
+    "moe_tier_fill", "moe_tier_rebalance",
     "MOE_Q4_B32", "MOE_Q2_B16", "MoeError", "MOE_OP_ROUTE_TOPK", "MOE_OP_PERMUTE", "MOE_OP_EXPERT_GEMV_Q",
     "MOE_OP_GROUPED_GEMM_Q", "MOE_OP_DECODE_STACK",
 ]
@@ -157,6 +158,30 @@ def moe_usage_update(topk_idx, layer, L, E, decay, step, rerank_every, top_n, hi
     check(_lib.load().moe_usage_update(_p(topk_idx), T, k, layer, L, E, float(decay), int(step), rerank_every, top_n,
                                        _p(hits_ws), _p(scores), _p(top_out), _stream(stream)))
     return scores, top_out
+
+
+def moe_tier_fill(scores, n_hot, home_table, slot_table, hot_owner, pool, record_bytes, swaps, n_swaps,
+                  stream=None):
+    """scores fp32 [L][E]; home_table / slot_table int32 [L][E+1]; hot_owner
+    int32 [n_hot]; swaps int32 [>= n_hot][4]; n_swaps int32 [1]."""
+    L, E = scores.shape
+    _dev(scores, home_table, slot_table, hot_owner, pool, swaps, n_swaps)
+    check(_lib.load().moe_tier_fill(_p(scores), L, E, n_hot, _p(home_table), _p(slot_table), _p(hot_owner), _p(pool),
+                                    record_bytes, _p(swaps), _p(n_swaps), _stream(stream)))
+    return slot_table, hot_owner
+
+
+def moe_tier_rebalance(scores, top_idx, n_hot, max_swaps, home_table, slot_table, hot_owner, pool, record_bytes,
+                       swaps, n_swaps, stream=None):
+    """top_idx int32 [n_top] flat indices in rank order (None: no candidates);
+    swaps int32 [>= max_swaps][4]."""
+    L, E = scores.shape
+    n_top = 0 if top_idx is None else top_idx.numel()
+    _dev(scores, top_idx, home_table, slot_table, hot_owner, pool, swaps, n_swaps)
+    check(_lib.load().moe_tier_rebalance(_p(scores), _p(top_idx), n_top, L, E, n_hot, max_swaps, _p(home_table),
+                                         _p(slot_table), _p(hot_owner), _p(pool), record_bytes, _p(swaps),
+                                         _p(n_swaps), _stream(stream)))
+    return slot_table, hot_owner
 
 
 def moe_decode_stack(x_in, F, E, k, w_router, bias, slot_table, pool, record_bytes, qfmt, x_out=None,

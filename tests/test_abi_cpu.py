@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -125,3 +125,29 @@ def test_decode_stack_rejects(lib):
     b = list(a); b[6] = 0
     assert f(*b) == _lib.MOE_ESHAPE
     assert f(*a) == _lib.MOE_EWORKSPACE               # 1 KiB is too small
+
+
+def test_tier_rejects(lib):
+    """Host-side validation of the hot-tier calls (no launch happens)."""
+    fill = lib.moe_tier_fill
+    a = [FAKE, 48, 512, 4096, FAKE, FAKE, FAKE, FAKE, 2_654_208, FAKE, FAKE, None]
+    b = list(a); b[3] = 0
+    assert fill(*b) == _lib.MOE_ESHAPE                # n_hot < 1
+    b = list(a); b[3] = 48 * 512 + 1
+    assert fill(*b) == _lib.MOE_ESHAPE                # n_hot > L*E
+    b = list(a); b[1] = 200
+    assert fill(*b) == _lib.MOE_ESHAPE                # L*E > 65536
+    b = list(a); b[8] = 2_654_208 + 16
+    assert fill(*b) == _lib.MOE_EALIGN                # record bytes not a multiple of 256
+    b = list(a); b[7] = FAKE + 16
+    assert fill(*b) == _lib.MOE_EALIGN                # pool not 256-byte aligned
+    b = list(a); b[6] = None
+    assert fill(*b) == _lib.MOE_EINVAL
+    reb = lib.moe_tier_rebalance
+    r = [FAKE, FAKE, 96, 48, 512, 4096, 96, FAKE, FAKE, FAKE, FAKE, 2_654_208, FAKE, FAKE, None]
+    b = list(r); b[2] = 2000
+    assert reb(*b) == _lib.MOE_ESHAPE                 # n_top > 1024
+    b = list(r); b[6] = -1
+    assert reb(*b) == _lib.MOE_ESHAPE                 # max_swaps < 0
+    b = list(r); b[1] = None
+    assert reb(*b) == _lib.MOE_EINVAL                 # top_idx missing with n_top > 0

@@ -488,3 +488,110 @@ def test_packer_on_gpu_is_a_valid_encoding(moe, qfmt):
             step = np.abs(A - W).max() * 2 + 1e-12
             assert np.abs(B - W).max() <= step * 1.01
             assert np.mean(A != B) < 1e-3
+
+
+# ---------------------------------------------------------------- hot tier
+
+from oracle import tier as TI  # noqa: E402
+
+
+def _tier_case(rng, L, E, n_hot, R):
+    """A pool of n_hot hot slots (zeroed) followed by every expert's home
+    record (random bytes) at a shuffled home slot."""
+    home = (n_hot + rng.permutation(L * (E + 1))).astype(np.int32).reshape(L, E + 1)
+    pool = torch.zeros((n_hot + L * (E + 1)) * R, dtype=torch.uint8, device="cuda")
+    pool[n_hot * R:] = torch.from_numpy(rng.integers(0, 256, size=L * (E + 1) * R, dtype=np.uint8)).cuda()
+    return home, pool
+
+
+def _tier_state_equal(moe_state, ref, E, check_swaps=True):
+    slot, owner, swaps, n_sw = moe_state
+    r_slot, r_owner, r_swaps = ref
+    assert np.array_equal(_np(slot), r_slot)
+    assert np.array_equal(_np(owner), r_owner)
+    assert int(n_sw.item()) == len(r_swaps)
+    if check_swaps and r_swaps:
+        assert np.array_equal(_np(swaps)[:len(r_swaps)], np.array(r_swaps, np.int32))
+
+
+def _tier_records_ok(pool, slot, home, R, E):
+    """Every routed expert's record, read through the slot table, is its home
+    record byte for byte."""
+    v = pool.view(-1, R)
+    s = torch.from_numpy(np.asarray(slot)[:, :E].reshape(-1).astype(np.int64)).cuda()
+    h = torch.from_numpy(np.asarray(home)[:, :E].reshape(-1).astype(np.int64)).cuda()
+    assert torch.equal(v[s], v[h])
+
+
+@pytest.mark.parametrize("L,E,n_hot,R", [(3, 16, 12, 4096), (2, 40, 80, 256), (48, 512, 4096, 256)])
+def test_tier_fill_and_rebalance(moe, L, E, n_hot, R):
+    """The tier's fill and several rebalance rounds (scores with many ties,
+    empty-slot-free and capped rounds, no candidates) against the oracle bit
+    for bit: slot table, hot-slot owners, swap list; every record read through
+    the slot table equals its home record."""
+    rng = np.random.default_rng(L * 1000 + E)
+    home, pool = _tier_case(rng, L, E, n_hot, R)
+    home_t = torch.from_numpy(home).cuda()
+    slot = torch.empty_like(home_t)
+    owner = torch.empty(n_hot, dtype=torch.int32, device="cuda")
+    swaps = torch.full((max(n_hot, 1024), 4), -7, dtype=torch.int32, device="cuda")
+    n_sw = torch.zeros(1, dtype=torch.int32, device="cuda")
+    prof = (rng.integers(0, 40, size=(L, E)) * 0.25).astype(np.float32)
+    moe.moe_tier_fill(torch.from_numpy(prof).cuda(), n_hot, home_t, slot, owner, pool, R, swaps, n_sw)
+    torch.cuda.synchronize()
+    ref = TI.tier_fill(prof, n_hot, home)
+    _tier_state_equal((slot, owner, swaps, n_sw), ref, E)
+    _tier_records_ok(pool, _np(slot), home, R, E)
+    r_slot, r_owner = ref[0], ref[1]
+    N = L * E
+    for rnd, (n_top, cap) in enumerate([(min(96, N), 96), (min(96, N), 5), (min(300, N), 1024), (0, 96),
+                                        (min(1024, N), 0), (min(64, N), 64)]):
+        sc = (rng.integers(0, 40, size=(L, E)) * 0.25).astype(np.float32)
+        top = TI.tier_rank(sc)[:n_top]
+        top_t = torch.tensor(top, dtype=torch.int32, device="cuda") if n_top else None
+        moe.moe_tier_rebalance(torch.from_numpy(sc).cuda(), top_t, n_hot, cap, home_t, slot, owner, pool, R, swaps,
+                               n_sw)
+        torch.cuda.synchronize()
+        ref = TI.tier_rebalance(sc, top, n_hot, cap, home, r_slot, r_owner)
+        _tier_state_equal((slot, owner, swaps, n_sw), ref, E)
+        r_slot, r_owner = ref[0], ref[1]
+        _tier_records_ok(pool, _np(slot), home, R, E)
+
+
+def test_tier_decode_reads_through_the_tier(moe):
+    """A 2-layer decode step through a tiered pool (hot copies after a fill and
+    a rebalance) is bit-identical to the same step on the home records."""
+    L, T = 2, 2
+    li = C.layer_case(5, T, 256, 16, 2, 128, qfmt=0, bias=True, L=L, gap=False, device="cuda")
+    n_hot, E, R = 8, 16, li.R
+    home_t = (li.S + n_hot).to(torch.int32).contiguous()
+    pool = torch.cat([torch.zeros(n_hot * R, dtype=torch.uint8, device="cuda"), li.pool])
+    x = li.x.contiguous()
+    ref = moe.moe_decode_stack(x, li.F, E, li.k, li.Wr, li.bias, home_t, pool, R, li.qfmt)
+    slot = torch.empty_like(home_t)
+    owner = torch.empty(n_hot, dtype=torch.int32, device="cuda")
+    swaps = torch.empty((1024, 4), dtype=torch.int32, device="cuda")
+    n_sw = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(4)
+    prof = torch.from_numpy(rng.uniform(0, 5, size=(L, E)).astype(np.float32)).cuda()
+    moe.moe_tier_fill(prof, n_hot, home_t, slot, owner, pool, R, swaps, n_sw)
+    sc = rng.uniform(0, 5, size=(L, E)).astype(np.float32)
+    top = torch.tensor(TI.tier_rank(sc)[:12], dtype=torch.int32, device="cuda")
+    moe.moe_tier_rebalance(torch.from_numpy(sc).cuda(), top, n_hot, 96, home_t, slot, owner, pool, R, swaps, n_sw)
+    torch.cuda.synchronize()
+    assert int((slot[:, :E] < n_hot).sum().item()) == n_hot  # the tier is in use
+    for path in ("persistent", "chain"):
+        import os
+        old = os.environ.get("MOE_DECODE_PATH")
+        os.environ["MOE_DECODE_PATH"] = path
+        try:
+            got = moe.moe_decode_stack(x, li.F, E, li.k, li.Wr, li.bias, slot, pool, R, li.qfmt)
+            base = moe.moe_decode_stack(x, li.F, E, li.k, li.Wr, li.bias, home_t, pool, R, li.qfmt)
+        finally:
+            if old is None:
+                del os.environ["MOE_DECODE_PATH"]
+            else:
+                os.environ["MOE_DECODE_PATH"] = old
+        torch.cuda.synchronize()
+        assert torch.equal(got, base), path
+    assert torch.isfinite(ref).all()
