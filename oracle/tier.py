@@ -18,12 +18,12 @@ Readings where the pages are silent:
     usage_update's re-rank returns;
   * fill: the n_hot first experts of that ranking become resident, hot slot i
     holding the i-th of them in flat-index order;
-  * rebalance: the re-ranked experts that are not resident are the
-    candidates, in rank order; the hot slots are the victims, empty slots first
-    (lower slot first), then by the held expert's score ascending, ties to the
-    higher flat index; candidate i replaces victim i while the slot is empty or
-    the candidate's score is strictly higher (equal scores never swap), at most
-    max_swaps times;
+  * rebalance: the experts that are not resident, in rank order, are the
+    candidates; the hot slots are the victims, empty slots first (lower slot
+    first), then by the held expert's score ascending, ties to the higher flat
+    index; candidate i replaces victim i while the slot is empty or the
+    candidate's score is strictly higher (equal scores never swap), at most
+    max_swaps times (96 on the pages);
   * the shared expert (column E of the slot table) is never part of the tier.
 """
 import numpy as np
@@ -59,7 +59,7 @@ def tier_fill(scores, n_hot, home):
     return slot, owner, swaps
 
 
-def tier_rebalance(scores, top_idx, n_hot, max_swaps, home, slot_table, owner):
+def tier_rebalance(scores, n_hot, max_swaps, home, slot_table, owner):
     """One adaptive step.  Returns (slot_table, owner, swaps); swaps:
     (expert swapped in, expert evicted or -1, hot slot, the new expert's home
     slot), in candidate order."""
@@ -69,7 +69,7 @@ def tier_rebalance(scores, top_idx, n_hot, max_swaps, home, slot_table, owner):
     slot = np.array(slot_table, dtype=np.int32, copy=True)
     own = np.array(owner, dtype=np.int32, copy=True)
     resident = set(int(f) for f in own if f >= 0)
-    candidates = [int(f) for f in top_idx if int(f) not in resident]
+    candidates = [f for f in tier_rank(s) if f not in resident]
 
     def victim_order(i):
         f = int(own[i])

@@ -330,31 +330,31 @@ def test_tier_worked_example():
     for i, f in enumerate(g["owner"]):
         start[f // E][f % E] = i
     sc = np.array(g["scores"], np.float32)
-    slot, owner, swaps = T.tier_rebalance(sc, g["top_idx"], n, g["max_swaps"], home, start, g["owner"])
+    slot, owner, swaps = T.tier_rebalance(sc, n, g["max_swaps"], home, start, g["owner"])
     assert [list(sw) for sw in swaps] == g["swaps"] and owner.tolist() == g["rebalance_owner"]
     _tier_consistent(slot, owner, home, E)
-    swaps3 = T.tier_rebalance(sc, g["top_idx"], n, 3, home, start, g["owner"])[2]
+    swaps3 = T.tier_rebalance(sc, n, 3, home, start, g["owner"])[2]
     assert [list(sw) for sw in swaps3] == g["max_swaps_3_swaps"]
     sc[0][0] = 2.0
-    swaps_tie = T.tier_rebalance(sc, g["top_idx"], n, 3, home, start, g["owner"])[2]
+    swaps_tie = T.tier_rebalance(sc, n, 3, home, start, g["owner"])[2]
     assert [list(sw) for sw in swaps_tie] == g["tie_swaps"]
     # residents 1 and 2 scored alike: the higher index (2, in slot 1) goes first
     sc2 = np.array(g["scores"], np.float32)
     sc2[0][1] = sc2[0][2] = 1.0
-    assert T.tier_rebalance(sc2, [6], n, 1, home, start, g["owner"])[2] == [(6, 2, 1, 10)]
+    assert T.tier_rebalance(sc2, n, 1, home, start, g["owner"])[2] == [(6, 2, 1, 10)]
     # empty slots are taken first, the lower slot first: owner [-1, 2, -1]
     part = home.copy()
     part[0][2] = 1
-    sw = T.tier_rebalance(np.array(g["scores"], np.float32), g["top_idx"], n, 3, home, part, [-1, 2, -1])[2]
+    sw = T.tier_rebalance(np.array(g["scores"], np.float32), n, 3, home, part, [-1, 2, -1])[2]
     assert [(c, v, d) for c, v, d, _ in sw] == [(6, -1, 0), (3, -1, 2), (0, 2, 1)]
 
 
 @pytest.mark.parametrize("seed", range(6))
 def test_tier_fill_and_rebalance_brute_force(seed):
     """Random tiers (ties, empty slots, caps): the fill holds exactly the
-    brute-force top n_hot; after a rebalance no re-ranked expert left outside
-    scores strictly above any resident, unless the swap cap stopped it, and
-    the swapped-in experts are the first candidates in rank order."""
+    brute-force top n_hot; after a rebalance no expert left outside scores
+    strictly above any resident, unless the swap cap stopped it, and the
+    swapped-in experts are the best-ranked non-residents, in rank order."""
     rng = np.random.default_rng(100 + seed)
     L, E = int(rng.integers(1, 4)), int(rng.integers(3, 12))
     N = L * E
@@ -377,17 +377,16 @@ def test_tier_fill_and_rebalance_brute_force(seed):
             slot[f // E][f % E] = i
     scores = rng.integers(0, 6, size=(L, E)).astype(np.float32) * 0.5
     flat = scores.reshape(-1)
-    n_top = int(rng.integers(1, N + 1))
-    top = sorted(range(N), key=key(scores))[:n_top]
-    cap = int(rng.integers(1, n_top + 2))
-    new_slot, new_owner, swaps = T.tier_rebalance(scores, top, n_hot, cap, home, slot, owner)
+    ranked = sorted(range(N), key=key(scores))
+    cap = int(rng.integers(1, N + 2))
+    new_slot, new_owner, swaps = T.tier_rebalance(scores, n_hot, cap, home, slot, owner)
     _tier_consistent(new_slot, new_owner, home, E)
-    cands = [f for f in top if f not in set(owner.tolist())]
+    cands = [f for f in ranked if f not in set(owner.tolist())]
     assert [sw[0] for sw in swaps] == cands[:len(swaps)] and len(swaps) <= cap
     empties_before = int((owner < 0).sum())
     assert [sw[1] for sw in swaps[:empties_before]] == [-1] * min(empties_before, len(swaps))
     residents = [int(f) for f in new_owner if f >= 0]
-    left_out = [f for f in top if f not in residents]
+    left_out = [f for f in range(N) if f not in residents]
     if len(swaps) < cap and residents and len(residents) == n_hot:
         assert all(flat[f] <= min(flat[r] for r in residents) for f in left_out)
     if len(swaps) < cap and len(residents) < n_hot:
