@@ -177,6 +177,75 @@ def decode_sweep(M, li, steps, warmup, use_graph):
     return rows
 
 
+TIER_HOT = 4096  # hot slots: 16.7% of the 24,576 routed experts
+
+
+def tier_bench(M, li, steps, profile_steps=16, top_n=96, every=4, decay=0.99):
+    """Capacity-limited hot tier on a synthetic trace: the tier is filled from
+    a usage profile of `profile_steps` decode steps on plain N(0,1) tokens,
+    then `steps` decode steps run on tokens shifted by a fixed seeded "topic"
+    vector (x = z + v), with moe_usage_update on every layer and a rebalance
+    of at most top_n swaps (the best non-resident experts) every `every`
+    steps.  Hit rate = the share of the
+    routed (layer, token, choice) lookups whose slot is a hot slot."""
+    import torch
+    import gen as G
+    dev = li.pool.device
+    L, E, H, F, k, R = li.L, li.E, li.H, li.F, li.k, li.R
+    n_hot = TIER_HOT
+    home = li.S.to(torch.int32).contiguous()
+    slot = home.clone()
+    owner = torch.full((n_hot,), -1, dtype=torch.int32, device=dev)
+    swaps = torch.empty((max(n_hot, 1024), 4), dtype=torch.int32, device=dev)
+    n_sw = torch.zeros(1, dtype=torch.int32, device=dev)
+    scores = torch.zeros((L, E), dtype=torch.float32, device=dev)
+    hits_ws = torch.empty(E, dtype=torch.int32, device=dev)
+    x_in = torch.empty((1, H), dtype=torch.float32, device=dev)
+    idx = torch.empty((L, 1, k), dtype=torch.int32, device=dev)
+    ws = M.workspace(M.MOE_OP_DECODE_STACK, dev, 1, k, E, H, F, li.qfmt)
+
+    def step(x, st):
+        x_in.copy_(x)
+        M.moe_decode_stack(x_in, F, E, k, li.Wr, li.bias, slot, li.pool, R, li.qfmt, topk_idx_out=idx, ws=ws)
+        hot = (torch.gather(slot[:, :E], 1, idx.view(L, k).long()) < n_hot).sum()
+        for l in range(L):
+            M.moe_usage_update(idx[l], l, L, E, decay, st, every, top_n, hits_ws, scores)
+        return hot
+
+    xs = G.draw_x(7, profile_steps, H, dev, tag="tier-profile")
+    for i in range(profile_steps):
+        step(xs[i:i + 1], i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    M.moe_tier_fill(scores, n_hot, home, slot, owner, li.pool, R, swaps, n_sw)
+    e1.record()
+    torch.cuda.synchronize()
+    fill_ms = e0.elapsed_time(e1)
+    v = G.draw_x(7, 1, H, dev, tag="tier-topic")
+    xs = G.draw_x(7, steps, H, dev, tag="tier-run") + v
+    hot_per_step, swaps_per, reb_ms = [], [], []
+    for i in range(steps):
+        reb = (i + 1) % every == 0
+        hot_per_step.append(step(xs[i:i + 1], i))
+        if reb:
+            e0.record()
+            M.moe_tier_rebalance(scores, n_hot, top_n, home, slot, owner, li.pool, R, swaps, n_sw)
+            e1.record()
+            torch.cuda.synchronize()
+            reb_ms.append(e0.elapsed_time(e1))
+            swaps_per.append(int(n_sw.item()))
+    hr = [float(h.item()) / (L * k) for h in hot_per_step]
+    q = max(1, steps // 4)
+    return {"hot_slots": n_hot, "hot_share_of_experts": round(n_hot / (L * E), 4),
+            "profile_steps": profile_steps, "trace": "decode T=1, x = N(0,1) + a fixed N(0,1) topic vector",
+            "hit_rate_first_4_steps": round(sum(hr[:4]) / 4, 4),
+            "hit_rate_last_quarter": round(sum(hr[-q:]) / q, 4),
+            "swaps_per_rebalance_mean": round(sum(swaps_per) / max(1, len(swaps_per)), 1),
+            "rebalance_ms_mean": round(sum(reb_ms) / max(1, len(reb_ms)), 4),
+            "fill_ms": round(fill_ms, 2), "fill_gb_copied": round(n_hot * R / 1e9, 2)}
+
+
 def decode_bytes(li, uniq_step, T):
     """Algorithmic HBM bytes of one step: every distinct expert's record plus
     the shared expert's, the router matrix, and the activations read and
@@ -256,6 +325,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the verify and prefill measurements")
     ap.add_argument("--sweep", action="store_true",
                     help="also time verify windows T = 1..8 at top-10 and T = 1, 4, 6 at top-6")
+    ap.add_argument("--tier", action="store_true",
+                    help="also emulate a hot tier of 4,096 expert slots (hit rate on a synthetic trace)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-ref-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (the reference kernel that scales "
@@ -287,7 +358,8 @@ def main():
     L, E, H, F, k = 48, 512, 2048, 768, 10
     t0 = time.perf_counter()
     li = G.make_layer_inputs(2, L, E, H, F, qfmt=0, bias=True, device=dev,
-                             progress=lambda l: log(f"pool: layer {l + 1}/{L}") if (l + 1) % 8 == 0 else None)
+                             progress=lambda l: log(f"pool: layer {l + 1}/{L}") if (l + 1) % 8 == 0 else None,
+                             hot_slots=TIER_HOT if args.tier else 0)
     li.k = k
     torch.cuda.synchronize()
     log(f"pool of {li.pool.numel() / 1e9:.1f} GB built in {time.perf_counter() - t0:.1f} s")
@@ -332,6 +404,10 @@ def main():
     if args.sweep:
         out.setdefault("extra", {})["decode_sweep"] = decode_sweep(M, li, min(args.steps, 32), args.warmup,
                                                                    not args.no_graph)
+    if args.tier:
+        tb = tier_bench(M, li, min(args.steps, 64))
+        log(f"tier: {json.dumps(tb)}")
+        out.setdefault("extra", {})["hot_tier"] = tb
     if not args.no_cpu_baseline:
         xs = G.draw_x(2, 1, H, dev, tag="bench-x")
         cb, _ = cpu_baseline(li, xs, args.cpu_budget)

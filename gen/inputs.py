@@ -290,10 +290,13 @@ class LayerInputs:
 
 
 def make_layer_inputs(seed, L, E, H, F, qfmt=QFMT_INT4, bias=False,
-                      device="cpu", progress=None):
-    """Routers [L][E][H] (bf16 bits), bias [L][E] or None, pool, slot table."""
+                      device="cpu", progress=None, hot_slots=0):
+    """Routers [L][E][H] (bf16 bits), bias [L][E] or None, pool, slot table.
+    hot_slots > 0 leaves that many empty record slots at the start of the
+    pool (a hot tier); the slot table then holds the home slots after them."""
     Wr = torch.stack([draw_router(seed, l, E, H, device) for l in range(L)])
     b = torch.stack([zipf_bias(seed, l, E) for l in range(L)]).to(device) if bias else None
-    pool, S, R = build_pool(seed, L, E, H, F, qfmt, device, progress=progress)
+    S0 = make_slot_table(seed, L, E) + hot_slots if hot_slots else None
+    pool, S, R = build_pool(seed, L, E, H, F, qfmt, device, slot_table=S0, progress=progress)
     return LayerInputs(seed=seed, L=L, E=E, H=H, F=F, qfmt=qfmt, Wr=Wr, bias=b,
                        pool=pool, S=S.to(device), R=R)

@@ -286,21 +286,20 @@ int moe_usage_update(const int32_t* topk_idx, int T, int k, int layer, int L,
  *   become resident, hot slot i holding the i-th of them in flat-index order.
  *   scores fp32 [L][E] (e.g. the scores of moe_usage_update).
  *
- * moe_tier_rebalance -- one adaptive step.  Candidates: the entries of top_idx
- *   [n_top] (flat indices in rank order, as moe_usage_update's top_out) that
- *   are not resident, in that order.  Victims: the hot slots, empty ones first
- *   (lower slot first), then by the held expert's score ascending, equal
- *   scores the higher flat index first.  Candidate i takes victim i's slot
- *   while that slot is empty or the candidate's score is strictly higher
+ * moe_tier_rebalance -- one adaptive step (e.g. every fourth decode step,
+ *   max_swaps = 96).  Candidates: the experts that are not resident, in the
+ *   order (scores desc, flat index asc).  Victims: the hot slots, empty ones
+ *   first (lower slot first), then by the held expert's score ascending,
+ *   equal scores the higher flat index first.  Candidate i takes victim i's
+ *   slot while that slot is empty or the candidate's score is strictly higher
  *   (equal scores never swap), at most max_swaps times; an evicted expert's
- *   entry returns to its home slot.  0 <= n_top <= min(L*E, 1024),
- *   0 <= max_swaps <= 1024. */
+ *   entry returns to its home slot.  0 <= max_swaps <= 1024. */
 int moe_tier_fill(const float* scores, int L, int E, int n_hot,
                   const int32_t* home_table, int32_t* slot_table,
                   int32_t* hot_owner, void* pool, int64_t record_bytes,
                   int32_t* swaps, int32_t* n_swaps, void* stream);
-int moe_tier_rebalance(const float* scores, const int32_t* top_idx, int n_top,
-                       int L, int E, int n_hot, int max_swaps,
+int moe_tier_rebalance(const float* scores, int L, int E, int n_hot,
+                       int max_swaps,
                        const int32_t* home_table, int32_t* slot_table,
                        int32_t* hot_owner, void* pool, int64_t record_bytes,
                        int32_t* swaps, int32_t* n_swaps, void* stream);

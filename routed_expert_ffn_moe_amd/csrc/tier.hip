@@ -16,12 +16,13 @@
 //   fill:      the top n_hot experts by (score desc, flat index asc) become
 //              resident, hot slot i holding the i-th of them in flat order
 //              (radix select of the n_hot-th key, then a scan in flat order);
-//   rebalance: the re-ranked experts that are not resident (candidates, in
-//              rank order) replace the emptiest / lowest-scored hot slots
-//              (victims: empty slots first, lower slot first, then score
-//              ascending, ties to the higher flat index) while the slot is
-//              empty or the candidate scores strictly higher, at most
-//              max_swaps of them.
+//   rebalance: the best-ranked experts that are not resident (candidates,
+//              found by a radix select over the non-residents' rank keys)
+//              replace the emptiest / lowest-scored hot slots (victims: empty
+//              slots first, lower slot first, then score ascending, ties to
+//              the higher flat index; a radix select over the hot slots)
+//              while the slot is empty or the candidate scores strictly
+//              higher, at most max_swaps of them.
 #include "moe_common.h"
 #include "moe_select.h"
 
@@ -84,37 +85,35 @@ __global__ __launch_bounds__(1024) void tier_fill_kernel(const float* __restrict
   if (tid == 0) *n_swaps = n_hot;
 }
 
-__global__ __launch_bounds__(1024) void tier_rebalance_kernel(const float* __restrict__ scores,
-                                                              const int32_t* __restrict__ top_idx, int n_top, int E,
+__global__ __launch_bounds__(1024) void tier_rebalance_kernel(const float* __restrict__ scores, int L, int E,
                                                               int n_hot, int max_swaps,
                                                               const int32_t* __restrict__ home, int32_t* slot,
                                                               int32_t* owner, int32_t* swaps, int32_t* n_swaps) {
-  __shared__ int cand[1024];
+  __shared__ uint64_t csel[1024];
   __shared__ uint64_t sel[1024];
   __shared__ int nsw_s;
-  const int tid = threadIdx.x;
-  // candidates: the re-ranked experts not resident, in rank order
-  int f = -1;
-  bool c = false;
-  if (tid < n_top) {
-    f = top_idx[tid];
-    c = slot[tier_row(f, E)] >= n_hot;
-  }
-  int n_cand;
-  const int pos = tier_block_exscan(c ? 1 : 0, &n_cand);
-  if (c) cand[pos] = f;
-  const int m = min(min(n_cand, max_swaps), n_hot);
+  const int tid = threadIdx.x, N = L * E;
+  // residents: count the occupied hot slots
+  int held = 0;
+  for (int i = tid; i < n_hot; i += 1024) held += owner[i] >= 0;
+  int n_held;
+  tier_block_exscan(held, &n_held);
+  const int m = min(min(N - n_held, max_swaps), n_hot);
   if (m == 0) {  // uniform over the workgroup
     if (tid == 0) *n_swaps = 0;
     return;
   }
+  // candidates: the m best-ranked non-resident experts, in rank order (a
+  // resident's key is 0, below every non-resident's; at least m are not)
+  moe_top_keys_sorted(
+      [&](int f) { return slot[tier_row(f, E)] >= n_hot ? tier_rank_key(scores, f) : 0ull; }, N, m, csel);
   // victims: the m largest of these keys, in descending order
   auto vkey = [&](int i) -> uint64_t {
     const int o = owner[i];
     if (o < 0) return (0xFFFFFFFFull << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)i);  // empty: lower slot first
     return ((uint64_t)(~moe_f32_order_key(scores[o])) << 32) | (uint32_t)o;            // low score, high index first
   };
-  moe_top_keys_sorted(vkey, n_hot, m, sel);  // its barriers also publish cand[]
+  moe_top_keys_sorted(vkey, n_hot, m, sel);
   if (tid == 0) nsw_s = m;
   __syncthreads();
   int vslot = -1, vo = -1, cf = -1;
@@ -127,7 +126,7 @@ __global__ __launch_bounds__(1024) void tier_rebalance_kernel(const float* __res
       vo = (int)lo;
       vslot = slot[tier_row(vo, E)];
     }
-    cf = cand[tid];
+    cf = (int)(0xFFFFFFFFu - (uint32_t)csel[tid]);
     // candidates descend and victims ascend in score: the first pair that
     // does not improve ends the swaps
     if (!(vo < 0 || scores[cf] > scores[vo])) atomicMin(&nsw_s, tid);
@@ -196,16 +195,14 @@ extern "C" int moe_tier_fill(const float* scores, int L, int E, int n_hot, const
   return moe_check_launch("tier fill");
 }
 
-extern "C" int moe_tier_rebalance(const float* scores, const int32_t* top_idx, int n_top, int L, int E, int n_hot,
-                                  int max_swaps, const int32_t* home_table, int32_t* slot_table, int32_t* hot_owner,
-                                  void* pool, int64_t record_bytes, int32_t* swaps, int32_t* n_swaps, void* stream) {
+extern "C" int moe_tier_rebalance(const float* scores, int L, int E, int n_hot, int max_swaps,
+                                  const int32_t* home_table, int32_t* slot_table, int32_t* hot_owner, void* pool,
+                                  int64_t record_bytes, int32_t* swaps, int32_t* n_swaps, void* stream) {
   TIER_COMMON_CHECKS();
-  MOE_REQUIRE(n_top >= 0 && n_top <= 1024 && n_top <= L * E, MOE_ESHAPE, "n_top=%d out of [0, min(L*E, 1024)]", n_top);
   MOE_REQUIRE(max_swaps >= 0 && max_swaps <= 1024, MOE_ESHAPE, "max_swaps=%d out of [0, 1024]", max_swaps);
-  MOE_REQUIRE(n_top == 0 || top_idx, MOE_EINVAL, "top_idx is required");
   hipStream_t st = moe_stream(stream);
-  tier_rebalance_kernel<<<1, 1024, 0, st>>>(scores, top_idx, n_top, E, n_hot, max_swaps, home_table, slot_table,
-                                            hot_owner, swaps, n_swaps);
+  tier_rebalance_kernel<<<1, 1024, 0, st>>>(scores, L, E, n_hot, max_swaps, home_table, slot_table, hot_owner, swaps,
+                                            n_swaps);
   tier_launch_copy(pool, record_bytes, swaps, n_swaps, min(max_swaps, n_hot), st);
   return moe_check_launch("tier rebalance");
 }

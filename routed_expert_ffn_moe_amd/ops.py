@@ -171,16 +171,14 @@ def moe_tier_fill(scores, n_hot, home_table, slot_table, hot_owner, pool, record
     return slot_table, hot_owner
 
 
-def moe_tier_rebalance(scores, top_idx, n_hot, max_swaps, home_table, slot_table, hot_owner, pool, record_bytes,
-                       swaps, n_swaps, stream=None):
-    """top_idx int32 [n_top] flat indices in rank order (None: no candidates);
-    swaps int32 [>= max_swaps][4]."""
+def moe_tier_rebalance(scores, n_hot, max_swaps, home_table, slot_table, hot_owner, pool, record_bytes, swaps,
+                       n_swaps, stream=None):
+    """scores fp32 [L][E]; swaps int32 [>= max_swaps][4]."""
     L, E = scores.shape
-    n_top = 0 if top_idx is None else top_idx.numel()
-    _dev(scores, top_idx, home_table, slot_table, hot_owner, pool, swaps, n_swaps)
-    check(_lib.load().moe_tier_rebalance(_p(scores), _p(top_idx), n_top, L, E, n_hot, max_swaps, _p(home_table),
-                                         _p(slot_table), _p(hot_owner), _p(pool), record_bytes, _p(swaps),
-                                         _p(n_swaps), _stream(stream)))
+    _dev(scores, home_table, slot_table, hot_owner, pool, swaps, n_swaps)
+    check(_lib.load().moe_tier_rebalance(_p(scores), L, E, n_hot, max_swaps, _p(home_table), _p(slot_table),
+                                         _p(hot_owner), _p(pool), record_bytes, _p(swaps), _p(n_swaps),
+                                         _stream(stream)))
     return slot_table, hot_owner
 
 

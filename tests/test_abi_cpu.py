@@ -144,10 +144,12 @@ def test_tier_rejects(lib):
     b = list(a); b[6] = None
     assert fill(*b) == _lib.MOE_EINVAL
     reb = lib.moe_tier_rebalance
-    r = [FAKE, FAKE, 96, 48, 512, 4096, 96, FAKE, FAKE, FAKE, FAKE, 2_654_208, FAKE, FAKE, None]
-    b = list(r); b[2] = 2000
-    assert reb(*b) == _lib.MOE_ESHAPE                 # n_top > 1024
-    b = list(r); b[6] = -1
+    r = [FAKE, 48, 512, 4096, 96, FAKE, FAKE, FAKE, FAKE, 2_654_208, FAKE, FAKE, None]
+    b = list(r); b[4] = 2000
+    assert reb(*b) == _lib.MOE_ESHAPE                 # max_swaps > 1024
+    b = list(r); b[4] = -1
     assert reb(*b) == _lib.MOE_ESHAPE                 # max_swaps < 0
-    b = list(r); b[1] = None
-    assert reb(*b) == _lib.MOE_EINVAL                 # top_idx missing with n_top > 0
+    b = list(r); b[3] = 0
+    assert reb(*b) == _lib.MOE_ESHAPE                 # n_hot < 1
+    b = list(r); b[11] = None
+    assert reb(*b) == _lib.MOE_EINVAL                 # n_swaps missing
