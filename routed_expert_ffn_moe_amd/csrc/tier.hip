@@ -12,7 +12,10 @@
 // copy of its record; the slot table then points at the copy, else at the
 // home record, so the expert kernels read through the slot table unchanged.
 // Both operations run on the device in one workgroup each, then a wide copy
-// kernel moves the records:
+// kernel moves the records.  The radix selects read their keys 9 times (8
+// digit passes and a gather), so the keys are first cached in LDS when they
+// fit (the 32-bit score keys of all L*E experts, and the hot slots' 64-bit
+// victim keys); otherwise they are re-read from global memory.
 //   fill:      the top n_hot experts by (score desc, flat index asc) become
 //              resident, hot slot i holding the i-th of them in flat order
 //              (radix select of the n_hot-th key, then a scan in flat order);
@@ -27,6 +30,9 @@
 #include "moe_select.h"
 
 #define TIER_CHUNK 65536  // bytes of a record copied by one workgroup
+#define TIER_STATIC_LDS (20 * 1024)  // the kernels' static LDS, rounded up
+
+extern __shared__ __attribute__((aligned(16))) uint8_t tier_lds[];
 
 __device__ __forceinline__ int tier_row(int f, int E) { return (f / E) * (E + 1) + f % E; }
 
@@ -59,19 +65,27 @@ __device__ int tier_block_exscan(int v, int* total) {
 
 __global__ __launch_bounds__(1024) void tier_fill_kernel(const float* __restrict__ scores, int L, int E, int n_hot,
                                                          const int32_t* __restrict__ home, int32_t* slot,
-                                                         int32_t* owner, int32_t* swaps, int32_t* n_swaps) {
+                                                         int32_t* owner, int32_t* swaps, int32_t* n_swaps,
+                                                         int cached) {
   const int N = L * E, tid = threadIdx.x;
+  uint32_t* hi = (uint32_t*)tier_lds;  // [N] score keys when cached
   for (int i = tid; i < L * (E + 1); i += 1024) slot[i] = home[i];
-  const uint64_t thr = moe_kth_largest_key([&](int i) { return tier_rank_key(scores, i); }, N, n_hot);
+  if (cached)
+    for (int f = tid; f < N; f += 1024) hi[f] = moe_f32_order_key(scores[f]);
+  __syncthreads();
+  auto rank_key = [&](int f) -> uint64_t {
+    return cached ? ((uint64_t)hi[f] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)f) : tier_rank_key(scores, f);
+  };
+  const uint64_t thr = moe_kth_largest_key(rank_key, N, n_hot);
   // thread t scans flat indices [t C, (t+1) C): hot slots in flat order
   const int C = (N + 1023) / 1024;
   const int f0 = min(tid * C, N), f1 = min(f0 + C, N);
   int cnt = 0;
-  for (int f = f0; f < f1; ++f) cnt += tier_rank_key(scores, f) >= thr;
+  for (int f = f0; f < f1; ++f) cnt += rank_key(f) >= thr;
   int total;
   int pos = tier_block_exscan(cnt, &total);  // its barriers also order the home copy above
   for (int f = f0; f < f1; ++f) {
-    if (tier_rank_key(scores, f) >= thr) {
+    if (rank_key(f) >= thr) {
       const int r = tier_row(f, E);
       slot[r] = pos;
       owner[pos] = f;
@@ -88,7 +102,8 @@ __global__ __launch_bounds__(1024) void tier_fill_kernel(const float* __restrict
 __global__ __launch_bounds__(1024) void tier_rebalance_kernel(const float* __restrict__ scores, int L, int E,
                                                               int n_hot, int max_swaps,
                                                               const int32_t* __restrict__ home, int32_t* slot,
-                                                              int32_t* owner, int32_t* swaps, int32_t* n_swaps) {
+                                                              int32_t* owner, int32_t* swaps, int32_t* n_swaps,
+                                                              int cache_c, int cache_v) {
   __shared__ uint64_t csel[1024];
   __shared__ uint64_t sel[1024];
   __shared__ int nsw_s;
@@ -103,17 +118,32 @@ __global__ __launch_bounds__(1024) void tier_rebalance_kernel(const float* __res
     if (tid == 0) *n_swaps = 0;
     return;
   }
-  // candidates: the m best-ranked non-resident experts, in rank order (a
-  // resident's key is 0, below every non-resident's; at least m are not)
-  moe_top_keys_sorted(
-      [&](int f) { return slot[tier_row(f, E)] >= n_hot ? tier_rank_key(scores, f) : 0ull; }, N, m, csel);
-  // victims: the m largest of these keys, in descending order
+  // LDS caches: chi[f] = the score key of expert f if it is not resident,
+  // else 0; vk[i] = the victim key of hot slot i (below)
+  uint32_t* chi = (uint32_t*)tier_lds;
+  uint64_t* vk = (uint64_t*)(tier_lds + (cache_c ? ((size_t)N * 4 + 7) / 8 * 8 : 0));
   auto vkey = [&](int i) -> uint64_t {
     const int o = owner[i];
     if (o < 0) return (0xFFFFFFFFull << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)i);  // empty: lower slot first
     return ((uint64_t)(~moe_f32_order_key(scores[o])) << 32) | (uint32_t)o;            // low score, high index first
   };
-  moe_top_keys_sorted(vkey, n_hot, m, sel);
+  if (cache_c)
+    for (int f = tid; f < N; f += 1024)
+      chi[f] = slot[tier_row(f, E)] >= n_hot ? moe_f32_order_key(scores[f]) : 0u;
+  if (cache_v)
+    for (int i = tid; i < n_hot; i += 1024) vk[i] = vkey(i);
+  __syncthreads();
+  // candidates: the m best-ranked non-resident experts, in rank order (a
+  // resident's key is 0, below every non-resident's, whose score keys are
+  // nonzero; at least m are not resident)
+  moe_top_keys_sorted(
+      [&](int f) -> uint64_t {
+        if (cache_c) return chi[f] ? ((uint64_t)chi[f] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)f) : 0ull;
+        return slot[tier_row(f, E)] >= n_hot ? tier_rank_key(scores, f) : 0ull;
+      },
+      N, m, csel);
+  // victims: the m largest victim keys, in descending order
+  moe_top_keys_sorted([&](int i) { return cache_v ? vk[i] : vkey(i); }, n_hot, m, sel);
   if (tid == 0) nsw_s = m;
   __syncthreads();
   int vslot = -1, vo = -1, cf = -1;
@@ -158,14 +188,37 @@ __global__ __launch_bounds__(256) void tier_copy_kernel(uint8_t* pool, int64_t R
   const uint4* in = reinterpret_cast<const uint4*>(pool + src * R);
   uint4* out = reinterpret_cast<uint4*>(pool + dst * R);
   for (int64_t i = w0 + threadIdx.x; i < w1; i += 4 * 256) {
-    uint4 v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (i + 256 * j < w1) v[j] = in[i + 256 * j];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (i + 256 * j < w1) out[i + 256 * j] = v[j];
+    // four named registers (an array here was placed in LDS by the compiler)
+    const uint4 zero = {0u, 0u, 0u, 0u};
+    const uint4 v0 = in[i];
+    const uint4 v1 = i + 256 < w1 ? in[i + 256] : zero;
+    const uint4 v2 = i + 512 < w1 ? in[i + 512] : zero;
+    const uint4 v3 = i + 768 < w1 ? in[i + 768] : zero;
+    out[i] = v0;
+    if (i + 256 < w1) out[i + 256] = v1;
+    if (i + 512 < w1) out[i + 512] = v2;
+    if (i + 768 < w1) out[i + 768] = v3;
   }
+}
+
+static size_t tier_lds_limit() {
+  static size_t lim = 0;
+  if (!lim) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeSharedMemPerBlockOptin, dev) == hipSuccess && v > 0)
+      lim = (size_t)v;
+    else
+      lim = 64 * 1024;
+  }
+  return lim;
+}
+
+static int tier_set_lds(const void* fn, size_t bytes) {
+  if (bytes == 0) return MOE_OK;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess)
+    return moe_fail(MOE_EHIP, "tier: cannot reserve %zu bytes of LDS", bytes);
+  return MOE_OK;
 }
 
 static int tier_launch_copy(void* pool, int64_t R, int32_t* swaps, int32_t* n_swaps, int max_swaps, hipStream_t st) {
@@ -190,7 +243,12 @@ extern "C" int moe_tier_fill(const float* scores, int L, int E, int n_hot, const
                              int32_t* swaps, int32_t* n_swaps, void* stream) {
   TIER_COMMON_CHECKS();
   hipStream_t st = moe_stream(stream);
-  tier_fill_kernel<<<1, 1024, 0, st>>>(scores, L, E, n_hot, home_table, slot_table, hot_owner, swaps, n_swaps);
+  const size_t need = (size_t)L * E * 4;
+  const int cached = need + TIER_STATIC_LDS <= tier_lds_limit();
+  const size_t lds = cached ? need : 0;
+  if (tier_set_lds((const void*)tier_fill_kernel, lds) != MOE_OK) return MOE_EHIP;
+  tier_fill_kernel<<<1, 1024, lds, st>>>(scores, L, E, n_hot, home_table, slot_table, hot_owner, swaps, n_swaps,
+                                         cached);
   tier_launch_copy(pool, record_bytes, swaps, n_swaps, n_hot, st);
   return moe_check_launch("tier fill");
 }
@@ -201,8 +259,13 @@ extern "C" int moe_tier_rebalance(const float* scores, int L, int E, int n_hot, 
   TIER_COMMON_CHECKS();
   MOE_REQUIRE(max_swaps >= 0 && max_swaps <= 1024, MOE_ESHAPE, "max_swaps=%d out of [0, 1024]", max_swaps);
   hipStream_t st = moe_stream(stream);
-  tier_rebalance_kernel<<<1, 1024, 0, st>>>(scores, L, E, n_hot, max_swaps, home_table, slot_table, hot_owner, swaps,
-                                            n_swaps);
+  const size_t need_c = ((size_t)L * E * 4 + 7) / 8 * 8, need_v = (size_t)n_hot * 8, lim = tier_lds_limit();
+  const int cache_c = need_c + TIER_STATIC_LDS <= lim;
+  const int cache_v = (cache_c ? need_c : 0) + need_v + TIER_STATIC_LDS <= lim;
+  const size_t lds = (cache_c ? need_c : 0) + (cache_v ? need_v : 0);
+  if (tier_set_lds((const void*)tier_rebalance_kernel, lds) != MOE_OK) return MOE_EHIP;
+  tier_rebalance_kernel<<<1, 1024, lds, st>>>(scores, L, E, n_hot, max_swaps, home_table, slot_table, hot_owner,
+                                              swaps, n_swaps, cache_c, cache_v);
   tier_launch_copy(pool, record_bytes, swaps, n_swaps, min(max_swaps, n_hot), st);
   return moe_check_launch("tier rebalance");
 }
