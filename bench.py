@@ -246,6 +246,29 @@ def tier_bench(M, li, steps, profile_steps=16, top_n=96, every=4, decay=0.99):
             "fill_ms": round(fill_ms, 2), "fill_gb_copied": round(n_hot * R / 1e9, 2)}
 
 
+def int2_bench(M, steps, warmup, use_graph):
+    """The int2 stack (blocks of 16 with fp16 scale and min; seed 4, Zipf
+    routing bias): decode at T = 1 and 4 through 48 layers, and one 16,384-token
+    prefill chunk through layer 0 with the bias (skewed groups)."""
+    import torch
+    import gen as G
+    L, E, H, F, k = 48, 512, 2048, 768, 10
+    li = G.make_layer_inputs(4, L, E, H, F, qfmt=1, bias=True, device=torch.device("cuda:0"))
+    li.k = k
+    out = {"pool_gb": round(li.pool.numel() / 1e9, 2), "record_bytes": li.R}
+    for T in (1, 4):
+        d = decode_bench(M, li, T, steps, warmup, use_graph, f"int2-x{T}")
+        ms = d["ms"] / steps
+        b = sum(decode_bytes(li, u, T) for u in d["uniq"]) / len(d["uniq"])
+        out[f"decode_t{T}"] = {"ms_per_step": round(ms, 4), "token_positions_per_s": round(T / (ms / 1e3), 1),
+                               "gbs": round(b / (ms / 1e3) / 1e9, 1),
+                               "hbm_frac": round(b / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    out["prefill_16k"] = prefill_bench(M, li, reps=5, warmup=2, T=16384, seed=4, use_bias=True)
+    del li
+    torch.cuda.empty_cache()
+    return out
+
+
 def decode_bytes(li, uniq_step, T):
     """Algorithmic HBM bytes of one step: every distinct expert's record plus
     the shared expert's, the router matrix, and the activations read and
@@ -253,14 +276,16 @@ def decode_bytes(li, uniq_step, T):
     return sum((u + 1) * li.R + li.E * li.H * 2 + 2 * T * li.H * 4 for u in uniq_step)
 
 
-def prefill_bench(M, li, reps, warmup):
-    """One 8,192-token bf16 chunk through layer 0 (no bias: near-uniform routing)."""
+def prefill_bench(M, li, reps, warmup, T=8192, seed=3, use_bias=False):
+    """One T-token bf16 chunk through layer 0 (without the routing bias:
+    near-uniform routing; with it: Zipf-skewed groups, some empty)."""
     import torch
     import gen as G
     dev = li.pool.device
-    T, H, E, k, F = 8192, li.H, li.E, li.k, li.F
-    x = G.draw_x(3, T, H, dev, tag="bench-prefill").to(torch.bfloat16)
+    H, E, k, F = li.H, li.E, li.k, li.F
+    x = G.draw_x(seed, T, H, dev, tag="bench-prefill").to(torch.bfloat16)
     Wr0 = li.Wr[0].contiguous()
+    b0 = li.bias[0].contiguous() if use_bias else None
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     ws_r = M.workspace(M.MOE_OP_ROUTE_TOPK, dev, T=T, E=E)
@@ -276,7 +301,7 @@ def prefill_bench(M, li, reps, warmup):
     st = torch.cuda.current_stream()
     names = ["route", "permute", "grouped_gemm", "combine"]
     ops = [
-        lambda: M.moe_route_topk(x, Wr0, None, k, topk_idx=idx, topk_w=w, ws=ws_r),
+        lambda: M.moe_route_topk(x, Wr0, b0, k, topk_idx=idx, topk_w=w, ws=ws_r),
         lambda: M.moe_permute(idx, E, counts, offsets, row_src, inv_row, ws=ws_p),
         lambda: M.moe_grouped_gemm_q(x, row_src, offsets, k, E, F, li.S, 0, li.pool, li.R, li.qfmt, y_perm=y_perm,
                                      y_shared=y_sh, ws=ws_g),
@@ -302,8 +327,8 @@ def prefill_bench(M, li, reps, warmup):
     gemm_s = per_op["grouped_gemm"] / 1e3
     tf_routed_equiv = (flop_routed + flop_shared) / gemm_s / 1e12
     return {
-        "workload": "8,192-token bf16 chunk, 1 layer, 512 experts top-10 + shared, int4 (median of "
-                    f"{reps})",
+        "workload": f"{T:,}-token bf16 chunk, 1 layer, 512 experts top-10 + shared, "
+                    f"{'int4' if li.qfmt == 0 else 'int2'}{', Zipf routing bias' if use_bias else ''} (median of {reps})",
         "tokens_per_s": round(T / (total / 1e3), 1),
         "ms_layer": round(total, 4),
         "ms_per_op": {n: round(v, 4) for n, v in per_op.items()},
@@ -327,6 +352,8 @@ def main():
                     help="also time verify windows T = 1..8 at top-10 and T = 1, 4, 6 at top-6")
     ap.add_argument("--tier", action="store_true",
                     help="also emulate a hot tier of 4,096 expert slots (hit rate on a synthetic trace)")
+    ap.add_argument("--int2", action="store_true",
+                    help="also time the int2 stack: decode T = 1, 4 and a 16,384-token prefill chunk")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-ref-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (the reference kernel that scales "
@@ -404,6 +431,10 @@ def main():
     if args.sweep:
         out.setdefault("extra", {})["decode_sweep"] = decode_sweep(M, li, min(args.steps, 32), args.warmup,
                                                                    not args.no_graph)
+    if args.int2:
+        i2 = int2_bench(M, args.steps, args.warmup, not args.no_graph)
+        log(f"int2: {json.dumps(i2)}")
+        out.setdefault("extra", {})["int2_stack"] = i2
     if args.tier:
         tb = tier_bench(M, li, min(args.steps, 64))
         log(f"tier: {json.dumps(tb)}")
