@@ -33,12 +33,20 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict_
                                                             int32_t* __restrict__ offsets) {
   __shared__ int s[1024];
   const int e = threadIdx.x;
+  // 8 chunk rows at a time: their loads are issued before any store (the
+  // compiler cannot tell that row c + 1 is not the word just stored)
+  constexpr int NB = 8;
   int run = 0;
   if (e < E) {
-    for (int c = 0; c < nchunk; ++c) {
-      const int v = chunk_counts[(size_t)c * E + e];
-      chunk_counts[(size_t)c * E + e] = run;
-      run += v;
+    for (int c0 = 0; c0 < nchunk; c0 += NB) {
+      int v[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) v[j] = c0 + j < nchunk ? chunk_counts[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (c0 + j < nchunk) chunk_counts[(size_t)(c0 + j) * E + e] = run;
+        run += v[j];
+      }
     }
   }
   s[e] = (e < E) ? run : 0;
@@ -54,7 +62,14 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict_
   if (e < E) {
     counts[e] = run;
     offsets[e] = excl;
-    for (int c = 0; c < nchunk; ++c) chunk_counts[(size_t)c * E + e] += excl;
+    for (int c0 = 0; c0 < nchunk; c0 += NB) {
+      int v[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) v[j] = c0 + j < nchunk ? chunk_counts[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        if (c0 + j < nchunk) chunk_counts[(size_t)(c0 + j) * E + e] = v[j] + excl;
+    }
   }
   if (e == E - 1) offsets[E] = s[e];
 }
