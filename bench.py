@@ -10,9 +10,12 @@ enqueued as one HIP graph replay.  Inputs are synthetic and seeded (gen/).
 
 Also measured and reported under "extra": the speculative-verify step (4
 tokens per step) and one 8,192-token prefill chunk through one layer (route,
-permute, grouped GEMM on the matrix cores, combine).
+permute, grouped GEMM on the matrix cores, combine).  On request:
+  --sweep  verify windows of 1..8 token positions at top-10, and top-6;
+  --int2   the int2 stack: decode at 1 and 4 tokens, a 16,384-token chunk;
+  --tier   a hot tier of 4,096 expert slots: hit rate on a synthetic trace.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--sweep] [--int2] [--tier]
 """
 import argparse
 import glob
