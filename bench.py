@@ -6,7 +6,7 @@ Headline (the JSON `value`): decode tokens/s through a 48-layer MoE-only stack
 blocks of 32 with fp16 scales, Zipf(1.1) router bias), batch 1, every weight
 resident in HBM behind the (layer, expert) -> slot table.  One step = one
 token through all 48 layers (router, top-k, expert gather-GEMV, combine),
-enqueued as one HIP graph replay.  Inputs are synthetic and seeded (gen/).
+the timed steps enqueued as one HIP graph.  Inputs are synthetic and seeded (gen/).
 
 Also measured and reported under "extra": the speculative-verify step (4
 tokens per step) and one 8,192-token prefill chunk through one layer (route,
@@ -106,56 +106,55 @@ def decode_bench(M, li, T, steps, warmup, use_graph, seed_tag, k=None):
     L, E, H, F = li.L, li.E, li.H, li.F
     k = li.k if k is None else k
     xs = G.draw_x(2, (steps + warmup) * T, H, dev, tag=seed_tag).view(steps + warmup, T, H)
-    x_in = torch.empty((T, H), dtype=torch.float32, device=dev)
-    x_out = torch.empty_like(x_in)
+    x_out = torch.empty((T, H), dtype=torch.float32, device=dev)
     idx_out = torch.empty((L, T, k), dtype=torch.int32, device=dev)
     ws = M.workspace(M.MOE_OP_DECODE_STACK, dev, T, k, E, H, F, li.qfmt)
 
-    def step():
+    def step(x_in):  # every step reads its own input, resident in HBM
         M.moe_decode_stack(x_in, F, E, k, li.Wr, li.bias, li.S, li.pool, li.R, li.qfmt, x_out=x_out,
                            topk_idx_out=idx_out, ws=ws)
 
-    x_in.copy_(xs[0])
-    step()
+    last = xs[warmup + steps - 1]
+    step(last)
     torch.cuda.synchronize()
     ref = x_out.clone()
     if not torch.isfinite(ref).all():
         raise RuntimeError("decode step produced non-finite values")
+    for i in range(warmup):
+        step(xs[i])
     graph = None
     if use_graph:
+        # one graph holds all the timed steps: no per-step launch from the host
         graph = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             with torch.cuda.graph(graph, stream=s):
-                step()
+                for i in range(steps):
+                    step(xs[warmup + i])
         torch.cuda.current_stream().wait_stream(s)
-        for rep in range(2):  # replays must match the eager step bit for bit
+        for rep in range(2):  # the replay's last step must match the eager step bit for bit
             x_out.zero_()
-            x_in.copy_(xs[0])
             graph.replay()
             torch.cuda.synchronize()
             if not torch.equal(x_out, ref):
                 raise RuntimeError("graph replay differs from the eager step")
-    run = graph.replay if graph is not None else step
-    for i in range(warmup):
-        x_in.copy_(xs[i])
-        run()
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(st)
-    for i in range(steps):
-        x_in.copy_(xs[warmup + i])
-        run()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(steps):
+            step(xs[warmup + i])
     e1.record(st)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
     # distinct experts per layer of every timed step (re-run untimed to read the routing)
     uniq = []
     for i in range(steps):
-        x_in.copy_(xs[warmup + i])
-        run()
+        step(xs[warmup + i])
         torch.cuda.synchronize()
         ids = idx_out.cpu()
         uniq.append([len(set(ids[l].reshape(-1).tolist())) for l in range(L)])
@@ -411,7 +410,8 @@ def main():
                    "experts": E, "top_k": k, "shared_experts": 1, "hidden": H, "ffn": F,
                    "weights": "int4 blocks of 32, fp16 scale", "router_bias": "Zipf(1.1)",
                    "pool_gb": round(li.pool.numel() / 1e9, 2),
-                   "launch": "hip-graph replay per step" if not args.no_graph else "eager"},
+                   "launch": "one hip graph of the timed steps, each reading its own resident input"
+                   if not args.no_graph else "eager, one launch per step"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_persistent_kernel: one launch = one 48-layer step (router, top-k, experts, sum)",
