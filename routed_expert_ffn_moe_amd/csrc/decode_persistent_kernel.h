@@ -1197,6 +1197,9 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     __syncthreads();
   }
   if (!ok) {
+    // the error word: the next call's set-up kernel then zeroes the tagged
+    // buffers and restarts the call count (this call's words carry a tag that
+    // the next call would otherwise reuse)
     if (tid == 0) __hip_atomic_store(a.hdr + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int i = g * PT_THREADS + tid; i < T * H; i += G * PT_THREADS) a.x_out[i] = __builtin_nanf("");
     return;
