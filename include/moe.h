@@ -333,7 +333,8 @@ int moe_tier_rebalance(const float* scores, int L, int E, int n_hot,
  * buffers in ws across calls: pass the same ws to every call of a stack and
  * do not use it for anything else in between (calls on one ws must not
  * overlap).  Its waits are bounded; if one times out (e.g. the GPU could not
- * keep all its workgroups resident) x_out is filled with NaN.
+ * keep all its workgroups resident) x_out is filled with NaN, and the next
+ * call on that ws re-initialises its tagged buffers first.
  * ws: moe_workspace_size(MOE_OP_DECODE_STACK, T, k, E, H, F, qfmt). */
 int moe_decode_stack(const float* x_in, int T, int H, int F, int E, int k,
                      int L, const uint16_t* w_router, const float* bias,
