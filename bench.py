@@ -363,8 +363,9 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the layer is data-parallel with a "
-              "replicated expert pool; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the layer scales data-parallel with a replicated expert pool (each "
+              "GPU runs these kernels unchanged) and there is no multi-GPU path. Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
