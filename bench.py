@@ -186,7 +186,8 @@ def tier_bench(M, li, steps, profile_steps=16, top_n=96, every=4, decay=0.99):
     """Capacity-limited hot tier on a synthetic trace: the tier is filled from
     a usage profile of `profile_steps` decode steps on plain N(0,1) tokens,
     then `steps` decode steps run on tokens shifted by a fixed seeded "topic"
-    vector (x = z + v), with moe_usage_update on every layer and a rebalance
+    vector (x = z + v), with the usage update of all layers after each step
+    (moe_usage_update_stack) and a rebalance
     of at most top_n swaps (the best non-resident experts) every `every`
     steps.  Hit rate = the share of the
     routed (layer, token, choice) lookups whose slot is a hot slot."""
@@ -201,7 +202,7 @@ def tier_bench(M, li, steps, profile_steps=16, top_n=96, every=4, decay=0.99):
     swaps = torch.empty((max(n_hot, 1024), 4), dtype=torch.int32, device=dev)
     n_sw = torch.zeros(1, dtype=torch.int32, device=dev)
     scores = torch.zeros((L, E), dtype=torch.float32, device=dev)
-    hits_ws = torch.empty(E, dtype=torch.int32, device=dev)
+    hits_ws = torch.empty((L, E), dtype=torch.int32, device=dev)
     x_in = torch.empty((1, H), dtype=torch.float32, device=dev)
     idx = torch.empty((L, 1, k), dtype=torch.int32, device=dev)
     ws = M.workspace(M.MOE_OP_DECODE_STACK, dev, 1, k, E, H, F, li.qfmt)
@@ -210,8 +211,7 @@ def tier_bench(M, li, steps, profile_steps=16, top_n=96, every=4, decay=0.99):
         x_in.copy_(x)
         M.moe_decode_stack(x_in, F, E, k, li.Wr, li.bias, slot, li.pool, R, li.qfmt, topk_idx_out=idx, ws=ws)
         hot = (torch.gather(slot[:, :E], 1, idx.view(L, k).long()) < n_hot).sum()
-        for l in range(L):
-            M.moe_usage_update(idx[l], l, L, E, decay, st, every, top_n, hits_ws, scores)
+        M.moe_usage_update_stack(idx, E, decay, st, every, top_n, hits_ws, scores)
         return hot
 
     xs = G.draw_x(7, profile_steps, H, dev, tag="tier-profile")

@@ -258,6 +258,17 @@ int moe_usage_update(const int32_t* topk_idx, int T, int k, int layer, int L,
                      int top_n, int32_t* hits_ws, float* scores,
                      int32_t* top_out, void* stream);
 
+/* moe_usage_update_stack -- the same for every layer of a step at once:
+ * exactly moe_usage_update(topk_idx + l*T*k, T, k, l, L, E, decay, step,
+ * rerank_every, top_n, hits_ws + l*E, scores, top_out) for l = 0..L-1 in
+ * order, in one launch (one workgroup per layer) plus the re-rank.
+ *   topk_idx int32 [L][T][k] (as moe_decode_stack's topk_idx_out);
+ *   hits_ws  int32 [L][E] scratch (device). */
+int moe_usage_update_stack(const int32_t* topk_idx, int T, int k, int L, int E,
+                           float decay, int64_t step, int rerank_every,
+                           int top_n, int32_t* hits_ws, float* scores,
+                           int32_t* top_out, void* stream);
+
 /* --------------------------------------------------------------------------
  * Capacity-limited hot tier of expert records.  Pages: "为什么 Strata 在小显存
  * 显卡上这么快", section "一台电脑就是一组水管" (a shipped usage profile ranks

@@ -29,6 +29,7 @@ SIGNATURES = {
                                 _vp]),
     "moe_combine": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
     "moe_usage_update": (_i, [_vp, _i, _i, _i, _i, _i, _f, _i64, _i, _i, _vp, _vp, _vp, _vp]),
+    "moe_usage_update_stack": (_i, [_vp, _i, _i, _i, _i, _f, _i64, _i, _i, _vp, _vp, _vp, _vp]),
     "moe_tier_fill": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
     "moe_tier_rebalance": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
     "moe_decode_stack": (_i, [_vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i64, _i, _vp, _vp, _vp, _vp, _vp,

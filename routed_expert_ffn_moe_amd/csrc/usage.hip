@@ -12,10 +12,15 @@
 #include "moe_common.h"
 #include "moe_select.h"
 
-__global__ __launch_bounds__(1024) void usage_decay_kernel(const int32_t* __restrict__ idx, int T, int k, int layer,
+// Workgroup b updates layer layer0 + b from its routing idx[b][T][k] (hits in
+// hits_ws[b][E]): one launch per layer, or one for a whole stack.
+__global__ __launch_bounds__(1024) void usage_decay_kernel(const int32_t* __restrict__ idx, int T, int k, int layer0,
                                                            int E, float decay, int32_t* __restrict__ hits_ws,
                                                            float* __restrict__ scores) {
   __shared__ int hits[MOE_MAX_E];
+  const int layer = layer0 + (int)blockIdx.x;
+  idx += (size_t)blockIdx.x * T * k;
+  hits_ws += (size_t)blockIdx.x * E;
   for (int e = threadIdx.x; e < E; e += 1024) hits[e] = 0;
   __syncthreads();
   const int n = T * k;
@@ -46,6 +51,24 @@ __global__ __launch_bounds__(1024) void usage_rerank_kernel(const float* __restr
   __shared__ uint64_t sel[1024];
   moe_top_keys_sorted([&](int i) { return usage_key(scores, i); }, N, top_n, sel);
   if (threadIdx.x < top_n) top_out[threadIdx.x] = (int32_t)(0xFFFFFFFFu - (uint32_t)sel[threadIdx.x]);
+}
+
+extern "C" int moe_usage_update_stack(const int32_t* topk_idx, int T, int k, int L, int E, float decay, int64_t step,
+                                      int rerank_every, int top_n, int32_t* hits_ws, float* scores, int32_t* top_out,
+                                      void* stream) {
+  MOE_REQUIRE(T >= 0 && (int64_t)T * k * L < (1ll << 31), MOE_ESHAPE, "T=%d out of range", T);
+  MOE_REQUIRE(E >= 1 && E <= MOE_MAX_E, MOE_ESHAPE, "E=%d out of [1, %d]", E, MOE_MAX_E);
+  MOE_REQUIRE(k >= 1 && k <= MOE_MAX_K && k <= E, MOE_ESHAPE, "k=%d out of [1, min(E, %d)]", k, MOE_MAX_K);
+  MOE_REQUIRE(L >= 1 && (int64_t)L * E <= 65536, MOE_ESHAPE, "L*E must be in [1, 65536]");
+  MOE_REQUIRE(rerank_every >= 1 && step >= 0, MOE_EINVAL, "rerank_every must be >= 1 and step >= 0");
+  MOE_REQUIRE(top_n >= 1 && top_n <= 1024 && top_n <= L * E, MOE_ESHAPE, "top_n=%d out of [1, min(L*E, 1024)]", top_n);
+  MOE_REQUIRE(__builtin_isfinite(decay) && decay >= 0.f, MOE_EINVAL, "decay must be finite and >= 0");
+  MOE_REQUIRE(hits_ws && scores && (T == 0 || topk_idx), MOE_EINVAL, "hits_ws, scores and topk_idx are required");
+  hipStream_t st = moe_stream(stream);
+  usage_decay_kernel<<<L, 1024, 0, st>>>(topk_idx, T, k, 0, E, decay, hits_ws, scores);
+  if (top_out && (step + 1) % rerank_every == 0)
+    usage_rerank_kernel<<<1, 1024, 0, st>>>(scores, L * E, top_n, top_out);
+  return moe_check_launch("usage update (stack)");
 }
 
 extern "C" int moe_usage_update(const int32_t* topk_idx, int T, int k, int layer, int L, int E, float decay,

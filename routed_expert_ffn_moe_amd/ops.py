@@ -17,7 +17,7 @@ from ._lib import (MOE_BF16, MOE_F32, MOE_OP_DECODE_STACK, MOE_OP_EXPERT_GEMV_Q,
 __all__ = [
     "moe_abi_version", "moe_record_bytes", "moe_workspace_size", "workspace", "moe_route_topk", "moe_permute",
     "moe_expert_gemv_q", "moe_grouped_gemm_q", "moe_combine", "moe_usage_update", "moe_decode_stack",
-    "moe_tier_fill", "moe_tier_rebalance",
+    "moe_tier_fill", "moe_tier_rebalance", "moe_usage_update_stack",
     "MOE_Q4_B32", "MOE_Q2_B16", "MoeError", "MOE_OP_ROUTE_TOPK", "MOE_OP_PERMUTE", "MOE_OP_EXPERT_GEMV_Q",
     "MOE_OP_GROUPED_GEMM_Q", "MOE_OP_DECODE_STACK",
 ]
@@ -180,6 +180,16 @@ def moe_tier_rebalance(scores, n_hot, max_swaps, home_table, slot_table, hot_own
                                          _p(hot_owner), _p(pool), record_bytes, _p(swaps), _p(n_swaps),
                                          _stream(stream)))
     return slot_table, hot_owner
+
+
+def moe_usage_update_stack(topk_idx, E, decay, step, rerank_every, top_n, hits_ws, scores, top_out=None,
+                           stream=None):
+    """topk_idx int32 [L][T][k]; hits_ws int32 [L][E]; scores fp32 [L][E]."""
+    L, T, k = topk_idx.shape
+    _dev(topk_idx, hits_ws, scores, top_out)
+    check(_lib.load().moe_usage_update_stack(_p(topk_idx), T, k, L, E, float(decay), int(step), rerank_every, top_n,
+                                             _p(hits_ws), _p(scores), _p(top_out), _stream(stream)))
+    return scores, top_out
 
 
 def moe_decode_stack(x_in, F, E, k, w_router, bias, slot_table, pool, record_bytes, qfmt, x_out=None,

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -153,3 +153,16 @@ def test_tier_rejects(lib):
     assert reb(*b) == _lib.MOE_ESHAPE                 # n_hot < 1
     b = list(r); b[11] = None
     assert reb(*b) == _lib.MOE_EINVAL                 # n_swaps missing
+
+
+def test_usage_update_stack_rejects(lib):
+    u = lib.moe_usage_update_stack
+    a = [FAKE, 1, 10, 48, 512, ctypes.c_float(0.99), 0, 4, 96, FAKE, FAKE, FAKE, None]
+    b = list(a); b[3] = 200
+    assert u(*b) == _lib.MOE_ESHAPE                   # L*E > 65536
+    b = list(a); b[8] = 2000
+    assert u(*b) == _lib.MOE_ESHAPE                   # top_n > 1024
+    b = list(a); b[7] = 0
+    assert u(*b) == _lib.MOE_EINVAL                   # rerank_every < 1
+    b = list(a); b[9] = None
+    assert u(*b) == _lib.MOE_EINVAL                   # hits_ws missing

@@ -316,6 +316,37 @@ def test_usage_rerank_full_size(moe):
     assert np.array_equal(_np(top), rtop)
 
 
+@pytest.mark.parametrize("T,step", [(1, 3), (4, 7), (4, 2)])
+def test_usage_update_stack(moe, T, step):
+    """All 48 layers of a step in one launch: bit for bit the oracle's layer
+    by layer updates (and its re-rank when the step is a re-rank step), and
+    the same as 48 single-layer calls."""
+    L, E, k = 48, 512, 10
+    rng = np.random.default_rng(40 + T + step)
+    s = (rng.integers(0, 50, size=(L, E)) * 0.25).astype(np.float32)
+    idx = np.stack([_random_idx(rng, T, k, E, skew=1.1) for _ in range(L)]).astype(np.int32)
+    scores = torch.from_numpy(s).cuda()
+    hits = torch.empty((L, E), dtype=torch.int32, device="cuda")
+    top = torch.full((96,), -1, dtype=torch.int32, device="cuda")
+    idx_t = torch.from_numpy(idx).cuda()
+    moe.moe_usage_update_stack(idx_t, E, 0.99, step, 4, 96, hits, scores, top)
+    ref, rtop = s, None
+    for l in range(L):
+        ref, t_l = O.usage_update(ref, idx[l], l, 0.99, step, 4, 96)
+        rtop = t_l if t_l is not None else rtop
+    assert np.array_equal(_np(scores), ref)
+    if rtop is not None:
+        assert np.array_equal(_np(top), rtop)
+    else:
+        assert np.all(_np(top) == -1)
+    scores2 = torch.from_numpy(s).cuda()
+    hits1 = torch.empty(E, dtype=torch.int32, device="cuda")
+    top2 = torch.full((96,), -1, dtype=torch.int32, device="cuda")
+    for l in range(L):
+        moe.moe_usage_update(idx_t[l], l, L, E, 0.99, step, 4, 96, hits1, scores2, top2)
+    assert torch.equal(scores2, scores) and torch.equal(top2, top)
+
+
 # ---------------------------------------------------------------- stacked decode
 
 def _stack_run(moe, li, x, path, ws=None):
