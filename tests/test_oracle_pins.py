@@ -437,3 +437,79 @@ def test_pages_structural_constants():
     idx = np.arange(c["top_k"])[None, :]
     counts, *_ = O.permute(idx, c["experts_per_layer"])
     assert counts.sum() == c["top_k"] and counts.max() == 1
+
+
+# ---------------------------------------------------------------- number formats and the slot table
+
+def test_bf16_to_f64_hand_picked_patterns():
+    """bf16 is the top half of an IEEE binary32 word: each pattern is checked
+    against Python's own binary32 decoder (struct) and against hand-derived
+    values, including sign handling of int16 inputs."""
+    cases = {
+        0x3F80: 1.0, 0xC000: -2.0, 0x0000: 0.0, 0x4049: 3.140625, 0x3E80: 0.25,
+        0x0080: 2.0 ** -126,                  # smallest normal
+        0x0001: 2.0 ** -133,                  # smallest subnormal: 2^-126 * 2^-7
+        0x007F: 127 * 2.0 ** -133,            # largest subnormal
+        0x7F7F: (2 - 2 ** -7) * 2.0 ** 127,   # largest finite
+        0xFF7F: -(2 - 2 ** -7) * 2.0 ** 127,
+        0x7F80: math.inf, 0xFF80: -math.inf,
+    }
+    bits = np.array(list(cases), np.uint16)
+    got = O.bf16_to_f64(bits)
+    for b, v, g in zip(bits, cases.values(), got):
+        assert g == v, hex(int(b))
+        assert g == struct.unpack(">f", bytes([int(b) >> 8, int(b) & 0xFF, 0, 0]))[0]
+    neg0 = O.bf16_to_f64(np.array([0x8000], np.uint16))[0]
+    assert neg0 == 0.0 and math.copysign(1.0, neg0) == -1.0
+    assert np.isnan(O.bf16_to_f64(np.array([0x7FC0, 0xFFC1], np.uint16))).all()
+    # the same patterns given as (negative) int16, as torch stores bf16 bits
+    as_i16 = bits.view(np.int16)
+    assert (as_i16 < 0).any()
+    np.testing.assert_array_equal(O.bf16_to_f64(as_i16), got)
+    np.testing.assert_array_equal(O.bf16_to_f64(as_i16.astype(np.int64)), got)
+    # every pattern agrees with torch's own bf16 widening
+    allb = np.arange(1 << 16, dtype=np.uint16)
+    ref = torch.from_numpy(allb.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    mine = O.bf16_to_f64(allb)
+    fin = np.isfinite(ref)
+    np.testing.assert_array_equal(mine[fin], ref[fin])
+    np.testing.assert_array_equal(np.isnan(mine), np.isnan(ref))
+
+
+def _constant_record(H, F, q, scale_bits):
+    """An int4 record whose every weight is q * scale: every nibble q + 8 and
+    every fp16 scale `scale_bits`, written straight from the format text
+    (q planes take the first 3HF/2 bytes, the two scale planes the rest)."""
+    R = G.record_bytes(0, H, F)
+    rec = np.empty(R, np.uint8)
+    n = q + 8
+    rec[:3 * H * F // 2] = n | (n << 4)
+    rec[3 * H * F // 2:] = np.frombuffer(struct.pack("<H", scale_bits) * ((R - 3 * H * F // 2) // 2), np.uint8)
+    return rec
+
+
+def test_expert_getter_follows_the_slot_table():
+    """Records at known slots of a padded pool: record s holds the constant
+    weight (s - 8) * 2^-3 (nibbles 0..14), so every decoded matrix names the slot it came
+    from.  The slot table is a non-trivial permutation of a 3 x 5 table whose
+    column E = 4 is each layer's shared expert; the record stride is larger
+    than a record, and the padding holds bytes that decode to other values."""
+    H, F, L, E = 128, 128, 3, 4
+    R0 = G.record_bytes(0, H, F)
+    stride = R0 + 512
+    n_slots = L * (E + 1)
+    pool = np.full(n_slots * stride, 0x77, np.uint8)  # padding: nibble 7 = q -1, scale bits 0x7777
+    for s in range(n_slots):
+        pool[s * stride:s * stride + R0] = _constant_record(H, F, s - 8, 0x3000)  # fp16 0x3000 = 2^-3
+    rng = np.random.default_rng(11)
+    S = rng.permutation(n_slots).astype(np.int32).reshape(L, E + 1)
+    assert not np.array_equal(S, np.arange(n_slots).reshape(L, E + 1))
+    for layer in range(L):
+        get = O.expert_getter(pool, S, layer, 0, H, F, stride)
+        for e in range(E + 1):
+            want = (int(S[layer, e]) - 8) * 0.125
+            for M in get(e):
+                assert M.shape in ((F, H), (H, F))
+                assert np.all(M == want), (layer, e)
+    # a transposed lookup S[e][layer] would read other slots
+    assert any(S[l, e] != S[e, l] for l in range(L) for e in range(L))
