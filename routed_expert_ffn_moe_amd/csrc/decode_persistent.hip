@@ -3,21 +3,38 @@
 // in decode_persistent_kernel.h; its instances in decode_persistent_mt*.hip.
 #include "decode_persistent_kernel.h"
 
-// Zeroes the tagged buffers once per workspace (recognised by a magic word),
-// and again after a call that set the error word (its words carry a tag that
-// the next call would reuse); restarts the call count.  Neither header word it
-// tests is written while it runs: the mark kernel after it sets the magic and
-// clears the error word.
-__global__ void decode_persistent_init_kernel(uint32_t* hdr, u64* buf, size_t nwords) {
-  if (hdr[0] == PT_MAGIC && hdr[2] == 0u) return;
+#include <mutex>
+
+// Tags.  Every call takes the tags base+1 .. base+L, where base is the tag
+// count reserved so far on this workspace (hdr[1]); the reservation is made
+// by the set-up kernel before the step starts, so a call's tags are larger
+// than every tag any earlier call on the workspace wrote, whatever its layer
+// count, token count or outcome.  A stale word therefore never matches.
+// The tagged region is zeroed (and the count restarted) when the header is
+// not a valid one (first use, or memory that held something else), after a
+// call that timed out, and before the 32-bit count would wrap.
+__device__ __forceinline__ bool pt_ws_needs_reset(const uint32_t* hdr, int L) {
+  return hdr[0] != PT_MAGIC || hdr[2] != 0u || hdr[3] != (hdr[1] ^ PT_CHECK) ||
+         hdr[1] > 0xFFFFFFFFu - 2u * (uint32_t)L;
+}
+// Zeroes every word of the workspace after the header when a reset is due.
+// No header word is written here (every workgroup tests the same values);
+// the reserve kernel after it does that.
+__global__ void decode_persistent_init_kernel(const uint32_t* hdr, u64* buf, size_t nwords, int L) {
+  if (!pt_ws_needs_reset(hdr, L)) return;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += (size_t)gridDim.x * blockDim.x)
     buf[i] = 0ull;
-  if (blockIdx.x == 0 && threadIdx.x == 0) hdr[1] = 0;
 }
-__global__ void decode_persistent_mark_kernel(uint32_t* hdr) {
+// Restarts the count after a reset, then reserves this call's L tags:
+// hdr[4] = this call's base, hdr[1] = the new count (with its check word).
+__global__ void decode_persistent_reserve_kernel(uint32_t* hdr, int L) {
   if (threadIdx.x == 0) {
-    hdr[0] = PT_MAGIC;
+    const uint32_t base = pt_ws_needs_reset(hdr, L) ? 0u : hdr[1];
+    hdr[4] = base;
+    hdr[1] = base + (uint32_t)L;
+    hdr[3] = (base + (uint32_t)L) ^ PT_CHECK;
     hdr[2] = 0u;
+    hdr[0] = PT_MAGIC;
   }
 }
 
@@ -76,6 +93,46 @@ static size_t pt_lds_limit() {
   return lim;
 }
 
+// The instance with the fewest token slots >= T (unused slots cost registers
+// and instructions: T=3 on 3 slots 2.21 -> 2.11 ms, T=5 and 6 on 6 slots instead
+// of 8 3.84 -> 3.39 and 4.23 -> 3.71 ms per 48-layer step), or NULL.
+static const void* pt_instance(int qfmt, int T, int E) {
+  const int mt = T <= 4 ? T : T <= 6 ? 6 : 8;
+  const int slots = E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : 16;
+  const void* fn = pt_kernel_mt12(qfmt, mt, slots);
+  if (!fn) fn = pt_kernel_mt34(qfmt, mt, slots);
+  if (!fn) fn = pt_kernel_mt68(qfmt, mt, slots);
+  return fn;
+}
+
+// Whether the device can hold all G workgroups of the instance at once (the
+// kernel's waits assume every workgroup is running).  The answer of the
+// occupancy query is cached per (instance, LDS bytes, device).
+bool moe_persistent_coresident(int T, int k, int E, int H, int F, int qfmt) {
+  const void* fn = pt_instance(qfmt, T, E);
+  if (!fn) return false;
+  const int G = pt_grid(H, E);
+  const PtLayout P = pt_layout(T, k, E, H, F, qfmt, G);
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+    return false;
+  struct Entry { const void* fn; size_t lds; int dev; bool ok; };
+  static std::mutex mu;
+  static Entry cache[64];
+  static int n = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < n; ++i)
+    if (cache[i].fn == fn && cache[i].lds == P.lds && cache[i].dev == dev) return cache[i].ok;
+  int per_cu = 0;
+  bool ok = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)P.lds) == hipSuccess &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, PT_THREADS, P.lds) == hipSuccess &&
+            (int64_t)per_cu * ncu >= G;
+  (void)hipGetLastError();  // a failed query leaves no sticky error behind
+  if (n < 64) cache[n++] = Entry{fn, P.lds, dev, ok};
+  return ok;
+}
+
 bool moe_persistent_supported(int T, int k, int E, int H, int F, int qfmt) {
   if (T < 1 || T > 8 || k > MOE_MAX_K) return false;
   const PtLayout P = pt_layout(T, k, E, H, F, qfmt, pt_grid(H, E));
@@ -89,7 +146,7 @@ int moe_launch_decode_persistent(const float* x_in, int T, int H, int F, int E, 
                                  const uint16_t* w_router, const float* bias, const int32_t* slot_table,
                                  const void* pool, int64_t record_bytes, int qfmt, float* x_out,
                                  int32_t* topk_idx_out, float* topk_w_out, float* x_hist, void* ws,
-                                 hipStream_t st) {
+                                 size_t ws_bytes, hipStream_t st) {
   const int G = pt_grid(H, E);
   const PtLayout P = pt_layout(T, k, E, H, F, qfmt, G);
   uint8_t* w = (uint8_t*)ws;
@@ -106,17 +163,12 @@ int moe_launch_decode_persistent(const float* x_in, int T, int H, int F, int E, 
     while (tpo > 1 && (size_t)T * P.rpw * tpo > PT_THREADS) tpo >>= 1;
     a.tpo = tpo;
   }
-  const size_t nwords = (P.total - P.xbuf) / 8;
-  decode_persistent_init_kernel<<<256, 256, 0, st>>>(a.hdr, a.xbuf, nwords);
-  decode_persistent_mark_kernel<<<1, 64, 0, st>>>(a.hdr);
-  // the instance with the fewest token slots >= T (unused slots cost registers
-  // and instructions: T=3 on 3 slots 2.21 -> 2.11 ms, T=5 and 6 on 6 slots instead
-  // of 8 3.84 -> 3.39 and 4.23 -> 3.71 ms per 48-layer step)
-  const int mt = T <= 4 ? T : T <= 6 ? 6 : 8;
-  const int slots = E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : 16;
-  const void* fn = pt_kernel_mt12(qfmt, mt, slots);
-  if (!fn) fn = pt_kernel_mt34(qfmt, mt, slots);
-  if (!fn) fn = pt_kernel_mt68(qfmt, mt, slots);
+  // a reset zeroes all of ws (not only this layout): a larger layout of an
+  // earlier call may have left tagged words further in
+  const size_t nwords = (ws_bytes - P.xbuf) / 8;
+  decode_persistent_init_kernel<<<256, 256, 0, st>>>(a.hdr, a.xbuf, nwords, L);
+  decode_persistent_reserve_kernel<<<1, 64, 0, st>>>(a.hdr, L);
+  const void* fn = pt_instance(qfmt, T, E);
   if (!fn) return moe_fail(MOE_EUNSUPPORTED, "decode persistent: no kernel for this shape");
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)P.lds) != hipSuccess)
     return moe_fail(MOE_EHIP, "decode persistent: cannot reserve %zu bytes of LDS", P.lds);

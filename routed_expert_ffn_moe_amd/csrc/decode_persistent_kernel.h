@@ -9,7 +9,9 @@
 //   * a producer writes 64-bit words (tag << 32 | payload) with relaxed
 //     agent-scope atomic stores (coherent across XCDs, single-copy atomic);
 //   * a consumer polls exactly the words it needs until every tag matches
-//     the current (call, layer) tag.  No counters, so nothing serialises.
+//     the current layer's tag (tags are never reused on a workspace: see
+//     the set-up kernels in decode_persistent.hip).  No counters, so nothing
+//     serialises.
 // Per layer l (tag t_l), workgroup g:
 //   A  read x_l (tagged, or x_in for l = 0); 1/rms per token in every wave;
 //      router rows e = g (mod G): logits of xn = x * inv, tagged.  Prepare
@@ -38,6 +40,7 @@
 #define PT_SPIN_MAX (1 << 18)
 #define PT_GROUP_BASE 4  // cost of a group's loads, in units of one token's dot passes
 #define PT_MAGIC 0x4d6f4531u
+#define PT_CHECK 0x9e3779b9u
 #define PT_EPS 1e-6f
 
 typedef unsigned long long u64;
@@ -54,7 +57,7 @@ struct PtArgs {
   int32_t* topk_idx_out;
   float* topk_w_out;
   float* x_hist;
-  uint32_t* hdr;  // [0] magic, [1] call counter, [2] error
+  uint32_t* hdr;  // [0] magic, [1] tags reserved, [2] error, [3] check of [1], [4] this call's tag base
   u64* xbuf;      // [T][H]
   u64* lbuf;      // [T][E]
   u64* pbuf;      // [(unit * T + i)][H]
@@ -106,9 +109,8 @@ __device__ inline bool pt_wait_sentinels(u64* base, uint32_t first, uint32_t str
     if (it > spin_max) return false;
   }
 }
-__device__ __forceinline__ uint32_t pt_tag(uint32_t call, int L, int l) {
-  return (uint32_t)(((uint64_t)call * (uint64_t)L + (uint64_t)l) % 0xFFFFFFFFull) + 1u;
-}
+// tag of layer l of the call whose tags start after `base`
+__device__ __forceinline__ uint32_t pt_tag(uint32_t base, int l) { return base + (uint32_t)l + 1u; }
 
 // ---------------------------------------------------------------- small helpers
 // The nibble / crumb masks of the dots, held in registers (made opaque once
@@ -573,7 +575,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
   float2* hc = (float2*)(smem + o.hc);        // [piece][MT]
   int* lslots = (int*)(smem + o.slots);        // [E+1] this layer's slot-table row
 
-  const uint32_t call = __hip_atomic_load(a.hdr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t base = __hip_atomic_load(a.hdr + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   bool ok = true;
   const int nrch = (H + 511) / 512;  // router chunks of 512 columns per row (<= 4)
 
@@ -583,7 +585,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     // live across the whole layer loop
     asm volatile("" : "+v"(tid));
     lane = tid & 63;
-    const uint32_t tag = pt_tag(call, L, l);
+    const uint32_t tag = pt_tag(base, l);
     // ------------------------------------------------------------ phase A
     // this wave's router row (if any) is requested before waiting for x_l
     // (indices are clamped into range so that every load is unconditional)
@@ -664,7 +666,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     if (l == 0) {
       for (int i = tid; i < T * H; i += PT_THREADS) xs[i] = a.x_in[i];
     } else {
-      const uint32_t ptag = pt_tag(call, L, l - 1);
+      const uint32_t ptag = pt_tag(base, l - 1);
       const int last = T * H - 1;
       // x is polled word by word (every word carries its tag): one round trip
       // less than waiting for per-producer sentinels first
@@ -1198,13 +1200,11 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
   }
   if (!ok) {
     // the error word: the next call's set-up kernel then zeroes the tagged
-    // buffers and restarts the call count (this call's words carry a tag that
-    // the next call would otherwise reuse)
+    // buffers (this call's tags stay reserved, so this is belt and braces)
     if (tid == 0) __hip_atomic_store(a.hdr + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int i = g * PT_THREADS + tid; i < T * H; i += G * PT_THREADS) a.x_out[i] = __builtin_nanf("");
     return;
   }
-  if (g == 0 && tid == 0) __hip_atomic_store(a.hdr + 1, call + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Address of the kernel instance for (qfmt, mt token slots, SLOTS), or NULL.

@@ -29,11 +29,12 @@ size_t moe_ws_decode_stack(int T, int k, int E, int H, int F, int qfmt) {
 }
 
 // MOE_DECODE_PATH=chain forces the per-layer kernel chain; otherwise the
-// persistent kernel is used whenever it supports the shape.
+// persistent kernel is used whenever it supports the shape and the device
+// can keep all of its workgroups resident at once.
 static bool use_persistent(int T, int k, int E, int H, int F, int qfmt) {
   const char* e = getenv("MOE_DECODE_PATH");
   if (e && strcmp(e, "chain") == 0) return false;
-  return moe_persistent_supported(T, k, E, H, F, qfmt);
+  return moe_persistent_supported(T, k, E, H, F, qfmt) && moe_persistent_coresident(T, k, E, H, F, qfmt);
 }
 
 // xn[t] = x[t] / sqrt(mean(x[t]^2) + eps); one workgroup per token, fixed-order
@@ -72,7 +73,7 @@ extern "C" int moe_decode_stack(const float* x_in, int T, int H, int F, int E, i
   hipStream_t st = moe_stream(stream);
   if (use_persistent(T, k, E, H, F, qfmt))
     return moe_launch_decode_persistent(x_in, T, H, F, E, k, L, w_router, bias, slot_table, pool, record_bytes, qfmt,
-                                        x_out, topk_idx_out, topk_w_out, x_hist, ws, st);
+                                        x_out, topk_idx_out, topk_w_out, x_hist, ws, ws_bytes, st);
   const MoeStackLayout W = moe_stack_layout(T, k, E, H, F, qfmt);
   uint8_t* w = (uint8_t*)ws;
   float* logits = (float*)(w + W.logits);

@@ -15,11 +15,12 @@ int moe_launch_combine(const float* y_rows, const int32_t* inv_row, const float*
 // Persistent single-kernel decode step (decode_persistent.hip).
 size_t moe_ws_stack_persistent(int T, int k, int E, int H, int F, int qfmt);
 bool moe_persistent_supported(int T, int k, int E, int H, int F, int qfmt);
+bool moe_persistent_coresident(int T, int k, int E, int H, int F, int qfmt);
 int moe_launch_decode_persistent(const float* x_in, int T, int H, int F, int E, int k, int L,
                                  const uint16_t* w_router, const float* bias, const int32_t* slot_table,
                                  const void* pool, int64_t record_bytes, int qfmt, float* x_out,
                                  int32_t* topk_idx_out, float* topk_w_out, float* x_hist, void* ws,
-                                 hipStream_t st);
+                                 size_t ws_bytes, hipStream_t st);
 
 // Workspace of moe_decode_stack: enough for whichever path it takes.
 size_t moe_ws_decode_stack(int T, int k, int E, int H, int F, int qfmt);
