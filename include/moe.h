@@ -41,7 +41,9 @@
  *     has been enqueued and moe_last_error() (thread-local) describes it.
  *     Arguments are validated on the host before any launch.  Index contents
  *     of device arrays (expert ids, slots, rows) are preconditions that are
- *     not checked on the host; an out-of-range value is undefined behaviour.
+ *     not read on the host; an out-of-range value is undefined behaviour.
+ *     The moe_validate_* functions (end of this file) check such arrays
+ *     once the caller has copied them to host memory.
  *   - bf16 and fp16 values are passed as uint16_t bit patterns.
  *   - Entry points keep no state between calls: calls on different streams
  *     with different workspaces may run concurrently.
@@ -158,6 +160,11 @@ size_t moe_workspace_size(int op, int T, int k, int E, int H, int F, int qfmt);
 
 /* --------------------------------------------------------------------------
  * moe_route_topk -- router logits, top-k selection and softmax weights.
+ * Pages: "Strata开源运行时：12GB显卡跑动125B参数Qwen3模型", section
+ * "模型本身：稀疏MoE带来的计算与存储鸿沟" (in every layer a light router
+ * picks 10 of the 512 experts for each token); "为什么 Strata 在小显存显卡上
+ * 这么快", section "一个 token，三路工人" (per layer the GPU runs the router
+ * first and the ids of the 10 chosen experts decide where the work goes).
  *   x        [T][H] activations, dtype x_dtype (MOE_F32 or MOE_BF16)
  *   w_router bf16 [E][H], bias fp32 [E] or NULL
  *   topk_idx int32 [T][k] out: chosen experts, larger logit first, ties to
@@ -175,6 +182,11 @@ int moe_route_topk(const void* x, int x_dtype, int T, int H,
 
 /* --------------------------------------------------------------------------
  * moe_permute -- group the T*k (token, choice) pairs by expert; stable.
+ * Page: "为什么 Strata 在小显存显卡上这么快", section "读长提示词：大块流式
+ * 读取" (a prompt is read in chunks of up to 8,192 or 16,384 tokens; such a
+ * chunk routes to nearly every expert of a layer and each expert's weights
+ * then serve all of the chunk's tokens that chose it -- grouping the pairs
+ * by expert is what lets one pass over an expert serve all of them).
  *   counts  int32 [E]   out: counts[e] = #{(t,j) : topk_idx[t][j] == e}
  *   offsets int32 [E+1] out: exclusive prefix sum, offsets[E] = T*k
  *   row_src int32 [T*k] out: row_src[r] = t*k+j of the pair placed at row r;
@@ -191,6 +203,14 @@ int moe_permute(const int32_t* topk_idx, int T, int k, int E,
 
 /* --------------------------------------------------------------------------
  * moe_expert_gemv_q -- decode / verify experts (1 <= T <= MOE_MAX_DECODE_T).
+ * Pages: "为什么 Strata 在小显存显卡上这么快", section "一个 token，三路工人"
+ * (the chosen experts of each layer are computed, then summed on the GPU);
+ * same page, section "先猜，再检查" (a verify step of several tokens reads
+ * the shared weights once, and only experts that the extra tokens route to
+ * add work -- hence each distinct expert is read once per call);
+ * "Strata开源运行时：12GB显卡跑动125B参数Qwen3模型", section "模型本身：稀疏
+ * MoE带来的计算与存储鸿沟" (10 routed experts plus one shared expert that
+ * always runs).
  *   x        fp32 [T][H]
  *   topk_idx int32 [T][k] (from moe_route_topk)
  *   y_parts  fp32 [T][k+1][H] out: y_parts[t][j] = y_{topk_idx[t][j]}(x_t)
@@ -205,15 +225,22 @@ int moe_expert_gemv_q(const float* x, int T, int H, int F,
 
 /* --------------------------------------------------------------------------
  * moe_grouped_gemm_q -- prefill experts over a permuted chunk.
- *   x        bf16 [T][H]; every |x| must be finite in fp16 (< 65504)
+ * Page: "为什么 Strata 在小显存显卡上这么快", section "读长提示词：大块流式
+ * 读取" (every expert a chunk routes to is used by the whole chunk, so its
+ * weight traffic is amortised over thousands of tokens: a dense contraction
+ * per expert); "Strata开源运行时：12GB显卡跑动125B参数Qwen3模型", section
+ * "模型本身：稀疏MoE带来的计算与存储鸿沟" (the shared expert always runs).
+ *   x        bf16 [T][H]; every |x| must be below 65520 (fp16's range)
  *   row_src, offsets: from moe_permute (rows of expert e are
  *            [offsets[e], offsets[e+1]))
  *   y_perm   fp32 [T*k][H] out: y_perm[r] = y_e(x[row_src[r]/k])
  *   y_shared fp32 [T][H]   out: y_shared[t] = y_shared(x[t])
- * Experts with no rows are skipped.  Internally x is multiplied in fp16
- * (exact for bf16 values of magnitude >= 2^-14), weights are dequantised to
- * fp16 (one rounding of s*q, resp. s*q+m), the SiLU*mul intermediate is
- * rounded to fp16 and all sums are fp32.
+ * Experts with no rows are skipped.  Internally x is multiplied in fp16:
+ * bf16 values with 2^-14 <= |x| < 65520 convert exactly; smaller ones round
+ * to fp16 subnormals (absolute error <= 2^-25); |x| >= 65520 becomes inf
+ * (not checked: the output is then inf/NaN for the tokens concerned).
+ * Weights are dequantised to fp16 (one rounding of s*q, resp. s*q+m), the
+ * SiLU*mul intermediate is rounded to fp16 and all sums are fp32.
  * ws: moe_workspace_size(MOE_OP_GROUPED_GEMM_Q, T, k, E, H, F, qfmt). */
 int moe_grouped_gemm_q(const uint16_t* x, int T, int H, int F,
                        const int32_t* row_src, const int32_t* offsets, int k,
@@ -224,6 +251,8 @@ int moe_grouped_gemm_q(const uint16_t* x, int T, int H, int F,
 
 /* --------------------------------------------------------------------------
  * moe_combine -- weighted sum of the expert outputs of each token.
+ * Page: "为什么 Strata 在小显存显卡上这么快", section "一个 token，三路工人"
+ * (the GPU adds up the experts' results before the next layer starts).
  *   inv_row == NULL: decode layout, y_rows is [T][k+1][H] as written by
  *     moe_expert_gemv_q (slot k = shared expert) and y_shared must be NULL.
  *   inv_row != NULL: prefill layout, y_rows is y_perm [T*k][H] and y_shared
@@ -340,12 +369,18 @@ int moe_tier_rebalance(const float* scores, int L, int E, int n_hot,
  * data through tagged words in ws (no host synchronisation, no grid
  * barrier); otherwise,
  * or when the environment variable MOE_DECODE_PATH=chain is set, as a chain
- * of kernels per layer.  The persistent path keeps a call counter and tagged
- * buffers in ws across calls: pass the same ws to every call of a stack and
- * do not use it for anything else in between (calls on one ws must not
- * overlap).  Its waits are bounded; if one times out (e.g. the GPU could not
- * keep all its workgroups resident) x_out is filled with NaN, and the next
- * call on that ws re-initialises its tagged buffers first.
+ * of kernels per layer.  The persistent path is taken only when the device
+ * reports that all its workgroups (one per CU) fit at once.
+ * Workspace: the persistent path keeps a header (a count of the exchange
+ * tags used so far, with check words) and tagged exchange buffers in ws
+ * across calls.  Every call uses tags no earlier call on the same ws used,
+ * so a ws may serve any sequence of calls (any L, T, k) as long as nothing
+ * else writes it in between and calls on one ws do not overlap.  A ws whose
+ * header is not valid (first use; memory that held other data) is zeroed
+ * in full before use; passing zero-filled memory the first time is the
+ * recommended practice.  The waits are bounded; if one times out (e.g.
+ * other work on the device kept some workgroups from starting) x_out is
+ * filled with NaN and the next call on that ws zeroes it first.
  * ws: moe_workspace_size(MOE_OP_DECODE_STACK, T, k, E, H, F, qfmt). */
 int moe_decode_stack(const float* x_in, int T, int H, int F, int E, int k,
                      int L, const uint16_t* w_router, const float* bias,
@@ -353,6 +388,29 @@ int moe_decode_stack(const float* x_in, int T, int H, int F, int E, int k,
                      int64_t record_bytes, int qfmt, float* x_out,
                      int32_t* topk_idx_out, float* topk_w_out, float* x_hist,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------------------
+ * Host-side index checks.  The entry points above take the index contents
+ * of their device arrays (expert ids, slots, rows) as preconditions and do
+ * not read them on the host; these functions check such arrays after the
+ * caller has copied them to HOST memory (a debugging aid: the Python
+ * binding runs them before every call when MOE_VALIDATE=1).  They touch no
+ * device.  Return MOE_OK, or MOE_EINVAL with moe_last_error() naming the
+ * first offending entry (MOE_ESHAPE for impossible sizes).
+ *
+ * moe_validate_routing -- topk_idx int32 [T][k]: every id in [0, E) and the
+ *   k ids of each token distinct (what moe_route_topk produces; required by
+ *   moe_permute, moe_expert_gemv_q and moe_usage_update).
+ * moe_validate_slot_table -- slot_table int32 [L][E+1]: every slot in
+ *   [0, n_slots), n_slots being the number of records the pool holds.
+ * moe_validate_rows -- offsets int32 [E+1], row_src int32 [n], inv_row
+ *   int32 [n] or NULL, n = T*k: offsets[0] = 0, non-decreasing, offsets[E]
+ *   = n; row_src a permutation of 0..n-1; inv_row its inverse (what
+ *   moe_permute produces; required by moe_grouped_gemm_q and moe_combine). */
+int moe_validate_routing(const int32_t* topk_idx, int T, int k, int E);
+int moe_validate_slot_table(const int32_t* slot_table, int L, int E, int64_t n_slots);
+int moe_validate_rows(const int32_t* offsets, const int32_t* row_src, const int32_t* inv_row, int T, int k,
+                      int E);
 
 #ifdef __cplusplus
 }

@@ -34,6 +34,9 @@ SIGNATURES = {
     "moe_tier_rebalance": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
     "moe_decode_stack": (_i, [_vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i64, _i, _vp, _vp, _vp, _vp, _vp,
                               _sz, _vp]),
+    "moe_validate_routing": (_i, [_vp, _i, _i, _i]),
+    "moe_validate_slot_table": (_i, [_vp, _i, _i, _i64]),
+    "moe_validate_rows": (_i, [_vp, _vp, _vp, _i, _i, _i]),
 }
 
 

@@ -1,6 +1,7 @@
 // Housekeeping entry points of libmoe: version, errors, sizes.
 #include <cstdarg>
 #include <cstdio>
+#include <vector>
 
 #include "moe_common.h"
 #include "moe_sizes.h"
@@ -62,4 +63,60 @@ extern "C" size_t moe_workspace_size(int op, int T, int k, int E, int H, int F, 
     case MOE_OP_DECODE_STACK: return moe_ws_decode_stack(T, k, E, H, F, qfmt);
     default: return 0;
   }
+}
+
+// ---------------------------------------------------------------- host-side index checks
+
+extern "C" int moe_validate_routing(const int32_t* topk_idx, int T, int k, int E) {
+  MOE_REQUIRE(T >= 0 && k >= 1 && E >= 1 && k <= E, MOE_ESHAPE, "T=%d, k=%d, E=%d", T, k, E);
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(topk_idx, MOE_EINVAL, "topk_idx is required");
+  for (int t = 0; t < T; ++t) {
+    const int32_t* row = topk_idx + (size_t)t * k;
+    for (int j = 0; j < k; ++j) {
+      MOE_REQUIRE(row[j] >= 0 && row[j] < E, MOE_EINVAL, "topk_idx[%d][%d] = %d is outside [0, %d)", t, j, row[j], E);
+      for (int i = 0; i < j; ++i)
+        MOE_REQUIRE(row[i] != row[j], MOE_EINVAL, "topk_idx[%d] holds expert %d twice (positions %d and %d)", t,
+                    row[j], i, j);
+    }
+  }
+  return MOE_OK;
+}
+
+extern "C" int moe_validate_slot_table(const int32_t* slot_table, int L, int E, int64_t n_slots) {
+  MOE_REQUIRE(L >= 1 && E >= 1 && n_slots >= 1, MOE_ESHAPE, "L=%d, E=%d, n_slots=%lld", L, E, (long long)n_slots);
+  MOE_REQUIRE(slot_table, MOE_EINVAL, "slot_table is required");
+  for (int l = 0; l < L; ++l)
+    for (int e = 0; e <= E; ++e) {
+      const int32_t s = slot_table[(size_t)l * (E + 1) + e];
+      MOE_REQUIRE(s >= 0 && s < n_slots, MOE_EINVAL, "slot_table[%d][%d] = %d is outside [0, %lld)", l, e, s,
+                  (long long)n_slots);
+    }
+  return MOE_OK;
+}
+
+extern "C" int moe_validate_rows(const int32_t* offsets, const int32_t* row_src, const int32_t* inv_row, int T,
+                                 int k, int E) {
+  MOE_REQUIRE(T >= 0 && k >= 1 && E >= 1 && (int64_t)T * k < (1ll << 31), MOE_ESHAPE, "T=%d, k=%d, E=%d", T, k, E);
+  MOE_REQUIRE(offsets, MOE_EINVAL, "offsets is required");
+  const int n = T * k;
+  MOE_REQUIRE(offsets[0] == 0, MOE_EINVAL, "offsets[0] = %d, not 0", offsets[0]);
+  for (int e = 0; e < E; ++e)
+    MOE_REQUIRE(offsets[e + 1] >= offsets[e], MOE_EINVAL, "offsets[%d] = %d < offsets[%d] = %d", e + 1,
+                offsets[e + 1], e, offsets[e]);
+  MOE_REQUIRE(offsets[E] == n, MOE_EINVAL, "offsets[%d] = %d, not T*k = %d", E, offsets[E], n);
+  if (n == 0) return MOE_OK;
+  MOE_REQUIRE(row_src, MOE_EINVAL, "row_src is required");
+  std::vector<int32_t> seen((size_t)n, -1);
+  for (int r = 0; r < n; ++r) {
+    const int32_t s = row_src[r];
+    MOE_REQUIRE(s >= 0 && s < n, MOE_EINVAL, "row_src[%d] = %d is outside [0, %d)", r, s, n);
+    MOE_REQUIRE(seen[(size_t)s] < 0, MOE_EINVAL, "row_src[%d] = %d repeats row_src[%d]", r, s, seen[(size_t)s]);
+    seen[(size_t)s] = r;
+  }
+  if (inv_row)
+    for (int i = 0; i < n; ++i)
+      MOE_REQUIRE(inv_row[i] == seen[(size_t)i], MOE_EINVAL, "inv_row[%d] = %d, but row_src[%d] = %d", i, inv_row[i],
+                  seen[(size_t)i], i);
+  return MOE_OK;
 }

@@ -7,6 +7,7 @@ raw device pointers and torch's current HIP stream.  Every step of the layer
 runs in the library's kernels; nothing here computes.
 """
 import ctypes
+import os
 
 import torch
 
@@ -55,6 +56,44 @@ def _half_bits(t):
     return t
 
 
+# ---------------------------------------------------------------- index checks
+# With MOE_VALIDATE=1 every call below first copies its index arrays to the
+# host and runs the library's host-side checks on them (a debugging aid: it
+# synchronises the stream).
+
+def _validating():
+    return os.environ.get("MOE_VALIDATE") == "1"
+
+
+def _host_i32(t):
+    return t.detach().to(device="cpu", dtype=torch.int32).contiguous()
+
+
+def validate_routing(topk_idx, E):
+    """topk_idx [T][k]: ids in [0, E), distinct per token (host check)."""
+    h = _host_i32(topk_idx)
+    T, k = h.shape
+    check(_lib.load().moe_validate_routing(_p(h), T, k, E))
+
+
+def validate_slot_table(slot_table, n_slots):
+    """slot_table [L][E+1]: every slot in [0, n_slots) (host check)."""
+    h = _host_i32(slot_table)
+    L, E1 = h.shape
+    check(_lib.load().moe_validate_slot_table(_p(h), L, E1 - 1, int(n_slots)))
+
+
+def validate_rows(offsets, row_src, T, k, inv_row=None):
+    """offsets [E+1] / row_src / inv_row [T*k] as moe_permute defines them (host check)."""
+    ho, hr = _host_i32(offsets), _host_i32(row_src)
+    hi = None if inv_row is None else _host_i32(inv_row)
+    check(_lib.load().moe_validate_rows(_p(ho), _p(hr), _p(hi), T, k, ho.numel() - 1))
+
+
+def _pool_slots(pool, record_bytes):
+    return pool.numel() * pool.element_size() // record_bytes
+
+
 def moe_abi_version():
     return _lib.load().moe_abi_version()
 
@@ -68,8 +107,12 @@ def moe_workspace_size(op, T=0, k=0, E=0, H=0, F=0, qfmt=0):
 
 
 def workspace(op, device, T=0, k=0, E=0, H=0, F=0, qfmt=0):
-    n = moe_workspace_size(op, T, k, E, H, F, qfmt)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    """Scratch for entry point `op`.  The decode-stack workspace is zero-filled
+    (its header then starts a fresh tag count); the others need no contents."""
+    n = max(moe_workspace_size(op, T, k, E, H, F, qfmt), 256)
+    if op == MOE_OP_DECODE_STACK:
+        return torch.zeros(n, dtype=torch.uint8, device=device)
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def moe_route_topk(x, w_router, bias, k, topk_idx=None, topk_w=None, logits_out=None, ws=None, stream=None):
@@ -103,6 +146,8 @@ def moe_permute(topk_idx, E, counts=None, offsets=None, row_src=None, inv_row=No
         x_perm = torch.empty((T * k, x.shape[1]), dtype=x.dtype, device=dev)
     ws = workspace(MOE_OP_PERMUTE, dev, T=T, k=k, E=E) if ws is None else ws
     _dev(topk_idx, counts, offsets, row_src, inv_row, x, x_perm, ws)
+    if _validating():
+        validate_routing(topk_idx, E)
     H = 0 if x is None else x.shape[1]
     xd = 0 if x is None else _x_dtype(x)
     check(_lib.load().moe_permute(_p(topk_idx), T, k, E, _p(counts), _p(offsets), _p(row_src), _p(inv_row), _p(x),
@@ -120,6 +165,9 @@ def moe_expert_gemv_q(x, topk_idx, E, F, slot_table, layer, pool, record_bytes, 
         y_parts = torch.empty((T, k + 1, H), dtype=torch.float32, device=dev)
     ws = workspace(MOE_OP_EXPERT_GEMV_Q, dev, T, k, E, H, F, qfmt) if ws is None else ws
     _dev(x, topk_idx, slot_table, pool, y_parts, ws)
+    if _validating():
+        validate_routing(topk_idx, E)
+        validate_slot_table(slot_table, _pool_slots(pool, record_bytes))
     check(_lib.load().moe_expert_gemv_q(_p(x), T, H, F, _p(topk_idx), k, E, _p(slot_table), layer, _p(pool),
                                         record_bytes, qfmt, _p(y_parts), _p(ws), ws.numel(), _stream(stream)))
     return y_parts
@@ -135,6 +183,9 @@ def moe_grouped_gemm_q(x, row_src, offsets, k, E, F, slot_table, layer, pool, re
     y_shared = torch.empty((T, H), dtype=torch.float32, device=dev) if y_shared is None else y_shared
     ws = workspace(MOE_OP_GROUPED_GEMM_Q, dev, T, k, E, H, F, qfmt) if ws is None else ws
     _dev(x, row_src, offsets, slot_table, pool, y_perm, y_shared, ws)
+    if _validating():
+        validate_rows(offsets, row_src, T, k)
+        validate_slot_table(slot_table, _pool_slots(pool, record_bytes))
     check(_lib.load().moe_grouped_gemm_q(_p(x), T, H, F, _p(row_src), _p(offsets), k, E, _p(slot_table), layer,
                                          _p(pool), record_bytes, qfmt, _p(y_perm), _p(y_shared), _p(ws), ws.numel(),
                                          _stream(stream)))
@@ -146,6 +197,9 @@ def moe_combine(y_rows, topk_w, inv_row=None, y_shared=None, residual=None, y_ou
     H = y_rows.shape[-1]
     y_out = torch.empty((T, H), dtype=torch.float32, device=y_rows.device) if y_out is None else y_out
     _dev(y_rows, topk_w, inv_row, y_shared, residual, y_out)
+    if _validating() and inv_row is not None:  # inv_row must be a permutation of the T*k rows
+        n = T * k
+        validate_rows(torch.tensor([0, n], dtype=torch.int32), inv_row, T, k)
     check(_lib.load().moe_combine(_p(y_rows), _p(inv_row), _p(y_shared), _p(topk_w), _p(residual), T, k, H, _p(y_out),
                                   _stream(stream)))
     return y_out
@@ -155,6 +209,8 @@ def moe_usage_update(topk_idx, layer, L, E, decay, step, rerank_every, top_n, hi
                      stream=None):
     T, k = topk_idx.shape
     _dev(topk_idx, hits_ws, scores, top_out)
+    if _validating():
+        validate_routing(topk_idx, E)
     check(_lib.load().moe_usage_update(_p(topk_idx), T, k, layer, L, E, float(decay), int(step), rerank_every, top_n,
                                        _p(hits_ws), _p(scores), _p(top_out), _stream(stream)))
     return scores, top_out
@@ -187,6 +243,8 @@ def moe_usage_update_stack(topk_idx, E, decay, step, rerank_every, top_n, hits_w
     """topk_idx int32 [L][T][k]; hits_ws int32 [L][E]; scores fp32 [L][E]."""
     L, T, k = topk_idx.shape
     _dev(topk_idx, hits_ws, scores, top_out)
+    if _validating():
+        validate_routing(topk_idx.reshape(L * T, k), E)
     check(_lib.load().moe_usage_update_stack(_p(topk_idx), T, k, L, E, float(decay), int(step), rerank_every, top_n,
                                              _p(hits_ws), _p(scores), _p(top_out), _stream(stream)))
     return scores, top_out
@@ -201,6 +259,8 @@ def moe_decode_stack(x_in, F, E, k, w_router, bias, slot_table, pool, record_byt
     x_out = torch.empty_like(x_in) if x_out is None else x_out
     ws = workspace(MOE_OP_DECODE_STACK, dev, T, k, E, H, F, qfmt) if ws is None else ws
     _dev(x_in, w_router, bias, slot_table, pool, x_out, topk_idx_out, topk_w_out, x_hist, ws)
+    if _validating():
+        validate_slot_table(slot_table, _pool_slots(pool, record_bytes))
     check(_lib.load().moe_decode_stack(_p(x_in), T, H, F, E, k, L, _p(w_router), _p(bias), _p(slot_table), _p(pool),
                                        record_bytes, qfmt, _p(x_out), _p(topk_idx_out), _p(topk_w_out), _p(x_hist),
                                        _p(ws), ws.numel(), _stream(stream)))

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -166,3 +166,75 @@ def test_usage_update_stack_rejects(lib):
     assert u(*b) == _lib.MOE_EINVAL                   # rerank_every < 1
     b = list(a); b[9] = None
     assert u(*b) == _lib.MOE_EINVAL                   # hits_ws missing
+
+
+# ---------------------------------------------------------------- host-side index checks
+
+def _i32(a):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def test_validate_routing(lib):
+    good, p = _i32([[3, 0, 7], [1, 2, 5]])
+    assert lib.moe_validate_routing(p, 2, 3, 8) == _lib.MOE_OK
+    assert lib.moe_validate_routing(p, 2, 3, 7) == _lib.MOE_EINVAL and "topk_idx[0][2] = 7" in _err(lib)
+    dup, pd = _i32([[3, 0, 7], [1, 5, 5]])
+    assert lib.moe_validate_routing(pd, 2, 3, 8) == _lib.MOE_EINVAL and "twice" in _err(lib)
+    neg, pn = _i32([[3, -1, 7]])
+    assert lib.moe_validate_routing(pn, 1, 3, 8) == _lib.MOE_EINVAL
+    assert lib.moe_validate_routing(None, 0, 3, 8) == _lib.MOE_OK
+    assert lib.moe_validate_routing(p, 2, 9, 8) == _lib.MOE_ESHAPE  # k > E
+
+
+def test_validate_slot_table(lib):
+    S, p = _i32([[0, 5, 2], [4, 1, 3]])
+    assert lib.moe_validate_slot_table(p, 2, 2, 6) == _lib.MOE_OK
+    assert lib.moe_validate_slot_table(p, 2, 2, 5) == _lib.MOE_EINVAL and "slot_table[0][1] = 5" in _err(lib)
+    assert lib.moe_validate_slot_table(None, 2, 2, 6) == _lib.MOE_EINVAL
+
+
+def test_validate_rows(lib):
+    import numpy as np
+    import oracle as O
+    idx = np.array([[2, 0], [0, 1], [2, 1]])
+    counts, offsets, row_src, inv_row = O.permute(idx, 4)
+    o, po = _i32(offsets)
+    r, pr = _i32(row_src)
+    i, pi = _i32(inv_row)
+    assert lib.moe_validate_rows(po, pr, pi, 3, 2, 4) == _lib.MOE_OK
+    assert lib.moe_validate_rows(po, pr, None, 3, 2, 4) == _lib.MOE_OK
+    bad_o, pbo = _i32([0, 2, 1, 6, 6])
+    assert lib.moe_validate_rows(pbo, pr, pi, 3, 2, 4) == _lib.MOE_EINVAL and "offsets[2]" in _err(lib)
+    short, pso = _i32([0, 2, 4, 5, 5])
+    assert lib.moe_validate_rows(pso, pr, pi, 3, 2, 4) == _lib.MOE_EINVAL
+    rep = r.copy()
+    rep[1] = rep[0]
+    _, prep = _i32(rep)
+    assert lib.moe_validate_rows(po, prep, None, 3, 2, 4) == _lib.MOE_EINVAL and "repeats" in _err(lib)
+    wrong_inv = i.copy()
+    wrong_inv[[0, 1]] = wrong_inv[[1, 0]]
+    _, pwi = _i32(wrong_inv)
+    assert lib.moe_validate_rows(po, pr, pwi, 3, 2, 4) == _lib.MOE_EINVAL and "inv_row" in _err(lib)
+    oob = r.copy()
+    oob[3] = 6
+    _, poob = _i32(oob)
+    assert lib.moe_validate_rows(po, poob, None, 3, 2, 4) == _lib.MOE_EINVAL
+
+
+def test_binding_validates_before_launching(monkeypatch):
+    """MOE_VALIDATE=1: the binding runs the host checks on a call's index
+    arrays (CPU tensors here) and raises before anything reaches the GPU."""
+    import torch
+    from routed_expert_ffn_moe_amd import ops
+    monkeypatch.setenv("MOE_VALIDATE", "1")
+    with pytest.raises(ops.MoeError, match="outside"):
+        ops.validate_routing(torch.tensor([[0, 16]]), 16)
+    with pytest.raises(ops.MoeError, match="twice"):
+        ops.validate_routing(torch.tensor([[3, 3]]), 16)
+    with pytest.raises(ops.MoeError, match="slot_table"):
+        ops.validate_slot_table(torch.tensor([[0, 1, 9]]), 9)
+    ops.validate_rows(torch.tensor([0, 1, 2]), torch.tensor([1, 0]), 1, 2)
+    with pytest.raises(ops.MoeError):
+        ops.validate_rows(torch.tensor([0, 1, 2]), torch.tensor([1, 1]), 1, 2)
