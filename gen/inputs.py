@@ -28,7 +28,7 @@ __all__ = [
     "normal", "draw_x", "draw_x_rejecting", "to_bf16_bits", "draw_router",
     "zipf_bias", "quantize_int4", "quantize_int2", "pack_int4", "pack_int2",
     "pack_record", "draw_expert_weights", "make_slot_table", "build_pool",
-    "LayerInputs", "make_layer_inputs", "draw_expert_chunks",
+    "LayerInputs", "make_layer_inputs", "draw_expert_chunks", "random_records", "build_random_pool",
 ]
 
 QFMT_INT4 = 0
@@ -282,6 +282,55 @@ def build_pool(seed, L, E, H, F, qfmt, device="cpu", rec_bytes=None,
     return pool, S, R
 
 
+def _random_f16(gen, n, lo, hi, p_zero, device):
+    """n fp16 values: 0 with probability p_zero, else +-U(lo, hi) (random sign)."""
+    mag = torch.rand(n, generator=gen, device=device) * (hi - lo) + lo
+    sign = torch.where(torch.rand(n, generator=gen, device=device) < 0.5, -1.0, 1.0)
+    zero = torch.rand(n, generator=gen, device=device) < p_zero
+    return torch.where(zero, torch.zeros_like(mag), mag * sign).to(torch.float16)
+
+
+def random_records(gen, qfmt, H, F, n, device="cpu"):
+    """n records of uniformly random quantised bytes (every nibble / crumb
+    value equally likely, so q = -8 and the int2 range ends occur), with
+    random fp16 scales: one in 16 exactly zero, the rest +-U(0.002, 0.008)
+    (int4) or +-U(0.004, 0.016) (int2, with mins +-U(0, 0.02), one in 16 zero).
+    The meta planes are the records' last bytes (include/moe.h): int4 scales
+    from 3HF/2 on, int2 (scale, min) pairs from 3HF/4 on."""
+    R = record_bytes(qfmt, H, F)
+    recs = torch.randint(0, 256, (n, R), generator=gen, device=device, dtype=torch.int32).to(torch.uint8)
+    HF = H * F
+    if qfmt == QFMT_INT4:
+        m0 = 3 * HF // 2
+        nm = (R - m0) // 2
+        meta = _random_f16(gen, n * nm, 0.002, 0.008, 1 / 16, device).reshape(n, nm)
+    else:
+        m0 = 3 * HF // 4
+        npair = (R - m0) // 4
+        sc = _random_f16(gen, n * npair, 0.004, 0.016, 1 / 16, device).reshape(n, npair)
+        mn = _random_f16(gen, n * npair, 0.0, 0.02, 1 / 16, device).reshape(n, npair)
+        meta = torch.stack([sc, mn], dim=-1).reshape(n, 2 * npair)
+    recs[:, m0:] = meta.contiguous().view(torch.uint8).reshape(n, -1)
+    return recs
+
+
+def build_random_pool(seed, L, E, H, F, qfmt, device="cpu", slot_table=None):
+    """A pool of random records (random_records) for all L*(E+1) experts.
+    Returns (pool uint8 [n*R], S, R)."""
+    R = record_bytes(qfmt, H, F)
+    S = make_slot_table(seed, L, E) if slot_table is None else slot_table
+    n_slots = int(S.max().item()) + 1
+    pool = torch.zeros(n_slots * R, dtype=torch.uint8, device=device)
+    view = pool.view(n_slots, R)
+    g = make_gen(device, seed, "random-records")
+    for l in range(L):
+        for c0 in range(0, E + 1, EXPERT_CHUNK):
+            nn = min(EXPERT_CHUNK, E + 1 - c0)
+            slots = S[l, c0:c0 + nn].to(device=device, dtype=torch.long)
+            view[slots] = random_records(g, qfmt, H, F, nn, device)
+    return pool, S, R
+
+
 class LayerInputs:
     """Everything one layer (or a stack) needs, as torch tensors."""
 
@@ -290,13 +339,18 @@ class LayerInputs:
 
 
 def make_layer_inputs(seed, L, E, H, F, qfmt=QFMT_INT4, bias=False,
-                      device="cpu", progress=None, hot_slots=0):
+                      device="cpu", progress=None, hot_slots=0, random_bytes=False):
     """Routers [L][E][H] (bf16 bits), bias [L][E] or None, pool, slot table.
     hot_slots > 0 leaves that many empty record slots at the start of the
-    pool (a hot tier); the slot table then holds the home slots after them."""
+    pool (a hot tier); the slot table then holds the home slots after them.
+    random_bytes: the records are random_records instead of quantised
+    N(0, 0.02) weights."""
     Wr = torch.stack([draw_router(seed, l, E, H, device) for l in range(L)])
     b = torch.stack([zipf_bias(seed, l, E) for l in range(L)]).to(device) if bias else None
     S0 = make_slot_table(seed, L, E) + hot_slots if hot_slots else None
-    pool, S, R = build_pool(seed, L, E, H, F, qfmt, device, slot_table=S0, progress=progress)
+    if random_bytes:
+        pool, S, R = build_random_pool(seed, L, E, H, F, qfmt, device, slot_table=S0)
+    else:
+        pool, S, R = build_pool(seed, L, E, H, F, qfmt, device, slot_table=S0, progress=progress)
     return LayerInputs(seed=seed, L=L, E=E, H=H, F=F, qfmt=qfmt, Wr=Wr, bias=b,
                        pool=pool, S=S.to(device), R=R)

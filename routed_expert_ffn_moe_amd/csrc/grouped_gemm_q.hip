@@ -16,21 +16,17 @@
 // converted to fp16 (exact in fp16's normal range) once, into the workspace,
 // before the gate/up pass; accumulation is fp32.
 //
-// Two kernels compute it (gemm2_kernel is the one used; gemm_kernel, the
-// first version, is kept behind MOE_GEMM_KERNEL=v1 for comparison).  Both
-// use workgroups of 4 waves where wave w owns weight rows nbase..nbase+63 =
-// two 32-wide MFMA column tiles over the tile's 32-row MFMA row tiles; for
-// the gate/up pass the record interleaves gate and up rows in runs of 32, so
-// a wave's two column tiles are gate and up of the same 32 f values and
-// SiLU*mul happens in registers.  The next K chunk's A tile and B words are
-// requested before the current chunk's MFMAs (A through registers into a
-// double-buffered LDS tile).
-//   gemm_kernel:  BM = 128 (a 160-row expert runs as 64 + 96 rows), K chunks
-//                 of 128, the MFMAs of absent row tiles skipped by branches.
-//   gemm2_kernel: BM = 160 (a typical expert is one tile, each dequantised
-//                 weight operand feeds up to 5 MFMAs), K chunks of 64, and a
-//                 K loop specialised on the row-tile count: no branches, so
-//                 the compiler's waits count only the loads a step needs.
+// gemm2_kernel uses workgroups of 4 waves where wave w owns weight rows
+// nbase..nbase+63 = two 32-wide MFMA column tiles over the tile's 32-row MFMA
+// row tiles; for the gate/up pass the record interleaves gate and up rows in
+// runs of 32, so a wave's two column tiles are gate and up of the same 32 f
+// values and SiLU*mul happens in registers.  The next K chunk's A tile and B
+// words are requested before the current chunk's MFMAs (A through registers
+// into a double-buffered LDS tile).  Tiles hold up to BM = 160 rows (a
+// typical expert is one tile, each dequantised weight operand feeds up to 5
+// MFMAs), K chunks of 64, and the K loop is specialised on the row-tile
+// count: no branches, so the compiler's waits count only the loads a step
+// needs.
 //
 // Blocks are renumbered so that consecutive work items (the column tiles of
 // one row tile, then the row tiles of one expert) land on the same XCD
@@ -42,12 +38,6 @@
 
 #include "moe_common.h"
 #include "moe_sizes.h"
-
-#define GEMM_BM MOE_GEMM_BM
-#define GEMM_BN 256
-#define GEMM_KC 128
-#define GEMM_NB (GEMM_KC / 32)  // int4 blocks per K chunk
-#define GEMM_LDS_STRIDE 136     // halves per staged row (128 + 8 pad)
 
 // tile_start[g] = first tile of group g (exclusive scan of ceil(M_g / BM), BM a
 // multiple of 32);
@@ -104,77 +94,6 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint4* __restrict__
   }
 }
 
-template <int QFMT>
-struct BRegs;  // raw weight words of one K chunk (128) for one lane and two column tiles
-
-template <>
-struct BRegs<MOE_Q4_B32> {
-  uint2 q[2][GEMM_NB];   // [sub][block in chunk]: dwords 2hh, 2hh+1 of the block
-  uint32_t s[2][2];      // [sub][block pair]: fp16 scales of blocks 2p, 2p+1
-};
-template <>
-struct BRegs<MOE_Q2_B16> {
-  uint4 q[2][2];         // [sub][unit]: q-unit (4 blocks)
-  uint4 m[2][2];         // [sub][unit]: meta-unit
-};
-
-__device__ __forceinline__ void load_b(BRegs<MOE_Q4_B32>& b, const uint8_t* rec, const MoePlanes& pl, int rows,
-                                       int row0, int hh, int c, bool gu) {
-  // rec is wave-uniform and a record is < 4 GiB: 32-bit offsets
-  const uint32_t q_off = (uint32_t)(gu ? pl.gu_q : pl.d_q), s_off = (uint32_t)(gu ? pl.gu_s : pl.d_s);
-  const uint32_t R = (uint32_t)rows;
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    const uint32_t r = (uint32_t)(row0 + 32 * sub);
-#pragma unroll
-    for (int bi = 0; bi < GEMM_NB; ++bi) {
-      const uint32_t kb = (uint32_t)(GEMM_NB * c + bi);
-      b.q[sub][bi] = *reinterpret_cast<const uint2*>(rec + (q_off + 16u * (kb * R + r) + 8u * (uint32_t)hh));
-    }
-    const uint32_t kb = (uint32_t)(GEMM_NB * c);  // a multiple of 4
-    if (gu) {  // 4-block groups: the chunk's 4 scales in one 8-byte word
-      const uint2 w = *reinterpret_cast<const uint2*>(rec + (s_off + 2u * ((kb >> 2) * R * 4u + 4u * r)));
-      b.s[sub][0] = w.x;
-      b.s[sub][1] = w.y;
-    } else {   // per block [kb][row]
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const uint32_t s0 = *reinterpret_cast<const uint16_t*>(rec + (s_off + 2u * ((kb + 2 * p) * R + r)));
-        const uint32_t s1 = *reinterpret_cast<const uint16_t*>(rec + (s_off + 2u * ((kb + 2 * p + 1) * R + r)));
-        b.s[sub][p] = s0 | (s1 << 16);
-      }
-    }
-  }
-}
-
-__device__ __forceinline__ void load_b(BRegs<MOE_Q2_B16>& b, const uint8_t* rec, const MoePlanes& pl, int rows,
-                                       int row0, int hh, int c, bool gu) {
-  const uint32_t q_off = (uint32_t)(gu ? pl.gu_q : pl.d_q), m_off = (uint32_t)(gu ? pl.gu_s : pl.d_s);
-  const uint32_t R = (uint32_t)rows;
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    const uint32_t r = (uint32_t)(row0 + 32 * sub);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t un = (uint32_t)(2 * c + u);  // 4-block unit (64 values of K)
-      if (gu) {
-        b.q[sub][u] = *reinterpret_cast<const uint4*>(rec + (q_off + 16u * (un * R + r)));
-        b.m[sub][u] = *reinterpret_cast<const uint4*>(rec + (m_off + 16u * (un * R + r)));
-      } else {   // per block [b][row]
-        uint32_t qw[4], mw[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          qw[j] = *reinterpret_cast<const uint32_t*>(rec + (q_off + 4u * ((4u * un + j) * R + r)));
-          mw[j] = *reinterpret_cast<const uint32_t*>(rec + (m_off + 4u * ((4u * un + j) * R + r)));
-        }
-        b.q[sub][u] = make_uint4(qw[0], qw[1], qw[2], qw[3]);
-        b.m[sub][u] = make_uint4(mw[0], mw[1], mw[2], mw[3]);
-      }
-    }
-  }
-  (void)hh;
-}
-
 // The nibble mask held in a register: (x & mask) | magic is then one
 // v_and_or_b32 (with both operands literal constants it takes two
 // instructions, the VOP3 encoding taking no literal here).
@@ -212,193 +131,6 @@ __device__ __forceinline__ half8v deq_q2(uint32_t w, int hh, half2v s2, half2v m
     r[2 * p + 1] = v[1];
   }
   return r;
-}
-
-template <int QFMT, bool GU>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict__ a_src, int T, int H, int F, int k,
-                                                      int E, const int32_t* __restrict__ row_src,
-                                                      const int32_t* __restrict__ offsets,
-                                                      const int32_t* __restrict__ tile_start,
-                                                      const int4* __restrict__ tile_info,
-                                                      const int32_t* __restrict__ slot_table, int layer,
-                                                      const uint8_t* __restrict__ pool, int64_t record_bytes,
-                                                      _Float16* __restrict__ h_out, float* __restrict__ y_perm,
-                                                      float* __restrict__ y_shared, int n_ntiles, int total_wg) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][GEMM_BM * GEMM_LDS_STRIDE];
-  __shared__ int arow[GEMM_BM];
-
-  // XCD-aware renumbering: block b runs on XCD b % 8; the real work count
-  // (known only here) is cut into 8 consecutive ranges, one per XCD.  The
-  // grid (total_wg, a multiple of 8) is an upper bound; surplus blocks exit.
-  const int bid = blockIdx.x;
-  const int nwork = tile_start[E + 1] * n_ntiles;
-  const int per_xcd = (nwork + 7) >> 3;
-  const int idx = bid >> 3;
-  const int work = (bid & 7) * per_xcd + idx;
-  if (idx >= per_xcd || work >= nwork) return;
-  const int tile = work / n_ntiles, nt = work % n_ntiles;
-  const int4 ti = tile_info[tile];
-  const int g = ti.x, m0 = ti.y, mv = ti.z, gbase = ti.w;  // gbase: first h row of the group
-  const int nrt = (mv + 31) / 32;                           // row tiles present (<= 4)
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hh = lane >> 5, ln = lane & 31;
-  const int K = GU ? H : F;
-  const int rows = GU ? 2 * F : H;  // rows of the stored weight matrix
-  const int nbase = nt * GEMM_BN + 64 * wave;
-  const bool active = nbase < rows;
-
-  if (tid < GEMM_BM) {
-    int r = -1;
-    if (tid < mv) {
-      if (GU) r = g < E ? row_src[gbase + m0 + tid] / k : m0 + tid;
-      else r = gbase + m0 + tid;
-    }
-    arow[tid] = r;
-  }
-  const int64_t slot = slot_table[(size_t)layer * (E + 1) + g];
-  const uint8_t* rec = pool + slot * record_bytes;
-  const MoePlanes pl = moe_planes(QFMT, H, F);
-  __syncthreads();
-
-  // A staging (fp16 rows): thread -> (row st_r, 32 values at st_c)
-  const int st_r = tid >> 1, st_c = (GEMM_KC / 2) * (tid & 1);
-  const int my_arow = arow[st_r];
-  constexpr int NA = GEMM_KC / 16;  // uint4 (8 halves) per staging thread
-  uint4 areg[NA];
-  const bool st_on = st_r < 32 * nrt;  // wave-uniform: wave w stages row tile w
-  auto load_a = [&](int c) {
-    if (!st_on) return;
-    if (my_arow >= 0) {
-      const uint4* p = reinterpret_cast<const uint4*>(a_src + (size_t)my_arow * K + c * GEMM_KC + st_c);
-#pragma unroll
-      for (int i = 0; i < NA; ++i) areg[i] = p[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < NA; ++i) areg[i] = make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_a = [&](int stage) {
-    if (!st_on) return;
-    uint4* d = reinterpret_cast<uint4*>(&As[stage][st_r * GEMM_LDS_STRIDE + st_c]);
-#pragma unroll
-    for (int i = 0; i < NA; ++i) d[i] = areg[i];
-  };
-
-  float16v acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][s][v] = 0.f;
-
-  const int nc = K / GEMM_KC;
-  const uint32_t m4 = moe_vgpr_const(0x000F000Fu), m2b = moe_vgpr_const(0x00030003u);
-  BRegs<QFMT> bcur, bnext;
-  load_a(0);
-  if (active) load_b(bcur, rec, pl, rows, nbase + ln, hh, 0, GU);
-  store_a(0);
-  __syncthreads();
-
-  for (int c = 0; c < nc; ++c) {
-    const int stage = c & 1;
-    if (c + 1 < nc) {
-      load_a(c + 1);
-      if (active) load_b(bnext, rec, pl, rows, nbase + ln, hh, c + 1, GU);
-    }
-    if (active) {
-      const _Float16* Ab = &As[stage][0];
-      if constexpr (QFMT == MOE_Q4_B32) {
-        const BRegs<MOE_Q4_B32>& B = bcur;
-#pragma unroll
-        for (int bi = 0; bi < GEMM_NB; ++bi) {
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            half8v bf[2];
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
-              const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(B.s[sub][bi >> 1] >> (16 * (bi & 1))));
-              const half2v s2 = {sc, sc};
-              bf[sub] = deq_q4(s == 0 ? B.q[sub][bi].x : B.q[sub][bi].y, s2, m4);
-            }
-            const int kk = 32 * bi + 16 * hh + 8 * s;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if (i >= nrt) break;
-              const half8v af = *reinterpret_cast<const half8v*>(&Ab[(32 * i + ln) * GEMM_LDS_STRIDE + kk]);
-#pragma unroll
-              for (int sub = 0; sub < 2; ++sub)
-                acc[i][sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[sub], acc[i][sub], 0, 0, 0);
-            }
-          }
-        }
-      } else {
-        const BRegs<MOE_Q2_B16>& B = bcur;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int u = jj >> 2, j = jj & 3;
-          half8v bf[2];
-#pragma unroll
-          for (int sub = 0; sub < 2; ++sub) {
-            const uint4 Q = B.q[sub][u], Mm = B.m[sub][u];
-            const uint32_t qw = j == 0 ? Q.x : j == 1 ? Q.y : j == 2 ? Q.z : Q.w;
-            const uint32_t mw = j == 0 ? Mm.x : j == 1 ? Mm.y : j == 2 ? Mm.z : Mm.w;
-            const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(mw & 0xffff));
-            const _Float16 mn = __builtin_bit_cast(_Float16, (uint16_t)(mw >> 16));
-            const half2v s2 = {sc, sc}, m2 = {mn, mn};
-            bf[sub] = deq_q2(qw, hh, s2, m2, m2b);
-          }
-          const int kk = 16 * jj + 8 * hh;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (i >= nrt) break;
-            const half8v af = *reinterpret_cast<const half8v*>(&Ab[(32 * i + ln) * GEMM_LDS_STRIDE + kk]);
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
-              acc[i][sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[sub], acc[i][sub], 0, 0, 0);
-          }
-        }
-      }
-    }
-    if (c + 1 < nc) store_a(stage ^ 1);
-    __syncthreads();
-    bcur = bnext;
-  }
-
-  if (!active) return;
-  // epilogue: lane holds column ln, rows 8*(v/4) + 4*hh + v%4 of each 32-row tile
-  if constexpr (GU) {
-    const int f = 32 * (nbase / 64) + ln;
-    _Float16* hb = h_out + (size_t)(gbase + m0) * F + f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i >= nrt) break;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (r < mv) {
-          const float gv = acc[i][0][v], uv = acc[i][1][v];
-          hb[(uint32_t)(r * F)] = (_Float16)(moe_silu_fast(gv) * uv);
-        }
-      }
-    }
-  } else {
-    float* yb = g < E ? y_perm + (size_t)(gbase + m0) * H : y_shared + (size_t)m0 * H;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int col = nbase + 32 * sub + ln;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i >= nrt) break;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (r < mv) yb[(uint32_t)(r * H + col)] = acc[i][sub][v];
-        }
-      }
-    }
-  }
 }
 
 // ---------------------------------------------------------------- gemm2
@@ -679,40 +411,21 @@ static int launch_gemm_t(const uint16_t* x, int T, int H, int F, const int32_t* 
   int4* tile_info = (int4*)((uint8_t*)ws + moe_gemm_info_offset(E));
   _Float16* h = (_Float16*)((uint8_t*)ws + moe_gemm_h_offset(T, k, E));
   uint16_t* x16 = (uint16_t*)((uint8_t*)ws + moe_gemm_x16_offset(T, k, E, F));
-  const char* kv = getenv("MOE_GEMM_KERNEL");
-  const bool v2 = !(kv && strcmp(kv, "v1") == 0);
-  gemm_schedule_kernel<<<1, 1024, 0, st>>>(offsets, E, T, k, v2 ? G2_BM : GEMM_BM, tile_start, tile_info);
+  gemm_schedule_kernel<<<1, 1024, 0, st>>>(offsets, E, T, k, G2_BM, tile_start, tile_info);
   {
     const size_t n8 = (size_t)T * H / 8;
     const int grid = (int)std::min<size_t>((n8 + 255) / 256, 4096);
     x_to_f16_kernel<<<grid, 256, 0, st>>>((const uint4*)x, n8, (uint4*)x16);
   }
-  const int max_tiles = moe_gemm_max_tiles(T, k, E);  // bounds the tile count for BM >= 128
-  if (v2) {
-    const int nnt_gu = (2 * F + G2_BN - 1) / G2_BN, nnt_d = (H + G2_BN - 1) / G2_BN;
-    const int tot_gu = (max_tiles * nnt_gu + 7) / 8 * 8, tot_d = (max_tiles * nnt_d + 7) / 8 * 8;
-    gemm2_kernel<QFMT, true><<<tot_gu, 256, 0, st>>>(x16, T, H, F, k, E, row_src, tile_start, tile_info, slot_table,
-                                                     layer, (const uint8_t*)pool, record_bytes, h, y_perm, y_shared,
-                                                     nnt_gu);
-    gemm2_kernel<QFMT, false><<<tot_d, 256, 0, st>>>((const uint16_t*)h, T, H, F, k, E, row_src, tile_start, tile_info,
-                                                      slot_table, layer, (const uint8_t*)pool, record_bytes, h, y_perm,
-                                                      y_shared, nnt_d);
-    return moe_check_launch("grouped gemm");
-  }
-  {
-    const int nnt = (2 * F + GEMM_BN - 1) / GEMM_BN;
-    const int total = (max_tiles * nnt + 7) / 8 * 8;
-    gemm_kernel<QFMT, true><<<total, 256, 0, st>>>(x16, T, H, F, k, E, row_src, offsets, tile_start, tile_info, slot_table, layer,
-                                                   (const uint8_t*)pool, record_bytes, h, y_perm, y_shared, nnt,
-                                                   total);
-  }
-  {
-    const int nnt = (H + GEMM_BN - 1) / GEMM_BN;
-    const int total = (max_tiles * nnt + 7) / 8 * 8;
-    gemm_kernel<QFMT, false><<<total, 256, 0, st>>>((const uint16_t*)h, T, H, F, k, E, row_src, offsets, tile_start,
-                                                    tile_info, slot_table, layer, (const uint8_t*)pool, record_bytes, h, y_perm,
-                                                    y_shared, nnt, total);
-  }
+  const int max_tiles = moe_gemm_max_tiles(T, k, E);  // bounds the tile count for BM >= MOE_GEMM_BM
+  const int nnt_gu = (2 * F + G2_BN - 1) / G2_BN, nnt_d = (H + G2_BN - 1) / G2_BN;
+  const int tot_gu = (max_tiles * nnt_gu + 7) / 8 * 8, tot_d = (max_tiles * nnt_d + 7) / 8 * 8;
+  gemm2_kernel<QFMT, true><<<tot_gu, 256, 0, st>>>(x16, T, H, F, k, E, row_src, tile_start, tile_info, slot_table,
+                                                   layer, (const uint8_t*)pool, record_bytes, h, y_perm, y_shared,
+                                                   nnt_gu);
+  gemm2_kernel<QFMT, false><<<tot_d, 256, 0, st>>>((const uint16_t*)h, T, H, F, k, E, row_src, tile_start, tile_info,
+                                                    slot_table, layer, (const uint8_t*)pool, record_bytes, h, y_perm,
+                                                    y_shared, nnt_d);
   return moe_check_launch("grouped gemm");
 }
 

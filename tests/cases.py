@@ -66,9 +66,10 @@ class LazyPool:
         return self.pool[sl].cpu().numpy()
 
 
-def layer_case(seed, T, H, E, k, F, qfmt=0, bias=False, device="cpu", x_bf16=False, L=1, gap=True):
+def layer_case(seed, T, H, E, k, F, qfmt=0, bias=False, device="cpu", x_bf16=False, L=1, gap=True,
+               random_bytes=False):
     """One or more layers of weights plus gap-safe tokens for layer 0."""
-    li = G.make_layer_inputs(seed, L, E, H, F, qfmt=qfmt, bias=bias, device=device)
+    li = G.make_layer_inputs(seed, L, E, H, F, qfmt=qfmt, bias=bias, device=device, random_bytes=random_bytes)
     b0 = None if li.bias is None else li.bias[0]
     acc = gap_acceptor(li.Wr[0], b0, k, as_bf16=x_bf16) if gap else (lambda x: np.ones(x.shape[0], bool))
     x, att = G.draw_x_rejecting(seed, T, H, acc, device=device)

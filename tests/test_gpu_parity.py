@@ -370,22 +370,32 @@ def _stack_run(moe, li, x, path, ws=None):
 
 
 def _check_stack(li, x, xo, idx_o, w_o, hist, layers):
+    """Each listed layer against the oracle fed the kernel's own layer input:
+    ids bit-exact, weights within W_ATOL and the layer's output (x_{l+1} - x_l)
+    within the MoE tolerance, token by token, for every token whose routing is
+    decided by a gap >= MIN_GAP (tokens are independent within a layer, so a
+    near tie in one token leaves the others checkable).  Returns (excluded,
+    checked) token counts; every token is one or the other."""
     L = hist.shape[0]
+    T = hist.shape[1]
     assert torch.equal(hist[0], x)
     assert torch.isfinite(xo).all()
-    excluded = 0
+    excluded = checked = 0
     for l in layers:
         xl = torch.from_numpy(O.rms_normalize(C.x_as_f64(hist[l])))
         ry, ri, rw, _, rl = C.oracle_layer(li, layer=l, x=xl)
         ok = O.gap_ok(rl, li.k, C.MIN_GAP)
         excluded += int((~ok).sum())
-        assert np.array_equal(_np(idx_o[l])[ok], ri[ok])
+        checked += int(ok.sum())
+        assert np.array_equal(_np(idx_o[l])[ok], ri[ok]), f"layer {l}"
         if ok.any():
             assert np.max(np.abs(_np(w_o[l])[ok] - rw[ok])) <= W_ATOL
         nxt = hist[l + 1] if l + 1 < L else xo
-        if ok.all():
-            C.assert_close_moe(_np(nxt - hist[l]), ry, f"layer {l}")
-    return excluded
+        d = _np(nxt - hist[l])
+        for t in np.nonzero(ok)[0]:
+            C.assert_close_moe(d[t], ry[t], f"layer {l} token {t}")
+    assert excluded + checked == T * len(list(layers))
+    return excluded, checked
 
 
 @pytest.mark.parametrize("path", ["chain", "persistent"])
@@ -396,7 +406,7 @@ def test_decode_stack_tiny(moe, qfmt, T, path):
     li = C.layer_case(5, T, 256, 16, 2, 128, qfmt=qfmt, bias=True, L=L, gap=False, device="cuda")
     x = li.x.contiguous()
     xo, idx_o, w_o, hist = _stack_run(moe, li, x, path)
-    excluded = _check_stack(li, x, xo, idx_o, w_o, hist, range(L))
+    excluded, checked = _check_stack(li, x, xo, idx_o, w_o, hist, range(L))
     assert excluded <= T * L // 4
 
 
@@ -413,9 +423,9 @@ def test_decode_stack_full_shape_persistent(moe, qfmt, T, k):
     x = li.x.contiguous()
     ws = moe.workspace(moe.MOE_OP_DECODE_STACK, "cuda", T, k, 512, 2048, 768, qfmt)
     xo, idx_o, w_o, hist = _stack_run(moe, li, x, "persistent", ws=ws)
-    excluded = _check_stack(li, x, xo, idx_o, w_o, hist, range(L))
+    excluded, _ = _check_stack(li, x, xo, idx_o, w_o, hist, range(L))
     xc, idx_c, w_c, hist_c = _stack_run(moe, li, x, "chain")
-    excluded += _check_stack(li, x, xc, idx_c, w_c, hist_c, range(L))
+    excluded += _check_stack(li, x, xc, idx_c, w_c, hist_c, range(L))[0]
     assert excluded <= 2 * T * L // 4
     # Layer 0: the same input.  The paths sum the router dot products in
     # different orders, so two nearly equal logits may come out in either
@@ -445,9 +455,9 @@ def test_decode_stack_wide_verify(moe, qfmt, T, k):
     x = li.x.contiguous()
     ws = moe.workspace(moe.MOE_OP_DECODE_STACK, "cuda", T, k, 512, 2048, 768, qfmt)
     xo, idx_o, w_o, hist = _stack_run(moe, li, x, "auto", ws=ws)
-    excluded = _check_stack(li, x, xo, idx_o, w_o, hist, range(L))
+    excluded, _ = _check_stack(li, x, xo, idx_o, w_o, hist, range(L))
     xc, idx_c, w_c, hist_c = _stack_run(moe, li, x, "chain")
-    excluded += _check_stack(li, x, xc, idx_c, w_c, hist_c, range(L))
+    excluded += _check_stack(li, x, xc, idx_c, w_c, hist_c, range(L))[0]
     assert excluded <= 2 * T * L // 4
     for rep in range(2):
         xo2, idx2, _, _ = _stack_run(moe, li, x, "auto", ws=ws)
@@ -465,7 +475,7 @@ def test_decode_stack_48_layers(moe, qfmt):
     x = li.x.contiguous()
     xo, idx_o, w_o, hist = _stack_run(moe, li, x, "persistent")
     assert bool(torch.isfinite(hist).all()) and bool(torch.isfinite(xo).all())
-    excluded = _check_stack(li, x, xo, idx_o, w_o, hist, [0, 16, 32, 47])
+    excluded, _ = _check_stack(li, x, xo, idx_o, w_o, hist, [0, 16, 32, 47])
     assert excluded <= 2  # layer 0 is gap-filtered; later layers may hold a near tie
 
 
