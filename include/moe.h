@@ -390,6 +390,29 @@ int moe_decode_stack(const float* x_in, int T, int H, int F, int E, int k,
                      void* ws, size_t ws_bytes, void* stream);
 
 /* --------------------------------------------------------------------------
+ * moe_decode_stack_noalloc -- moe_decode_stack (same arguments, same
+ * results, same kernels) without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Its scratch is a
+ * library-owned device array of MOE_NOALLOC_WS_BYTES bytes, one per GPU the
+ * library runs on, held until the process ends; the entry point allocates
+ * nothing (no hipMalloc, no allocating library call).  Sizes whose
+ * moe_workspace_size(MOE_OP_DECODE_STACK, ...) exceeds MOE_NOALLOC_WS_BYTES
+ * are rejected with MOE_EWORKSPACE before anything is enqueued (at H = 2048,
+ * E = 512, k = 10: T <= 5 fits, i.e. decode and verify windows of up to 4
+ * drafted tokens; T = 6 and 8 need 25 and 34 MB and are rejected).  Every call on a GPU shares that GPU's
+ * array, which keeps the previous call's contents (its tag header is valid
+ * across calls; see moe_decode_stack): calls that overlap on one GPU, on
+ * any streams, race and give wrong results.  The first call on a device
+ * looks up the array's address (hipGetSymbolAddress) with that device
+ * current. */
+#define MOE_NOALLOC_WS_BYTES (24 << 20)
+int moe_decode_stack_noalloc(const float* x_in, int T, int H, int F, int E, int k, int L,
+                             const uint16_t* w_router, const float* bias, const int32_t* slot_table,
+                             const void* pool, int64_t record_bytes, int qfmt, float* x_out,
+                             int32_t* topk_idx_out, float* topk_w_out, float* x_hist, void* stream);
+
+/* --------------------------------------------------------------------------
  * Host-side index checks.  The entry points above take the index contents
  * of their device arrays (expert ids, slots, rows) as preconditions and do
  * not read them on the host; these functions check such arrays after the

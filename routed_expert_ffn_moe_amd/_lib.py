@@ -14,6 +14,7 @@ MOE_Q4_B32, MOE_Q2_B16 = 0, 1
 (MOE_OP_ROUTE_TOPK, MOE_OP_PERMUTE, MOE_OP_EXPERT_GEMV_Q, MOE_OP_GROUPED_GEMM_Q, MOE_OP_COMBINE,
  MOE_OP_USAGE_UPDATE, MOE_OP_DECODE_STACK) = range(7)
 MOE_MAX_E, MOE_MAX_K, MOE_MAX_DECODE_T = 1024, 16, 8
+MOE_NOALLOC_WS_BYTES = 24 << 20
 
 _vp, _i, _i64, _sz, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
 
@@ -34,6 +35,8 @@ SIGNATURES = {
     "moe_tier_rebalance": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
     "moe_decode_stack": (_i, [_vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i64, _i, _vp, _vp, _vp, _vp, _vp,
                               _sz, _vp]),
+    "moe_decode_stack_noalloc": (_i, [_vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i64, _i, _vp, _vp, _vp,
+                                      _vp, _vp]),
     "moe_validate_routing": (_i, [_vp, _i, _i, _i]),
     "moe_validate_slot_table": (_i, [_vp, _i, _i, _i64]),
     "moe_validate_rows": (_i, [_vp, _vp, _vp, _i, _i, _i]),

@@ -53,11 +53,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   for (int h = threadIdx.x; h < H; h += 256) xn[(size_t)blockIdx.x * H + h] = xr[h] * inv;
 }
 
-extern "C" int moe_decode_stack(const float* x_in, int T, int H, int F, int E, int k, int L,
-                                const uint16_t* w_router, const float* bias, const int32_t* slot_table,
-                                const void* pool, int64_t record_bytes, int qfmt, float* x_out,
-                                int32_t* topk_idx_out, float* topk_w_out, float* x_hist, void* ws, size_t ws_bytes,
-                                void* stream) {
+int moe_decode_stack_check(const float* x_in, int T, int H, int F, int E, int k, int L, const uint16_t* w_router,
+                           const int32_t* slot_table, const void* pool, int64_t record_bytes, int qfmt,
+                           const float* x_out, const float* x_hist) {
   int rc = moe_check_expert_shapes(H, F, E, k, qfmt, pool, record_bytes, slot_table, 0);
   if (rc) return rc;
   MOE_REQUIRE(T >= 1 && T <= MOE_MAX_DECODE_T, MOE_ESHAPE, "T=%d out of [1, %d]", T, MOE_MAX_DECODE_T);
@@ -67,10 +65,29 @@ extern "C" int moe_decode_stack(const float* x_in, int T, int H, int F, int E, i
   MOE_REQUIRE(moe_aligned(x_in, 16) && moe_aligned(x_out, 16) && moe_aligned(w_router, 16) &&
                   (!x_hist || moe_aligned(x_hist, 16)),
               MOE_EALIGN, "x_in, x_out, x_hist and w_router must be 16-byte aligned");
+  return MOE_OK;
+}
+
+extern "C" int moe_decode_stack(const float* x_in, int T, int H, int F, int E, int k, int L,
+                                const uint16_t* w_router, const float* bias, const int32_t* slot_table,
+                                const void* pool, int64_t record_bytes, int qfmt, float* x_out,
+                                int32_t* topk_idx_out, float* topk_w_out, float* x_hist, void* ws, size_t ws_bytes,
+                                void* stream) {
+  int rc = moe_decode_stack_check(x_in, T, H, F, E, k, L, w_router, slot_table, pool, record_bytes, qfmt, x_out,
+                                  x_hist);
+  if (rc) return rc;
   const size_t need = moe_ws_decode_stack(T, k, E, H, F, qfmt);
   MOE_REQUIRE(ws && ws_bytes >= need && moe_aligned(ws, 256), MOE_EWORKSPACE,
               "ws needs %zu bytes, 256-byte aligned", need);
-  hipStream_t st = moe_stream(stream);
+  return moe_decode_stack_run(x_in, T, H, F, E, k, L, w_router, bias, slot_table, pool, record_bytes, qfmt, x_out,
+                              topk_idx_out, topk_w_out, x_hist, ws, ws_bytes, moe_stream(stream));
+}
+
+int moe_decode_stack_run(const float* x_in, int T, int H, int F, int E, int k, int L, const uint16_t* w_router,
+                         const float* bias, const int32_t* slot_table, const void* pool, int64_t record_bytes,
+                         int qfmt, float* x_out, int32_t* topk_idx_out, float* topk_w_out, float* x_hist, void* ws,
+                         size_t ws_bytes, hipStream_t st) {
+  int rc = MOE_OK;
   if (use_persistent(T, k, E, H, F, qfmt))
     return moe_launch_decode_persistent(x_in, T, H, F, E, k, L, w_router, bias, slot_table, pool, record_bytes, qfmt,
                                         x_out, topk_idx_out, topk_w_out, x_hist, ws, ws_bytes, st);

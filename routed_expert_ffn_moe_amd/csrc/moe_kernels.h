@@ -24,3 +24,13 @@ int moe_launch_decode_persistent(const float* x_in, int T, int H, int F, int E, 
 
 // Workspace of moe_decode_stack: enough for whichever path it takes.
 size_t moe_ws_decode_stack(int T, int k, int E, int H, int F, int qfmt);
+
+// moe_decode_stack's argument checks (everything but the workspace) and its
+// body once the workspace is known to be large enough.
+int moe_decode_stack_check(const float* x_in, int T, int H, int F, int E, int k, int L, const uint16_t* w_router,
+                           const int32_t* slot_table, const void* pool, int64_t record_bytes, int qfmt,
+                           const float* x_out, const float* x_hist);
+int moe_decode_stack_run(const float* x_in, int T, int H, int F, int E, int k, int L, const uint16_t* w_router,
+                         const float* bias, const int32_t* slot_table, const void* pool, int64_t record_bytes,
+                         int qfmt, float* x_out, int32_t* topk_idx_out, float* topk_w_out, float* x_hist, void* ws,
+                         size_t ws_bytes, hipStream_t st);

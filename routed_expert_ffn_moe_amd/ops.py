@@ -18,9 +18,9 @@ from ._lib import (MOE_BF16, MOE_F32, MOE_OP_DECODE_STACK, MOE_OP_EXPERT_GEMV_Q,
 __all__ = [
     "moe_abi_version", "moe_record_bytes", "moe_workspace_size", "workspace", "moe_route_topk", "moe_permute",
     "moe_expert_gemv_q", "moe_grouped_gemm_q", "moe_combine", "moe_usage_update", "moe_decode_stack",
-    "moe_tier_fill", "moe_tier_rebalance", "moe_usage_update_stack",
+    "moe_tier_fill", "moe_tier_rebalance", "moe_usage_update_stack", "moe_decode_stack_noalloc",
     "MOE_Q4_B32", "MOE_Q2_B16", "MoeError", "MOE_OP_ROUTE_TOPK", "MOE_OP_PERMUTE", "MOE_OP_EXPERT_GEMV_Q",
-    "MOE_OP_GROUPED_GEMM_Q", "MOE_OP_DECODE_STACK",
+    "MOE_OP_GROUPED_GEMM_Q", "MOE_OP_DECODE_STACK", "validate_routing", "validate_slot_table", "validate_rows",
 ]
 
 
@@ -264,4 +264,21 @@ def moe_decode_stack(x_in, F, E, k, w_router, bias, slot_table, pool, record_byt
     check(_lib.load().moe_decode_stack(_p(x_in), T, H, F, E, k, L, _p(w_router), _p(bias), _p(slot_table), _p(pool),
                                        record_bytes, qfmt, _p(x_out), _p(topk_idx_out), _p(topk_w_out), _p(x_hist),
                                        _p(ws), ws.numel(), _stream(stream)))
+    return x_out
+
+
+def moe_decode_stack_noalloc(x_in, F, E, k, w_router, bias, slot_table, pool, record_bytes, qfmt, x_out=None,
+                             topk_idx_out=None, topk_w_out=None, x_hist=None, stream=None):
+    """moe_decode_stack on the library's own per-device scratch (no workspace
+    argument; the C entry point allocates nothing).  Pass x_out to keep this
+    call free of torch allocations too."""
+    T, H = x_in.shape
+    L = w_router.shape[0]
+    x_out = torch.empty_like(x_in) if x_out is None else x_out
+    _dev(x_in, w_router, bias, slot_table, pool, x_out, topk_idx_out, topk_w_out, x_hist)
+    if _validating():
+        validate_slot_table(slot_table, _pool_slots(pool, record_bytes))
+    check(_lib.load().moe_decode_stack_noalloc(_p(x_in), T, H, F, E, k, L, _p(w_router), _p(bias), _p(slot_table),
+                                               _p(pool), record_bytes, qfmt, _p(x_out), _p(topk_idx_out),
+                                               _p(topk_w_out), _p(x_hist), _stream(stream)))
     return x_out

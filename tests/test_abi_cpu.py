@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -238,3 +238,18 @@ def test_binding_validates_before_launching(monkeypatch):
     ops.validate_rows(torch.tensor([0, 1, 2]), torch.tensor([1, 0]), 1, 2)
     with pytest.raises(ops.MoeError):
         ops.validate_rows(torch.tensor([0, 1, 2]), torch.tensor([1, 1]), 1, 2)
+
+
+def test_noalloc_checks_arguments_before_any_device_call(lib):
+    """The no-alloc decode step validates its arguments like moe_decode_stack
+    before it looks up a device; with valid ones and no GPU it stops at the
+    device lookup with MOE_EHIP."""
+    R = lib.moe_record_bytes(0, 2048, 768)
+    args = [FAKE, 1, 2048, 768, 512, 10, 48, FAKE, None, FAKE, FAKE, R, 0, FAKE + 0x1000, None, None, None, None]
+    bad = list(args)
+    bad[1] = 9  # T > MOE_MAX_DECODE_T
+    assert lib.moe_decode_stack_noalloc(*bad) == _lib.MOE_ESHAPE
+    bad = list(args)
+    bad[13] = FAKE  # x_out aliases x_in
+    assert lib.moe_decode_stack_noalloc(*bad) == _lib.MOE_EINVAL
+    assert lib.moe_decode_stack_noalloc(*args) == _lib.MOE_EHIP and "no-alloc" in _err(lib)
