@@ -68,8 +68,8 @@ static PtLayout pt_layout(int T, int k, int E, int H, int F, int qfmt, int G) {
   P.prep_bytes = moe_prep_bytes(H, qfmt);
   P.hdr = 0;
   P.xbuf = 256;
-  P.lbuf = P.xbuf + moe_ws_up((size_t)T * H * 8);
-  P.pbuf = P.lbuf + moe_ws_up((size_t)T * E * 8);
+  P.lbuf = P.xbuf + moe_ws_up((size_t)PT_REPL * T * H * 8);  // one copy of x per XCD
+  P.pbuf = P.lbuf + moe_ws_up((size_t)PT_REPL * T * E * 8);  // one copy of the logits per XCD
   P.total = P.pbuf + moe_ws_up((size_t)G * T * H * 8);  // one partial vector per (workgroup, token)
   P.lds = pt_lds(qfmt, T, k, E, H, P.prep_bytes).total;
   return P;
