@@ -142,6 +142,15 @@ bool moe_persistent_supported(int T, int k, int E, int H, int F, int qfmt) {
   return P.lds <= pt_lds_limit() && H <= 2048 && H % 256 == 0 && T * k <= 64;
 }
 
+#ifdef MOE_PT_STAMPS
+// the phase timestamps of the last step (instrumented builds only)
+static unsigned long long* g_stamps = nullptr;
+extern "C" int moe_pt_read_stamps(void* dst) {
+  if (!g_stamps) return -1;
+  return (int)hipMemcpy(dst, g_stamps, sizeof(unsigned long long) * 64 * 256 * 16, hipMemcpyDeviceToHost);
+}
+#endif
+
 int moe_launch_decode_persistent(const float* x_in, int T, int H, int F, int E, int k, int L,
                                  const uint16_t* w_router, const float* bias, const int32_t* slot_table,
                                  const void* pool, int64_t record_bytes, int qfmt, float* x_out,
@@ -155,6 +164,11 @@ int moe_launch_decode_persistent(const float* x_in, int T, int H, int F, int E, 
   a.w_router = w_router; a.bias = bias; a.slot_table = slot_table; a.pool = (const uint8_t*)pool;
   a.record_bytes = record_bytes; a.x_out = x_out; a.topk_idx_out = topk_idx_out; a.topk_w_out = topk_w_out;
   a.x_hist = x_hist; a.hdr = (uint32_t*)(w + P.hdr); a.xbuf = (u64*)(w + P.xbuf); a.lbuf = (u64*)(w + P.lbuf);
+  a.stamps = nullptr;
+#ifdef MOE_PT_STAMPS
+  if (!g_stamps && hipMalloc(&g_stamps, sizeof(unsigned long long) * 64 * 256 * 16) != hipSuccess) g_stamps = nullptr;
+  a.stamps = g_stamps;
+#endif
   a.pbuf = (u64*)(w + P.pbuf); a.G = G; a.nfs = P.nfs; a.rpw = P.rpw; a.prep_bytes = P.prep_bytes;
   {  // threads per output row in the final sum: a power of two <= 32 (with 256
      // workgroups, 8 partials a thread: one load each of the NQ in flight;

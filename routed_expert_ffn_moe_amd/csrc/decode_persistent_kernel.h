@@ -68,7 +68,24 @@ struct PtArgs {
   u64* pbuf;      // [(unit * T + i)][H]
   int G, nfs, rpw, tpo;
   size_t prep_bytes;
+  unsigned long long* stamps;  // phase timestamps (builds with MOE_PT_STAMPS only), else unused
 };
+
+// Phase timestamps for performance analysis: with MOE_PT_STAMPS defined,
+// thread 0 of each workgroup records the 100 MHz wall clock at the phase
+// boundaries of layers < 64 into stamps[(layer * 256 + workgroup) * 16 + i];
+// otherwise the macro is empty.
+#ifdef MOE_PT_STAMPS
+#define PT_STAMP(i)                                                                                 \
+  do {                                                                                              \
+    if (threadIdx.x == 0 && l < 64 && a.stamps)                                                     \
+      a.stamps[((size_t)l * 256 + blockIdx.x) * 16 + (i)] = __builtin_amdgcn_s_memrealtime();        \
+  } while (0)
+#else
+#define PT_STAMP(i) \
+  do {              \
+  } while (0)
+#endif
 
 __device__ __forceinline__ void pt_put(u64* p, uint32_t tag, float v) {
   __hip_atomic_store(p, ((u64)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -102,13 +119,49 @@ __device__ __forceinline__ int pt_tid() {
 }
 __device__ __forceinline__ int pt_lane() { return pt_tid() & 63; }
 
-// Polling: each thread reloads its own not-yet-tagged words until they all
-// carry the tag, with no sleep and no workgroup barrier between rounds; one
-// barrier follows.  In an exchange microbenchmark (256 workgroups, one per
+// Polling: each thread reloads its own words until they all carry the tag,
+// with no sleep and no workgroup barrier between rounds; one barrier
+// follows.  In an exchange microbenchmark (256 workgroups, one per
 // CU) this took an all-to-all hand-off from 2.9 to 2.1 us (x, 2,048 words),
 // 2.5 to 2.3 us (logits, 512 words) and 4.3 to 3.4-3.6 us (partial sums,
 // 8 rows of 256 producers) against polling in lock-step with a barrier per
 // round; a sleep between rounds only delayed the detection.
+// Polls words base[off + tid + PT_THREADS q] (q < NQ, indices past `last`
+// clamped to it) until every one carries `tag`; w receives them.  SPARSE:
+// reload only the words still missing (fewer loads per round, but the
+// per-word state costs registers), else reload all of them each round.
+// Returns false on timeout.  Per thread, no barrier.
+template <int NQ, bool SPARSE>
+__device__ __forceinline__ bool pt_poll(u64 (&w)[NQ], u64* base, uint32_t off, int tid, int last, uint32_t tag) {
+  if (SPARSE) {
+    bool need[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) need[q] = true;
+    for (int it = 0;; ++it) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        if (need[q]) w[q] = pt_load(base, off + (uint32_t)min(tid + q * PT_THREADS, last));
+      bool any = false;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        need[q] = need[q] && (uint32_t)(w[q] >> 32) != tag;
+        any |= need[q];
+      }
+      if (!any) return true;
+      if (it > PT_SPIN_MAX) return false;
+    }
+  }
+  for (int it = 0;; ++it) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) w[q] = pt_load(base, off + (uint32_t)min(tid + q * PT_THREADS, last));
+    bool mine = true;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) mine &= (uint32_t)(w[q] >> 32) == tag;
+    if (mine) return true;
+    if (it > PT_SPIN_MAX) return false;
+  }
+}
+
 // tag of layer l of the call whose tags start after `base`
 __device__ __forceinline__ uint32_t pt_tag(uint32_t base, int l) { return base + (uint32_t)l + 1u; }
 
@@ -505,7 +558,7 @@ __device__ __forceinline__ void pt_prep_word(const float* v, float scale, bool v
 // ---------------------------------------------------------------- LDS layout
 // Section offsets (bytes, 16-byte aligned) shared by the kernel and the host.
 struct PtLds {
-  size_t xs, xprep, lg, topi, topw, p_exp, p_ntok, p_tok, p_j, p_roff, p_cum, p_misc, red, hp, hc, slots, total;
+  size_t xs, xprep, lg, topi, topw, p_exp, p_ntok, p_tok, p_j, p_roff, p_cum, p_misc, red, hp, hc, slots, ss, total;
 };
 #define PT_PB_MAX 5    // pieces per batch: 4 of row slot A, 1 of row slot B
 #define PT_SLOTS 80    // gate/up row slots per batch (16 per piece)
@@ -540,6 +593,7 @@ __host__ __device__ inline PtLds pt_lds(int qfmt, int T, int k, int E, int H, si
   o.hp = take((size_t)PT_PB_MAX * ts * 4 * 4);         // [piece][token slot][4] prepared h words
   o.hc = take((size_t)PT_PB_MAX * ts * 8);             // [piece][token slot] corrections
   o.slots = take((size_t)(E + 1) * 4);
+  o.ss = take((size_t)PT_WAVES * 8 * 4);  // [wave][token slot] sums of squares
   o.total = off;
   return o;
 }
@@ -574,6 +628,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
   uint32_t* hp = (uint32_t*)(smem + o.hp);    // [piece][MT][4]
   float2* hc = (float2*)(smem + o.hc);        // [piece][MT]
   int* lslots = (int*)(smem + o.slots);        // [E+1] this layer's slot-table row
+  float* ssred = (float*)(smem + o.ss);        // [wave][MT] per-wave sums of squares of x_l
 
   const uint32_t base = __hip_atomic_load(a.hdr + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   bool ok = true;
@@ -586,6 +641,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     asm volatile("" : "+v"(tid));
     lane = tid & 63;
     const uint32_t tag = pt_tag(base, l);
+    PT_STAMP(0);
     // ------------------------------------------------------------ phase A
     // this wave's router row (if any) is requested before waiting for x_l
     // (indices are clamped into range so that every load is unconditional)
@@ -663,44 +719,53 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
       }
     }
     constexpr int NX = 4 * MT;  // words of x per thread: T * H <= 512 * NX
-    if (l == 0) {
-      for (int i = tid; i < T * H; i += PT_THREADS) xs[i] = a.x_in[i];
-    } else {
-      const uint32_t ptag = pt_tag(base, l - 1);
+    // x_l into LDS.  One token: each thread also sums the squares of its
+    // words (word tid + 512 q in order, then the wave's butterfly), so 1/rms
+    // needs no second pass over x.
+    float ssq[1] = {0.f};
+    {
       const int last = T * H - 1;
-      const uint32_t xoff = (uint32_t)(pt_xcc() * T * H);
-      // each thread polls its own words until they carry the tag, reloading
-      // only the ones not yet there (no workgroup barrier per polling round)
       u64 w[NX];
-      bool need[NX];
-#pragma unroll
-      for (int q = 0; q < NX; ++q) need[q] = tid + q * PT_THREADS <= last;
-      for (int it = 0;; ++it) {
+      if (l == 0) {
 #pragma unroll
         for (int q = 0; q < NX; ++q)
-          if (need[q]) w[q] = pt_load(a.xbuf, xoff + (uint32_t)(tid + q * PT_THREADS));
-        bool any = false;
-#pragma unroll
-        for (int q = 0; q < NX; ++q) {
-          need[q] = need[q] && (uint32_t)(w[q] >> 32) != ptag;
-          any |= need[q];
-        }
-        if (!any) break;
-        if (it > PT_SPIN_MAX) { ok = false; break; }
+          w[q] = (u64)__float_as_uint(a.x_in[min(tid + q * PT_THREADS, last)]);
+      } else {
+        const uint32_t ptag = pt_tag(base, l - 1);
+        const uint32_t xoff = (uint32_t)(pt_xcc() * T * H);
+        // each thread polls its own words until they all carry the tag (no
+        // workgroup barrier per polling round); pt_poll reloads only the words
+        // still missing where registers allow it (one token)
+        ok = pt_poll<NX, MT == 1>(w, a.xbuf, xoff, tid, last, ptag);
       }
 #pragma unroll
-      for (int q = 0; q < NX; ++q)
-        if (tid + q * PT_THREADS <= last) xs[tid + q * PT_THREADS] = __uint_as_float((uint32_t)w[q]);
+      for (int q = 0; q < NX; ++q) {
+        const int i = tid + q * PT_THREADS;
+        if (i <= last) {
+          const float v = __uint_as_float((uint32_t)w[q]);
+          xs[i] = v;
+          if (MT == 1) ssq[0] = fmaf(v, v, ssq[0]);
+        }
+      }
+      if (MT == 1) {
+        const float v = moe_wave_sum(ssq[0]);
+        if (lane == 0) ssred[wave] = v;
+      }
       if (!__syncthreads_and(ok)) { ok = false; break; }
     }
-    __syncthreads();
-    // 1 / rms of every token, taken by every wave for itself (no barrier): lane
-    // l sums the squares of its 8-value chunks 512 c + 8 l, then the wave sums
+    PT_STAMP(1);  // x_l received
+    // 1 / rms of every token.  One token: the 8 waves' sums of squares in
+    // order.  More tokens (whose words a thread does not sort by token
+    // cheaply): every wave for itself, lane l summing the squares of its
+    // 8-value chunks 512 c + 8 l, then the wave's butterfly.
     float invr[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       float ss = 0.f;
-      if (t < T) {
+      if (MT == 1) {
+#pragma unroll
+        for (int w8 = 0; w8 < PT_WAVES; ++w8) ss += ssred[w8];
+      } else if (t < T) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int h0 = 512 * c + 8 * lane;
@@ -711,10 +776,11 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
             ss = fmaf(v1.x, v1.x, ss); ss = fmaf(v1.y, v1.y, ss); ss = fmaf(v1.z, v1.z, ss); ss = fmaf(v1.w, v1.w, ss);
           }
         }
+        ss = moe_wave_sum(ss);
       }
-      ss = moe_wave_sum(ss);
       invr[t] = 1.0f / sqrtf(ss / (float)H + PT_EPS);
     }
+    PT_STAMP(10);  // 1/rms
     if (a.x_hist && g == 0)
       for (int i = tid; i < T * H; i += PT_THREADS) a.x_hist[(size_t)l * T * H + i] = xs[i];
     // router rows: the prefetched one, then any further rows of this wave
@@ -756,6 +822,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         }
       }
     }
+    PT_STAMP(11);  // router rows published
     // prepared xn for the gate/up dot products: one 8-value word per thread
     {
       const int nwords = T * H / 8;
@@ -772,33 +839,20 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
                            (float2*)(out + 2 * (size_t)H) + b, sub);
       }
     }
+    PT_STAMP(2);  // x prepared
     // ------------------------------------------------------------ phase B
     {
       constexpr int NLG = MT * SLOTS / 8 > 0 ? MT * SLOTS / 8 : 1;  // T * E <= 512 * NLG
       const int last = T * E - 1;
       const uint32_t loff = (uint32_t)(pt_xcc() * T * E);
       u64 w[NLG];
-      bool need[NLG];
-#pragma unroll
-      for (int q = 0; q < NLG; ++q) need[q] = tid + q * PT_THREADS <= last;
-      for (int it = 0;; ++it) {
-#pragma unroll
-        for (int q = 0; q < NLG; ++q)
-          if (need[q]) w[q] = pt_load(a.lbuf, loff + (uint32_t)(tid + q * PT_THREADS));
-        bool any = false;
-#pragma unroll
-        for (int q = 0; q < NLG; ++q) {
-          need[q] = need[q] && (uint32_t)(w[q] >> 32) != tag;
-          any |= need[q];
-        }
-        if (!any) break;
-        if (it > PT_SPIN_MAX) { ok = false; break; }
-      }
+      ok = pt_poll<NLG, MT == 1>(w, a.lbuf, loff, tid, last, tag);
 #pragma unroll
       for (int q = 0; q < NLG; ++q)
         if (tid + q * PT_THREADS <= last) lg[tid + q * PT_THREADS] = __uint_as_float((uint32_t)w[q]);
     }
     if (!__syncthreads_and(ok)) { ok = false; break; }
+    PT_STAMP(3);  // logits received
 #pragma unroll
     for (int c = 0; c < 3; ++c)
       if (tid + PT_THREADS * c <= E) lslots[tid + PT_THREADS * c] = srow[c];
@@ -809,6 +863,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
       if (MT > 1) pt_topk_weights(my_key, k, topw + wave * k);
     }
     __syncthreads();
+    PT_STAMP(4);  // top-k done
     // With one token, unit u < k is top-k choice u and unit k the shared
     // expert: no plan, and the weights are taken once this workgroup's weight
     // loads are in flight (below).  With more tokens: the plan (wave 0).
@@ -1040,6 +1095,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         uint32_t gsN[4];
         if (MT > 1) load_gu(min(gi + 1, gi1 - 1), gqN, gsN);
         __syncthreads();
+        PT_STAMP(5);  // gate/up dots done
         // ---- h = silu(gate) * up, 8 threads per (piece, token slot), then the
         // prepared word of the 8 h values for the down dots
         {
@@ -1088,6 +1144,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
           }
         }
         __syncthreads();
+        PT_STAMP(6);  // SiLU done
         // ---- down dots: rows tid + 512 c, the group's 4 pieces
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
@@ -1132,6 +1189,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
           }
         }
         __syncthreads();  // red, hp, hc are reused by the next batch
+        PT_STAMP(7);  // group done
         if (MT > 1) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -1169,9 +1227,9 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
       const int nout = T * a.rpw;
       const int tpo = a.tpo;
       constexpr int NQ = MT == 1 ? 8 : MT == 2 ? 12 : MT <= 4 ? 24 : 32;
-      // each thread polls its NQ partial words until they carry the tag,
-      // reloading only the missing ones (no workgroup barrier per round, no
-      // per-producer sentinel pass), then sums them in a fixed order
+      // each thread polls its NQ partial words until they all carry the tag
+      // (no workgroup barrier per round, no per-producer sentinel pass),
+      // then sums them in a fixed order
       for (int ob = 0; ob < nout; ob += PT_THREADS / tpo) {
         const int oo = ob + tid / tpo, sub = tid % tpo;
         const bool act = oo < nout;
@@ -1179,20 +1237,20 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         float sum = 0.f;
         for (int p0 = sub; p0 < G && ok; p0 += tpo * NQ) {
           u64 w[NQ];
-          bool need[NQ];
+          bool need[NQ];  // (one token: reload only the missing words)
 #pragma unroll
           for (int qq = 0; qq < NQ; ++qq) need[qq] = act && p0 + tpo * qq < G;
           for (int it = 0;; ++it) {
+            bool mine = true;
 #pragma unroll
             for (int qq = 0; qq < NQ; ++qq)
-              if (need[qq]) w[qq] = pt_load(a.pbuf, (uint32_t)(((p0 + tpo * qq) * T + t) * H + rr));
-            bool any = false;
+              if (MT > 1 || need[qq]) w[qq] = pt_load(a.pbuf, (uint32_t)((min(p0 + tpo * qq, G - 1) * T + t) * H + rr));
 #pragma unroll
             for (int qq = 0; qq < NQ; ++qq) {
-              need[qq] = need[qq] && (uint32_t)(w[qq] >> 32) != tag;
-              any |= need[qq];
+              if (MT == 1) need[qq] = need[qq] && (uint32_t)(w[qq] >> 32) != tag;
+              mine &= !(act && p0 + tpo * qq < G) || (uint32_t)(w[qq] >> 32) == tag;
             }
-            if (!any) break;
+            if (mine) break;
             if (it > PT_SPIN_MAX) { ok = false; break; }
           }
 #pragma unroll
@@ -1200,6 +1258,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
             if (act && p0 + tpo * qq < G) sum += __uint_as_float((uint32_t)w[qq]);
         }
         if (!__syncthreads_and(ok)) { ok = false; break; }
+        PT_STAMP(8);  // partial sums received
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1)
           if (m < tpo) sum += __shfl_xor(sum, m, 64);
@@ -1217,6 +1276,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
       if (!ok) break;
     }
     __syncthreads();
+    PT_STAMP(9);  // layer done
   }
   if (!ok) {
     // the error word: the next call's set-up kernel then zeroes the tagged
