@@ -652,12 +652,19 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     for (int c = 0; c < 3; ++c)
       srow[c] = a.slot_table[(size_t)l * (E + 1) + min(tid + PT_THREADS * c, E)];
     const uint16_t* wr = a.w_router + (size_t)l * E * H;  // wave-uniform; 32-bit offsets below
-    const int e_row = g + G * wave;
+    // Router work of this workgroup: its rows e = g + G r (nrow of them) for
+    // each of the T tokens, as items i = t * nrow + r spread over the waves
+    // (wave w takes items w, w + 8, ...); each item is one token's dot
+    // product with one row.  The row of the wave's first item is requested
+    // here, before waiting for x_l.
+    const int nrow = (E - g + G - 1) / G;
+    const int nitem = T * nrow;
+    const int e_row = g + G * (wave % nrow);
     // its routing bias too (a load issued only after the dot product would
     // put a memory round trip between x's arrival and the published logit)
     const float b_row = a.bias ? a.bias[(size_t)l * E + min(e_row, E - 1)] : 0.f;
     uint4 rw[4];
-    if (e_row < E) {  // wave-uniform
+    if (wave < nitem) {  // wave-uniform
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const uint32_t h0 = 512 * c + 8 * lane;
@@ -754,72 +761,70 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
       if (!__syncthreads_and(ok)) { ok = false; break; }
     }
     PT_STAMP(1);  // x_l received
-    // 1 / rms of every token.  One token: the 8 waves' sums of squares in
-    // order.  More tokens (whose words a thread does not sort by token
-    // cheaply): every wave for itself, lane l summing the squares of its
-    // 8-value chunks 512 c + 8 l, then the wave's butterfly.
+    // 1 / rms of every token: thread tid sums the squares of the token's
+    // words tid + 512 q in order, the wave adds its threads (butterfly), and
+    // the 8 waves' sums are added in order.  One token: from the polled words
+    // above (no second pass); more tokens: from LDS, one more barrier.  The
+    // order is the same for every token count, so a token's 1/rms does not
+    // depend on the window it is verified in.
+    if (MT > 1) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        float ss = 0.f;
+        if (t < T)
+          for (int h = tid; h < H; h += PT_THREADS) ss = fmaf(xs[t * H + h], xs[t * H + h], ss);
+        ss = moe_wave_sum(ss);
+        if (lane == 0) ssred[wave * MT + t] = ss;
+      }
+      __syncthreads();
+    }
     float invr[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       float ss = 0.f;
-      if (MT == 1) {
 #pragma unroll
-        for (int w8 = 0; w8 < PT_WAVES; ++w8) ss += ssred[w8];
-      } else if (t < T) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int h0 = 512 * c + 8 * lane;
-          if (h0 < H) {
-            const float4 v0 = *reinterpret_cast<const float4*>(xs + t * H + h0);
-            const float4 v1 = *reinterpret_cast<const float4*>(xs + t * H + h0 + 4);
-            ss = fmaf(v0.x, v0.x, ss); ss = fmaf(v0.y, v0.y, ss); ss = fmaf(v0.z, v0.z, ss); ss = fmaf(v0.w, v0.w, ss);
-            ss = fmaf(v1.x, v1.x, ss); ss = fmaf(v1.y, v1.y, ss); ss = fmaf(v1.z, v1.z, ss); ss = fmaf(v1.w, v1.w, ss);
-          }
-        }
-        ss = moe_wave_sum(ss);
-      }
+      for (int w8 = 0; w8 < PT_WAVES; ++w8) ss += ssred[w8 * MT + t];
       invr[t] = 1.0f / sqrtf(ss / (float)H + PT_EPS);
     }
     PT_STAMP(10);  // 1/rms
     if (a.x_hist && g == 0)
       for (int i = tid; i < T * H; i += PT_THREADS) a.x_hist[(size_t)l * T * H + i] = xs[i];
-    // router rows: the prefetched one, then any further rows of this wave
-    for (int e = e_row; e < E; e += G * PT_WAVES) {
-      if (e != e_row) {
+    // router items of this wave: the prefetched row first, another row only
+    // when an item needs one (a wave keeps one row when nrow divides 8)
+    {
+      int e_cur = e_row;
+      float b_cur = b_row;
+      for (int i = wave; i < nitem; i += PT_WAVES) {
+        const int t = i / nrow, e = g + G * (i % nrow);
+        if (e != e_cur) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t h0 = 512 * c + 8 * lane;
+            rw[c] = *reinterpret_cast<const uint4*>(wr + (uint32_t)e * (uint32_t)H + (h0 < (uint32_t)H ? h0 : 0u));
+          }
+          b_cur = a.bias ? a.bias[(size_t)l * E + e] : 0.f;
+          e_cur = e;
+        }
+        const float* xt = xs + (size_t)t * H;
+        float acc = 0.f;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const uint32_t h0 = 512 * c + 8 * lane;
-          rw[c] = *reinterpret_cast<const uint4*>(wr + (uint32_t)e * (uint32_t)H + (h0 < (uint32_t)H ? h0 : 0u));
-        }
-      }
-      float acc[MT];
+          const int h0 = 512 * c + 8 * lane;
+          if (c < nrch && h0 < H) {
+            const uint32_t ww[4] = {rw[c].x, rw[c].y, rw[c].z, rw[c].w};
 #pragma unroll
-      for (int t = 0; t < MT; ++t) acc[t] = 0.f;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int h0 = 512 * c + 8 * lane;
-        if (c < nrch && h0 < H) {
-          const uint32_t ww[4] = {rw[c].x, rw[c].y, rw[c].z, rw[c].w};
-#pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            if (t < T) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {  // the 4 words (8 bf16) of the chunk
-                acc[t] = fmaf(xs[t * H + h0 + 2 * i], __uint_as_float(ww[i] << 16), acc[t]);
-                acc[t] = fmaf(xs[t * H + h0 + 2 * i + 1], __uint_as_float(ww[i] & 0xffff0000u), acc[t]);
-              }
+            for (int q = 0; q < 4; ++q) {  // the 4 words (8 bf16) of the chunk
+              acc = fmaf(xt[h0 + 2 * q], __uint_as_float(ww[q] << 16), acc);
+              acc = fmaf(xt[h0 + 2 * q + 1], __uint_as_float(ww[q] & 0xffff0000u), acc);
             }
           }
         }
-      }
-      const float b = e == e_row ? b_row : a.bias ? a.bias[(size_t)l * E + e] : 0.f;
+        float it = invr[0];
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        if (t < T) {
-          const float s = moe_wave_sum(acc[t]);
-          if (lane < PT_REPL)  // lane r writes the copy of XCD r
-            pt_put(pt_at(a.lbuf, (uint32_t)((lane * T + t) * E + e)), tag, s * invr[t] + b);
-        }
+        for (int q = 1; q < MT; ++q) it = t == q ? invr[q] : it;
+        const float sdot = moe_wave_sum(acc);
+        if (lane < PT_REPL)  // lane r writes the copy of XCD r
+          pt_put(pt_at(a.lbuf, (uint32_t)((lane * T + t) * E + e)), tag, sdot * it + b_cur);
       }
     }
     PT_STAMP(11);  // router rows published
