@@ -13,9 +13,14 @@ tokens per step) and one 8,192-token prefill chunk through one layer (route,
 permute, grouped GEMM on the matrix cores, combine).  On request:
   --sweep  verify windows of 1..8 token positions at top-10, and top-6;
   --int2   the int2 stack: decode at 1 and 4 tokens, a 16,384-token chunk;
-  --tier   a hot tier of 4,096 expert slots: hit rate on a synthetic trace.
+  --tier   a hot tier of 4,096 expert slots: hit rate on a synthetic trace;
+  --c2     one decode layer timed on its own, rotated over the 48 layers;
+  --ceilings  the device's practical HBM read and MFMA rates (probe kernels).
+The int2 run also takes one 16,384-token chunk through all 48 layers, with
+the usage update of every layer.  The CPU baseline times the oracle on the
+decode step and on a sample of the prefill chunk's expert groups.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--sweep] [--int2] [--tier]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--sweep] [--int2] [--tier] [--c2] [--ceilings]
 """
 import argparse
 import glob
@@ -95,6 +100,71 @@ def cpu_baseline(li, x_tok, budget_s):
             "cores_available": os.cpu_count(), "kind": "oracle",
             "sample": f"1 token through the first {n} of {li.L} layers (fp64 NumPy, records decoded per layer), "
                       f"{wall:.1f} s, scaled to {li.L} layers"}, np
+
+
+def host_info():
+    """The host the oracle runs on: CPU model, logical cores, BLAS library and threads."""
+    info = {"cpu_count": os.cpu_count()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        import threadpoolctl
+        info["blas"] = [{"api": d.get("internal_api"), "version": d.get("version"), "threads": d.get("num_threads")}
+                        for d in threadpoolctl.threadpool_info() if d.get("user_api") == "blas"]
+    except Exception as e:  # threadpoolctl missing or failing: say so
+        info["blas"] = f"unknown ({type(e).__name__})"
+    return info
+
+
+def prefill_cpu_baseline(li, x_bf16, idx, budget_s):
+    """The oracle on a sample of one prefill chunk through layer 0: the
+    routed experts' whole groups (in expert order, until half the budget is
+    used), the shared expert on 256 tokens and the router + top-k on 256
+    tokens, each timed and extrapolated to the chunk (every routed row, the
+    shared expert on every token, the router on every token)."""
+    import numpy as np
+    import oracle as O
+    T, k = idx.shape
+    E = li.E
+    S = li.S.cpu().numpy()
+    xf = x_bf16.detach().cpu().to(dtype=__import__("torch").float64).numpy()
+    ids = idx.detach().cpu().numpy()
+    c0 = os.times()
+    t_all = time.perf_counter()
+    get = O.expert_getter(LazyPool(li.pool), S, 0, li.qfmt, li.H, li.F, li.R)
+    rows_done, t_routed, n_exp = 0, 0.0, 0
+    t0 = time.perf_counter()
+    for e in range(E):
+        toks = np.nonzero((ids == e).any(axis=1))[0]
+        if toks.size:
+            O.expert_ffn(*get(e), xf[toks])
+            rows_done += toks.size
+            n_exp += 1
+        t_routed = time.perf_counter() - t0
+        if t_routed > budget_s / 2:
+            break
+    sample = np.arange(min(256, T))
+    t0 = time.perf_counter()
+    O.expert_ffn(*get(E), xf[sample])
+    t_shared = (time.perf_counter() - t0) / sample.size
+    Wr = O.bf16_to_f64(li.Wr[0].cpu().numpy())
+    t0 = time.perf_counter()
+    O.topk_select(O.router_logits(xf[sample], Wr), k)
+    t_router = (time.perf_counter() - t0) / sample.size
+    wall = time.perf_counter() - t_all
+    c1 = os.times()
+    est = t_routed / rows_done * (T * k) + (t_shared + t_router) * T
+    return {"value": round(T / est, 3), "unit": "tokens/s", "kind": "oracle",
+            "cores": round(((c1.user - c0.user) + (c1.system - c0.system)) / wall, 2),
+            "sample": f"{n_exp} whole expert groups ({rows_done:,} of {T * k:,} routed rows), the shared expert and "
+                      f"the router on {sample.size} tokens; {wall:.1f} s, extrapolated to the {T:,}-token chunk",
+            "est_s_per_chunk": round(est, 1)}
 
 
 def decode_bench(M, li, T, steps, warmup, use_graph, seed_tag, k=None):
@@ -266,6 +336,7 @@ def int2_bench(M, steps, warmup, use_graph):
                                "gbs": round(b / (ms / 1e3) / 1e9, 1),
                                "hbm_frac": round(b / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
     out["prefill_16k"] = prefill_bench(M, li, reps=5, warmup=2, T=16384, seed=4, use_bias=True)
+    out["prefill_16k_48_layers"] = prefill_stack_bench(M, li, T=16384, seed=4, reps=1)
     del li
     torch.cuda.empty_cache()
     return out
@@ -342,6 +413,114 @@ def prefill_bench(M, li, reps, warmup, T=8192, seed=3, use_bias=False):
     }
 
 
+def prefill_stack_bench(M, li, T, seed=4, reps=1):
+    """One T-token chunk through all li.L layers as a pre-norm residual chain:
+    per layer the norm (to bf16), route (with the routing bias), permute,
+    grouped GEMM, combine into the residual stream and the layer's usage
+    update (decay 0.99, top-96 re-rank after every 4th step).  The whole pass
+    is timed (median of reps after one untimed pass)."""
+    import torch
+    import gen as G
+    dev = li.pool.device
+    L, H, E, k, F = li.L, li.H, li.E, li.k, li.F
+    x0 = G.draw_x(seed, T, H, dev, tag="bench-prefill-stack")
+    x = torch.empty_like(x0)
+    xb = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    ws_r = M.workspace(M.MOE_OP_ROUTE_TOPK, dev, T=T, E=E)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_src = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv_row = torch.empty(T * k, dtype=torch.int32, device=dev)
+    ws_p = M.workspace(M.MOE_OP_PERMUTE, dev, T=T, k=k, E=E)
+    y_perm = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+    y_sh = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws_g = M.workspace(M.MOE_OP_GROUPED_GEMM_Q, dev, T, k, E, H, F, li.qfmt)
+    scores = torch.zeros((L, E), dtype=torch.float32, device=dev)
+    hits = torch.empty(E, dtype=torch.int32, device=dev)
+    top = torch.empty(96, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream()
+
+    def one_pass(step, ev=None):
+        x.copy_(x0)
+        if ev is not None:
+            ev[0].record(st)
+        for l in range(L):
+            M.moe_rmsnorm(x, out=xb)
+            M.moe_route_topk(xb, li.Wr[l], li.bias[l] if li.bias is not None else None, k, topk_idx=idx,
+                             topk_w=w, ws=ws_r)
+            M.moe_permute(idx, E, counts, offsets, row_src, inv_row, ws=ws_p)
+            M.moe_grouped_gemm_q(xb, row_src, offsets, k, E, F, li.S, l, li.pool, li.R, li.qfmt, y_perm=y_perm,
+                                 y_shared=y_sh, ws=ws_g)
+            M.moe_combine(y_perm, w, inv_row=inv_row, y_shared=y_sh, residual=x, y_out=x)
+            M.moe_usage_update(idx, l, L, E, 0.99, step, 4, 96, hits, scores, top)
+        if ev is not None:
+            ev[1].record(st)
+
+    one_pass(0)
+    torch.cuda.synchronize()
+    if not torch.isfinite(x).all():
+        raise RuntimeError("prefill stack produced non-finite values")
+    times = []
+    for r in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+        one_pass(r + 1, ev)
+        torch.cuda.synchronize()
+        times.append(ev[0].elapsed_time(ev[1]))
+    ms = sorted(times)[len(times) // 2]
+    flop = 2.0 * T * (k + 1) * 3 * H * F * L
+    return {"workload": f"{T:,}-token chunk through {L} layers ({'int4' if li.qfmt == 0 else 'int2'}, routing bias), "
+                        f"norm + route + permute + grouped GEMM + combine + usage update per layer",
+            "ms_chunk": round(ms, 3), "ms_per_layer": round(ms / L, 4), "tokens_per_s": round(T / (ms / 1e3), 1),
+            "expert_tflops_whole_pass": round(flop / (ms / 1e3) / 1e12, 1)}
+
+
+def single_layer_bench(M, li, reps=8):
+    """One decode layer on its own (T = 1): a one-layer persistent step on
+    layer l, rotated over all li.L layers so that consecutive calls read
+    different records (48 x 28.5 MB, well over the 256 MB memory-side cache);
+    the timed calls are one HIP graph."""
+    import torch
+    import gen as G
+    dev = li.pool.device
+    L, E, H, F, k = li.L, li.E, li.H, li.F, li.k
+    x = G.draw_x(1, 1, H, dev, tag="bench-c2")
+    xo = torch.empty_like(x)
+    ws = M.workspace(M.MOE_OP_DECODE_STACK, dev, 1, k, E, H, F, li.qfmt)
+    layers = [(li.Wr[l:l + 1], li.bias[l:l + 1], li.S[l:l + 1]) for l in range(L)]
+    idx = torch.empty((1, 1, k), dtype=torch.int32, device=dev)
+
+    def call(l):
+        Wr, b, S = layers[l]
+        M.moe_decode_stack(x, F, E, k, Wr, b, S, li.pool, li.R, li.qfmt, x_out=xo, topk_idx_out=idx, ws=ws)
+
+    for l in range(L):
+        call(l)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for r in range(reps):
+                for l in range(L):
+                    call(l)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * L)
+    b = 11 * li.R + E * H * 2 + 2 * H * 4
+    return {"workload": "one decode layer (1 token, top-10 + shared, int4), a one-layer persistent step per call, "
+                        f"rotated over {L} layers", "us_per_layer": round(us, 2), "bytes_per_layer": b,
+            "gbs": round(b / (us / 1e6) / 1e9, 1), "hbm_frac": round(b / (us / 1e6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -356,6 +535,9 @@ def main():
                     help="also emulate a hot tier of 4,096 expert slots (hit rate on a synthetic trace)")
     ap.add_argument("--int2", action="store_true",
                     help="also time the int2 stack: decode T = 1, 4 and a 16,384-token prefill chunk")
+    ap.add_argument("--c2", action="store_true", help="also time one decode layer on its own, rotated over the layers")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="also measure the practical HBM streaming-read and MFMA-only rates (probe kernels)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-ref-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (the reference kernel that scales "
@@ -439,6 +621,28 @@ def main():
         i2 = int2_bench(M, args.steps, args.warmup, not args.no_graph)
         log(f"int2: {json.dumps(i2)}")
         out.setdefault("extra", {})["int2_stack"] = i2
+    if args.c2:
+        c2 = single_layer_bench(M, li)
+        log(f"c2: {json.dumps(c2)}")
+        out.setdefault("extra", {})["single_layer_c2"] = c2
+    if args.ceilings:
+        from routed_expert_ffn_moe_amd import probes
+        ce = {"hbm_stream_read_gbs": round(probes.stream_read_gbs(device=dev), 1),
+              "mfma_f16_register_loop_tflops": round(probes.mfma_tflops(device=dev), 1)}
+        a16 = torch.randn((8192, 8192), device=dev, dtype=torch.float16)
+        b16 = torch.randn((8192, 8192), device=dev, dtype=torch.float16)
+        torch.matmul(a16, b16)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            torch.matmul(a16, b16)
+        e1.record()
+        torch.cuda.synchronize()
+        ce["library_fp16_gemm_8192_tflops"] = round(2 * 8192 ** 3 * 5 / (e0.elapsed_time(e1) / 1e3) / 1e12, 1)
+        del a16, b16
+        log(f"ceilings: {json.dumps(ce)}")
+        out.setdefault("extra", {})["ceilings"] = ce
     if args.tier:
         tb = tier_bench(M, li, min(args.steps, 64))
         log(f"tier: {json.dumps(tb)}")
@@ -446,8 +650,15 @@ def main():
     if not args.no_cpu_baseline:
         xs = G.draw_x(2, 1, H, dev, tag="bench-x")
         cb, _ = cpu_baseline(li, xs, args.cpu_budget)
+        cb["host"] = host_info()
         out["cpu_baseline"] = cb
         log(f"cpu baseline: {cb}")
+        if "extra" in out and "prefill_c4" in out["extra"]:
+            xp = G.draw_x(3, 8192, H, dev, tag="bench-prefill").to(torch.bfloat16)
+            idx_p, _ = M.moe_route_topk(xp, li.Wr[0].contiguous(), None, k)
+            pc = prefill_cpu_baseline(li, xp, idx_p, args.cpu_budget)
+            out["extra"]["prefill_c4"]["cpu_baseline"] = pc
+            log(f"prefill cpu baseline: {pc}")
     print(json.dumps(out), flush=True)
 
 

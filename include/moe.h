@@ -390,6 +390,17 @@ int moe_decode_stack(const float* x_in, int T, int H, int F, int E, int k,
                      void* ws, size_t ws_bytes, void* stream);
 
 /* --------------------------------------------------------------------------
+ * moe_rmsnorm -- the pre-norm of a stack of layers (see moe_decode_stack):
+ *   out[t][h] = x[t][h] / sqrt(mean_h(x[t]^2) + eps)   (unit gain)
+ * x fp32 [T][H]; out [T][H] in out_dtype: MOE_F32, or MOE_BF16 (each value
+ * rounded once, to nearest even) to feed a prefill chunk's moe_route_topk and
+ * moe_grouped_gemm_q.  Sums in fp32 in a fixed order.  out may not alias x.
+ * With moe_combine(..., residual = x, y_out = x) this chains a prefill chunk
+ * through the layers of a stack exactly as moe_decode_stack chains a decode
+ * step. */
+int moe_rmsnorm(const float* x, int T, int H, float eps, void* out, int out_dtype, void* stream);
+
+/* --------------------------------------------------------------------------
  * moe_decode_stack_noalloc -- moe_decode_stack (same arguments, same
  * results, same kernels) without a workspace argument, for callers that
  * cannot allocate device memory: code under HIP graph capture, tight

@@ -37,6 +37,13 @@ SIGNATURES = {
                               _sz, _vp]),
     "moe_decode_stack_noalloc": (_i, [_vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i64, _i, _vp, _vp, _vp,
                                       _vp, _vp]),
+    "moe_rmsnorm": (_i, [_vp, _i, _i, _f, _vp, _i, _vp]),
+    # measurement probes (include/moe_probes.h)
+    "moe_probe_stream_read": (_i, [_vp, _sz, _vp, _vp]),
+    "moe_probe_stream_read_blocks": (_i, []),
+    "moe_probe_mfma": (_i, [_i, _vp, _vp]),
+    "moe_probe_mfma_blocks": (_i, []),
+    "moe_probe_mfma_flops": (ctypes.c_double, [_i]),
     "moe_validate_routing": (_i, [_vp, _i, _i, _i]),
     "moe_validate_slot_table": (_i, [_vp, _i, _i, _i64]),
     "moe_validate_rows": (_i, [_vp, _vp, _vp, _i, _i, _i]),

@@ -37,22 +37,6 @@ static bool use_persistent(int T, int k, int E, int H, int F, int qfmt) {
   return moe_persistent_supported(T, k, E, H, F, qfmt) && moe_persistent_coresident(T, k, E, H, F, qfmt);
 }
 
-// xn[t] = x[t] / sqrt(mean(x[t]^2) + eps); one workgroup per token, fixed-order
-// fp32 reduction.
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int H, float eps,
-                                                      float* __restrict__ xn) {
-  __shared__ float part[4];
-  const float* xr = x + (size_t)blockIdx.x * H;
-  float s = 0.f;
-  for (int h = threadIdx.x; h < H; h += 256) s = fmaf(xr[h], xr[h], s);
-  s = moe_wave_sum(s);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
-  __syncthreads();
-  const float ms = ((part[0] + part[1]) + (part[2] + part[3])) / (float)H;
-  const float inv = 1.0f / sqrtf(ms + eps);
-  for (int h = threadIdx.x; h < H; h += 256) xn[(size_t)blockIdx.x * H + h] = xr[h] * inv;
-}
-
 int moe_decode_stack_check(const float* x_in, int T, int H, int F, int E, int k, int L, const uint16_t* w_router,
                            const int32_t* slot_table, const void* pool, int64_t record_bytes, int qfmt,
                            const float* x_out, const float* x_hist) {
@@ -105,7 +89,8 @@ int moe_decode_stack_run(const float* x_in, int T, int H, int F, int E, int k, i
     float* wt = topk_w_out ? topk_w_out + (size_t)l * T * k : (float*)(w + W.w);
     if (x_hist && hipMemcpyAsync(x_hist + (size_t)l * T * H, x_out, xbytes, hipMemcpyDeviceToDevice, st) != hipSuccess)
       return moe_fail(MOE_EHIP, "decode stack: copy to x_hist failed");
-    rmsnorm_kernel<<<T, 256, 0, st>>>(x_out, H, MOE_STACK_EPS, xn);
+    rc = moe_launch_rmsnorm(x_out, T, H, MOE_STACK_EPS, xn, MOE_F32, st);
+    if (rc) return rc;
     rc = moe_launch_route(xn, MOE_F32, T, H, w_router + (size_t)l * E * H, bias ? bias + (size_t)l * E : nullptr,
                           E, k, idx, wt, logits, st);
     if (rc) return rc;

@@ -34,3 +34,6 @@ int moe_decode_stack_run(const float* x_in, int T, int H, int F, int E, int k, i
                          const float* bias, const int32_t* slot_table, const void* pool, int64_t record_bytes,
                          int qfmt, float* x_out, int32_t* topk_idx_out, float* topk_w_out, float* x_hist, void* ws,
                          size_t ws_bytes, hipStream_t st);
+
+// The stack's pre-norm (rmsnorm.hip), fp32 or bf16 output.
+int moe_launch_rmsnorm(const float* x, int T, int H, float eps, void* out, int out_dtype, hipStream_t st);

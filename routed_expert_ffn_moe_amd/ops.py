@@ -18,7 +18,7 @@ from ._lib import (MOE_BF16, MOE_F32, MOE_OP_DECODE_STACK, MOE_OP_EXPERT_GEMV_Q,
 __all__ = [
     "moe_abi_version", "moe_record_bytes", "moe_workspace_size", "workspace", "moe_route_topk", "moe_permute",
     "moe_expert_gemv_q", "moe_grouped_gemm_q", "moe_combine", "moe_usage_update", "moe_decode_stack",
-    "moe_tier_fill", "moe_tier_rebalance", "moe_usage_update_stack", "moe_decode_stack_noalloc",
+    "moe_tier_fill", "moe_tier_rebalance", "moe_usage_update_stack", "moe_decode_stack_noalloc", "moe_rmsnorm",
     "MOE_Q4_B32", "MOE_Q2_B16", "MoeError", "MOE_OP_ROUTE_TOPK", "MOE_OP_PERMUTE", "MOE_OP_EXPERT_GEMV_Q",
     "MOE_OP_GROUPED_GEMM_Q", "MOE_OP_DECODE_STACK", "validate_routing", "validate_slot_table", "validate_rows",
 ]
@@ -282,3 +282,16 @@ def moe_decode_stack_noalloc(x_in, F, E, k, w_router, bias, slot_table, pool, re
                                                _p(pool), record_bytes, qfmt, _p(x_out), _p(topk_idx_out),
                                                _p(topk_w_out), _p(x_hist), _stream(stream)))
     return x_out
+
+
+def moe_rmsnorm(x, eps=1e-6, out=None, out_dtype=torch.bfloat16, stream=None):
+    """x fp32 [T][H] -> x / rms(x) in fp32 or bf16 (the stack's pre-norm)."""
+    T, H = x.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=x.device)
+    od = MOE_F32 if out.dtype == torch.float32 else MOE_BF16
+    if od == MOE_BF16:
+        _half_bits(out)
+    _dev(x, out)
+    check(_lib.load().moe_rmsnorm(_p(x), T, H, float(eps), _p(out), od, _stream(stream)))
+    return out

@@ -1,0 +1,50 @@
+"""Python side of the measurement probes (include/moe_probes.h): the device's
+practical HBM streaming-read rate and MFMA-only rate."""
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import check
+
+__all__ = ["stream_read_gbs", "mfma_tflops"]
+
+
+def _time(fn, reps):
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    fn()
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(reps):
+        fn()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / reps
+
+
+def stream_read_gbs(nbytes=4 << 30, reps=10, device="cuda"):
+    """GB/s of one read of nbytes (default 4 GiB, 16x the memory-side cache)."""
+    lib = _lib.load()
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device=device)
+    sink = torch.empty(lib.moe_probe_stream_read_blocks(), dtype=torch.int32, device=device)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def run():
+        check(lib.moe_probe_stream_read(ctypes.c_void_p(src.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), s))
+    t = _time(run, reps)
+    del src
+    return nbytes / t / 1e9
+
+
+def mfma_tflops(iters=20000, reps=5, device="cuda"):
+    """TFLOP/s of the register-only v_mfma_f32_32x32x16_f16 loop."""
+    lib = _lib.load()
+    sink = torch.empty(lib.moe_probe_mfma_blocks(), dtype=torch.float32, device=device)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def run():
+        check(lib.moe_probe_mfma(iters, ctypes.c_void_p(sink.data_ptr()), s))
+    t = _time(run, reps)
+    return lib.moe_probe_mfma_flops(iters) / t / 1e12

@@ -13,6 +13,7 @@ from routed_expert_ffn_moe_amd import _lib
 import gen as G
 
 HEADER = os.path.join(os.path.dirname(__file__), "..", "include", "moe.h")
+PROBES = os.path.join(os.path.dirname(__file__), "..", "include", "moe_probes.h")
 FAKE = 0x10000  # non-null, 256-byte aligned dummy "device" address (never dereferenced)
 
 
@@ -21,15 +22,15 @@ def lib():
     return _lib.load()
 
 
-def declared_functions():
-    txt = open(HEADER).read()
+def declared_functions(header=HEADER):
+    txt = open(header).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(moe_\w+)\s*\(", txt, flags=re.M)))
 
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -253,3 +254,21 @@ def test_noalloc_checks_arguments_before_any_device_call(lib):
     bad[13] = FAKE  # x_out aliases x_in
     assert lib.moe_decode_stack_noalloc(*bad) == _lib.MOE_EINVAL
     assert lib.moe_decode_stack_noalloc(*args) == _lib.MOE_EHIP and "no-alloc" in _err(lib)
+
+
+def test_rmsnorm_rejects(lib):
+    assert lib.moe_rmsnorm(FAKE, 4, 256, 1e-6, FAKE + 0x1000, 7, None) == _lib.MOE_EUNSUPPORTED
+    assert lib.moe_rmsnorm(FAKE, -1, 256, 1e-6, FAKE + 0x1000, 0, None) == _lib.MOE_ESHAPE
+    assert lib.moe_rmsnorm(FAKE, 4, 256, -1.0, FAKE + 0x1000, 0, None) == _lib.MOE_EINVAL
+    assert lib.moe_rmsnorm(FAKE, 4, 256, 1e-6, FAKE, 1, None) == _lib.MOE_EINVAL  # aliasing
+    assert lib.moe_rmsnorm(None, 0, 256, 1e-6, None, 1, None) == _lib.MOE_OK      # nothing to do
+
+
+def test_probe_header_symbols_are_exported(lib):
+    names = declared_functions(PROBES)
+    assert len(names) == 5, names
+    for n in names:
+        assert hasattr(lib, n) and n in _lib.SIGNATURES, n
+    assert lib.moe_probe_stream_read(None, 16, FAKE, None) == _lib.MOE_EINVAL
+    assert lib.moe_probe_stream_read(FAKE + 4, 16, FAKE, None) == _lib.MOE_EALIGN
+    assert lib.moe_probe_mfma(0, FAKE, None) == _lib.MOE_EINVAL

@@ -253,3 +253,61 @@ def test_grouped_gemm_int2_16k_whole_groups(moe):
     idx, w, counts, inv_row, y_perm, y_sh, y = _prefill_layer(moe, li, li.x)
     _, offsets, row_src, _, _ = moe.moe_permute(idx, E)
     _check_whole_groups(li, counts, offsets, row_src, y_perm, y_sh, k)
+
+
+# ---------------------------------------------------------------- pre-norm and the chained prefill chunk
+
+def test_rmsnorm_f32_and_bf16(moe):
+    """moe_rmsnorm against the oracle's rms_normalize: fp32 output within
+    fp32 rounding (1e-6 relative), bf16 output within one bf16 rounding of
+    the exact value: bf16 keeps 8 significant bits, so half an ulp is at most
+    2^-8 of the value (plus the fp32 arithmetic before the rounding)."""
+    g = torch.Generator().manual_seed(8)
+    x = (torch.randn((37, 2048), generator=g) * 3.0).cuda()
+    ref = O.rms_normalize(C.x_as_f64(x))
+    f32 = moe.moe_rmsnorm(x, out_dtype=torch.float32)
+    assert np.max(np.abs(_np(f32) - ref) / np.maximum(np.abs(ref), 1e-30)) <= 1e-6
+    b16 = moe.moe_rmsnorm(x, out_dtype=torch.bfloat16)
+    got = C.x_as_f64(b16)
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * (2.0 ** -8 + 1e-6) + 1e-30)
+
+
+def test_prefill_chunk_through_int2_layers(moe):
+    """A 2,048-token chunk through 3 int2 layers with the routing bias, as a
+    pre-norm residual chain (moe_rmsnorm to bf16, route, permute, grouped
+    GEMM, combine into the residual stream) with the usage update of every
+    layer.  Each layer against the oracle fed the GPU's own bf16 layer input:
+    ids bit-exact on every gap-safe token (near ties counted), outputs on 64
+    sampled gap-safe tokens, the usage scores bit-exact."""
+    L, T, H, E, k, F = 3, 2048, 2048, 512, 10, 768
+    li = C.layer_case(17, T, H, E, k, F, qfmt=1, bias=True, L=L, gap=False, device="cuda")
+    x = li.x.clone()
+    scores = torch.zeros((L, E), dtype=torch.float32, device="cuda")
+    hits = torch.empty(E, dtype=torch.int32, device="cuda")
+    ref_scores = np.zeros((L, E), np.float32)
+    excluded = 0
+    rng = np.random.default_rng(17)
+    for l in range(L):
+        xb = moe.moe_rmsnorm(x)
+        idx, w = moe.moe_route_topk(xb, li.Wr[l], li.bias[l], k)
+        counts, offsets, row_src, inv_row, _ = moe.moe_permute(idx, E)
+        y_perm, y_sh = moe.moe_grouped_gemm_q(xb, row_src, offsets, k, E, F, li.S, l, li.pool, li.R, li.qfmt)
+        x_before = x.clone()
+        moe.moe_combine(y_perm, w, inv_row=inv_row, y_shared=y_sh, residual=x, y_out=x)
+        moe.moe_usage_update(idx, l, L, E, 0.99, 0, 4, 96, hits, scores)
+        torch.cuda.synchronize()
+        xf = C.x_as_f64(xb)
+        b = li.bias[l].cpu().double().numpy()
+        rl = O.router_logits(xf, C.router_f64(li.Wr[l]), b)
+        ri, rw = O.topk_select(rl, k)
+        ok = O.gap_ok(rl, k, C.MIN_GAP)
+        excluded += int((~ok).sum())
+        gi = _np(idx)
+        assert np.array_equal(gi[ok], ri[ok]), f"layer {l}"
+        assert np.max(np.abs(_np(w)[ok] - rw[ok])) <= W_ATOL
+        sample = rng.choice(np.nonzero(ok)[0], size=64, replace=False)
+        ry = C.oracle_layer(li, layer=l, x=xb, tokens=sample)[0]
+        C.assert_close_moe(_np(x - x_before)[sample], ry, f"layer {l} (sampled)")
+        ref_scores, _ = O.usage_update(ref_scores, gi, l, 0.99, 0, 4, 96)
+        assert np.array_equal(_np(scores), ref_scores), f"usage after layer {l}"
+    assert excluded <= T * L // 10
