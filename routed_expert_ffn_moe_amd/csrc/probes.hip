@@ -1,10 +1,13 @@
 // Measurement probes (include/moe_probes.h): the practical HBM streaming-read
 // rate and the MFMA-only rate of the device, the ceilings the layer's
-// kernels are compared with.
+// kernels are compared with.  The read probe's shape (16,384 workgroups,
+// eight nontemporal 16-byte loads in flight per thread) was the fastest of
+// 1,024-16,384 workgroups, 4 or 8 loads, with or without the hint (6.9 TB/s
+// over 4 GiB).
 #include "moe_common.h"
 #include "../../include/moe_probes.h"
 
-#define PROBE_READ_BLOCKS 4096
+#define PROBE_READ_BLOCKS 16384
 #define PROBE_MFMA_WAVES 16  // per workgroup: 4 per SIMD
 
 __global__ __launch_bounds__(256) void probe_read_kernel(const uint4* __restrict__ src, size_t n16,
@@ -12,9 +15,12 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const uint4* __restrict
   uint32_t acc = 0u;
   const size_t stride = (size_t)gridDim.x * 256;
   size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {  // four 16-byte loads in flight per thread
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  for (; i + 7 * stride < n16; i += 8 * stride) {  // eight 16-byte nontemporal loads in flight per thread
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = moe_ld_stream16(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; i < n16; i += stride) {
     const uint4 a = src[i];
