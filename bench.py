@@ -536,6 +536,9 @@ def main():
     ap.add_argument("--int2", action="store_true",
                     help="also time the int2 stack: decode T = 1, 4 and a 16,384-token prefill chunk")
     ap.add_argument("--c2", action="store_true", help="also time one decode layer on its own, rotated over the layers")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the 8,192-token prefill chunk on a one-layer pool (for profiling the grouped GEMM); "
+                         "prints that measurement, not the headline line")
     ap.add_argument("--ceilings", action="store_true",
                     help="also measure the practical HBM streaming-read and MFMA-only rates (probe kernels)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
@@ -568,6 +571,12 @@ def main():
         del src, dst
 
     L, E, H, F, k = 48, 512, 2048, 768, 10
+    if args.prefill_only:
+        li = G.make_layer_inputs(2, 1, E, H, F, qfmt=0, bias=True, device=dev)
+        li.k = k
+        pf = prefill_bench(M, li, reps=args.steps, warmup=args.warmup)
+        print(json.dumps({"prefill_c4": pf}), flush=True)
+        return
     t0 = time.perf_counter()
     li = G.make_layer_inputs(2, L, E, H, F, qfmt=0, bias=True, device=dev,
                              progress=lambda l: log(f"pool: layer {l + 1}/{L}") if (l + 1) % 8 == 0 else None,
