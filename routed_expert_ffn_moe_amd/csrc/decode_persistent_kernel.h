@@ -78,7 +78,7 @@ struct PtArgs {
 #ifdef MOE_PT_STAMPS
 #define PT_STAMP(i)                                                                                 \
   do {                                                                                              \
-    if (threadIdx.x == 0 && l < 64 && a.stamps)                                                     \
+    if (threadIdx.x == 0 && l < 64 && blockIdx.x < 256 && a.stamps)                                 \
       a.stamps[((size_t)l * 256 + blockIdx.x) * 16 + (i)] = __builtin_amdgcn_s_memrealtime();        \
   } while (0)
 #else
