@@ -73,17 +73,29 @@ struct PtArgs {
 
 // Phase timestamps for performance analysis: with MOE_PT_STAMPS defined,
 // thread 0 of each workgroup records the 100 MHz wall clock at the phase
-// boundaries of layers < 64 into stamps[(layer * 256 + workgroup) * 16 + i];
-// otherwise the macro is empty.
+// boundaries of layers < 64 in LDS (a global store would be counted by the
+// next wait for loads, which then also waits for the store) and copies them
+// at the end to stamps[(layer * 256 + workgroup) * 16 + i]; otherwise the
+// macros are empty.
 #ifdef MOE_PT_STAMPS
-#define PT_STAMP(i)                                                                                 \
-  do {                                                                                              \
-    if (threadIdx.x == 0 && l < 64 && blockIdx.x < 256 && a.stamps)                                 \
-      a.stamps[((size_t)l * 256 + blockIdx.x) * 16 + (i)] = __builtin_amdgcn_s_memrealtime();        \
+#define PT_STAMP_DECL __shared__ unsigned long long pt_stamp_lds[64 * 16]
+#define PT_STAMP(i)                                                                 \
+  do {                                                                              \
+    if (threadIdx.x == 0 && l < 64) pt_stamp_lds[l * 16 + (i)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define PT_STAMP_FLUSH()                                                            \
+  do {                                                                              \
+    if (threadIdx.x == 0 && blockIdx.x < 256 && a.stamps)                           \
+      for (int ls = 0; ls < 64 * 16 && ls < a.L * 16; ++ls)                         \
+        a.stamps[((size_t)(ls >> 4) * 256 + blockIdx.x) * 16 + (ls & 15)] = pt_stamp_lds[ls]; \
   } while (0)
 #else
+#define PT_STAMP_DECL
 #define PT_STAMP(i) \
   do {              \
+  } while (0)
+#define PT_STAMP_FLUSH() \
+  do {                   \
   } while (0)
 #endif
 
@@ -109,6 +121,42 @@ __device__ __forceinline__ u64 pt_load(u64* base, uint32_t i) {
 __device__ __forceinline__ int pt_xcc() {
   return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & (PT_REPL - 1);  // HW_REG_XCC_ID[3:0]
 }
+// Sum over the wave's 64 lanes, returned in every lane: sums over 16, 8, 4
+// and 2 lanes inside each row of 16 with DPP row shifts (lane 15 of a row
+// then holds the row's sum), rows 0 + 1 and 2 + 3 with row_bcast:15, and the
+// two halves with row_bcast:31 (lane 63 then holds the total), which is read
+// back as a scalar.  VALU operations with a lane-shift modifier, where a
+// butterfly of shuffles takes a round trip through the LDS crossbar per step.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float pt_dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, true));
+}
+__device__ __forceinline__ float pt_wave_sum(float v) {
+  v += pt_dpp<0x111, 0xf>(v);  // row_shr:1
+  v += pt_dpp<0x112, 0xf>(v);  // row_shr:2
+  v += pt_dpp<0x114, 0xf>(v);  // row_shr:4
+  v += pt_dpp<0x118, 0xf>(v);  // row_shr:8
+  v += pt_dpp<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += pt_dpp<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+// The value of lane l ^ 1 and of lane l ^ 2 (DPP quad permutes), and of lane
+// l + 4 inside the lane's row of 16 (0 past the row's end).
+__device__ __forceinline__ float pt_xor1(float v) { return pt_dpp<0xB1, 0xf>(v); }
+__device__ __forceinline__ float pt_xor2(float v) { return pt_dpp<0x4E, 0xf>(v); }
+__device__ __forceinline__ float pt_next4(float v) { return pt_dpp<0x104, 0xf>(v); }
+// Sums over aligned segments of n lanes (n a power of two <= 32), left in the
+// segment's last lane: running sums over 2, 4, 8, 16 lanes with row shifts,
+// and for n = 32 the two rows of each half joined with row_bcast:15.
+__device__ __forceinline__ float pt_segment_sum(float v, int n) {
+  if (n > 1) v += pt_dpp<0x111, 0xf>(v);   // row_shr:1
+  if (n > 2) v += pt_dpp<0x112, 0xf>(v);   // row_shr:2
+  if (n > 4) v += pt_dpp<0x114, 0xf>(v);   // row_shr:4
+  if (n > 8) v += pt_dpp<0x118, 0xf>(v);   // row_shr:8
+  if (n > 16) v += pt_dpp<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  return v;
+}
+
 // The thread index and lane, made opaque at each call: values derived from
 // them inside the layer loop are then computed where used instead of being
 // hoisted out of the loop and kept live (or spilled) for the whole kernel.
@@ -533,8 +581,8 @@ __device__ __forceinline__ void pt_prep_word(const float* v, float scale, bool v
       c0 = moe_dot2(a2, k0, c0);
       c0 = moe_dot2(a3, k1, c0);
     }
-    c0 += __shfl_xor(c0, 1, 64);
-    c0 += __shfl_xor(c0, 2, 64);
+    c0 += pt_xor1(c0);
+    c0 += pt_xor2(c0);
     if (valid && sub == 0) *corr = make_float2(c0, 0.f);
   } else {
     const half2v k1024 = {(_Float16)1024.f, (_Float16)1024.f};
@@ -549,8 +597,8 @@ __device__ __forceinline__ void pt_prep_word(const float* v, float scale, bool v
         c1 = moe_dot2(a, kc, c1);
       }
     }
-    c0 += __shfl_xor(c0, 1, 64);
-    c1 += __shfl_xor(c1, 1, 64);
+    c0 += pt_xor1(c0);
+    c1 += pt_xor1(c1);
     if (valid && sub == 0) *corr = make_float2(c0, c1);
   }
 }
@@ -602,6 +650,7 @@ __host__ __device__ inline PtLds pt_lds(int qfmt, int T, int k, int E, int H, si
 template <int QFMT, int MT, int SLOTS>
 __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  PT_STAMP_DECL;
   const int T = a.T, H = a.H, F = a.F, E = a.E, k = a.k, L = a.L, G = a.G;
   const int g = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -633,6 +682,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
   const uint32_t base = __hip_atomic_load(a.hdr + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   bool ok = true;
   const int nrch = (H + 511) / 512;  // router chunks of 512 columns per row (<= 4)
+  const float inv_h = 1.0f / (float)H;
 
   for (int l = 0; l < L && ok; ++l) {
     // the thread index is made opaque once per layer, so that the compiler
@@ -755,7 +805,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         }
       }
       if (MT == 1) {
-        const float v = moe_wave_sum(ssq[0]);
+        const float v = pt_wave_sum(ssq[0]);
         if (lane == 0) ssred[wave] = v;
       }
       if (!__syncthreads_and(ok)) { ok = false; break; }
@@ -773,7 +823,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         float ss = 0.f;
         if (t < T)
           for (int h = tid; h < H; h += PT_THREADS) ss = fmaf(xs[t * H + h], xs[t * H + h], ss);
-        ss = moe_wave_sum(ss);
+        ss = pt_wave_sum(ss);
         if (lane == 0) ssred[wave * MT + t] = ss;
       }
       __syncthreads();
@@ -784,7 +834,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
       float ss = 0.f;
 #pragma unroll
       for (int w8 = 0; w8 < PT_WAVES; ++w8) ss += ssred[w8 * MT + t];
-      invr[t] = 1.0f / sqrtf(ss / (float)H + PT_EPS);
+      invr[t] = __builtin_amdgcn_rsqf(ss * inv_h + PT_EPS);
     }
     PT_STAMP(10);  // 1/rms
     if (a.x_hist && g == 0)
@@ -806,23 +856,29 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
           e_cur = e;
         }
         const float* xt = xs + (size_t)t * H;
-        float acc = 0.f;
+        float accs[4] = {0.f, 0.f, 0.f, 0.f};  // one per chunk: four short FMA chains
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int h0 = 512 * c + 8 * lane;
           if (c < nrch && h0 < H) {
             const uint32_t ww[4] = {rw[c].x, rw[c].y, rw[c].z, rw[c].w};
+            const float4 xa = *reinterpret_cast<const float4*>(xt + h0);
+            const float4 xb = *reinterpret_cast<const float4*>(xt + h0 + 4);
+            const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {  // the 4 words (8 bf16) of the chunk
-              acc = fmaf(xt[h0 + 2 * q], __uint_as_float(ww[q] << 16), acc);
-              acc = fmaf(xt[h0 + 2 * q + 1], __uint_as_float(ww[q] & 0xffff0000u), acc);
+              accs[c] = fmaf(xv[2 * q], __uint_as_float(ww[q] << 16), accs[c]);
+              accs[c] = fmaf(xv[2 * q + 1], __uint_as_float(ww[q] & 0xffff0000u), accs[c]);
             }
           }
         }
+        const float acc = (accs[0] + accs[1]) + (accs[2] + accs[3]);
+        PT_STAMP(12);  // router dot: lane sums
         float it = invr[0];
 #pragma unroll
         for (int q = 1; q < MT; ++q) it = t == q ? invr[q] : it;
-        const float sdot = moe_wave_sum(acc);
+        const float sdot = pt_wave_sum(acc);
+        PT_STAMP(13);  // router dot: wave sum
         if (lane < PT_REPL)  // lane r writes the copy of XCD r
           pt_put(pt_at(a.lbuf, (uint32_t)((lane * T + t) * E + e)), tag, sdot * it + b_cur);
       }
@@ -845,6 +901,11 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
       }
     }
     PT_STAMP(2);  // x prepared
+    // this layer's slot-table row into LDS (made visible by the barrier after
+    // the logits arrive)
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+      if (tid + PT_THREADS * c <= E) lslots[tid + PT_THREADS * c] = srow[c];
     // ------------------------------------------------------------ phase B
     {
       constexpr int NLG = MT * SLOTS / 8 > 0 ? MT * SLOTS / 8 : 1;  // T * E <= 512 * NLG
@@ -858,10 +919,6 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     }
     if (!__syncthreads_and(ok)) { ok = false; break; }
     PT_STAMP(3);  // logits received
-#pragma unroll
-    for (int c = 0; c < 3; ++c)
-      if (tid + PT_THREADS * c <= E) lslots[tid + PT_THREADS * c] = srow[c];
-    __syncthreads();
     uint32_t my_key = 0u;  // wave t < T: the key of top-k position `lane` of token t
     if (wave < T) {  // `red` is free until the work pieces: 64 candidate words per token
       my_key = pt_topk_select<SLOTS>(lg + (size_t)wave * E, E, k, topi + wave * k, (u64*)red + 64 * wave);
@@ -1117,7 +1174,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
             }
             hv = moe_silu(sg) * su;
           }
-          const float hn = __shfl_xor(hv, 1, 64);  // partner value of the pair
+          const float hn = pt_xor1(hv);  // partner value of the pair
           const int pk = fi >> 1;                   // pair index within the word
           float c0 = 0.f, c1 = 0.f;
           uint32_t pw = 0u;
@@ -1138,11 +1195,12 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
               c1 = moe_dot2(a2, kc, 0.f);
             }
           }
-          // corrections summed over the 4 pairs (lanes fi = 0, 2, 4, 6 of the item)
-          c0 += __shfl_xor(c0, 2, 64);
-          c0 += __shfl_xor(c0, 4, 64);
-          c1 += __shfl_xor(c1, 2, 64);
-          c1 += __shfl_xor(c1, 4, 64);
+          // corrections summed over the 4 pairs (lanes fi = 0, 2, 4, 6 of the
+          // item; the sum is complete in lane fi = 0, the one that stores it)
+          c0 += pt_xor2(c0);
+          c0 += pt_next4(c0);
+          c1 += pt_xor2(c1);
+          c1 += pt_next4(c1);
           if (iv && item < PT_PB_MAX * MT) {
             if ((fi & 1) == 0) hp[item * 4 + pk] = pw;
             if (fi == 0) hc[item] = make_float2(c0, c1);
@@ -1227,7 +1285,8 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     {
       // outputs (t, r) for r in this workgroup's rows; TPO threads per output,
       // thread `sub` summing the partials of workgroups sub, sub + TPO, ... in
-      // order, then a butterfly over the TPO lanes (a fixed order for a given T)
+      // order, then the sum over the TPO lanes (pt_segment_sum, complete in the
+      // last of them; a fixed order for a given T)
       const int r0 = g * a.rpw;
       const int nout = T * a.rpw;
       const int tpo = a.tpo;
@@ -1264,10 +1323,8 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         }
         if (!__syncthreads_and(ok)) { ok = false; break; }
         PT_STAMP(8);  // partial sums received
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1)
-          if (m < tpo) sum += __shfl_xor(sum, m, 64);
-        if (act && sub == 0) {
+        sum = pt_segment_sum(sum, tpo);
+        if (act && sub == tpo - 1) {
           const float xn = xs[t * H + rr] + sum;
           if (l + 1 < L) {
 #pragma unroll
@@ -1283,6 +1340,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     __syncthreads();
     PT_STAMP(9);  // layer done
   }
+  PT_STAMP_FLUSH();
   if (!ok) {
     // the error word: the next call's set-up kernel then zeroes the tagged
     // buffers (this call's tags stay reserved, so this is belt and braces)

@@ -13,7 +13,8 @@ per-phase times averaged over layers 1..47 and the workgroups, with the mean
 over layers of the slowest workgroup's time in each phase.
 
 Stamps per layer (index: boundary): 0 layer start, 1 x_l received, 10 1/rms,
-11 router rows published, 2 x_l prepared, 3 logits received, 4 top-k done,
+11 router rows published (12, 13 inside the
+router dot: lane sums done, wave sum done), 2 x_l prepared, 3 logits received, 4 top-k done,
 5 gate/up dots done, 6 SiLU done, 7 group done, 8 partial sums received,
 9 layer done.  With several groups per workgroup, 5-7 are those of its last
 group (the gate/up phase then spans the earlier groups).
@@ -27,7 +28,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 STAMP_LIB = os.path.join(HERE, "libmoe_stamps.so")
 PHASES = [("wait x", 0, 1), ("router+prep", 1, 2), ("wait logits", 2, 3), ("top-k", 3, 4),
           ("gate/up", 4, 5), ("silu", 5, 6), ("down", 6, 7), ("wait partials", 7, 8), ("final", 8, 9)]
-DETAIL = [("1/rms", 1, 10), ("router dot+put", 10, 11), ("xprep", 11, 2)]
+DETAIL = [("1/rms", 1, 10), ("router dot+put", 10, 11), ("  lane sums", 10, 12), ("  wave sum", 12, 13),
+          ("  put", 13, 11), ("xprep", 11, 2)]
 NSTAMP, MAXL, MAXG = 16, 64, 256
 
 
