@@ -411,8 +411,9 @@ int moe_rmsnorm(const float* x, int T, int H, float eps, void* out, int out_dtyp
  * moe_workspace_size(MOE_OP_DECODE_STACK, ...) exceeds MOE_NOALLOC_WS_BYTES
  * are rejected with MOE_EWORKSPACE before anything is enqueued (at H = 2048,
  * E = 512, k = 10: T <= 5 fits, i.e. decode and verify windows of up to 4
- * drafted tokens; T = 6 and 8 need 25 and 34 MB and are rejected).  Every call on a GPU shares that GPU's
- * array, which keeps the previous call's contents (its tag header is valid
+ * drafted tokens; T = 6 and 8 need 26.9 and 35.9 MB and are rejected).
+ * Every call on a GPU shares that GPU's array, which keeps the previous
+ * call's contents (its tag header is valid
  * across calls; see moe_decode_stack): calls that overlap on one GPU, on
  * any streams, race and give wrong results.  The first call on a device
  * looks up the array's address (hipGetSymbolAddress) with that device
