@@ -75,13 +75,17 @@ struct PtArgs {
 // thread 0 of each workgroup records the 100 MHz wall clock at the phase
 // boundaries of layers < 64 in LDS (a global store would be counted by the
 // next wait for loads, which then also waits for the store) and copies them
-// at the end to stamps[(layer * 256 + workgroup) * 16 + i]; otherwise the
-// macros are empty.
+// at the end to stamps[(layer * 256 + workgroup) * 16 + i] (PT_MARK stores
+// a value there instead of the clock); otherwise the macros are empty.
 #ifdef MOE_PT_STAMPS
 #define PT_STAMP_DECL __shared__ unsigned long long pt_stamp_lds[64 * 16]
 #define PT_STAMP(i)                                                                 \
   do {                                                                              \
     if (threadIdx.x == 0 && l < 64) pt_stamp_lds[l * 16 + (i)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define PT_MARK(i, v)                                                               \
+  do {                                                                              \
+    if (threadIdx.x == 0 && l < 64) pt_stamp_lds[l * 16 + (i)] = (unsigned long long)(v); \
   } while (0)
 #define PT_STAMP_FLUSH()                                                            \
   do {                                                                              \
@@ -93,6 +97,9 @@ struct PtArgs {
 #define PT_STAMP_DECL
 #define PT_STAMP(i) \
   do {              \
+  } while (0)
+#define PT_MARK(i, v) \
+  do {                \
   } while (0)
 #define PT_STAMP_FLUSH() \
   do {                   \
@@ -873,12 +880,10 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
           }
         }
         const float acc = (accs[0] + accs[1]) + (accs[2] + accs[3]);
-        PT_STAMP(12);  // router dot: lane sums
         float it = invr[0];
 #pragma unroll
         for (int q = 1; q < MT; ++q) it = t == q ? invr[q] : it;
         const float sdot = pt_wave_sum(acc);
-        PT_STAMP(13);  // router dot: wave sum
         if (lane < PT_REPL)  // lane r writes the copy of XCD r
           pt_put(pt_at(a.lbuf, (uint32_t)((lane * T + t) * E + e)), tag, sdot * it + b_cur);
       }
@@ -986,6 +991,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         gi0 = first_at((int64_t)g * C / G);
         gi1 = first_at((int64_t)(g + 1) * C / G);
       }
+      PT_MARK(14, gi1 - gi0);  // this workgroup's group count
       constexpr int NRD = 4;  // down rows per thread (H <= 2048)
       float y[NRD][MT];
 #pragma unroll
@@ -1158,6 +1164,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         if (MT > 1) load_gu(min(gi + 1, gi1 - 1), gqN, gsN);
         __syncthreads();
         PT_STAMP(5);  // gate/up dots done
+        if (gi == gi0 + 1) PT_STAMP(12);  // (second group)
         // ---- h = silu(gate) * up, 8 threads per (piece, token slot), then the
         // prepared word of the 8 h values for the down dots
         {
@@ -1208,16 +1215,25 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         }
         __syncthreads();
         PT_STAMP(6);  // SiLU done
-        // ---- down dots: rows tid + 512 c, the group's 4 pieces
+        if (gi == gi0 + 1) PT_STAMP(13);  // (second group)
+        // ---- down dots: rows tid + 512 c, the group's 4 pieces.  Per window
+        // token tt (a register index of y) the unit's entry lt for it, if any
+        // (uniform over the workgroup), so that each product is added to one
+        // accumulator without selecting among the token slots.
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          if (MT > 1 && t >= ntok) break;
-          const int tk = MT == 1 ? 0 : p_tok[u * TS + t], jj = MT == 1 ? u : p_j[u * TS + t];
-          const float wgt = jj < k ? topw[tk * k + jj] : 1.f;
+        for (int tt = 0; tt < MT; ++tt) {
+          int lt = MT == 1 ? 0 : -1;
+          if (MT > 1 && tt < T)
+            for (int t = 0; t < ntok; ++t)
+              if (p_tok[u * TS + t] == tt) lt = t;
+          lt = __builtin_amdgcn_readfirstlane(lt);
+          if (lt < 0) continue;
+          const int jj = MT == 1 ? u : p_j[u * TS + lt];
+          const float wgt = jj < k ? topw[tt * k + jj] : 1.f;
 #pragma unroll
           for (int pi = 0; pi < 4; ++pi) {
-            const uint32_t* hw4 = hp + (pi * MT + t) * 4;
-            const float2 cc = hc[pi * MT + t];
+            const uint32_t* hw4 = hp + (pi * MT + lt) * 4;
+            const float2 cc = hc[pi * MT + lt];
 #pragma unroll
             for (int c = 0; c < NRD; ++c) {
               float v;
@@ -1229,9 +1245,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
                 const uint32_t m = pi < 2 ? dq[c].z : dq[c].w;
                 v = pt_q2_word(w, moe_f16_to_f32((uint16_t)(m & 0xffff)), moe_f16_to_f32((uint16_t)(m >> 16)), hw4, cc, mk);
               }
-#pragma unroll
-              for (int tt = 0; tt < MT; ++tt)
-                if (tt == tk) y[c][tt] = fmaf(wgt, v, y[c][tt]);
+              y[c][tt] = fmaf(wgt, v, y[c][tt]);
             }
           }
         }
@@ -1253,6 +1267,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         }
         __syncthreads();  // red, hp, hc are reused by the next batch
         PT_STAMP(7);  // group done
+        if (gi == gi0) PT_STAMP(15);  // first group done
         if (MT > 1) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {

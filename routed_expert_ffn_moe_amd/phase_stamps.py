@@ -13,10 +13,10 @@ per-phase times averaged over layers 1..47 and the workgroups, with the mean
 over layers of the slowest workgroup's time in each phase.
 
 Stamps per layer (index: boundary): 0 layer start, 1 x_l received, 10 1/rms,
-11 router rows published (12, 13 inside the
-router dot: lane sums done, wave sum done), 2 x_l prepared, 3 logits received, 4 top-k done,
+11 router rows published, 2 x_l prepared, 3 logits received, 4 top-k done,
 5 gate/up dots done, 6 SiLU done, 7 group done, 8 partial sums received,
-9 layer done.  With several groups per workgroup, 5-7 are those of its last
+9 layer done, 15 first group done, 12 and 13 the second group's gate/up dots
+and SiLU done, and 14 the workgroup's group count.  With several groups per workgroup, 5-7 are those of its last
 group (the gate/up phase then spans the earlier groups).
 """
 import argparse
@@ -28,8 +28,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 STAMP_LIB = os.path.join(HERE, "libmoe_stamps.so")
 PHASES = [("wait x", 0, 1), ("router+prep", 1, 2), ("wait logits", 2, 3), ("top-k", 3, 4),
           ("gate/up", 4, 5), ("silu", 5, 6), ("down", 6, 7), ("wait partials", 7, 8), ("final", 8, 9)]
-DETAIL = [("1/rms", 1, 10), ("router dot+put", 10, 11), ("  lane sums", 10, 12), ("  wave sum", 12, 13),
-          ("  put", 13, 11), ("xprep", 11, 2)]
+DETAIL = [("1/rms", 1, 10), ("router dot+put", 10, 11), ("xprep", 11, 2)]
 NSTAMP, MAXL, MAXG = 16, 64, 256
 
 
@@ -88,6 +87,21 @@ def run(ts, qfmt=0, L=48, E=512, H=2048, F=768, k=10, seed=2):
         for name, i, j in DETAIL:
             d = (st[1:, :, j] - st[1:, :, i]) / 100.0
             lines.append(f"    {name:18s} {d.mean():6.2f} us")
+        # the group phase (top-k done -> last group done) against the workgroup's group count
+        ng_wg = st[1:, :, 14]
+        gp = (st[1:, :, 7] - st[1:, :, 4]) / 100.0
+        parts = []
+        for n in sorted(set(ng_wg.ravel().tolist())):
+            sel = ng_wg == n
+            parts.append(f"{n} groups: {sel.mean() * 100:.0f}% of workgroups, {gp[sel].mean():.2f} us")
+        lines.append("  group phase by group count: " + "; ".join(parts))
+        first = (st[1:, :, 15] - st[1:, :, 4]) / 100.0
+        later = np.where(ng_wg > 1, (st[1:, :, 7] - st[1:, :, 15]) / np.maximum(ng_wg - 1, 1) / 100.0, np.nan)
+        lines.append(f"  first group {first.mean():.2f} us, each later group {np.nanmean(later) if np.isfinite(later).any() else 0:.2f} us")
+        two = ng_wg >= 2
+        if two.any():
+            g2 = [(st[1:, :, b] - st[1:, :, a_])[two].mean() / 100.0 for a_, b in ((15, 12), (12, 13))]
+            lines.append(f"  second group: start -> gate/up dots done {g2[0]:.2f} us, SiLU {g2[1]:.2f} us")
         ends = st[1:, :, 9]
         lines.append(f"  layer-end skew across workgroups: mean {((ends.max(1) - ends.min(1)) / 100.0).mean():.2f} us")
         print("\n".join(lines), flush=True)
