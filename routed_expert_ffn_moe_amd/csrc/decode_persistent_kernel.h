@@ -147,6 +147,22 @@ __device__ __forceinline__ float pt_wave_sum(float v) {
   v += pt_dpp<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+// Inclusive prefix sum over the wave's 64 lanes (integers): within each row
+// of 16 with row shifts of 1, 2, 4, 8, then rows 1 and 3 add lane 15 of rows
+// 0 and 2 (row_bcast:15), and rows 2 and 3 add lane 31 (row_bcast:31).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int pt_dppi(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, true);
+}
+__device__ __forceinline__ int pt_wave_scan(int v) {
+  v += pt_dppi<0x111, 0xf>(v);
+  v += pt_dppi<0x112, 0xf>(v);
+  v += pt_dppi<0x114, 0xf>(v);
+  v += pt_dppi<0x118, 0xf>(v);
+  v += pt_dppi<0x142, 0xa>(v);
+  v += pt_dppi<0x143, 0xc>(v);
+  return v;
+}
 // The value of lane l ^ 1 and of lane l ^ 2 (DPP quad permutes), and of lane
 // l + 4 inside the lane's row of 16 (0 past the row's end).
 __device__ __forceinline__ float pt_xor1(float v) { return pt_dpp<0xB1, 0xf>(v); }
@@ -482,10 +498,12 @@ __device__ __forceinline__ void pt_topk_weights(uint32_t my_key, int k, float* w
 // (ts >= T: a unit holds each token at most once);
 // then, if with_shared, the shared expert with every token (top-k position
 // k); p_roff[u] is the byte offset of the unit's record in the pool;
-// p_misc[0] = the number of units.  n = T * k <= 64.
+// p_misc[0] = the number of units.  n = T * k <= 64.  scr_mask, scr_unit:
+// LDS scratch of E entries each.
 __device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, const int32_t* slots, int64_t rbytes,
                                         bool with_shared, int ts, int* p_exp, int* p_ntok, int* p_tok, int* p_j,
-                                        int64_t* p_roff, int* p_cum, int* p_misc) {
+                                        int64_t* p_roff, int* p_cum, int* p_misc, uint32_t* scr_mask,
+                                        int* scr_unit) {
   const int lane = pt_lane(), n = T * k;
   if (T == 1) {  // one token: its k experts are distinct, in top-k order
     if (lane < k) {
@@ -508,27 +526,39 @@ __device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, co
     }
     return;
   }
-  const int e = lane < n ? topi[lane] : -1 - lane;  // distinct negatives for idle lanes
-  int first = lane, before = 0, total = 0;           // first lane with this expert; count before; count
-  for (int q = 0; q < n; ++q) {
-    const int eq = __builtin_amdgcn_readlane(e, q);
-    if (eq == e) {
-      first = min(first, q);
-      before += q < lane;
-      ++total;
-    }
-  }
-  const uint64_t firsts = __ballot(lane < n && first == lane);
-  const int u_first = (int)__popcll(firsts & ((1ull << lane) - 1ull));  // rank among first occurrences
-  const int u = __shfl(u_first, first, 64);
+  // Entry `lane` = (token t, position j).  A token's k experts are distinct,
+  // so per expert the bitmask of the tokens that chose it (scr_mask[e],
+  // cleared first by the lanes that use it, then OR-ed) gives each entry the
+  // number of earlier tokens with the same expert (`before`: its place in the
+  // unit's token list), the expert's token count, and whether the entry is
+  // the expert's first occurrence (before == 0).  The units are numbered by
+  // their first occurrences in entry order; scr_unit[e] hands the number to
+  // the other entries of the expert.
+  const bool act = lane < n;
+  const int t = act ? lane / k : 0, j = act ? lane - t * k : 0;
+  const int e = act ? topi[lane] : 0;
+  if (act) scr_mask[e] = 0u;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  if (act) __hip_atomic_fetch_or(scr_mask + e, 1u << t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const uint32_t msk = act ? scr_mask[e] : 0u;
+  const int before = (int)__popc(msk & ((1u << t) - 1u)), total = (int)__popc(msk);
+  const bool isf = act && before == 0;
+  const uint64_t firsts = __ballot(isf);
   const int U = (int)__popcll(firsts);
-  if (lane < n) {
-    const int t = lane / k, j = lane % k;
-    if (first == lane) {
-      p_exp[u] = e;
-      p_ntok[u] = total;
-      p_roff[u] = (int64_t)slots[e] * rbytes;
-    }
+  if (isf) {
+    const int u = (int)__popcll(firsts & ((1ull << lane) - 1ull));  // rank among first occurrences
+    scr_unit[e] = u;
+    p_exp[u] = e;
+    p_ntok[u] = total;
+    p_roff[u] = (int64_t)slots[e] * rbytes;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  if (act) {
+    const int u = scr_unit[e];
     p_tok[u * ts + before] = t;
     p_j[u * ts + before] = j;
   }
@@ -548,12 +578,7 @@ __device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, co
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   const int c = lane < U ? PT_GROUP_BASE + p_ntok[lane] : 0;
-  int incl = c;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(incl, d, 64);
-    incl += lane >= d ? v : 0;
-  }
+  const int incl = pt_wave_scan(c);
   if (lane < U) p_cum[lane] = incl - c;
   const int sum_r = U > 0 ? __builtin_amdgcn_readlane(incl, U - 1) : 0;
   if (lane == 0) {
@@ -943,8 +968,10 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     if (MT > 1) {
       emit_topk();
       if (wave == 0)
-        pt_plan(topi, T, k, E, lslots, a.record_bytes, true, TS, p_exp, p_ntok, p_tok, p_j, p_roff, p_cum, p_misc);
+        pt_plan(topi, T, k, E, lslots, a.record_bytes, true, TS, p_exp, p_ntok, p_tok, p_j, p_roff, p_cum, p_misc,
+                (uint32_t*)red, (int*)red + E);  // `red` is free until the work pieces
       __syncthreads();
+      PT_STAMP(13);  // plan done
     }
     // ------------------------------------------------------------ work pieces
     // The layer's expert work is cut into pieces of 8 f values: (unit u, piece
@@ -1215,7 +1242,6 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         }
         __syncthreads();
         PT_STAMP(6);  // SiLU done
-        if (gi == gi0 + 1) PT_STAMP(13);  // (second group)
         // ---- down dots: rows tid + 512 c, the group's 4 pieces.  Per window
         // token tt (a register index of y) the unit's entry lt for it, if any
         // (uniform over the workgroup), so that each product is added to one

@@ -15,8 +15,8 @@ over layers of the slowest workgroup's time in each phase.
 Stamps per layer (index: boundary): 0 layer start, 1 x_l received, 10 1/rms,
 11 router rows published, 2 x_l prepared, 3 logits received, 4 top-k done,
 5 gate/up dots done, 6 SiLU done, 7 group done, 8 partial sums received,
-9 layer done, 15 first group done, 12 and 13 the second group's gate/up dots
-and SiLU done, and 14 the workgroup's group count.  With several groups per workgroup, 5-7 are those of its last
+9 layer done, 15 first group done, 12 the second group's gate/up dots done,
+13 the plan done (several tokens), and 14 the workgroup's group count.  With several groups per workgroup, 5-7 are those of its last
 group (the gate/up phase then spans the earlier groups).
 """
 import argparse
@@ -100,8 +100,10 @@ def run(ts, qfmt=0, L=48, E=512, H=2048, F=768, k=10, seed=2):
         lines.append(f"  first group {first.mean():.2f} us, each later group {np.nanmean(later) if np.isfinite(later).any() else 0:.2f} us")
         two = ng_wg >= 2
         if two.any():
-            g2 = [(st[1:, :, b] - st[1:, :, a_])[two].mean() / 100.0 for a_, b in ((15, 12), (12, 13))]
-            lines.append(f"  second group: start -> gate/up dots done {g2[0]:.2f} us, SiLU {g2[1]:.2f} us")
+            g2 = (st[1:, :, 12] - st[1:, :, 15])[two].mean() / 100.0
+            lines.append(f"  second group: start -> gate/up dots done {g2:.2f} us")
+        if T > 1:
+            lines.append(f"  plan (after top-k) {((st[1:, :, 13] - st[1:, :, 4]) / 100.0).mean():.2f} us")
         ends = st[1:, :, 9]
         lines.append(f"  layer-end skew across workgroups: mean {((ends.max(1) - ends.min(1)) / 100.0).mean():.2f} us")
         print("\n".join(lines), flush=True)
