@@ -811,7 +811,14 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
     // x_l into LDS.  One token: each thread also sums the squares of its
     // words (word tid + 512 q in order, then the wave's butterfly), so 1/rms
     // needs no second pass over x.
-    float ssq[1] = {0.f};
+    float ssq[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) ssq[t] = 0.f;
+    // several tokens with H a multiple of 512: word q of a thread belongs to
+    // token q / (H / 512), so the squares can be summed from the polled words
+    // too, in the same order as the LDS pass below
+    const bool ssq_poll = MT == 1 || H % PT_THREADS == 0;
+    const int wpt = H / PT_THREADS;  // words of a token per thread (ssq_poll)
     {
       const int last = T * H - 1;
       u64 w[NX];
@@ -833,23 +840,32 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
         if (i <= last) {
           const float v = __uint_as_float((uint32_t)w[q]);
           xs[i] = v;
-          if (MT == 1) ssq[0] = fmaf(v, v, ssq[0]);
+          if (MT == 1) {
+            ssq[0] = fmaf(v, v, ssq[0]);
+          } else {
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+              if (q >= t * wpt && q < (t + 1) * wpt) ssq[t] = fmaf(v, v, ssq[t]);
+          }
         }
       }
-      if (MT == 1) {
-        const float v = pt_wave_sum(ssq[0]);
-        if (lane == 0) ssred[wave] = v;
+      if (ssq_poll) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const float v = pt_wave_sum(ssq[t]);
+          if (lane == 0) ssred[wave * MT + t] = v;
+        }
       }
       if (!__syncthreads_and(ok)) { ok = false; break; }
     }
     PT_STAMP(1);  // x_l received
     // 1 / rms of every token: thread tid sums the squares of the token's
-    // words tid + 512 q in order, the wave adds its threads (butterfly), and
-    // the 8 waves' sums are added in order.  One token: from the polled words
-    // above (no second pass); more tokens: from LDS, one more barrier.  The
-    // order is the same for every token count, so a token's 1/rms does not
-    // depend on the window it is verified in.
-    if (MT > 1) {
+    // words tid + 512 q in order, the wave adds its threads (DPP), and the 8
+    // waves' sums are added in order.  From the polled words above (no second
+    // pass) for one token, and for several when H is a multiple of 512; else
+    // from LDS, one more barrier.  The order is the same for every token
+    // count, so a token's 1/rms does not depend on the window it is verified in.
+    if (!ssq_poll) {
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         float ss = 0.f;
