@@ -243,7 +243,7 @@ def decode_sweep(M, li, steps, warmup, use_graph):
         u = sum(sum(x) for x in d["uniq"]) / (len(d["uniq"]) * li.L)
         row = {"T": T, "k": k, "ms_per_step": round(ms, 4), "token_positions_per_s": round(T / (ms / 1e3), 1),
                "mean_distinct_experts_per_layer": round(u, 2), "gbs": round(b / (ms / 1e3) / 1e9, 1),
-               "path": "persistent" if T * k <= 64 else "kernel chain"}
+               "path": "persistent"}
         log(f"sweep: {json.dumps(row)}")
         rows.append(row)
     return rows

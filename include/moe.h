@@ -364,7 +364,7 @@ int moe_tier_rebalance(const float* scores, int L, int E, int n_hot,
  *   x_{l+1} = x_l + MoE_l(xn_l)
  * where MoE_l(xn_l) is exactly what moe_route_topk + moe_expert_gemv_q +
  * moe_combine compute on xn_l with layer l's router, bias and slots.
- * Execution: for 1 <= T <= 8 with T * k <= 64 (and shapes whose working set
+ * Execution: for 1 <= T <= 8 (and shapes whose working set
  * fits in LDS) the step runs as ONE persistent kernel whose workgroups pass
  * data through tagged words in ws (no host synchronisation, no grid
  * barrier); otherwise,

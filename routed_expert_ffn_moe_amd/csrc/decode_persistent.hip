@@ -139,7 +139,7 @@ bool moe_persistent_supported(int T, int k, int E, int H, int F, int qfmt) {
   // x words per thread (T * H / 512), router chunks (H / 512) and down rows
   // per thread (H / 512) are unrolled up to 4 * MT, 4 and 4; gate/up K units
   // of 128 per wave up to 2: 256 <= H <= 2048
-  return P.lds <= pt_lds_limit() && H <= 2048 && H % 256 == 0 && T * k <= 64;
+  return P.lds <= pt_lds_limit() && H <= 2048 && H % 256 == 0 && T * k <= 128;
 }
 
 #ifdef MOE_PT_STAMPS

@@ -498,7 +498,7 @@ __device__ __forceinline__ void pt_topk_weights(uint32_t my_key, int k, float* w
 // (ts >= T: a unit holds each token at most once);
 // then, if with_shared, the shared expert with every token (top-k position
 // k); p_roff[u] is the byte offset of the unit's record in the pool;
-// p_misc[0] = the number of units.  n = T * k <= 64.  scr_mask, scr_unit:
+// p_misc[0] = the number of units.  n = T * k <= 128.  scr_mask, scr_unit:
 // LDS scratch of E entries each.
 __device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, const int32_t* slots, int64_t rbytes,
                                         bool with_shared, int ts, int* p_exp, int* p_ntok, int* p_tok, int* p_j,
@@ -526,41 +526,63 @@ __device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, co
     }
     return;
   }
-  // Entry `lane` = (token t, position j).  A token's k experts are distinct,
-  // so per expert the bitmask of the tokens that chose it (scr_mask[e],
-  // cleared first by the lanes that use it, then OR-ed) gives each entry the
-  // number of earlier tokens with the same expert (`before`: its place in the
-  // unit's token list), the expert's token count, and whether the entry is
-  // the expert's first occurrence (before == 0).  The units are numbered by
-  // their first occurrences in entry order; scr_unit[e] hands the number to
-  // the other entries of the expert.
-  const bool act = lane < n;
-  const int t = act ? lane / k : 0, j = act ? lane - t * k : 0;
-  const int e = act ? topi[lane] : 0;
-  if (act) scr_mask[e] = 0u;
+  // Entry i = (token t, position j), i < n <= 128: lane l holds entries l
+  // and l + 64.  A token's k experts are distinct, so per expert the bitmask
+  // of the tokens that chose it (scr_mask[e], cleared first by the lanes that
+  // use it, then OR-ed) gives each entry the number of earlier tokens with the
+  // same expert (`before`: its place in the unit's token list), the expert's
+  // token count, and whether the entry is the expert's first occurrence
+  // (before == 0).  The units are numbered by their first occurrences in
+  // entry order; scr_unit[e] hands the number to the other entries of the
+  // expert.
+  bool act[2];
+  int tv[2], jv[2], ev[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int i = lane + 64 * r;
+    act[r] = i < n;
+    tv[r] = act[r] ? i / k : 0;
+    jv[r] = act[r] ? i - tv[r] * k : 0;
+    ev[r] = act[r] ? topi[i] : 0;
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    if (act[r]) scr_mask[ev[r]] = 0u;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  if (act) __hip_atomic_fetch_or(scr_mask + e, 1u << t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    if (act[r]) __hip_atomic_fetch_or(scr_mask + ev[r], 1u << tv[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  const uint32_t msk = act ? scr_mask[e] : 0u;
-  const int before = (int)__popc(msk & ((1u << t) - 1u)), total = (int)__popc(msk);
-  const bool isf = act && before == 0;
-  const uint64_t firsts = __ballot(isf);
-  const int U = (int)__popcll(firsts);
-  if (isf) {
-    const int u = (int)__popcll(firsts & ((1ull << lane) - 1ull));  // rank among first occurrences
-    scr_unit[e] = u;
-    p_exp[u] = e;
-    p_ntok[u] = total;
-    p_roff[u] = (int64_t)slots[e] * rbytes;
+  int before[2];
+  uint64_t firsts[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const uint32_t msk = act[r] ? scr_mask[ev[r]] : 0u;
+    before[r] = (int)__popc(msk & ((1u << tv[r]) - 1u));
+    firsts[r] = __ballot(act[r] && before[r] == 0);
+  }
+  const int U0 = (int)__popcll(firsts[0]), U = U0 + (int)__popcll(firsts[1]);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (act[r] && before[r] == 0) {
+      const int u = (r == 0 ? 0 : U0) + (int)__popcll(firsts[r] & ((1ull << lane) - 1ull));  // rank among first occurrences
+      scr_unit[ev[r]] = u;
+      p_exp[u] = ev[r];
+      p_ntok[u] = (int)__popc(scr_mask[ev[r]]);
+      p_roff[u] = (int64_t)slots[ev[r]] * rbytes;
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  if (act) {
-    const int u = scr_unit[e];
-    p_tok[u * ts + before] = t;
-    p_j[u * ts + before] = j;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (act[r]) {
+      const int u = scr_unit[ev[r]];
+      p_tok[u * ts + before[r]] = tv[r];
+      p_j[u * ts + before[r]] = jv[r];
+    }
   }
   if (with_shared) {
     if (lane < T) {
@@ -577,10 +599,13 @@ __device__ __forceinline__ void pt_plan(const int* topi, int T, int k, int E, co
   // PT_GROUP_BASE + (its token count); p_cum[U1] = all of them
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  const int c = lane < U ? PT_GROUP_BASE + p_ntok[lane] : 0;
-  const int incl = pt_wave_scan(c);
-  if (lane < U) p_cum[lane] = incl - c;
-  const int sum_r = U > 0 ? __builtin_amdgcn_readlane(incl, U - 1) : 0;
+  const int c0 = lane < U ? PT_GROUP_BASE + p_ntok[lane] : 0;
+  const int c1 = lane + 64 < U ? PT_GROUP_BASE + p_ntok[lane + 64] : 0;
+  const int incl0 = pt_wave_scan(c0);
+  const int incl1 = pt_wave_scan(c1) + __builtin_amdgcn_readlane(incl0, 63);
+  if (lane < U) p_cum[lane] = incl0 - c0;
+  if (lane + 64 < U) p_cum[lane + 64] = incl1 - c1;
+  const int sum_r = U == 0 ? 0 : U <= 64 ? __builtin_amdgcn_readlane(incl0, U - 1) : __builtin_amdgcn_readlane(incl1, U - 65);
   if (lane == 0) {
     p_cum[U] = sum_r;
     if (with_shared) p_cum[U + 1] = sum_r + PT_GROUP_BASE + T;

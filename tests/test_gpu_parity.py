@@ -446,8 +446,8 @@ def test_decode_stack_full_shape_persistent(moe, qfmt, T, k):
 @pytest.mark.parametrize("T,k", [(5, 10), (6, 10), (8, 10), (6, 6), (8, 8)])
 def test_decode_stack_wide_verify(moe, qfmt, T, k):
     """Verify windows of 5, 6 and 8 token positions, 4 layers of the full
-    shape: the default path (the persistent kernel while T * k <= 64, else
-    the per-layer kernel chain) and the chain, each layer checked against the
+    shape: the default path (the persistent kernel) and the per-layer kernel
+    chain, each layer checked against the
     oracle on the path's own layer inputs, and the same step repeated bit for
     bit on the same workspace."""
     L = 4
