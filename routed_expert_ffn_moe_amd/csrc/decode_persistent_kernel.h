@@ -1166,7 +1166,7 @@ __global__ __launch_bounds__(PT_THREADS) void decode_persistent_kernel(PtArgs a)
               }
             } else {
               const int un = 2 * kuq + (lq & 1);
-#pragma unroll
+#pragma unroll 2
               for (int jb = 0; jb < 4; ++jb) {
                 uint32_t xw[8];  // the prepared x of block 4 un + jb
 #pragma unroll
