@@ -15,7 +15,8 @@ permute, grouped GEMM on the matrix cores, combine).  On request:
   --int2   the int2 stack: decode at 1 and 4 tokens, a 16,384-token chunk;
   --tier   a hot tier of 4,096 expert slots: hit rate on a synthetic trace;
   --c2     one decode layer timed on its own, rotated over the 48 layers;
-  --ceilings  the device's practical HBM read and MFMA rates (probe kernels).
+  --ceilings  the device's practical HBM read and MFMA rates and the decode
+              kernel's all-to-all hand-offs on their own (probe kernels).
 The int2 run also takes one 16,384-token chunk through all 48 layers, with
 the usage update of every layer.  The CPU baseline times the oracle on the
 decode step and on a sample of the prefill chunk's expert groups.
@@ -649,6 +650,9 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         ce["library_fp16_gemm_8192_tflops"] = round(2 * 8192 ** 3 * 5 / (e0.elapsed_time(e1) / 1e3) / 1e12, 1)
+        # the decode kernel's three hand-offs on their own: the exchange floor of a layer
+        ce["exchange_us_per_round"] = {name: round(probes.exchange_us(pat, device=dev), 3)
+                                       for pat, name in probes.EXCHANGE_PATTERNS.items()}
         del a16, b16
         log(f"ceilings: {json.dumps(ce)}")
         out.setdefault("extra", {})["ceilings"] = ce

@@ -44,6 +44,9 @@ SIGNATURES = {
     "moe_probe_mfma": (_i, [_i, _vp, _vp]),
     "moe_probe_mfma_blocks": (_i, []),
     "moe_probe_mfma_flops": (ctypes.c_double, [_i]),
+    "moe_probe_exchange": (_i, [_i, _i, _vp, _sz, _vp, _vp, _vp]),
+    "moe_probe_exchange_blocks": (_i, []),
+    "moe_probe_exchange_ws_bytes": (_sz, []),
     "moe_validate_routing": (_i, [_vp, _i, _i, _i]),
     "moe_validate_slot_table": (_i, [_vp, _i, _i, _i64]),
     "moe_validate_rows": (_i, [_vp, _vp, _vp, _i, _i, _i]),

@@ -90,3 +90,102 @@ extern "C" int moe_probe_mfma(int iters, float* sink, void* stream) {
   probe_mfma_kernel<<<probe_cus(), 64 * PROBE_MFMA_WAVES, 0, moe_stream(stream)>>>(iters, sink);
   return moe_check_launch("probe mfma");
 }
+
+// ---------------------------------------------------------------- exchange
+// The all-to-all hand-offs of the persistent decode kernel with no other work:
+// one 512-thread workgroup per CU (G of them, all resident), tagged 8-byte
+// words (tag = round + 1 in the high half), relaxed agent-scope stores and
+// loads, each thread polling its own words until they carry the round's tag
+// (or a later one),
+// then one workgroup barrier per round.  Patterns: 0 = x (every workgroup
+// publishes 2,048 / G words to each of the 8 per-XCD copies and reads the
+// 2,048 words of its XCD's copy), 1 = logits (512 words, likewise), 2 =
+// partial sums (every workgroup writes 2,048 words and reads its 2,048 / G
+// rows of all G producers).  ticks[g]: the 100 MHz wall-clock ticks
+// workgroup g spent on the rounds; err[0] counts workgroups whose wait ran
+// past its bound (the probe then stops).
+#define PROBE_XCHG_SPIN (1 << 18)
+__global__ __launch_bounds__(512) void probe_exchange_kernel(int pattern, int rounds, unsigned long long* buf,
+                                                             long long* ticks, int* err) {
+  const int g = blockIdx.x, G = gridDim.x, tid = threadIdx.x;
+  const int xcc = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7;
+  const int NW = pattern == 1 ? 512 : 2048;  // words of the exchanged vector
+  const int per = NW / G;                    // words each workgroup publishes (or rows it reads, pattern 2)
+  const long long t0 = __builtin_amdgcn_s_memrealtime();
+  for (int r = 0; r < rounds; ++r) {
+    const unsigned long long tag = (unsigned long long)(r + 1) << 32;
+    if (pattern < 2) {
+      for (int i = tid; i < 8 * per; i += 512) {  // my words, into all 8 copies
+        const int c = i / per, w = g * per + i % per;
+        __hip_atomic_store(buf + (size_t)c * NW + w, tag | (unsigned)(g + w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      for (int i = tid; i < 2048; i += 512)
+        __hip_atomic_store(buf + (size_t)g * 2048 + i, tag | (unsigned)i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    bool ok = true;
+    // my words to poll: pattern < 2: the NW words of my XCD's copy; pattern
+    // 2: rows g * per .. of every producer (G * per = 2,048 words)
+    for (int i0 = 0; i0 < (pattern < 2 ? NW : 2048); i0 += 4 * 512) {
+      unsigned long long w[4];
+      bool need[4];
+      size_t off[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = i0 + tid + 512 * q;
+        need[q] = i < (pattern < 2 ? NW : 2048);
+        const int ic = need[q] ? i : 0;
+        off[q] = pattern < 2 ? (size_t)xcc * NW + ic : (size_t)(ic / per) * 2048 + (size_t)g * per + ic % per;
+      }
+      for (int it = 0;; ++it) {
+        bool any = false;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (need[q]) w[q] = __hip_atomic_load(buf + off[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          // (a word may already carry a later round's tag: rounds here are not
+          // chained by data, so a fast producer can run one round ahead)
+          need[q] = need[q] && (w[q] >> 32) < (unsigned long long)(r + 1);
+          any |= need[q];
+        }
+        if (!any) break;
+        if (it > PROBE_XCHG_SPIN) { ok = false; break; }
+      }
+    }
+    if (!__syncthreads_and(ok)) {
+      if (tid == 0) atomicAdd(err, 1);
+      break;
+    }
+  }
+  if (tid == 0) ticks[g] = __builtin_amdgcn_s_memrealtime() - t0;
+}
+
+__global__ void probe_exchange_clear_kernel(unsigned long long* buf, size_t n, int* err) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) buf[i] = 0ull;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *err = 0;
+}
+
+extern "C" int moe_probe_exchange_blocks(void) { return probe_cus(); }
+extern "C" size_t moe_probe_exchange_ws_bytes(void) {
+  const size_t G = (size_t)probe_cus();
+  return (G * 2048 > 8 * 2048 ? G * 2048 : 8 * 2048) * 8;
+}
+
+extern "C" int moe_probe_exchange(int pattern, int rounds, void* ws, size_t ws_bytes, long long* ticks, int* err,
+                                  void* stream) {
+  MOE_REQUIRE(pattern >= 0 && pattern <= 2, MOE_EINVAL, "pattern %d must be 0, 1 or 2", pattern);
+  MOE_REQUIRE(rounds >= 1, MOE_EINVAL, "rounds must be >= 1");
+  MOE_REQUIRE(ws && ticks && err, MOE_EINVAL, "ws, ticks and err are required");
+  MOE_REQUIRE(ws_bytes >= moe_probe_exchange_ws_bytes() && moe_aligned(ws, 8), MOE_EWORKSPACE,
+              "ws needs %zu bytes, 8-byte aligned", moe_probe_exchange_ws_bytes());
+  const int G = probe_cus();
+  MOE_REQUIRE(G <= 512 && 2048 % G == 0 && 512 % G == 0, MOE_EUNSUPPORTED,
+              "the exchange probe needs a CU count dividing 512 (have %d)", G);
+  int per_cu = 0;
+  MOE_REQUIRE(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)probe_exchange_kernel, 512, 0) ==
+                      hipSuccess && per_cu >= 1,
+              MOE_EUNSUPPORTED, "the exchange probe's workgroups cannot all be resident");
+  hipStream_t st = moe_stream(stream);
+  probe_exchange_clear_kernel<<<256, 256, 0, st>>>((unsigned long long*)ws, ws_bytes / 8, err);
+  probe_exchange_kernel<<<G, 512, 0, st>>>(pattern, rounds, (unsigned long long*)ws, ticks, err);
+  return moe_check_launch("probe exchange");
+}

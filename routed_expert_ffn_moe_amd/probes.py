@@ -48,3 +48,24 @@ def mfma_tflops(iters=20000, reps=5, device="cuda"):
         check(lib.moe_probe_mfma(iters, ctypes.c_void_p(sink.data_ptr()), s))
     t = _time(run, reps)
     return lib.moe_probe_mfma_flops(iters) / t / 1e12
+
+
+EXCHANGE_PATTERNS = {0: "x", 1: "logits", 2: "partials"}
+
+
+def exchange_us(pattern, rounds=2000, device="cuda"):
+    """Microseconds per round of one all-to-all hand-off of the decode kernel
+    on its own (pattern 0 x, 1 logits, 2 partial sums): the slowest
+    workgroup's time over the rounds, divided by the rounds."""
+    lib = _lib.load()
+    G = lib.moe_probe_exchange_blocks()
+    ws = torch.empty(lib.moe_probe_exchange_ws_bytes(), dtype=torch.uint8, device=device)
+    ticks = torch.zeros(G, dtype=torch.int64, device=device)
+    err = torch.zeros(1, dtype=torch.int32, device=device)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    check(lib.moe_probe_exchange(pattern, rounds, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                 ctypes.c_void_p(ticks.data_ptr()), ctypes.c_void_p(err.data_ptr()), s))
+    torch.cuda.synchronize()
+    if int(err.item()) != 0:
+        raise RuntimeError(f"exchange probe pattern {pattern}: {int(err.item())} workgroups timed out")
+    return float(ticks.max().item()) / 100.0 / rounds

@@ -266,9 +266,12 @@ def test_rmsnorm_rejects(lib):
 
 def test_probe_header_symbols_are_exported(lib):
     names = declared_functions(PROBES)
-    assert len(names) == 5, names
+    assert len(names) == 8, names
     for n in names:
         assert hasattr(lib, n) and n in _lib.SIGNATURES, n
     assert lib.moe_probe_stream_read(None, 16, FAKE, None) == _lib.MOE_EINVAL
     assert lib.moe_probe_stream_read(FAKE + 4, 16, FAKE, None) == _lib.MOE_EALIGN
     assert lib.moe_probe_mfma(0, FAKE, None) == _lib.MOE_EINVAL
+    assert lib.moe_probe_exchange(3, 10, FAKE, 1 << 30, FAKE, FAKE, None) == _lib.MOE_EINVAL
+    assert lib.moe_probe_exchange(0, 0, FAKE, 1 << 30, FAKE, FAKE, None) == _lib.MOE_EINVAL
+    assert lib.moe_probe_exchange(0, 10, FAKE, 8, FAKE, FAKE, None) == _lib.MOE_EWORKSPACE
