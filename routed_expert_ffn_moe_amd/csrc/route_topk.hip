@@ -8,6 +8,7 @@
 #include "moe_common.h"
 #include "moe_sizes.h"
 #include "moe_kernels.h"
+#include "moe_topk.h"
 
 // ---------------------------------------------------------------- logits, few tokens
 // One wave per router row e (4 rows per 256-thread workgroup).  Lane l owns the
@@ -62,27 +63,52 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const XT* __restrict__
 // bf16 x bf16 products are exact and accumulate in fp32, like the VALU path
 // (only the summation order differs).  Workgroup tile 128 tokens x 128
 // experts, wave (wm, wn) owns tokens 64wm.. and experts 64wn.. (2 x 2 MFMA
-// tiles).  Both operands go straight from global memory into registers: an
-// MFMA sums over K, so A and B only have to agree on the K order, and within
-// each 32 of K lane group hh = lane / 32 holds K values 16hh + 8s + i in step
-// s (i < 8) -- 32 contiguous bytes of its row.  K is walked 64 at a time with
-// the next chunk prefetched.  Rows past T and experts past E are clamped on
-// load and not stored.  Needs H % 64 == 0.
+// tiles).  K is walked 64 at a time; each chunk of both operands (2 x 16 KB)
+// is loaded with 16-byte coalesced reads (8 threads per 128-byte row
+// segment), stored to one of two LDS stages and read back as MFMA fragments,
+// so that a workgroup reads each of its 128 + 128 rows once (1 MB at H =
+// 2048; a CU's load rate, not the matrix cores, bounds this kernel).  Two
+// chunks are in flight while the MFMAs of a third run.  Rows past T and
+// experts past E are clamped on load and not stored.  Needs H % 128 == 0.
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
-__global__ __launch_bounds__(256, 2) void router_mfma_kernel(const uint16_t* __restrict__ x, int T, int H,
-                                                             const uint16_t* __restrict__ wr,
-                                                             const float* __restrict__ bias, int E,
-                                                             float* __restrict__ logits) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#define RL_BM 128        // tokens (and experts) per workgroup tile
+#define RL_KC 64         // K per chunk
+#define RL_ST (RL_KC + 8)  // halves per LDS row: 16-byte fragment reads of 16 rows hit distinct banks
+__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x, int T, int H,
+                                                          const uint16_t* __restrict__ wr,
+                                                          const float* __restrict__ bias, int E,
+                                                          float* __restrict__ logits) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ls[2][2][RL_BM * RL_ST];  // [stage][x | Wr]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1, ln = lane & 31, hh = lane >> 5;
-  const int t0 = blockIdx.x * 128 + 64 * wm, e0 = blockIdx.y * 128 + 64 * wn;
-  const uint16_t* ap[2];
-  const uint16_t* bp[2];
+  const int t0 = blockIdx.x * RL_BM, e0 = blockIdx.y * RL_BM;
+  // staging: thread tid moves 16-byte word tid % 8 of rows tid / 8 + 32 j (j < 4) of both operands
+  const int wc = tid & 7, r0 = tid >> 3;
+  const uint16_t* ga[4];
+  const uint16_t* gb[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    ap[i] = x + (size_t)min(t0 + 32 * i + ln, T - 1) * H + 16 * hh;
-    bp[i] = wr + (size_t)min(e0 + 32 * i + ln, E - 1) * H + 16 * hh;
+  for (int j = 0; j < 4; ++j) {
+    ga[j] = x + (size_t)min(t0 + r0 + 32 * j, T - 1) * H + 8 * wc;
+    gb[j] = wr + (size_t)min(e0 + r0 + 32 * j, E - 1) * H + 8 * wc;
   }
+  // two register sets of staged words (plain vector loads and stores: a
+  // HIP uint4 copy would go through a private-memory temporary)
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 ra[8], sa[8];  // [j] = x row r0 + 32 j, [4 + j] = Wr row r0 + 32 j
+  auto gload = [&](u32x4 (&S)[8], int c) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      S[j] = *reinterpret_cast<const u32x4*>(ga[j] + c * RL_KC);
+      S[4 + j] = *reinterpret_cast<const u32x4*>(gb[j] + c * RL_KC);
+    }
+  };
+  auto lstore = [&](const u32x4 (&S)[8], int stage) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<u32x4*>(&Ls[stage][0][(r0 + 32 * j) * RL_ST + 8 * wc]) = S[j];
+      *reinterpret_cast<u32x4*>(&Ls[stage][1][(r0 + 32 * j) * RL_ST + 8 * wc]) = S[4 + j];
+    }
+  };
   float16v acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -90,56 +116,57 @@ __global__ __launch_bounds__(256, 2) void router_mfma_kernel(const uint16_t* __r
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  // chunk of 64: 2 sub-chunks of 32, 2 uint4 (steps) each
-  uint4 a[2][4], b[2][4], an[2][4], bn[2][4];
-  auto load = [&](uint4 (&A)[2][4], uint4 (&B)[2][4], int c) {
+  // lane (ln, hh) holds K values 16s + 8hh .. +8 of row ln of each tile in step s
+  auto mfmas = [&](int stage) {
+    const uint16_t* As = &Ls[stage][0][(64 * wm + ln) * RL_ST + 8 * hh];
+    const uint16_t* Bs = &Ls[stage][1][(64 * wn + ln) * RL_ST + 8 * hh];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int s = 0; s < RL_KC / 16; ++s) {
+      uint4 a[2], b[2];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const uint4* pa = reinterpret_cast<const uint4*>(ap[i] + c * 64 + 32 * q);
-        const uint4* pb = reinterpret_cast<const uint4*>(bp[i] + c * 64 + 32 * q);
-        A[i][2 * q] = pa[0];
-        A[i][2 * q + 1] = pa[1];
-        B[i][2 * q] = pb[0];
-        B[i][2 * q + 1] = pb[1];
+      for (int i = 0; i < 2; ++i) {
+        a[i] = *reinterpret_cast<const uint4*>(As + 32 * i * RL_ST + 16 * s);
+        b[i] = *reinterpret_cast<const uint4*>(Bs + 32 * i * RL_ST + 16 * s);
       }
-  };
-  const int nc = H / 64;  // even: H is a multiple of 128
-  auto mfmas = [&](const uint4 (&A)[2][4], const uint4 (&B)[2][4]) {
-#pragma unroll
-    for (int s8 = 0; s8 < 4; ++s8)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, A[i][s8]),
-                                                             __builtin_bit_cast(bf16x8v, B[j][s8]), acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, a[i]),
+                                                             __builtin_bit_cast(bf16x8v, b[j]), acc[i][j], 0, 0, 0);
+    }
   };
-  // two register buffers in turn (no copy between them, which would make
-  // the compiler wait for the prefetch at the end of every chunk); every
-  // prefetch is unconditional (the last chunks request themselves again)
-  // and issued before the MFMAs of the chunk in hand
-  load(a, b, 0);
+  // chunk c + 1 is stored to LDS while chunk c + 2 is in flight; every load
+  // is unconditional (the last chunks request themselves again), so the
+  // wait before each store leaves the newer loads outstanding
+  const int nc = H / RL_KC;  // even: H is a multiple of 128
+  gload(ra, 0);
+  gload(sa, min(1, nc - 1));
+  lstore(ra, 0);
+  __syncthreads();
   for (int c = 0; c < nc; c += 2) {
-    load(an, bn, min(c + 1, nc - 1));
+    gload(ra, min(c + 2, nc - 1));
+    __builtin_amdgcn_sched_barrier(0);  // (the scheduler would sink the loads below the stores)
+    mfmas(0);
+    lstore(sa, 1);  // chunk c + 1
+    __syncthreads();
+    gload(sa, min(c + 3, nc - 1));
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(a, b);
-    load(a, b, min(c + 2, nc - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(an, bn);
+    mfmas(1);
+    lstore(ra, 0);  // chunk c + 2 (after the last chunk: a harmless rewrite)
+    __syncthreads();
   }
   // lane holds expert column ln, tokens 8*(v/4) + 4*hh + v%4 of each 32 x 32 tile
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int e = e0 + 32 * j + ln;
+    const int e = e0 + 64 * wn + 32 * j + ln;
     if (e >= E) continue;
     const float be = bias ? bias[e] : 0.f;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int t = t0 + 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
+        const int t = t0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
         if (t < T) logits[(size_t)t * E + e] = acc[i][j][v] + be;
       }
   }
@@ -199,60 +226,18 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const XT* __restrict_
 }
 
 // ---------------------------------------------------------------- top-k
-// One wave per token.  Lane l holds the keys of experts l, l+64, ...; a key is
-// (order-preserving logit bits) << 32 | ~e, so the wave maximum is the larger
-// logit and, among equal logits, the lower index.  k rounds of wave argmax.
-__device__ void moe_topk_wave(const float* __restrict__ lg, int E, int k, int32_t* __restrict__ idx_out,
-                              float* __restrict__ w_out) {
-  const int lane = threadIdx.x & 63;
-  uint64_t key[MOE_MAX_E / 64];
-#pragma unroll
-  for (int i = 0; i < MOE_MAX_E / 64; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = (e < E) ? (((uint64_t)moe_f32_order_key(lg[e]) << 32) | (uint32_t)(~(uint32_t)e)) : 0ull;
-  }
-  float chosen[MOE_MAX_K];
-  int chosen_e[MOE_MAX_K];
-#pragma unroll
-  for (int j = 0; j < MOE_MAX_K; ++j) {
-    if (j < k) {
-      uint64_t m = 0;
-#pragma unroll
-      for (int i = 0; i < MOE_MAX_E / 64; ++i) m = key[i] > m ? key[i] : m;
-      m = moe_wave_max_u64(m);
-      const uint32_t e = ~(uint32_t)m;
-      chosen_e[j] = (int)e;
-      chosen[j] = moe_order_key_f32((uint32_t)(m >> 32));
-#pragma unroll
-      for (int i = 0; i < MOE_MAX_E / 64; ++i)
-        if (key[i] == m) key[i] = 0ull;
-    }
-  }
-  if (lane == 0) {
-    float z[MOE_MAX_K];
-    float sum = 0.f;
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_K; ++j) {
-      if (j < k) {
-        z[j] = expf(chosen[j] - chosen[0]);
-        sum += z[j];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_K; ++j) {
-      if (j < k) {
-        idx_out[j] = chosen_e[j];
-        w_out[j] = z[j] / sum;
-      }
-    }
-  }
-}
-
+// One wave per token (moe_topk_select: a 16-bit threshold on the lane maxima
+// found with ballots, the keys above it ranked in LDS, extraction rounds when
+// more than 64 keys tie), then the softmax weights of the chosen logits.
+template <int SLOTS>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                    int32_t* __restrict__ idx, float* __restrict__ w) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  moe_topk_wave(logits + (size_t)t * E, E, k, idx + (size_t)t * k, w + (size_t)t * k);
+  __shared__ uint64_t cand[4][64];
+  const int wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;  // whole waves; no workgroup barrier follows
+  const uint32_t key = moe_topk_select<SLOTS>(logits + (size_t)t * E, E, k, idx + (size_t)t * k, cand[wave]);
+  moe_topk_weights(key, k, w + (size_t)t * k);
 }
 
 // ---------------------------------------------------------------- launcher
@@ -276,7 +261,10 @@ int moe_launch_route(const void* x, int x_dtype, int T, int H, const uint16_t* w
   }
   int rc = moe_check_launch("router logits");
   if (rc) return rc;
-  topk_kernel<<<(T + 3) / 4, 256, 0, st>>>(logits, T, E, k, topk_idx, topk_w);
+  if (E <= 512)
+    topk_kernel<8><<<(T + 3) / 4, 256, 0, st>>>(logits, T, E, k, topk_idx, topk_w);
+  else
+    topk_kernel<MOE_MAX_E / 64><<<(T + 3) / 4, 256, 0, st>>>(logits, T, E, k, topk_idx, topk_w);
   return moe_check_launch("top-k");
 }
 

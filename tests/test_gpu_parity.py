@@ -41,11 +41,14 @@ def _check_routing(idx_gpu, w_gpu, idx_ref, w_ref):
 
 # ---------------------------------------------------------------- router / top-k
 
-@pytest.mark.parametrize("T,E,k,bias,bf16", [(4, 16, 2, False, False), (4, 16, 2, True, True),
-                                            (67, 16, 2, False, False), (200, 37, 5, True, True),
-                                            (3, 1000, 16, False, False), (5, 16, 16, False, False)])
-def test_route_topk_small(moe, T, E, k, bias, bf16):
-    H = 256
+@pytest.mark.parametrize("T,E,k,bias,bf16,H", [(4, 16, 2, False, False, 256), (4, 16, 2, True, True, 256),
+                                              (67, 16, 2, False, False, 256), (200, 37, 5, True, True, 256),
+                                              (3, 1000, 16, False, False, 256), (5, 16, 16, False, False, 256),
+                                              # bf16 chunks on the matrix cores: ragged 128-token and
+                                              # 128-expert tiles, E > 512 (16 keys per lane in top-k)
+                                              (200, 37, 5, True, True, 384), (300, 512, 10, True, True, 2048),
+                                              (33, 40, 6, False, True, 512), (9, 600, 8, True, True, 256)])
+def test_route_topk_small(moe, T, E, k, bias, bf16, H):
     Wr = G.draw_router(0, 0, E, H)
     b = G.zipf_bias(0, 0, E) if bias else None
     x, _ = G.draw_x_rejecting(0, T, H, C.gap_acceptor(Wr, b, k, as_bf16=bf16))
