@@ -130,6 +130,32 @@ def test_permute_empty(moe):
     assert _np(counts).tolist() == [0] * 7 and _np(offsets).tolist() == [0] * 8
 
 
+@pytest.mark.parametrize("k", list(range(1, 17)))
+def test_combine_every_k(moe, k):
+    """Both row layouts (prefill: permuted rows + shared; decode: T x (k+1)
+    rows) for every k, H not a multiple of 1,024 (a partial workgroup), and
+    the residual given as the output buffer itself (the decode chain's use)."""
+    T, H = 7, 1028
+    g = torch.Generator().manual_seed(100 + k)
+    w = torch.rand((T, k), generator=g)
+    w = (w / w.sum(1, keepdim=True)).float()
+    routed = torch.randn((T, k, H), generator=g)
+    shared = torch.randn((T, H), generator=g)
+    resid = torch.randn((T, H), generator=g)
+    ref = O.combine(routed.double().numpy(), w.double().numpy(), shared.double().numpy(), resid.double().numpy())
+    perm = torch.randperm(T * k, generator=g)
+    y_perm = torch.empty((T * k, H))
+    y_perm[perm] = routed.reshape(T * k, H)
+    inv_row = perm.to(torch.int32).reshape(T, k)
+    out = resid.clone().cuda()
+    moe.moe_combine(y_perm.cuda(), w.cuda(), inv_row=inv_row.cuda(), y_shared=shared.cuda(), residual=out, y_out=out)
+    tol = 1e-5 * (np.abs(ref).max() + 1)
+    assert np.max(np.abs(_np(out) - ref)) <= tol
+    rows = torch.cat([routed, shared.unsqueeze(1)], 1).reshape(T * (k + 1), H)
+    y = moe.moe_combine(rows.cuda(), w.cuda(), residual=resid.cuda())
+    assert torch.equal(y.cpu(), out.cpu())  # same sums in the same order
+
+
 # ---------------------------------------------------------------- decode experts
 
 def _layer_outputs_decode(moe, li, x, layer=0):
