@@ -5,24 +5,46 @@
 #include "moe_common.h"
 #include "moe_kernels.h"
 
+// KC > 0: k == KC at compile time, so that a thread requests all of its rows
+// before the first add; KC == 0: any k, one row after another.
+template <int KC>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_rows,
                                                       const int32_t* __restrict__ inv_row,
                                                       const float* __restrict__ y_shared,
                                                       const float* __restrict__ topk_w,
-                                                      const float* residual, int k, int H,
+                                                      const float* residual, int k_rt, int H,
                                                       float* y_out) {
+  const int k = KC > 0 ? KC : k_rt;
   const int t = blockIdx.y;
   const int h = 4 * (blockIdx.x * 256 + threadIdx.x);
   if (h >= H) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
+  auto row_of = [&](int j) {
+    return inv_row ? (size_t)inv_row[(size_t)t * k + j] : (size_t)t * (k + 1) + j;
+  };
+  auto add = [&](int j, float4 v) {
     const float w = topk_w[(size_t)t * k + j];
-    const size_t row = inv_row ? (size_t)inv_row[(size_t)t * k + j] : (size_t)t * (k + 1) + j;
-    const float4 v = *reinterpret_cast<const float4*>(y_rows + row * H + h);
     acc.x = fmaf(w, v.x, acc.x);
     acc.y = fmaf(w, v.y, acc.y);
     acc.z = fmaf(w, v.z, acc.z);
     acc.w = fmaf(w, v.w, acc.w);
+  };
+  if constexpr (KC > 0) {
+    size_t row[KC];
+    if (inv_row) {
+#pragma unroll
+      for (int j = 0; j < KC; ++j) row[j] = (size_t)inv_row[(size_t)t * KC + j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < KC; ++j) row[j] = (size_t)t * (KC + 1) + j;
+    }
+    float4 v[KC];
+#pragma unroll
+    for (int j = 0; j < KC; ++j) v[j] = *reinterpret_cast<const float4*>(y_rows + row[j] * H + h);
+#pragma unroll
+    for (int j = 0; j < KC; ++j) add(j, v[j]);
+  } else {
+    for (int j = 0; j < k; ++j) add(j, *reinterpret_cast<const float4*>(y_rows + row_of(j) * H + h));
   }
   const float* sh = inv_row ? y_shared + (size_t)t * H : y_rows + ((size_t)t * (k + 1) + k) * H;
   const float4 s = *reinterpret_cast<const float4*>(sh + h);
@@ -38,7 +60,13 @@ int moe_launch_combine(const float* y_rows, const int32_t* inv_row, const float*
                        const float* residual, int T, int k, int H, float* y_out, hipStream_t st) {
   if (T == 0) return MOE_OK;
   dim3 grid((H / 4 + 255) / 256, T);
-  combine_kernel<<<grid, 256, 0, st>>>(y_rows, inv_row, y_shared, topk_w, residual, k, H, y_out);
+  switch (k) {
+    case 2: combine_kernel<2><<<grid, 256, 0, st>>>(y_rows, inv_row, y_shared, topk_w, residual, k, H, y_out); break;
+    case 6: combine_kernel<6><<<grid, 256, 0, st>>>(y_rows, inv_row, y_shared, topk_w, residual, k, H, y_out); break;
+    case 8: combine_kernel<8><<<grid, 256, 0, st>>>(y_rows, inv_row, y_shared, topk_w, residual, k, H, y_out); break;
+    case 10: combine_kernel<10><<<grid, 256, 0, st>>>(y_rows, inv_row, y_shared, topk_w, residual, k, H, y_out); break;
+    default: combine_kernel<0><<<grid, 256, 0, st>>>(y_rows, inv_row, y_shared, topk_w, residual, k, H, y_out);
+  }
   return moe_check_launch("combine");
 }
 

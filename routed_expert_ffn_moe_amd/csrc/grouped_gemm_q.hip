@@ -16,17 +16,16 @@
 // converted to fp16 (exact in fp16's normal range) once, into the workspace,
 // before the gate/up pass; accumulation is fp32.
 //
-// gemm2_kernel uses workgroups of 4 waves where wave w owns weight rows
+// gemm3_kernel uses workgroups of 4 waves where wave w owns weight rows
 // nbase..nbase+63 = two 32-wide MFMA column tiles over the tile's 32-row MFMA
 // row tiles; for the gate/up pass the record interleaves gate and up rows in
 // runs of 32, so a wave's two column tiles are gate and up of the same 32 f
-// values and SiLU*mul happens in registers.  The next K chunk's A tile and B
-// words are requested before the current chunk's MFMAs (A through registers
-// into a double-buffered LDS tile).  Tiles hold up to BM = 160 rows (a
-// typical expert is one tile, each dequantised weight operand feeds up to 5
-// MFMAs), K chunks of 64, and the K loop is specialised on the row-tile
-// count: no branches, so the compiler's waits count only the loads a step
-// needs.
+// values and SiLU*mul happens in registers.  Tiles hold up to BM = 192 rows
+// (an expert of a chunk that routes about 160 rows to each expert is one
+// tile, and each dequantised weight operand feeds up to 6 MFMAs), K chunks of
+// 64.  A chunks are copied from global memory straight into a three-stage LDS
+// ring, two chunks ahead of the MFMAs, and the K loop is specialised on the
+// row-tile count, with no branches.
 //
 // Blocks are renumbered so that consecutive work items (the column tiles of
 // one row tile, then the row tiles of one expert) land on the same XCD
@@ -133,26 +132,29 @@ __device__ __forceinline__ half8v deq_q2(uint32_t w, int hh, half2v s2, half2v m
   return r;
 }
 
-// ---------------------------------------------------------------- gemm2
-// The same contraction with tiles of up to 160 rows (5 MFMA row tiles) x 256
-// weight rows and K chunks of 64.  Wave w owns two 32-wide column tiles (for
-// gate/up: the gate and the up columns of the same 32 f values, which the
-// record interleaves in runs of 32, so SiLU*mul happens in registers); each
-// dequantised B operand feeds up to 5 MFMAs (a 160-row expert is one tile,
-// not 64 + 96 rows) and each A operand read from LDS feeds 2.
-#define G2_BM 160
-#define G2_BN 256
-#define G2_KC 64
-#define G2_NB (G2_KC / 32)  // int4 blocks per K chunk
-#define G2_STRIDE 72        // halves per staged row (64 + 8 pad)
-#define G2_RT (G2_BM / 32)  // MFMA row tiles per workgroup tile
-#define G2_NA ((G2_BM * G2_KC / 8 + 255) / 256)  // 16-byte A words per staging thread
+// ---------------------------------------------------------------- tile kernel
+// Tiles of up to 192 rows (6 MFMA row tiles; 160 for int2) x 256 weight rows,
+// K chunks of 64.  Wave w owns two 32-wide column tiles (for gate/up: the gate
+// and the up columns of the same 32 f values, which the record interleaves in
+// runs of 32, so SiLU*mul happens in registers); each dequantised B operand
+// feeds up to 6 MFMAs and each A operand read from LDS feeds 2.  An expert of
+// up to 192 rows is one tile, so its weights are read and dequantised once.
+#define G3_BM 192  // rows of a staged A chunk (the largest tile)
+#define G3_BN 256
+#define G3_KC 64
+#define G3_NB (G3_KC / 32)              // int4 blocks per K chunk
+// MFMA row tiles per workgroup tile: 6 for int4; 5 for int2, whose raw
+// weight words of a K chunk take more registers (two 16-byte words per
+// column tile)
+template <int QFMT>
+constexpr int g3_rt() { return QFMT == MOE_Q4_B32 ? 6 : 5; }
+#define G3_STAGE_B (G3_BM * G3_KC * 2)  // bytes of one staged A chunk
 
 template <int QFMT>
 struct B2Regs;  // raw weight words of one K chunk (64) for one lane and one column tile
 template <>
 struct B2Regs<MOE_Q4_B32> {
-  uint2 q[G2_NB];  // [block in chunk]: dwords 2hh, 2hh+1 of the block
+  uint2 q[G3_NB];  // [block in chunk]: dwords 2hh, 2hh+1 of the block
   uint32_t s;      // fp16 scales of the chunk's two blocks
 };
 template <>
@@ -171,11 +173,11 @@ __device__ __forceinline__ void load_b2(B2Regs<MOE_Q4_B32>& b, const uint8_t* re
   const uint32_t q_off = (uint32_t)(gu ? pl.gu_q : pl.d_q), s_off = (uint32_t)(gu ? pl.gu_s : pl.d_s);
   const uint32_t R = (uint32_t)rows, ur = (uint32_t)r;
 #pragma unroll
-  for (int bi = 0; bi < G2_NB; ++bi) {
-    const uint32_t kb = (uint32_t)(G2_NB * c + bi);
+  for (int bi = 0; bi < G3_NB; ++bi) {
+    const uint32_t kb = (uint32_t)(G3_NB * c + bi);
     b.q[bi] = *reinterpret_cast<const uint2*>(rec + (q_off + 16u * (kb * R + ur) + 8u * (uint32_t)hh));
   }
-  const uint32_t kb0 = (uint32_t)(G2_NB * c);  // even
+  const uint32_t kb0 = (uint32_t)(G3_NB * c);  // even
   if (gu)  // 4-block groups [kb/4][row][4]: the two scales are half of the group's word
     b.s = *reinterpret_cast<const uint32_t*>(rec + (s_off + 2u * ((kb0 >> 2) * R * 4u + 4u * ur + (kb0 & 3u))));
   else {   // per block [kb][row]
@@ -205,109 +207,132 @@ __device__ __forceinline__ void load_b2(B2Regs<MOE_Q2_B16>& b, const uint8_t* re
   (void)hh;
 }
 
-// The K loop of gemm2 for NRT row tiles: A chunks staged through registers
-// into a double-buffered LDS tile (the next chunk's A and B words are
-// requested before the current chunk's MFMAs), B dequantised in registers.
-template <int QFMT, bool GU, int NRT>
-__device__ __forceinline__ void gemm2_k_loop(const uint16_t* __restrict__ a_src, int K, int rows, const uint8_t* rec,
-                                             const MoePlanes& pl, int nbase, const int* arow,
-                                             _Float16 (*As)[G2_BM * G2_STRIDE], float16v (&acc)[G2_RT][2]) {
-  const int tid = threadIdx.x, lane = tid & 63;
+// s_waitcnt on the vector-memory count alone (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt and lgkmcnt at their maxima, so not waited on).
+template <int N>
+__device__ __forceinline__ void g3_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+#define G3_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// The K loop for NRT row tiles.  A chunks go straight from global memory into
+// a ring of three LDS stages (global_load_lds, 16 bytes per lane, through no
+// registers), two chunks ahead of the MFMAs; the B words (raw quantised words,
+// dequantised in registers) one chunk ahead.  Staged layout: row r of a chunk
+// (64 halves = eight 16-byte units) at r * 128 bytes, its logical unit u at
+// physical unit u ^ ((r >> 1) & 7), so that the 16 rows one ds_read_b128
+// phase touches fall on 16 distinct 4-bank groups.  One load instruction of
+// a wave fills 64 consecutive units (8 rows).
+// Step c: wait until only this wave's last NRT loads (its staging of chunk
+// c + 1) may be in flight, barrier (every wave's chunk c has landed, and every
+// wave is done with the stage chunk c + 2 overwrites), request B of chunk
+// c + 1 and then A of chunk c + 2, then the MFMAs of chunk c.  Requests past
+// the last chunk repeat the last one, so that every step issues its staging
+// loads last.
+template <int QFMT, bool GU, int NRT, int RT>
+__device__ __forceinline__ void gemm3_k_loop(const uint8_t* a_bytes, int K, int rows, const uint8_t* rec,
+                                             const MoePlanes& pl, int nbase, const int* arow, uint8_t* As0,
+                                             uint8_t* As1, float16v (&acc)[RT][2]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, ln = lane & 31;
-  constexpr int NW = NRT * 32 * G2_KC / 8;     // 16-byte A words of a chunk
-  constexpr int NA = (NW + 255) / 256;         // per thread
-  int src[NA];     // source row (clamped) of each staged word
-  bool live[NA];   // the row has a source (else the word is zero)
+  // this lane's source for each of its NRT staging loads: tile row
+  // 32j + 8*wave + lane/8, logical unit (lane & 7) ^ (that row's swizzle);
+  // rows without a source read row 0 (their results are never stored)
+  uint32_t voff[NRT];
+  {
+    const uint32_t u = (uint32_t)((lane & 7) ^ ((4 * wave + (lane >> 4)) & 7));
 #pragma unroll
-  for (int j = 0; j < NA; ++j) {
-    const int i = min(tid + 256 * j, NW - 1);
-    const int r = arow[i >> 3];
-    live[j] = r >= 0;
-    src[j] = r >= 0 ? r : 0;
+    for (int j = 0; j < NRT; ++j) {
+      const int r = arow[32 * j + 8 * wave + (lane >> 3)];
+      voff[j] = (uint32_t)(r < 0 ? 0 : r) * (uint32_t)(2 * K) + 16u * u;
+    }
   }
-  uint4 areg[NA];
-  auto load_a = [&](int c) {
+  // byte offsets in a stage of this lane's A fragments (row tile 0) for the
+  // four MFMA k-steps of a chunk
+  uint32_t aoff[4];
+  {
+    const int sw = (ln >> 1) & 7;
 #pragma unroll
-    for (int j = 0; j < NA; ++j) {
-      const int i = min(tid + 256 * j, NW - 1);
-      const uint4 v = *reinterpret_cast<const uint4*>(a_src + (size_t)src[j] * K + c * G2_KC + 8 * (i & 7));
-      areg[j] = live[j] ? v : make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < 4; ++q) {
+      const int u = QFMT == MOE_Q4_B32 ? 4 * (q >> 1) + 2 * hh + (q & 1) : 2 * q + hh;
+      aoff[q] = (uint32_t)(ln * 128 + 16 * (u ^ sw));
     }
-  };
-  auto store_a = [&](int stage) {
-#pragma unroll
-    for (int j = 0; j < NA; ++j) {
-      const int i = tid + 256 * j;
-      if (i < NW) *reinterpret_cast<uint4*>(&As[stage][(i >> 3) * G2_STRIDE + 8 * (i & 7)]) = areg[j];
-    }
-  };
+  }
   const int brow0 = min(nbase + ln, rows - 1), brow1 = min(nbase + 32 + ln, rows - 1);
-  const int nc = K / G2_KC;
+  const int nc = K / G3_KC;
   const uint32_t m4 = moe_vgpr_const(0x000F000Fu), m2b = moe_vgpr_const(0x00030003u);
-  B2Pair<QFMT> bcur, bnext;
-  load_a(0);
-  load_b2(bcur.t[0], rec, pl, rows, brow0, hh, 0, GU);
-  load_b2(bcur.t[1], rec, pl, rows, brow1, hh, 0, GU);
-  store_a(0);
-  __syncthreads();
-  for (int c = 0; c < nc; ++c) {
-    const int stage = c & 1;
-    const int cn = min(c + 1, nc - 1);  // the last chunk requests itself again (unused)
-    load_a(cn);
-    load_b2(bnext.t[0], rec, pl, rows, brow0, hh, cn, GU);
-    load_b2(bnext.t[1], rec, pl, rows, brow1, hh, cn, GU);
-    const _Float16* Ab = &As[stage][0];
-    if constexpr (QFMT == MOE_Q4_B32) {
+  B2Pair<QFMT> b0, b1;
+
+  auto issue_a = [&](int c, uint8_t* stage) {
+    const uint8_t* src = a_bytes + (size_t)c * (G3_KC * 2);
+    uint8_t* dst = stage + 1024 * wave;
 #pragma unroll
-      for (int bi = 0; bi < G2_NB; ++bi) {
+    for (int j = 0; j < NRT; ++j) __builtin_amdgcn_global_load_lds(src + voff[j], G3_LDS(dst + 4096 * j), 16, 0, 0);
+  };
+  auto issue_b = [&](int c, B2Pair<QFMT>& b) {
+    load_b2(b.t[0], rec, pl, rows, brow0, hh, c, GU);
+    load_b2(b.t[1], rec, pl, rows, brow1, hh, c, GU);
+  };
+  auto compute = [&](const uint8_t* Ab, const B2Pair<QFMT>& b) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int kk = 32 * bi + 16 * hh + 8 * s;
-          half8v af[NRT];
+    for (int q = 0; q < 4; ++q) {
+      half8v bf[2];
 #pragma unroll
-          for (int i = 0; i < NRT; ++i) af[i] = *reinterpret_cast<const half8v*>(&Ab[(32 * i + ln) * G2_STRIDE + kk]);
-#pragma unroll
-          for (int sub = 0; sub < 2; ++sub) {
-            const B2Regs<QFMT>& B = bcur.t[sub];
-            const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(B.s >> (16 * bi)));
-            const half2v s2 = {sc, sc};
-            const half8v bf = deq_q4(s == 0 ? B.q[bi].x : B.q[bi].y, s2, m4);
-#pragma unroll
-            for (int i = 0; i < NRT; ++i)
-              acc[i][sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf, acc[i][sub], 0, 0, 0);
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int kk = 16 * jj + 8 * hh;
-        half8v af[NRT];
-#pragma unroll
-        for (int i = 0; i < NRT; ++i) af[i] = *reinterpret_cast<const half8v*>(&Ab[(32 * i + ln) * G2_STRIDE + kk]);
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          const B2Regs<QFMT>& B = bcur.t[sub];
-          const uint32_t qw = jj == 0 ? B.q.x : jj == 1 ? B.q.y : jj == 2 ? B.q.z : B.q.w;
-          const uint32_t mw = jj == 0 ? B.m.x : jj == 1 ? B.m.y : jj == 2 ? B.m.z : B.m.w;
+      for (int sub = 0; sub < 2; ++sub) {
+        const B2Regs<QFMT>& B = b.t[sub];
+        if constexpr (QFMT == MOE_Q4_B32) {
+          const int bi = q >> 1, s = q & 1;
+          const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(B.s >> (16 * bi)));
+          const half2v s2 = {sc, sc};
+          bf[sub] = deq_q4(s == 0 ? B.q[bi].x : B.q[bi].y, s2, m4);
+        } else {
+          const uint32_t qw = q == 0 ? B.q.x : q == 1 ? B.q.y : q == 2 ? B.q.z : B.q.w;
+          const uint32_t mw = q == 0 ? B.m.x : q == 1 ? B.m.y : q == 2 ? B.m.z : B.m.w;
           const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(mw & 0xffff));
           const _Float16 mn = __builtin_bit_cast(_Float16, (uint16_t)(mw >> 16));
           const half2v s2 = {sc, sc}, m2 = {mn, mn};
-          const half8v bf = deq_q2(qw, hh, s2, m2, m2b);
-#pragma unroll
-          for (int i = 0; i < NRT; ++i)
-            acc[i][sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf, acc[i][sub], 0, 0, 0);
+          bf[sub] = deq_q2(qw, hh, s2, m2, m2b);
         }
       }
+#pragma unroll
+      for (int i = 0; i < NRT; ++i) {
+        const half8v af = *reinterpret_cast<const half8v*>(Ab + aoff[q] + 4096 * i);
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[0], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[1], acc[i][1], 0, 0, 0);
+      }
     }
-    store_a(stage ^ 1);  // (after the last chunk: a harmless rewrite of the free stage)
-    __syncthreads();
-    bcur = bnext;
+  };
+  // one step: chunk c from stage `cur` with B words `bcur`, after requesting
+  // B of chunk c + 1 into `bnext` and A of chunk c + 1 into stage `nxt`.  The
+  // two stages are separate LDS arrays, alternating at compile time, so that
+  // the compiler can tell the stage being read from the one being filled and
+  // does not wait for the fill before reading.
+  auto step = [&](int c, const uint8_t* cur, uint8_t* nxt, const B2Pair<QFMT>& bcur, B2Pair<QFMT>& bnext) {
+    g3_wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    const int cn = min(c + 1, nc - 1);
+    issue_b(cn, bnext);
+    issue_a(cn, nxt);
+    // keep the requests ahead of the MFMAs (the scheduler would sink them)
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur, bcur);
+  };
+  issue_b(0, b0);
+  issue_a(0, As0);
+  int c = 0;
+  for (; c + 2 <= nc; c += 2) {
+    step(c, As0, As1, b0, b1);
+    step(c + 1, As1, As0, b1, b0);
   }
+  if (c < nc) step(c, As0, As1, b0, b1);
+  // no staging load may still be writing LDS when the workgroup ends
+  g3_wait_vmcnt<0>();
 }
 
 template <int QFMT, bool GU>
-__global__ __launch_bounds__(256, 2) void gemm2_kernel(const uint16_t* __restrict__ a_src, int T, int H, int F, int k,
+__global__ __launch_bounds__(256, 2) void gemm3_kernel(const uint16_t* __restrict__ a_src, int T, int H, int F, int k,
                                                        int E, const int32_t* __restrict__ row_src,
                                                        const int32_t* __restrict__ tile_start,
                                                        const int4* __restrict__ tile_info,
@@ -315,8 +340,9 @@ __global__ __launch_bounds__(256, 2) void gemm2_kernel(const uint16_t* __restric
                                                        const uint8_t* __restrict__ pool, int64_t record_bytes,
                                                        _Float16* __restrict__ h_out, float* __restrict__ y_perm,
                                                        float* __restrict__ y_shared, int n_ntiles) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][G2_BM * G2_STRIDE];
-  __shared__ int arow[G2_BM];
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[G3_STAGE_B];
+  __shared__ __attribute__((aligned(1024))) uint8_t As1[G3_STAGE_B];
+  __shared__ int arow[G3_BM];
 
   // XCD-aware renumbering (block b runs on XCD b % 8): the work count is cut
   // into 8 consecutive ranges, one per XCD, so that the column tiles of one
@@ -330,16 +356,16 @@ __global__ __launch_bounds__(256, 2) void gemm2_kernel(const uint16_t* __restric
   const int tile = work / n_ntiles, nt = work % n_ntiles;
   const int4 ti = tile_info[tile];
   const int g = ti.x, m0 = ti.y, mv = ti.z, gbase = ti.w;
-  const int nrt = (mv + 31) / 32;  // row tiles present (<= 5)
+  const int nrt = (mv + 31) / 32;  // row tiles present (<= g3_rt<QFMT>())
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, ln = lane & 31;
   const int K = GU ? H : F;
   const int rows = GU ? 2 * F : H;
-  const int nbase = nt * G2_BN + 64 * wave;  // this wave's 64 weight rows
+  const int nbase = nt * G3_BN + 64 * wave;  // this wave's 64 weight rows
   const bool active = nbase < rows;
 
-  if (tid < G2_BM) {
+  if (tid < G3_BM) {
     int r = -1;
     if (tid < mv) {
       if (GU) r = g < E ? row_src[gbase + m0 + tid] / k : m0 + tid;
@@ -352,23 +378,25 @@ __global__ __launch_bounds__(256, 2) void gemm2_kernel(const uint16_t* __restric
   const MoePlanes pl = moe_planes(QFMT, H, F);
   __syncthreads();
 
-  float16v acc[G2_RT][2];
+  constexpr int RT = g3_rt<QFMT>();
+  float16v acc[RT][2];
 #pragma unroll
-  for (int i = 0; i < G2_RT; ++i)
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][sub][v] = 0.f;
-  // The K loop, specialised on the row-tile count (uniform per workgroup),
-  // so that it has no branches: its loads are unconditional (indices clamped
-  // into range; rows without a source are zeroed after the load) and the
-  // waits the compiler places count only the loads a step really needs.
+  // the K loop, specialised on the row-tile count (uniform per workgroup)
+  const uint8_t* ab = reinterpret_cast<const uint8_t*>(a_src);
   switch (nrt) {
-    case 1: gemm2_k_loop<QFMT, GU, 1>(a_src, K, rows, rec, pl, nbase, arow, As, acc); break;
-    case 2: gemm2_k_loop<QFMT, GU, 2>(a_src, K, rows, rec, pl, nbase, arow, As, acc); break;
-    case 3: gemm2_k_loop<QFMT, GU, 3>(a_src, K, rows, rec, pl, nbase, arow, As, acc); break;
-    case 4: gemm2_k_loop<QFMT, GU, 4>(a_src, K, rows, rec, pl, nbase, arow, As, acc); break;
-    default: gemm2_k_loop<QFMT, GU, 5>(a_src, K, rows, rec, pl, nbase, arow, As, acc); break;
+    case 1: gemm3_k_loop<QFMT, GU, 1, RT>(ab, K, rows, rec, pl, nbase, arow, As0, As1, acc); break;
+    case 2: gemm3_k_loop<QFMT, GU, 2, RT>(ab, K, rows, rec, pl, nbase, arow, As0, As1, acc); break;
+    case 3: gemm3_k_loop<QFMT, GU, 3, RT>(ab, K, rows, rec, pl, nbase, arow, As0, As1, acc); break;
+    case 4: gemm3_k_loop<QFMT, GU, 4, RT>(ab, K, rows, rec, pl, nbase, arow, As0, As1, acc); break;
+    case 5: gemm3_k_loop<QFMT, GU, 5, RT>(ab, K, rows, rec, pl, nbase, arow, As0, As1, acc); break;
+    default:
+      if constexpr (RT >= 6) gemm3_k_loop<QFMT, GU, 6, RT>(ab, K, rows, rec, pl, nbase, arow, As0, As1, acc);
+      break;
   }
 
   // epilogue: lane holds column ln, rows 8*(v/4) + 4*hh + v%4 of each 32-row tile
@@ -377,7 +405,7 @@ __global__ __launch_bounds__(256, 2) void gemm2_kernel(const uint16_t* __restric
     const int f = 32 * (nbase / 64) + ln;
     _Float16* hb = h_out + (size_t)(gbase + m0) * F + f;
 #pragma unroll
-    for (int i = 0; i < G2_RT; ++i) {
+    for (int i = 0; i < RT; ++i) {
       if (i >= nrt) break;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -391,7 +419,7 @@ __global__ __launch_bounds__(256, 2) void gemm2_kernel(const uint16_t* __restric
     for (int sub = 0; sub < 2; ++sub) {
       const int col = nbase + 32 * sub + ln;
 #pragma unroll
-      for (int i = 0; i < G2_RT; ++i) {
+      for (int i = 0; i < RT; ++i) {
         if (i >= nrt) break;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -411,19 +439,19 @@ static int launch_gemm_t(const uint16_t* x, int T, int H, int F, const int32_t* 
   int4* tile_info = (int4*)((uint8_t*)ws + moe_gemm_info_offset(E));
   _Float16* h = (_Float16*)((uint8_t*)ws + moe_gemm_h_offset(T, k, E));
   uint16_t* x16 = (uint16_t*)((uint8_t*)ws + moe_gemm_x16_offset(T, k, E, F));
-  gemm_schedule_kernel<<<1, 1024, 0, st>>>(offsets, E, T, k, G2_BM, tile_start, tile_info);
+  gemm_schedule_kernel<<<1, 1024, 0, st>>>(offsets, E, T, k, 32 * g3_rt<QFMT>(), tile_start, tile_info);
   {
     const size_t n8 = (size_t)T * H / 8;
     const int grid = (int)std::min<size_t>((n8 + 255) / 256, 4096);
     x_to_f16_kernel<<<grid, 256, 0, st>>>((const uint4*)x, n8, (uint4*)x16);
   }
   const int max_tiles = moe_gemm_max_tiles(T, k, E);  // bounds the tile count for BM >= MOE_GEMM_BM
-  const int nnt_gu = (2 * F + G2_BN - 1) / G2_BN, nnt_d = (H + G2_BN - 1) / G2_BN;
+  const int nnt_gu = (2 * F + G3_BN - 1) / G3_BN, nnt_d = (H + G3_BN - 1) / G3_BN;
   const int tot_gu = (max_tiles * nnt_gu + 7) / 8 * 8, tot_d = (max_tiles * nnt_d + 7) / 8 * 8;
-  gemm2_kernel<QFMT, true><<<tot_gu, 256, 0, st>>>(x16, T, H, F, k, E, row_src, tile_start, tile_info, slot_table,
+  gemm3_kernel<QFMT, true><<<tot_gu, 256, 0, st>>>(x16, T, H, F, k, E, row_src, tile_start, tile_info, slot_table,
                                                    layer, (const uint8_t*)pool, record_bytes, h, y_perm, y_shared,
                                                    nnt_gu);
-  gemm2_kernel<QFMT, false><<<tot_d, 256, 0, st>>>((const uint16_t*)h, T, H, F, k, E, row_src, tile_start, tile_info,
+  gemm3_kernel<QFMT, false><<<tot_d, 256, 0, st>>>((const uint16_t*)h, T, H, F, k, E, row_src, tile_start, tile_info,
                                                     slot_table, layer, (const uint8_t*)pool, record_bytes, h, y_perm,
                                                     y_shared, nnt_d);
   return moe_check_launch("grouped gemm");
