@@ -218,19 +218,17 @@ __device__ __forceinline__ void g3_wait_vmcnt() {
 #define G3_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 // The K loop for NRT row tiles.  A chunks go straight from global memory into
-// a ring of three LDS stages (global_load_lds, 16 bytes per lane, through no
-// registers), two chunks ahead of the MFMAs; the B words (raw quantised words,
-// dequantised in registers) one chunk ahead.  Staged layout: row r of a chunk
-// (64 halves = eight 16-byte units) at r * 128 bytes, its logical unit u at
-// physical unit u ^ ((r >> 1) & 7), so that the 16 rows one ds_read_b128
-// phase touches fall on 16 distinct 4-bank groups.  One load instruction of
-// a wave fills 64 consecutive units (8 rows).
-// Step c: wait until only this wave's last NRT loads (its staging of chunk
-// c + 1) may be in flight, barrier (every wave's chunk c has landed, and every
-// wave is done with the stage chunk c + 2 overwrites), request B of chunk
-// c + 1 and then A of chunk c + 2, then the MFMAs of chunk c.  Requests past
-// the last chunk repeat the last one, so that every step issues its staging
-// loads last.
+// two LDS stages (global_load_lds, 16 bytes per lane, through no registers);
+// the B words (raw quantised words, dequantised in registers) into two
+// register sets; both one chunk ahead of the MFMAs.  Staged layout: row r of a
+// chunk (64 halves = eight 16-byte units) at r * 128 bytes, its logical unit u
+// at physical unit u ^ ((r >> 1) & 7), so that the 16 rows one ds_read_b128
+// phase touches fall on 16 distinct 4-bank groups.  One load instruction of a
+// wave fills 64 consecutive units (8 rows).
+// Step c: wait for this wave's loads of chunk c, barrier (every wave's chunk
+// c has landed, and every wave is done with the stage chunk c + 1
+// overwrites), request B and then A of chunk c + 1, then the MFMAs of chunk
+// c.  Requests past the last chunk repeat the last one.
 template <int QFMT, bool GU, int NRT, int RT>
 __device__ __forceinline__ void gemm3_k_loop(const uint8_t* a_bytes, int K, int rows, const uint8_t* rec,
                                              const MoePlanes& pl, int nbase, const int* arow, uint8_t* As0,
@@ -424,7 +422,9 @@ __global__ __launch_bounds__(256, 2) void gemm3_kernel(const uint16_t* __restric
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (r < mv) yb[(uint32_t)(r * H + col)] = acc[i][sub][v];
+          // written once, read once by the combine, far larger than the
+          // caches: the nontemporal hint keeps them from displacing weights
+          if (r < mv) __builtin_nontemporal_store(acc[i][sub][v], &yb[(uint32_t)(r * H + col)]);
         }
       }
     }
