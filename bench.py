@@ -16,12 +16,16 @@ permute, grouped GEMM on the matrix cores, combine).  On request:
   --tier   a hot tier of 4,096 expert slots: hit rate on a synthetic trace;
   --c2     one decode layer timed on its own, rotated over the 48 layers;
   --ceilings  the device's practical HBM read and MFMA rates and the decode
-              kernel's all-to-all hand-offs on their own (probe kernels).
+              kernel's all-to-all hand-offs on their own (probe kernels);
+  --cold-cache  T=1 steps one by one, as they come and after evicting the
+              caches (the per-step router and shared-expert bytes then come
+              from HBM).
 The int2 run also takes one 16,384-token chunk through all 48 layers, with
 the usage update of every layer.  The CPU baseline times the oracle on the
 decode step and on a sample of the prefill chunk's expert groups.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--sweep] [--int2] [--tier] [--c2] [--ceilings]
+                    [--cold-cache]
 """
 import argparse
 import glob
@@ -522,6 +526,49 @@ def single_layer_bench(M, li, reps=8):
             "gbs": round(b / (us / 1e6) / 1e9, 1), "hbm_frac": round(b / (us / 1e6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def cold_cache_bench(M, li, steps=16, flush_mib=1024):
+    """T = 1 decode steps timed one by one (events around each step), first
+    as they come, then each after a streaming read of flush_mib MiB that
+    evicts the L2s and the 256 MB memory-side cache: the router matrices
+    and the shared experts (about 230 MB re-read by every step) then come
+    from HBM.  The difference is what those caches save a step."""
+    import torch
+    import gen as G
+    dev = li.pool.device
+    L, E, H, F, k = li.L, li.E, li.H, li.F, li.k
+    xs = G.draw_x(2, 2 * steps + 2, H, dev, tag="bench-cold").view(2 * steps + 2, 1, H)
+    x_out = torch.empty((1, H), dtype=torch.float32, device=dev)
+    ws = M.workspace(M.MOE_OP_DECODE_STACK, dev, 1, k, E, H, F, li.qfmt)
+    flush = torch.ones(flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+
+    def step(x_in):
+        M.moe_decode_stack(x_in, F, E, k, li.Wr, li.bias, li.S, li.pool, li.R, li.qfmt, x_out=x_out, ws=ws)
+
+    step(xs[0])
+    step(xs[1])
+    torch.cuda.synchronize()
+    res = {}
+    for name, cold in (("warm", False), ("cold", True)):
+        times = []
+        for i in range(steps):
+            if cold:
+                flush.sum()  # reads the whole buffer before the step
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step(xs[2 + (steps if cold else 0) + i])
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        res[name + "_ms_median"] = round(times[len(times) // 2], 4)
+    del flush
+    res["flush_mib"] = flush_mib
+    res["cold_minus_warm_us"] = round((res["cold_ms_median"] - res["warm_ms_median"]) * 1e3, 1)
+    res["workload"] = ("48-layer T=1 decode step, eager, one step per event pair (includes the two small "
+                       "workspace kernels); cold: after a streaming read of flush_mib MiB")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -537,6 +584,8 @@ def main():
     ap.add_argument("--int2", action="store_true",
                     help="also time the int2 stack: decode T = 1, 4 and a 16,384-token prefill chunk")
     ap.add_argument("--c2", action="store_true", help="also time one decode layer on its own, rotated over the layers")
+    ap.add_argument("--cold-cache", action="store_true",
+                    help="also time T=1 steps one by one with and without evicting the caches before each step")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the 8,192-token prefill chunk on a one-layer pool (for profiling the grouped GEMM); "
                          "prints that measurement, not the headline line")
@@ -635,6 +684,10 @@ def main():
         c2 = single_layer_bench(M, li)
         log(f"c2: {json.dumps(c2)}")
         out.setdefault("extra", {})["single_layer_c2"] = c2
+    if args.cold_cache:
+        cc = cold_cache_bench(M, li)
+        log(f"cold cache: {json.dumps(cc)}")
+        out.setdefault("extra", {})["cold_cache"] = cc
     if args.ceilings:
         from routed_expert_ffn_moe_amd import probes
         ce = {"hbm_stream_read_gbs": round(probes.stream_read_gbs(device=dev), 1),

@@ -45,36 +45,44 @@
 __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __restrict__ offsets, int E, int T,
                                                              int k, int BM, int32_t* __restrict__ tile_start,
                                                              int4* __restrict__ tile_info) {
-  __shared__ int s[2048];
+  // thread t owns groups 2t and 2t + 1 (E + 1 <= 2048 groups); one scan:
+  // within the wave (shuffles), then over the 16 waves' totals
+  __shared__ int wsum[16];
   const int G = E + 1;
-  for (int g = threadIdx.x; g < 2048; g += 1024) {
-    int n = 0;
-    if (g < E) n = (offsets[g + 1] - offsets[g] + BM - 1) / BM;
-    else if (g == E) n = (T + BM - 1) / BM;
-    s[g] = n;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int n[2], Mg[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int g = 2 * t + j;
+    Mg[j] = g < E ? offsets[g + 1] - offsets[g] : g == E ? T : 0;
+    n[j] = (Mg[j] + BM - 1) / BM;
   }
+  const int v = n[0] + n[1];
+  int x = v;  // inclusive scan over the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
   __syncthreads();
-  // inclusive scan over 2048 entries, two per thread
-  for (int d = 1; d < 2048; d <<= 1) {
-    const int i0 = threadIdx.x, i1 = threadIdx.x + 1024;
-    const int v0 = i0 >= d ? s[i0 - d] : 0;
-    const int v1 = i1 >= d ? s[i1 - d] : 0;
-    __syncthreads();
-    s[i0] += v0;
-    s[i1] += v1;
-    __syncthreads();
-  }
-  for (int g = threadIdx.x; g <= G; g += 1024) tile_start[g] = g == 0 ? 0 : s[g - 1];
-  for (int g = threadIdx.x; g < G; g += 1024) {
-    const int t0 = g == 0 ? 0 : s[g - 1], n = s[g] - t0;
-    const int Mg = g < E ? offsets[g + 1] - offsets[g] : T;
-    const int gbase = g < E ? offsets[g] : T * k;
-    const int nrt_g = (Mg + 31) / 32;
-    for (int lt = 0; lt < n; ++lt) {
-      const int rt0 = lt * nrt_g / n, nrt = (lt + 1) * nrt_g / n - rt0;
-      const int m0 = 32 * rt0;
-      tile_info[t0 + lt] = make_int4(g, m0, min(32 * nrt, Mg - m0), gbase);
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  int start = before + x - v;  // first tile of group 2t
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int g = 2 * t + j;
+    if (g <= G) tile_start[g] = start;  // tile_start[G] = the tile count (n = 0 there)
+    if (g < G) {
+      const int gbase = g < E ? offsets[g] : T * k;
+      const int nrt_g = (Mg[j] + 31) / 32;
+      for (int lt = 0; lt < n[j]; ++lt) {
+        const int rt0 = lt * nrt_g / n[j], nrt = (lt + 1) * nrt_g / n[j] - rt0;
+        const int m0 = 32 * rt0;
+        tile_info[start + lt] = make_int4(g, m0, min(32 * nrt, Mg[j] - m0), gbase);
+      }
     }
+    start += n[j];
   }
 }
 
