@@ -372,8 +372,8 @@ def prefill_bench(M, li, reps, warmup, T=8192, seed=3, use_bias=False):
     row_src = torch.empty(T * k, dtype=torch.int32, device=dev)
     inv_row = torch.empty(T * k, dtype=torch.int32, device=dev)
     ws_p = M.workspace(M.MOE_OP_PERMUTE, dev, T=T, k=k, E=E)
-    y_perm = torch.empty((T * k, H), dtype=torch.float32, device=dev)
-    y_sh = torch.empty((T, H), dtype=torch.float32, device=dev)
+    y_perm = torch.empty((T * k, H), dtype=torch.float16, device=dev)  # the expert rows as fp16
+    y_sh = torch.empty((T, H), dtype=torch.float16, device=dev)
     ws_g = M.workspace(M.MOE_OP_GROUPED_GEMM_Q, dev, T, k, E, H, F, li.qfmt)
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
     st = torch.cuda.current_stream()
@@ -439,8 +439,8 @@ def prefill_stack_bench(M, li, T, seed=4, reps=1):
     row_src = torch.empty(T * k, dtype=torch.int32, device=dev)
     inv_row = torch.empty(T * k, dtype=torch.int32, device=dev)
     ws_p = M.workspace(M.MOE_OP_PERMUTE, dev, T=T, k=k, E=E)
-    y_perm = torch.empty((T * k, H), dtype=torch.float32, device=dev)
-    y_sh = torch.empty((T, H), dtype=torch.float32, device=dev)
+    y_perm = torch.empty((T * k, H), dtype=torch.float16, device=dev)  # the expert rows as fp16
+    y_sh = torch.empty((T, H), dtype=torch.float16, device=dev)
     ws_g = M.workspace(M.MOE_OP_GROUPED_GEMM_Q, dev, T, k, E, H, F, li.qfmt)
     scores = torch.zeros((L, E), dtype=torch.float32, device=dev)
     hits = torch.empty(E, dtype=torch.int32, device=dev)

@@ -120,6 +120,7 @@ extern "C" {
 /* activation dtypes */
 #define MOE_F32  0
 #define MOE_BF16 1
+#define MOE_F16  2  /* expert output rows of the prefill path */
 
 /* weight formats */
 #define MOE_Q4_B32 0
@@ -233,8 +234,11 @@ int moe_expert_gemv_q(const float* x, int T, int H, int F,
  *   x        bf16 [T][H]; every |x| must be below 65520 (fp16's range)
  *   row_src, offsets: from moe_permute (rows of expert e are
  *            [offsets[e], offsets[e+1]))
- *   y_perm   fp32 [T*k][H] out: y_perm[r] = y_e(x[row_src[r]/k])
- *   y_shared fp32 [T][H]   out: y_shared[t] = y_shared(x[t])
+ *   y_perm   [T*k][H] out, dtype y_dtype: y_perm[r] = y_e(x[row_src[r]/k])
+ *   y_shared [T][H]   out, dtype y_dtype: y_shared[t] = y_shared(x[t])
+ *   y_dtype  MOE_F32, or MOE_F16 (one rounding of the fp32 sum; half the
+ *            bytes written here and read by moe_combine; |y| >= 65520
+ *            becomes inf, not checked)
  * Experts with no rows are skipped.  Internally x is multiplied in fp16:
  * bf16 values with 2^-14 <= |x| < 65520 convert exactly; smaller ones round
  * to fp16 subnormals (absolute error <= 2^-25); |x| >= 65520 becomes inf
@@ -246,7 +250,7 @@ int moe_grouped_gemm_q(const uint16_t* x, int T, int H, int F,
                        const int32_t* row_src, const int32_t* offsets, int k,
                        int E, const int32_t* slot_table, int layer,
                        const void* pool, int64_t record_bytes, int qfmt,
-                       float* y_perm, float* y_shared, void* ws,
+                       void* y_perm, void* y_shared, int y_dtype, void* ws,
                        size_t ws_bytes, void* stream);
 
 /* --------------------------------------------------------------------------
@@ -257,12 +261,14 @@ int moe_grouped_gemm_q(const uint16_t* x, int T, int H, int F,
  *     moe_expert_gemv_q (slot k = shared expert) and y_shared must be NULL.
  *   inv_row != NULL: prefill layout, y_rows is y_perm [T*k][H] and y_shared
  *     is [T][H].
+ *   rows_dtype: MOE_F32 or MOE_F16, the dtype of y_rows and y_shared (fp16
+ *     as moe_grouped_gemm_q writes them with y_dtype = MOE_F16).
  *   y_out[t] = sum_{j<k} topk_w[t][j] * row(t,j) + shared(t) (+ residual[t])
  *   summed in that order in fp32.  residual may be NULL; y_out may alias
  *   residual.
  */
-int moe_combine(const float* y_rows, const int32_t* inv_row,
-                const float* y_shared, const float* topk_w,
+int moe_combine(const void* y_rows, int rows_dtype, const int32_t* inv_row,
+                const void* y_shared, const float* topk_w,
                 const float* residual, int T, int k, int H, float* y_out,
                 void* stream);
 

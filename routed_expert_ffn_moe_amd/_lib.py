@@ -9,7 +9,7 @@ HEADER = os.path.join(HERE, "..", "include", "moe.h")
 
 # constants of include/moe.h
 MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EALIGN, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4, -5, -6
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_F16 = 0, 1, 2
 MOE_Q4_B32, MOE_Q2_B16 = 0, 1
 (MOE_OP_ROUTE_TOPK, MOE_OP_PERMUTE, MOE_OP_EXPERT_GEMV_Q, MOE_OP_GROUPED_GEMM_Q, MOE_OP_COMBINE,
  MOE_OP_USAGE_UPDATE, MOE_OP_DECODE_STACK) = range(7)
@@ -26,9 +26,9 @@ SIGNATURES = {
     "moe_route_topk": (_i, [_vp, _i, _i, _i, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_permute": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp]),
     "moe_expert_gemv_q": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _vp, _i, _vp, _i64, _i, _vp, _vp, _sz, _vp]),
-    "moe_grouped_gemm_q": (_i, [_vp, _i, _i, _i, _vp, _vp, _i, _i, _vp, _i, _vp, _i64, _i, _vp, _vp, _vp, _sz,
+    "moe_grouped_gemm_q": (_i, [_vp, _i, _i, _i, _vp, _vp, _i, _i, _vp, _i, _vp, _i64, _i, _vp, _vp, _i, _vp, _sz,
                                 _vp]),
-    "moe_combine": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
+    "moe_combine": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
     "moe_usage_update": (_i, [_vp, _i, _i, _i, _i, _i, _f, _i64, _i, _i, _vp, _vp, _vp, _vp]),
     "moe_usage_update_stack": (_i, [_vp, _i, _i, _i, _i, _f, _i64, _i, _i, _vp, _vp, _vp, _vp]),
     "moe_tier_fill": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),

@@ -96,7 +96,7 @@ int moe_decode_stack_run(const float* x_in, int T, int H, int F, int E, int k, i
     if (rc) return rc;
     rc = moe_launch_gemv(xn, T, H, F, idx, k, E, slot_table, l, pool, record_bytes, qfmt, yparts, gws, st);
     if (rc) return rc;
-    rc = moe_launch_combine(yparts, nullptr, nullptr, wt, x_out, T, k, H, x_out, st);
+    rc = moe_launch_combine(yparts, MOE_F32, nullptr, nullptr, wt, x_out, T, k, H, x_out, st);
     if (rc) return rc;
   }
   return MOE_OK;

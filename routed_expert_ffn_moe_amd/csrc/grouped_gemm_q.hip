@@ -337,6 +337,7 @@ __device__ __forceinline__ void gemm3_k_loop(const uint8_t* a_bytes, int K, int 
   g3_wait_vmcnt<0>();
 }
 
+// y_f16: the down pass writes its output rows as fp16 (else fp32).
 template <int QFMT, bool GU>
 __global__ __launch_bounds__(256, 2) void gemm3_kernel(const uint16_t* __restrict__ a_src, int T, int H, int F, int k,
                                                        int E, const int32_t* __restrict__ row_src,
@@ -344,8 +345,8 @@ __global__ __launch_bounds__(256, 2) void gemm3_kernel(const uint16_t* __restric
                                                        const int4* __restrict__ tile_info,
                                                        const int32_t* __restrict__ slot_table, int layer,
                                                        const uint8_t* __restrict__ pool, int64_t record_bytes,
-                                                       _Float16* __restrict__ h_out, float* __restrict__ y_perm,
-                                                       float* __restrict__ y_shared, int n_ntiles) {
+                                                       _Float16* __restrict__ h_out, void* __restrict__ y_perm,
+                                                       void* __restrict__ y_shared, int y_f16, int n_ntiles) {
   __shared__ __attribute__((aligned(1024))) uint8_t As0[G3_STAGE_B];
   __shared__ __attribute__((aligned(1024))) uint8_t As1[G3_STAGE_B];
   __shared__ int arow[G3_BM];
@@ -420,29 +421,36 @@ __global__ __launch_bounds__(256, 2) void gemm3_kernel(const uint16_t* __restric
       }
     }
   } else {
-    float* yb = g < E ? y_perm + (size_t)(gbase + m0) * H : y_shared + (size_t)m0 * H;
+    const size_t ybase = g < E ? (size_t)(gbase + m0) * H : (size_t)m0 * H;
+    void* yv = g < E ? y_perm : y_shared;
+    // written once, read once by the combine, far larger than the caches:
+    // the nontemporal hint keeps them from displacing weights
+    auto store_rows = [&](auto* yb, auto cvt) {
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int col = nbase + 32 * sub + ln;
+      for (int sub = 0; sub < 2; ++sub) {
+        const int col = nbase + 32 * sub + ln;
 #pragma unroll
-      for (int i = 0; i < RT; ++i) {
-        if (i >= nrt) break;
+        for (int i = 0; i < RT; ++i) {
+          if (i >= nrt) break;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
-          // written once, read once by the combine, far larger than the
-          // caches: the nontemporal hint keeps them from displacing weights
-          if (r < mv) __builtin_nontemporal_store(acc[i][sub][v], &yb[(uint32_t)(r * H + col)]);
+          for (int v = 0; v < 16; ++v) {
+            const int r = 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
+            if (r < mv) __builtin_nontemporal_store(cvt(acc[i][sub][v]), &yb[(uint32_t)(r * H + col)]);
+          }
         }
       }
-    }
+    };
+    if (y_f16)
+      store_rows((uint16_t*)yv + ybase, [](float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); });
+    else
+      store_rows((float*)yv + ybase, [](float v) { return v; });
   }
 }
 
 template <int QFMT>
 static int launch_gemm_t(const uint16_t* x, int T, int H, int F, const int32_t* row_src, const int32_t* offsets,
                          int k, int E, const int32_t* slot_table, int layer, const void* pool, int64_t record_bytes,
-                         float* y_perm, float* y_shared, void* ws, hipStream_t st) {
+                         void* y_perm, void* y_shared, int y_f16, void* ws, hipStream_t st) {
   int32_t* tile_start = (int32_t*)ws;
   int4* tile_info = (int4*)((uint8_t*)ws + moe_gemm_info_offset(E));
   _Float16* h = (_Float16*)((uint8_t*)ws + moe_gemm_h_offset(T, k, E));
@@ -458,22 +466,27 @@ static int launch_gemm_t(const uint16_t* x, int T, int H, int F, const int32_t* 
   const int tot_gu = (max_tiles * nnt_gu + 7) / 8 * 8, tot_d = (max_tiles * nnt_d + 7) / 8 * 8;
   gemm3_kernel<QFMT, true><<<tot_gu, 256, 0, st>>>(x16, T, H, F, k, E, row_src, tile_start, tile_info, slot_table,
                                                    layer, (const uint8_t*)pool, record_bytes, h, y_perm, y_shared,
-                                                   nnt_gu);
+                                                   y_f16, nnt_gu);
   gemm3_kernel<QFMT, false><<<tot_d, 256, 0, st>>>((const uint16_t*)h, T, H, F, k, E, row_src, tile_start, tile_info,
                                                     slot_table, layer, (const uint8_t*)pool, record_bytes, h, y_perm,
-                                                    y_shared, nnt_d);
+                                                    y_shared, y_f16, nnt_d);
   return moe_check_launch("grouped gemm");
 }
 
 extern "C" int moe_grouped_gemm_q(const uint16_t* x, int T, int H, int F, const int32_t* row_src,
                                   const int32_t* offsets, int k, int E, const int32_t* slot_table, int layer,
-                                  const void* pool, int64_t record_bytes, int qfmt, float* y_perm, float* y_shared,
-                                  void* ws, size_t ws_bytes, void* stream) {
+                                  const void* pool, int64_t record_bytes, int qfmt, void* y_perm, void* y_shared,
+                                  int y_dtype, void* ws, size_t ws_bytes, void* stream) {
   int rc = moe_check_expert_shapes(H, F, E, k, qfmt, pool, record_bytes, slot_table, layer);
   if (rc) return rc;
+  MOE_REQUIRE(y_dtype == MOE_F32 || y_dtype == MOE_F16, MOE_EUNSUPPORTED, "y_dtype=%d must be MOE_F32 or MOE_F16",
+              y_dtype);
   MOE_REQUIRE(T >= 0, MOE_ESHAPE, "T=%d must be >= 0", T);
   MOE_REQUIRE(((int64_t)T * k + T) * (int64_t)(H > F ? H : F) < (1ll << 31) * 8ll, MOE_ESHAPE, "T too large");
   MOE_REQUIRE((int64_t)T * k + T < (1ll << 31), MOE_ESHAPE, "T*k too large");
+  // the staging loads address the fp16 copies of x and h with 32-bit byte offsets
+  MOE_REQUIRE((int64_t)T * H * 2 < (1ll << 32) && ((int64_t)T * k + T) * F * 2 < (1ll << 32), MOE_ESHAPE,
+              "T=%d too large: T*H and (T*k+T)*F fp16 values must stay below 4 GiB", T);
   if (T == 0) return MOE_OK;
   MOE_REQUIRE(x && row_src && offsets && y_perm && y_shared, MOE_EINVAL,
               "x, row_src, offsets, y_perm and y_shared are required");
@@ -482,9 +495,10 @@ extern "C" int moe_grouped_gemm_q(const uint16_t* x, int T, int H, int F, const 
   MOE_REQUIRE(ws && ws_bytes >= need && moe_aligned(ws, 256), MOE_EWORKSPACE,
               "ws needs %zu bytes, 256-byte aligned", need);
   hipStream_t st = moe_stream(stream);
+  const int y_f16 = y_dtype == MOE_F16;
   if (qfmt == MOE_Q4_B32)
     return launch_gemm_t<MOE_Q4_B32>(x, T, H, F, row_src, offsets, k, E, slot_table, layer, pool, record_bytes,
-                                     y_perm, y_shared, ws, st);
+                                     y_perm, y_shared, y_f16, ws, st);
   return launch_gemm_t<MOE_Q2_B16>(x, T, H, F, row_src, offsets, k, E, slot_table, layer, pool, record_bytes, y_perm,
-                                   y_shared, ws, st);
+                                   y_shared, y_f16, ws, st);
 }

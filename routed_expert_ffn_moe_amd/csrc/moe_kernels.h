@@ -9,8 +9,8 @@ int moe_launch_gemv(const float* x, int T, int H, int F, const int32_t* topk_idx
                     const int32_t* slot_table, int layer, const void* pool, int64_t record_bytes, int qfmt,
                     float* y_parts, void* ws, hipStream_t st);
 
-int moe_launch_combine(const float* y_rows, const int32_t* inv_row, const float* y_shared, const float* topk_w,
-                       const float* residual, int T, int k, int H, float* y_out, hipStream_t st);
+int moe_launch_combine(const void* y_rows, int rows_dtype, const int32_t* inv_row, const void* y_shared,
+                       const float* topk_w, const float* residual, int T, int k, int H, float* y_out, hipStream_t st);
 
 // Persistent single-kernel decode step (decode_persistent.hip).
 size_t moe_ws_stack_persistent(int T, int k, int E, int H, int F, int qfmt);

@@ -12,7 +12,7 @@ import os
 import torch
 
 from . import _lib
-from ._lib import (MOE_BF16, MOE_F32, MOE_OP_DECODE_STACK, MOE_OP_EXPERT_GEMV_Q, MOE_OP_GROUPED_GEMM_Q,
+from ._lib import (MOE_BF16, MOE_F16, MOE_F32, MOE_OP_DECODE_STACK, MOE_OP_EXPERT_GEMV_Q, MOE_OP_GROUPED_GEMM_Q,
                    MOE_OP_PERMUTE, MOE_OP_ROUTE_TOPK, MOE_Q2_B16, MOE_Q4_B32, MoeError, check)
 
 __all__ = [
@@ -173,35 +173,53 @@ def moe_expert_gemv_q(x, topk_idx, E, F, slot_table, layer, pool, record_bytes, 
     return y_parts
 
 
+def _rows_dtype(t):
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.float16:
+        return MOE_F16
+    raise TypeError(f"expert output rows must be float32 or float16, got {t.dtype}")
+
+
 def moe_grouped_gemm_q(x, row_src, offsets, k, E, F, slot_table, layer, pool, record_bytes, qfmt, y_perm=None,
-                       y_shared=None, ws=None, stream=None):
-    """x bf16 [T][H]; returns (y_perm fp32 [T*k][H], y_shared fp32 [T][H])."""
+                       y_shared=None, ws=None, stream=None, y_dtype=torch.float16):
+    """x bf16 [T][H]; returns (y_perm [T*k][H], y_shared [T][H]) in y_dtype
+    (float16 by default, or float32; given output tensors set it)."""
     T, H = x.shape
     dev = x.device
     _half_bits(x)
-    y_perm = torch.empty((T * k, H), dtype=torch.float32, device=dev) if y_perm is None else y_perm
-    y_shared = torch.empty((T, H), dtype=torch.float32, device=dev) if y_shared is None else y_shared
+    if y_perm is not None:
+        y_dtype = y_perm.dtype
+    y_perm = torch.empty((T * k, H), dtype=y_dtype, device=dev) if y_perm is None else y_perm
+    y_shared = torch.empty((T, H), dtype=y_dtype, device=dev) if y_shared is None else y_shared
+    yd = _rows_dtype(y_perm)
+    if y_shared.dtype != y_perm.dtype:
+        raise TypeError("y_perm and y_shared must have the same dtype")
     ws = workspace(MOE_OP_GROUPED_GEMM_Q, dev, T, k, E, H, F, qfmt) if ws is None else ws
     _dev(x, row_src, offsets, slot_table, pool, y_perm, y_shared, ws)
     if _validating():
         validate_rows(offsets, row_src, T, k)
         validate_slot_table(slot_table, _pool_slots(pool, record_bytes))
     check(_lib.load().moe_grouped_gemm_q(_p(x), T, H, F, _p(row_src), _p(offsets), k, E, _p(slot_table), layer,
-                                         _p(pool), record_bytes, qfmt, _p(y_perm), _p(y_shared), _p(ws), ws.numel(),
-                                         _stream(stream)))
+                                         _p(pool), record_bytes, qfmt, _p(y_perm), _p(y_shared), yd, _p(ws),
+                                         ws.numel(), _stream(stream)))
     return y_perm, y_shared
 
 
 def moe_combine(y_rows, topk_w, inv_row=None, y_shared=None, residual=None, y_out=None, stream=None):
+    """y_rows (and y_shared) float32 or float16; y_out float32 [T][H]."""
     T, k = topk_w.shape
     H = y_rows.shape[-1]
+    rd = _rows_dtype(y_rows)
+    if y_shared is not None and y_shared.dtype != y_rows.dtype:
+        raise TypeError("y_rows and y_shared must have the same dtype")
     y_out = torch.empty((T, H), dtype=torch.float32, device=y_rows.device) if y_out is None else y_out
     _dev(y_rows, topk_w, inv_row, y_shared, residual, y_out)
     if _validating() and inv_row is not None:  # inv_row must be a permutation of the T*k rows
         n = T * k
         validate_rows(torch.tensor([0, n], dtype=torch.int32), inv_row, T, k)
-    check(_lib.load().moe_combine(_p(y_rows), _p(inv_row), _p(y_shared), _p(topk_w), _p(residual), T, k, H, _p(y_out),
-                                  _stream(stream)))
+    check(_lib.load().moe_combine(_p(y_rows), rd, _p(inv_row), _p(y_shared), _p(topk_w), _p(residual), T, k, H,
+                                  _p(y_out), _stream(stream)))
     return y_out
 
 

@@ -93,22 +93,29 @@ def test_expert_ops_reject(lib):
     assert call(3, 700) == _lib.MOE_ESHAPE           # F % 128
     assert call(5, 17) == _lib.MOE_ESHAPE            # k > 16
     h = lib.moe_grouped_gemm_q
-    gb = [FAKE, 8192, 2048, 768, FAKE, FAKE, 10, 512, FAKE, 0, FAKE, 2_654_208, 0, FAKE, FAKE, FAKE, 0, None]
+    gb = [FAKE, 8192, 2048, 768, FAKE, FAKE, 10, 512, FAKE, 0, FAKE, 2_654_208, 0, FAKE, FAKE, _lib.MOE_F16, FAKE, 0,
+          None]
     assert h(*gb) == _lib.MOE_EWORKSPACE
     gb2 = list(gb); gb2[0] = FAKE + 2
-    gb2[16] = 1 << 40
+    gb2[17] = 1 << 40
     assert h(*gb2) == _lib.MOE_EALIGN
     gb3 = list(gb); gb3[7] = 4096
     assert h(*gb3) == _lib.MOE_ESHAPE
+    gb4 = list(gb); gb4[15] = _lib.MOE_BF16          # output rows: fp32 or fp16 only
+    assert h(*gb4) == _lib.MOE_EUNSUPPORTED
+    gb5 = list(gb); gb5[1] = 1 << 20                 # fp16 copies past 32-bit byte offsets
+    assert h(*gb5) == _lib.MOE_ESHAPE
 
 
 def test_permute_combine_usage_reject(lib):
     assert lib.moe_permute(FAKE, 10, 2, 0, FAKE, FAKE, FAKE, FAKE, None, 0, 0, None, FAKE, 1 << 20, None) == _lib.MOE_ESHAPE
     assert lib.moe_permute(FAKE, 10, 2, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 256, None, FAKE, 1 << 20, None) == _lib.MOE_EINVAL
     assert lib.moe_permute(FAKE, 1000, 10, 512, FAKE, FAKE, FAKE, FAKE, None, 0, 0, None, FAKE, 8, None) == _lib.MOE_EWORKSPACE
-    assert lib.moe_combine(FAKE, FAKE, None, FAKE, None, 4, 2, 256, FAKE, None) == _lib.MOE_EINVAL
-    assert lib.moe_combine(FAKE, None, None, FAKE, None, 4, 2, 254, FAKE, None) == _lib.MOE_ESHAPE
-    assert lib.moe_combine(FAKE + 4, None, None, FAKE, None, 4, 2, 256, FAKE, None) == _lib.MOE_EALIGN
+    F32, F16 = _lib.MOE_F32, _lib.MOE_F16
+    assert lib.moe_combine(FAKE, F32, FAKE, None, FAKE, None, 4, 2, 256, FAKE, None) == _lib.MOE_EINVAL
+    assert lib.moe_combine(FAKE, F16, None, None, FAKE, None, 4, 2, 254, FAKE, None) == _lib.MOE_ESHAPE
+    assert lib.moe_combine(FAKE + 4, F32, None, None, FAKE, None, 4, 2, 256, FAKE, None) == _lib.MOE_EALIGN
+    assert lib.moe_combine(FAKE, _lib.MOE_BF16, None, None, FAKE, None, 4, 2, 256, FAKE, None) == _lib.MOE_EUNSUPPORTED
     u = lib.moe_usage_update
     assert u(FAKE, 1, 10, 48, 48, 512, ctypes.c_float(0.99), 0, 4, 96, FAKE, FAKE, FAKE, None) == _lib.MOE_EINVAL
     assert u(FAKE, 1, 10, 0, 200, 512, ctypes.c_float(0.99), 0, 4, 96, FAKE, FAKE, FAKE, None) == _lib.MOE_ESHAPE

@@ -154,6 +154,12 @@ def test_combine_every_k(moe, k):
     rows = torch.cat([routed, shared.unsqueeze(1)], 1).reshape(T * (k + 1), H)
     y = moe.moe_combine(rows.cuda(), w.cuda(), residual=resid.cuda())
     assert torch.equal(y.cpu(), out.cpu())  # same sums in the same order
+    # fp16 rows: the same sums as over their exact fp32 values
+    y16 = moe.moe_combine(y_perm.half().cuda(), w.cuda(), inv_row=inv_row.cuda(), y_shared=shared.half().cuda(),
+                          residual=resid.cuda())
+    y32 = moe.moe_combine(y_perm.half().float().cuda(), w.cuda(), inv_row=inv_row.cuda(),
+                          y_shared=shared.half().float().cuda(), residual=resid.cuda())
+    assert torch.equal(y16, y32)
 
 
 # ---------------------------------------------------------------- decode experts
@@ -221,12 +227,12 @@ def test_gemv_slot_permutation_invariance(moe):
 
 # ---------------------------------------------------------------- prefill experts
 
-def _prefill_layer(moe, li, x_bf16):
+def _prefill_layer(moe, li, x_bf16, y_dtype=torch.float16):
     idx, w = moe.moe_route_topk(x_bf16.cuda(), li.Wr[0].cuda().contiguous(),
                                 None if li.bias is None else li.bias[0].cuda().contiguous(), li.k)
     counts, offsets, row_src, inv_row, _ = moe.moe_permute(idx, li.E)
     y_perm, y_sh = moe.moe_grouped_gemm_q(x_bf16.cuda(), row_src, offsets, li.k, li.E, li.F, li.S.cuda(), 0,
-                                          li.pool.cuda(), li.R, li.qfmt)
+                                          li.pool.cuda(), li.R, li.qfmt, y_dtype=y_dtype)
     y = moe.moe_combine(y_perm, w, inv_row=inv_row, y_shared=y_sh)
     return idx, w, counts, inv_row, y_perm, y_sh, y
 
@@ -235,14 +241,22 @@ def _prefill_layer(moe, li, x_bf16):
 @pytest.mark.parametrize("T,E,k,bias", [(4, 16, 2, False), (300, 16, 2, True), (2000, 16, 2, False),
                                         (333, 40, 6, True)])
 def test_grouped_gemm_small(moe, qfmt, T, E, k, bias):
+    """Both output dtypes against the oracle; the fp16 rows are the fp32 rows
+    rounded to nearest even, bit for bit (same sums, one rounding)."""
     li = C.layer_case(2, T, 256, E, k, 128, qfmt=qfmt, bias=bias, x_bf16=True)
-    idx, w, counts, inv_row, y_perm, y_sh, y = _prefill_layer(moe, li, li.x)
     ry, ri, rw, rparts, _ = C.oracle_layer(li)
-    _check_routing(idx, w, ri, rw)
-    rows = _np(y_perm)[_np(inv_row).reshape(T, k)]
-    C.assert_close_moe(rows, rparts[:, :k], "routed rows")
-    C.assert_close_moe(_np(y_sh), rparts[:, k], "shared")
-    C.assert_close_moe(_np(y), ry, "y")
+    out = {}
+    for yd in (torch.float16, torch.float32):
+        idx, w, counts, inv_row, y_perm, y_sh, y = _prefill_layer(moe, li, li.x, y_dtype=yd)
+        assert y_perm.dtype == yd and y_sh.dtype == yd
+        _check_routing(idx, w, ri, rw)
+        rows = _np(y_perm)[_np(inv_row).reshape(T, k)]
+        C.assert_close_moe(rows, rparts[:, :k], f"routed rows ({yd})")
+        C.assert_close_moe(_np(y_sh), rparts[:, k], f"shared ({yd})")
+        C.assert_close_moe(_np(y), ry, f"y ({yd})")
+        out[yd] = (y_perm, y_sh)
+    assert torch.equal(out[torch.float16][0], out[torch.float32][0].half())
+    assert torch.equal(out[torch.float16][1], out[torch.float32][1].half())
 
 
 def test_grouped_gemm_empty_groups(moe):
