@@ -82,8 +82,9 @@ class LazyPool:
 
 
 def cpu_baseline(li, x_tok, budget_s):
-    """The oracle (as it stands) on the host: one token through as many of the
-    48 layers as fit in the time budget (at least 2), scaled to 48 layers."""
+    """The oracle (as it stands) on the host: the T tokens of x_tok [T][H]
+    (one decode step, or a verify window) through as many of the 48 layers as
+    fit in the time budget (at least 2), scaled to 48 layers."""
     import numpy as np
     import oracle as O
     S = li.S.cpu().numpy()
@@ -100,10 +101,12 @@ def cpu_baseline(li, x_tok, budget_s):
     wall = time.perf_counter() - t0
     c1 = os.times()
     cpu = (c1.user - c0.user) + (c1.system - c0.system)
-    per_token = wall / n * li.L
-    return {"value": round(1.0 / per_token, 6), "unit": "tokens/s", "cores": round(cpu / wall, 2),
-            "cores_available": os.cpu_count(), "kind": "oracle",
-            "sample": f"1 token through the first {n} of {li.L} layers (fp64 NumPy, records decoded per layer), "
+    per_step = wall / n * li.L
+    T = x.shape[0]
+    what = "1 token" if T == 1 else f"a window of {T} tokens"
+    return {"value": round(T / per_step, 6), "unit": "tokens/s" if T == 1 else "token positions/s",
+            "cores": round(cpu / wall, 2), "cores_available": os.cpu_count(), "kind": "oracle",
+            "sample": f"{what} through the first {n} of {li.L} layers (fp64 NumPy, records decoded per layer), "
                       f"{wall:.1f} s, scaled to {li.L} layers"}, np
 
 
@@ -323,10 +326,12 @@ def tier_bench(M, li, steps, profile_steps=16, top_n=96, every=4, decay=0.99):
             "fill_ms": round(fill_ms, 2), "fill_gb_copied": round(n_hot * R / 1e9, 2)}
 
 
-def int2_bench(M, steps, warmup, use_graph):
+def int2_bench(M, steps, warmup, use_graph, cpu_budget=None):
     """The int2 stack (blocks of 16 with fp16 scale and min; seed 4, Zipf
     routing bias): decode at T = 1 and 4 through 48 layers, and one 16,384-token
-    prefill chunk through layer 0 with the bias (skewed groups)."""
+    prefill chunk through layer 0 with the bias (skewed groups); with a
+    cpu_budget, the oracle on a sample of that chunk's layer (per layer, and
+    scaled to the 48 layers)."""
     import torch
     import gen as G
     L, E, H, F, k = 48, 512, 2048, 768, 10
@@ -342,6 +347,13 @@ def int2_bench(M, steps, warmup, use_graph):
                                "hbm_frac": round(b / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
     out["prefill_16k"] = prefill_bench(M, li, reps=5, warmup=2, T=16384, seed=4, use_bias=True)
     out["prefill_16k_48_layers"] = prefill_stack_bench(M, li, T=16384, seed=4, reps=1)
+    if cpu_budget:
+        xp = G.draw_x(4, 16384, H, li.pool.device, tag="bench-prefill").to(torch.bfloat16)
+        idx_p, _ = M.moe_route_topk(xp, li.Wr[0].contiguous(), li.bias[0].contiguous(), k)
+        pc = prefill_cpu_baseline(li, xp, idx_p, cpu_budget)
+        pc["est_s_per_48_layer_chunk"] = round(pc["est_s_per_chunk"] * L, 1)
+        pc["sample"] += f"; x {L} layers: {pc['est_s_per_48_layer_chunk']} s per chunk (extrapolated)"
+        out["prefill_16k"]["cpu_baseline"] = pc
     del li
     torch.cuda.empty_cache()
     return out
@@ -677,7 +689,8 @@ def main():
         out.setdefault("extra", {})["decode_sweep"] = decode_sweep(M, li, min(args.steps, 32), args.warmup,
                                                                    not args.no_graph)
     if args.int2:
-        i2 = int2_bench(M, args.steps, args.warmup, not args.no_graph)
+        i2 = int2_bench(M, args.steps, args.warmup, not args.no_graph,
+                        cpu_budget=None if args.no_cpu_baseline else args.cpu_budget)
         log(f"int2: {json.dumps(i2)}")
         out.setdefault("extra", {})["int2_stack"] = i2
     if args.c2:
@@ -719,6 +732,11 @@ def main():
         cb["host"] = host_info()
         out["cpu_baseline"] = cb
         log(f"cpu baseline: {cb}")
+        if "extra" in out and "verify_t4" in out["extra"]:
+            x4 = G.draw_x(2, 4, H, dev, tag="bench-x4")
+            c4, _ = cpu_baseline(li, x4, args.cpu_budget / 3)
+            out["extra"]["verify_t4"]["cpu_baseline"] = c4
+            log(f"verify cpu baseline: {c4}")
         if "extra" in out and "prefill_c4" in out["extra"]:
             xp = G.draw_x(3, 8192, H, dev, tag="bench-prefill").to(torch.bfloat16)
             idx_p, _ = M.moe_route_topk(xp, li.Wr[0].contiguous(), None, k)
