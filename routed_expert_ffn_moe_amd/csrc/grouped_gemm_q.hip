@@ -42,9 +42,8 @@
 // multiple of 32);
 // tile_info[t] = {group, first row m0, rows, first h row of the group}: the
 // group's 32-row tiles split as evenly as possible over its BM-row tiles.
-__global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __restrict__ offsets, int E, int T,
-                                                             int k, int BM, int32_t* __restrict__ tile_start,
-                                                             int4* __restrict__ tile_info) {
+__device__ __forceinline__ void gemm_schedule(const int32_t* __restrict__ offsets, int E, int T, int k, int BM,
+                                              int32_t* __restrict__ tile_start, int4* __restrict__ tile_info) {
   // thread t owns groups 2t and 2t + 1 (E + 1 <= 2048 groups); one scan:
   // within the wave (shuffles), then over the 16 waves' totals
   __shared__ int wsum[16];
@@ -86,9 +85,19 @@ __global__ __launch_bounds__(1024) void gemm_schedule_kernel(const int32_t* __re
   }
 }
 
-// x (bf16) -> fp16, 8 values per thread (n8 = T * H / 8)
-__global__ __launch_bounds__(256) void x_to_f16_kernel(const uint4* __restrict__ x, size_t n8, uint4* __restrict__ y) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
+// Before the two passes, one launch: workgroup 0 builds the tile schedule
+// while the others convert x (bf16) to fp16, 8 values per thread
+// (n8 = T * H / 8), grid-stride.
+__global__ __launch_bounds__(1024) void gemm_prepare_kernel(const int32_t* __restrict__ offsets, int E, int T, int k,
+                                                            int BM, int32_t* __restrict__ tile_start,
+                                                            int4* __restrict__ tile_info, const uint4* __restrict__ x,
+                                                            size_t n8, uint4* __restrict__ y) {
+  if (blockIdx.x == 0) {
+    gemm_schedule(offsets, E, T, k, BM, tile_start, tile_info);
+    return;
+  }
+  const size_t stride = (size_t)(gridDim.x - 1) * 1024;
+  for (size_t i = (size_t)(blockIdx.x - 1) * 1024 + threadIdx.x; i < n8; i += stride) {
     const uint4 v = x[i];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t o[4];
@@ -455,11 +464,11 @@ static int launch_gemm_t(const uint16_t* x, int T, int H, int F, const int32_t* 
   int4* tile_info = (int4*)((uint8_t*)ws + moe_gemm_info_offset(E));
   _Float16* h = (_Float16*)((uint8_t*)ws + moe_gemm_h_offset(T, k, E));
   uint16_t* x16 = (uint16_t*)((uint8_t*)ws + moe_gemm_x16_offset(T, k, E, F));
-  gemm_schedule_kernel<<<1, 1024, 0, st>>>(offsets, E, T, k, 32 * g3_rt<QFMT>(), tile_start, tile_info);
   {
     const size_t n8 = (size_t)T * H / 8;
-    const int grid = (int)std::min<size_t>((n8 + 255) / 256, 4096);
-    x_to_f16_kernel<<<grid, 256, 0, st>>>((const uint4*)x, n8, (uint4*)x16);
+    const int grid = 1 + (int)std::min<size_t>((n8 + 1023) / 1024, 1024);
+    gemm_prepare_kernel<<<grid, 1024, 0, st>>>(offsets, E, T, k, 32 * g3_rt<QFMT>(), tile_start, tile_info,
+                                               (const uint4*)x, n8, (uint4*)x16);
   }
   const int max_tiles = moe_gemm_max_tiles(T, k, E);  // bounds the tile count for BM >= MOE_GEMM_BM
   const int nnt_gu = (2 * F + G3_BN - 1) / G3_BN, nnt_d = (H + G3_BN - 1) / G3_BN;
