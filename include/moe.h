@@ -236,6 +236,7 @@ int moe_expert_gemv_q(const float* x, int T, int H, int F,
  *            [offsets[e], offsets[e+1]))
  *   y_perm   [T*k][H] out, dtype y_dtype: y_perm[r] = y_e(x[row_src[r]/k])
  *   y_shared [T][H]   out, dtype y_dtype: y_shared[t] = y_shared(x[t])
+ *            (x, y_perm and y_shared 16-byte aligned, else MOE_EALIGN)
  *   y_dtype  MOE_F32, or MOE_F16 (one rounding of the fp32 sum; half the
  *            bytes written here and read by moe_combine; |y| >= 65520
  *            becomes inf, not checked)

@@ -156,6 +156,9 @@ __device__ __forceinline__ half8v deq_q2(uint32_t w, int hh, half2v s2, half2v m
 // runs of 32, so SiLU*mul happens in registers); each dequantised B operand
 // feeds up to 6 MFMAs and each A operand read from LDS feeds 2.  An expert of
 // up to 192 rows is one tile, so its weights are read and dequantised once.
+typedef _Float16 g3_f16x4 __attribute__((ext_vector_type(4)));
+typedef float g3_f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t g3_u32x4 __attribute__((ext_vector_type(4)));
 #define G3_BM 192  // rows of a staged A chunk (the largest tile)
 #define G3_BN 256
 #define G3_KC 64
@@ -166,6 +169,8 @@ __device__ __forceinline__ half8v deq_q2(uint32_t w, int hh, half2v s2, half2v m
 template <int QFMT>
 constexpr int g3_rt() { return QFMT == MOE_Q4_B32 ? 6 : 5; }
 #define G3_STAGE_B (G3_BM * G3_KC * 2)  // bytes of one staged A chunk
+#define G3_EPI_WAVE_B (32 * 144)        // a wave's output staging in the down epilogue
+static_assert(4 * G3_EPI_WAVE_B <= G3_STAGE_B, "the down epilogue stages in one A stage");
 
 template <int QFMT>
 struct B2Regs;  // raw weight words of one K chunk (64) for one lane and one column tile
@@ -314,8 +319,11 @@ __device__ __forceinline__ void gemm3_k_loop(const uint8_t* a_bytes, int K, int 
 #pragma unroll
       for (int i = 0; i < NRT; ++i) {
         const half8v af = *reinterpret_cast<const half8v*>(Ab + aoff[q] + 4096 * i);
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[0], acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[1], acc[i][1], 0, 0, 0);
+        // weights as the first operand: the accumulators come out transposed
+        // (a lane holds one token row and 16 weight rows), so that the
+        // epilogue stores 4 consecutive output columns per instruction
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[0], af, acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[1], af, acc[i][1], 0, 0, 0);
       }
     }
   };
@@ -415,44 +423,87 @@ __global__ __launch_bounds__(256, 2) void gemm3_kernel(const uint16_t* __restric
       break;
   }
 
-  // epilogue: lane holds column ln, rows 8*(v/4) + 4*hh + v%4 of each 32-row tile
-  if (!active) return;
+  // epilogue: lane (ln, hh) holds token row 32*i + ln of row tile i and, in
+  // acc[i][sub][4*c + e], weight row nbase + 32*sub + 8*c + 4*hh + e: four
+  // consecutive output columns per c
   if constexpr (GU) {
-    const int f = 32 * (nbase / 64) + ln;
-    _Float16* hb = h_out + (size_t)(gbase + m0) * F + f;
+    if (!active) return;
+    // gate rows in sub 0, the matching up rows in sub 1 (interleaved per 32)
+    _Float16* hb = h_out + (size_t)(gbase + m0) * F + 32 * (nbase / 64) + 4 * hh;
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
       if (i >= nrt) break;
+      const int r = 32 * i + ln;
+      if (r >= mv) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (r < mv) hb[(uint32_t)(r * F)] = (_Float16)(moe_silu_fast(acc[i][0][v]) * acc[i][1][v]);
+      for (int c = 0; c < 4; ++c) {
+        g3_f16x4 hv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          hv[e] = (_Float16)(moe_silu_fast(acc[i][0][4 * c + e]) * acc[i][1][4 * c + e]);
+        *reinterpret_cast<g3_f16x4*>(hb + (uint32_t)(r * F + 8 * c)) = hv;
       }
     }
   } else {
-    const size_t ybase = g < E ? (size_t)(gbase + m0) * H : (size_t)m0 * H;
+    // Each wave stages 32 rows x 128 bytes of its output (one row tile in
+    // fp16, half of one in fp32) in LDS, row stride 144 bytes, and writes
+    // them back 16 bytes per lane: one store instruction covers 8 rows of
+    // whole 128-byte segments (from the accumulators, 16 bytes in each of 32
+    // rows).  Written once, read once by the combine, far larger than the
+    // caches: nontemporal, so that they do not displace weights.
+    __syncthreads();  // every wave is done reading the last A stage
+    if (!active) return;
+    const size_t ybase = (g < E ? (size_t)(gbase + m0) * H : (size_t)m0 * H) + nbase;
     void* yv = g < E ? y_perm : y_shared;
-    // written once, read once by the combine, far larger than the caches:
-    // the nontemporal hint keeps them from displacing weights
-    auto store_rows = [&](auto* yb, auto cvt) {
+    uint8_t* stg = As0 + G3_EPI_WAVE_B * wave;
+    const int rr = lane >> 3, cu = lane & 7;  // read-back: rows rr + 8q, 16-byte unit cu
+    auto write_back = [&](int i, int col0, bool f16) {
+      __builtin_amdgcn_wave_barrier();
+      g3_u32x4 v[4];
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int col = nbase + 32 * sub + ln;
+      for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const g3_u32x4*>(stg + (8 * q + rr) * 144 + 16 * cu);
 #pragma unroll
-        for (int i = 0; i < RT; ++i) {
-          if (i >= nrt) break;
+      for (int q = 0; q < 4; ++q) {
+        const int r = 32 * i + 8 * q + rr;
+        if (r >= mv) continue;
+        const uint32_t o = (uint32_t)(r * H + col0);
+        g3_u32x4* dst = f16 ? reinterpret_cast<g3_u32x4*>((_Float16*)yv + ybase + o + 8 * cu)
+                            : reinterpret_cast<g3_u32x4*>((float*)yv + ybase + o + 4 * cu);
+        __builtin_nontemporal_store(v[q], dst);
+      }
+      __builtin_amdgcn_wave_barrier();
+    };
+    if (y_f16) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int r = 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
-            if (r < mv) __builtin_nontemporal_store(cvt(acc[i][sub][v]), &yb[(uint32_t)(r * H + col)]);
+      for (int i = 0; i < RT; ++i) {
+        if (i >= nrt) break;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float16v& a = acc[i][sub];
+            const g3_f16x4 hv = {(_Float16)a[4 * c], (_Float16)a[4 * c + 1], (_Float16)a[4 * c + 2],
+                                 (_Float16)a[4 * c + 3]};
+            *reinterpret_cast<g3_f16x4*>(stg + ln * 144 + 64 * sub + 16 * c + 8 * hh) = hv;
           }
+        write_back(i, 0, true);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        if (i >= nrt) break;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float16v& a = acc[i][sub];
+            const g3_f32x4 fv = {a[4 * c], a[4 * c + 1], a[4 * c + 2], a[4 * c + 3]};
+            *reinterpret_cast<g3_f32x4*>(stg + ln * 144 + 32 * c + 16 * hh) = fv;
+          }
+          write_back(i, 32 * sub, false);
         }
       }
-    };
-    if (y_f16)
-      store_rows((uint16_t*)yv + ybase, [](float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); });
-    else
-      store_rows((float*)yv + ybase, [](float v) { return v; });
+    }
   }
 }
 
@@ -499,7 +550,8 @@ extern "C" int moe_grouped_gemm_q(const uint16_t* x, int T, int H, int F, const 
   if (T == 0) return MOE_OK;
   MOE_REQUIRE(x && row_src && offsets && y_perm && y_shared, MOE_EINVAL,
               "x, row_src, offsets, y_perm and y_shared are required");
-  MOE_REQUIRE(moe_aligned(x, 16), MOE_EALIGN, "x must be 16-byte aligned");
+  MOE_REQUIRE(moe_aligned(x, 16) && moe_aligned(y_perm, 16) && moe_aligned(y_shared, 16), MOE_EALIGN,
+              "x, y_perm and y_shared must be 16-byte aligned");
   const size_t need = moe_ws_gemm(T, k, E, H, F);
   MOE_REQUIRE(ws && ws_bytes >= need && moe_aligned(ws, 256), MOE_EWORKSPACE,
               "ws needs %zu bytes, 256-byte aligned", need);

@@ -105,6 +105,10 @@ def test_expert_ops_reject(lib):
     assert h(*gb4) == _lib.MOE_EUNSUPPORTED
     gb5 = list(gb); gb5[1] = 1 << 20                 # fp16 copies past 32-bit byte offsets
     assert h(*gb5) == _lib.MOE_ESHAPE
+    for i in (13, 14):                               # y_perm, y_shared: 16-byte vector stores
+        gb6 = list(gb); gb6[i] = FAKE + 8
+        gb6[17] = 1 << 40
+        assert h(*gb6) == _lib.MOE_EALIGN
 
 
 def test_permute_combine_usage_reject(lib):
