@@ -177,7 +177,9 @@ struct B2Regs;  // raw weight words of one K chunk (64) for one lane and one col
 template <>
 struct B2Regs<MOE_Q4_B32> {
   uint2 q[G3_NB];  // [block in chunk]: dwords 2hh, 2hh+1 of the block
-  uint32_t s;      // fp16 scales of the chunk's two blocks
+  uint32_t s;      // fp16 scales of the chunk's two blocks (down: the first block's)
+  uint32_t s1;     // down: the second block's scale, kept apart so that the two
+                   // loads are not combined (and waited for) as they are issued
 };
 template <>
 struct B2Regs<MOE_Q2_B16> {
@@ -203,9 +205,8 @@ __device__ __forceinline__ void load_b2(B2Regs<MOE_Q4_B32>& b, const uint8_t* re
   if (gu)  // 4-block groups [kb/4][row][4]: the two scales are half of the group's word
     b.s = *reinterpret_cast<const uint32_t*>(rec + (s_off + 2u * ((kb0 >> 2) * R * 4u + 4u * ur + (kb0 & 3u))));
   else {   // per block [kb][row]
-    const uint32_t s0 = *reinterpret_cast<const uint16_t*>(rec + (s_off + 2u * (kb0 * R + ur)));
-    const uint32_t s1 = *reinterpret_cast<const uint16_t*>(rec + (s_off + 2u * ((kb0 + 1u) * R + ur)));
-    b.s = s0 | (s1 << 16);
+    b.s = *reinterpret_cast<const uint16_t*>(rec + (s_off + 2u * (kb0 * R + ur)));
+    b.s1 = *reinterpret_cast<const uint16_t*>(rec + (s_off + 2u * ((kb0 + 1u) * R + ur)));
   }
 }
 
@@ -304,7 +305,8 @@ __device__ __forceinline__ void gemm3_k_loop(const uint8_t* a_bytes, int K, int 
         const B2Regs<QFMT>& B = b.t[sub];
         if constexpr (QFMT == MOE_Q4_B32) {
           const int bi = q >> 1, s = q & 1;
-          const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(B.s >> (16 * bi)));
+          const _Float16 sc = __builtin_bit_cast(
+              _Float16, (uint16_t)(GU ? B.s >> (16 * bi) : bi == 0 ? B.s : B.s1));
           const half2v s2 = {sc, sc};
           bf[sub] = deq_q4(s == 0 ? B.q[bi].x : B.q[bi].y, s2, m4);
         } else {
