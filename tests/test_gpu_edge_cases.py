@@ -60,11 +60,13 @@ def test_random_records_decode(moe, qfmt):
 
 
 @pytest.mark.parametrize("qfmt", [0, 1])
-@pytest.mark.parametrize("T,H,E,k,F", [(2000, 256, 16, 2, 128), (256, 2048, 512, 10, 768)])
+@pytest.mark.parametrize("T,H,E,k,F", [(2000, 256, 16, 2, 128), (600, 384, 16, 2, 384),
+                                       (256, 2048, 512, 10, 768)])
 def test_random_records_prefill(moe, qfmt, T, H, E, k, F):
     """Random-byte records through route, permute, grouped GEMM and combine:
-    a small layer with ~250 rows per expert (two 160-row tiles) and the
-    full-size layer with a few rows per expert."""
+    a small layer with ~250 rows per expert (two tiles), one whose down pass
+    ends in a half-filled column tile (H = 384), and the full-size layer with
+    a few rows per expert."""
     li = C.layer_case(14, T, H, E, k, F, qfmt=qfmt, x_bf16=True, device="cuda", random_bytes=True)
     idx, w, counts, inv_row, y_perm, y_sh, y = _prefill_layer(moe, li, li.x)
     ry, ri, rw, rparts, _ = C.oracle_layer(li)

@@ -238,12 +238,14 @@ def _prefill_layer(moe, li, x_bf16, y_dtype=torch.float16):
 
 
 @pytest.mark.parametrize("qfmt", [0, 1])
-@pytest.mark.parametrize("T,E,k,bias", [(4, 16, 2, False), (300, 16, 2, True), (2000, 16, 2, False),
-                                        (333, 40, 6, True)])
-def test_grouped_gemm_small(moe, qfmt, T, E, k, bias):
+@pytest.mark.parametrize("T,E,k,bias,H", [(4, 16, 2, False, 256), (300, 16, 2, True, 256), (2000, 16, 2, False, 256),
+                                          (333, 40, 6, True, 256), (600, 16, 2, True, 384)])
+def test_grouped_gemm_small(moe, qfmt, T, E, k, bias, H):
     """Both output dtypes against the oracle; the fp16 rows are the fp32 rows
-    rounded to nearest even, bit for bit (same sums, one rounding)."""
-    li = C.layer_case(2, T, 256, E, k, 128, qfmt=qfmt, bias=bias, x_bf16=True)
+    rounded to nearest even, bit for bit (same sums, one rounding).  H = 384:
+    the down pass's last 256-column tile has 128 columns, so half of its
+    waves have no columns and only help stage the token rows."""
+    li = C.layer_case(2, T, H, E, k, 128, qfmt=qfmt, bias=bias, x_bf16=True)
     ry, ri, rw, rparts, _ = C.oracle_layer(li)
     out = {}
     for yd in (torch.float16, torch.float32):
