@@ -169,7 +169,7 @@ typedef uint32_t g3_u32x4 __attribute__((ext_vector_type(4)));
 template <int QFMT>
 constexpr int g3_rt() { return QFMT == MOE_Q4_B32 ? 6 : 5; }
 #define G3_STAGE_B (G3_BM * G3_KC * 2)  // bytes of one staged A chunk
-#define G3_EPI_WAVE_B (32 * 144)        // a wave's output staging in the down epilogue
+#define G3_EPI_WAVE_B (32 * 128)        // a wave's output staging in the down epilogue
 static_assert(4 * G3_EPI_WAVE_B <= G3_STAGE_B, "the down epilogue stages in one A stage");
 
 template <int QFMT>
@@ -448,8 +448,10 @@ __global__ __launch_bounds__(256, 2) void gemm3_kernel(const uint16_t* __restric
     }
   } else {
     // Each wave stages 32 rows x 128 bytes of its output (one row tile in
-    // fp16, half of one in fp32) in LDS, row stride 144 bytes, and writes
-    // them back 16 bytes per lane: one store instruction covers 8 rows of
+    // fp16, half of one in fp32) in LDS, 16-byte unit u of row r at unit
+    // u ^ (r & 7) (no bank conflicts for the 8- and 16-byte writes of 8
+    // consecutive rows, nor for the reads), and writes them back 16 bytes
+    // per lane: one store instruction covers 8 rows of
     // whole 128-byte segments (from the accumulators, 16 bytes in each of 32
     // rows).  Written once, read once by the combine, far larger than the
     // caches: nontemporal, so that they do not displace weights.
@@ -463,7 +465,7 @@ __global__ __launch_bounds__(256, 2) void gemm3_kernel(const uint16_t* __restric
       __builtin_amdgcn_wave_barrier();
       g3_u32x4 v[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const g3_u32x4*>(stg + (8 * q + rr) * 144 + 16 * cu);
+      for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const g3_u32x4*>(stg + (8 * q + rr) * 128 + 16 * (cu ^ rr));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = 32 * i + 8 * q + rr;
@@ -486,7 +488,7 @@ __global__ __launch_bounds__(256, 2) void gemm3_kernel(const uint16_t* __restric
             const float16v& a = acc[i][sub];
             const g3_f16x4 hv = {(_Float16)a[4 * c], (_Float16)a[4 * c + 1], (_Float16)a[4 * c + 2],
                                  (_Float16)a[4 * c + 3]};
-            *reinterpret_cast<g3_f16x4*>(stg + ln * 144 + 64 * sub + 16 * c + 8 * hh) = hv;
+            *reinterpret_cast<g3_f16x4*>(stg + ln * 128 + 16 * ((4 * sub + c) ^ (ln & 7)) + 8 * hh) = hv;
           }
         write_back(i, 0, true);
       }
@@ -500,7 +502,7 @@ __global__ __launch_bounds__(256, 2) void gemm3_kernel(const uint16_t* __restric
           for (int c = 0; c < 4; ++c) {
             const float16v& a = acc[i][sub];
             const g3_f32x4 fv = {a[4 * c], a[4 * c + 1], a[4 * c + 2], a[4 * c + 3]};
-            *reinterpret_cast<g3_f32x4*>(stg + ln * 144 + 32 * c + 16 * hh) = fv;
+            *reinterpret_cast<g3_f32x4*>(stg + ln * 128 + 16 * ((2 * c + hh) ^ (ln & 7))) = fv;
           }
           write_back(i, 32 * sub, false);
         }
