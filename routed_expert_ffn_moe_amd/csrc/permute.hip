@@ -28,6 +28,10 @@ __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __rest
 }
 
 // Turns chunk_counts[c][e] into the first row of chunk c's pairs of expert e.
+// NREG > 0 (nchunk <= NREG): thread e holds its whole column in registers, so
+// the column is read in one round of loads and written once; NREG == 0: any
+// nchunk, 8 chunk rows at a time, read twice.
+template <int NREG>
 __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict__ chunk_counts, int nchunk, int E,
                                                             int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets) {
@@ -36,16 +40,28 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict_
   // 8 chunk rows at a time: their loads are issued before any store (the
   // compiler cannot tell that row c + 1 is not the word just stored)
   constexpr int NB = 8;
+  int col[NREG > 0 ? NREG : 1];  // NREG > 0: exclusive prefix of the column
   int run = 0;
   if (e < E) {
-    for (int c0 = 0; c0 < nchunk; c0 += NB) {
-      int v[NB];
+    if constexpr (NREG > 0) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) v[j] = c0 + j < nchunk ? chunk_counts[(size_t)(c0 + j) * E + e] : 0;
+      for (int c = 0; c < NREG; ++c) col[c] = c < nchunk ? chunk_counts[(size_t)c * E + e] : 0;
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        if (c0 + j < nchunk) chunk_counts[(size_t)(c0 + j) * E + e] = run;
-        run += v[j];
+      for (int c = 0; c < NREG; ++c) {
+        const int v = col[c];
+        col[c] = run;
+        run += v;
+      }
+    } else {
+      for (int c0 = 0; c0 < nchunk; c0 += NB) {
+        int v[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) v[j] = c0 + j < nchunk ? chunk_counts[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          if (c0 + j < nchunk) chunk_counts[(size_t)(c0 + j) * E + e] = run;
+          run += v[j];
+        }
       }
     }
   }
@@ -62,13 +78,19 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict_
   if (e < E) {
     counts[e] = run;
     offsets[e] = excl;
-    for (int c0 = 0; c0 < nchunk; c0 += NB) {
-      int v[NB];
+    if constexpr (NREG > 0) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) v[j] = c0 + j < nchunk ? chunk_counts[(size_t)(c0 + j) * E + e] : 0;
+      for (int c = 0; c < NREG; ++c)
+        if (c < nchunk) chunk_counts[(size_t)c * E + e] = col[c] + excl;
+    } else {
+      for (int c0 = 0; c0 < nchunk; c0 += NB) {
+        int v[NB];
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-        if (c0 + j < nchunk) chunk_counts[(size_t)(c0 + j) * E + e] = v[j] + excl;
+        for (int j = 0; j < NB; ++j) v[j] = c0 + j < nchunk ? chunk_counts[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          if (c0 + j < nchunk) chunk_counts[(size_t)(c0 + j) * E + e] = v[j] + excl;
+      }
     }
   }
   if (e == E - 1) offsets[E] = s[e];
@@ -87,10 +109,21 @@ __global__ __launch_bounds__(64) void permute_scatter_kernel(const int32_t* __re
   const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
   const int base = blockIdx.x * MOE_PERMUTE_CHUNK;
   const int end = min(base + MOE_PERMUTE_CHUNK, n);
-  for (int i0 = base; i0 < end; i0 += 64) {
+  // the chunk's expert ids, all requested before the first batch
+  constexpr int NIT = MOE_PERMUTE_CHUNK / 64;
+  int ev[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int i = base + 64 * it + lane;
+    ev[it] = i < end ? idx[i] : 0;
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int i0 = base + 64 * it;
+    if (i0 >= end) break;
     const int i = i0 + lane;
     const bool valid = i < end;
-    const int e = valid ? idx[i] : 0;
+    const int e = ev[it];
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
@@ -141,7 +174,10 @@ extern "C" int moe_permute(const int32_t* topk_idx, int T, int k, int E, int32_t
   hipStream_t st = moe_stream(stream);
   int32_t* cc = (int32_t*)ws;
   if (nchunk > 0) permute_hist_kernel<<<nchunk, 256, 0, st>>>(topk_idx, n, E, cc);
-  permute_scan_kernel<<<1, 1024, 0, st>>>(cc, nchunk, E, counts, offsets);
+  if (nchunk <= 88)  // 88 column registers fit the 128 of a 1024-thread workgroup
+    permute_scan_kernel<88><<<1, 1024, 0, st>>>(cc, nchunk, E, counts, offsets);
+  else
+    permute_scan_kernel<0><<<1, 1024, 0, st>>>(cc, nchunk, E, counts, offsets);
   if (nchunk > 0) permute_scatter_kernel<<<nchunk, 64, 0, st>>>(topk_idx, n, E, cc, row_src, inv_row);
   if (x_perm && n > 0) {
     const int esize = x_dtype == MOE_F32 ? 4 : 2;
