@@ -8,9 +8,10 @@
 //   1. per chunk: count the experts (LDS integer atomics; order-free).
 //   2. one workgroup: per expert, exclusive prefix over chunks, then an
 //      exclusive scan over experts -> offsets and each chunk's base row.
-//   3. per chunk, one wave walks the chunk in order, 64 pairs at a time; lanes
-//      holding the same expert find each other with bit-sliced ballots, so the
-//      rank inside a batch is the number of lower lanes with that expert.
+//   3. per chunk, four waves each walk a quarter of it in order, 64 pairs at a
+//      time, from per-expert rows offset by the quarters before; lanes holding
+//      the same expert find each other with bit-sliced ballots, so the rank
+//      inside a batch is the number of lower lanes with that expert.
 // Every step is integer and order-deterministic, so the result is bit-exact.
 #include "moe_common.h"
 #include "moe_sizes.h"
@@ -96,27 +97,54 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict_
   if (e == E - 1) offsets[E] = s[e];
 }
 
-__global__ __launch_bounds__(64) void permute_scatter_kernel(const int32_t* __restrict__ idx, int n, int E,
-                                                             const int32_t* __restrict__ chunk_base,
-                                                             int32_t* __restrict__ row_src,
-                                                             int32_t* __restrict__ inv_row) {
-  __shared__ int run[MOE_MAX_E];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) run[e] = chunk_base[(size_t)blockIdx.x * E + e];
-  __syncthreads();
-  int nbits = 1;
-  while ((1 << nbits) < E) ++nbits;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-  const int base = blockIdx.x * MOE_PERMUTE_CHUNK;
-  const int end = min(base + MOE_PERMUTE_CHUNK, n);
-  // the chunk's expert ids, all requested before the first batch
-  constexpr int NIT = MOE_PERMUTE_CHUNK / 64;
+// Four waves per chunk: wave w walks pairs [256w, 256w + 256) of it, its
+// running row of expert e starting at the chunk's base row of e plus the
+// pairs of e in the quarters before it (counted in LDS first); the rows come
+// out in the same stable order as with one wave walking the whole chunk.
+#define PS_WAVES 4
+__global__ __launch_bounds__(64 * PS_WAVES) void permute_scatter_kernel(const int32_t* __restrict__ idx, int n,
+                                                                        int E,
+                                                                        const int32_t* __restrict__ chunk_base,
+                                                                        int32_t* __restrict__ row_src,
+                                                                        int32_t* __restrict__ inv_row) {
+  __shared__ int run[PS_WAVES][MOE_MAX_E];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int QUARTER = MOE_PERMUTE_CHUNK / PS_WAVES;
+  static_assert(QUARTER % 64 == 0, "a wave walks whole batches of 64 pairs");
+  constexpr int NIT = QUARTER / 64;
+  const int base = blockIdx.x * MOE_PERMUTE_CHUNK + wave * QUARTER;
+  const int end = min(base + QUARTER, n);  // <= base when this quarter is past n
+  // this wave's expert ids, all requested before the first batch
   int ev[NIT];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int i = base + 64 * it + lane;
     ev[it] = i < end ? idx[i] : 0;
   }
+#pragma unroll
+  for (int w = 0; w < PS_WAVES; ++w)
+    for (int e = tid; e < E; e += 64 * PS_WAVES) run[w][e] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < NIT; ++it)
+    if (base + 64 * it + lane < end) atomicAdd(&run[wave][ev[it]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += 64 * PS_WAVES) {
+    int acc = chunk_base[(size_t)blockIdx.x * E + e];
+#pragma unroll
+    for (int w = 0; w < PS_WAVES; ++w) {
+      const int c = run[w][e];
+      run[w][e] = acc;
+      acc += c;
+    }
+  }
+  __syncthreads();
+  // from here on each wave touches only its own run[wave]: no workgroup
+  // barrier (the waves' batch counts differ in the last chunk)
+  int* myrun = run[wave];
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int i0 = base + 64 * it;
@@ -131,10 +159,10 @@ __global__ __launch_bounds__(64) void permute_scatter_kernel(const int32_t* __re
       peers &= bit ? m : ~m;
     }
     const int rank = __popcll(peers & lt_mask);
-    const int r0 = valid ? run[e] : 0;
-    __syncthreads();
-    if (valid && rank == 0) run[e] = r0 + __popcll(peers);
-    __syncthreads();
+    const int r0 = valid ? myrun[e] : 0;
+    __builtin_amdgcn_wave_barrier();  // every lane has read before the leaders write
+    if (valid && rank == 0) myrun[e] = r0 + __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
     if (valid) {
       const int row = r0 + rank;
       row_src[row] = i;
@@ -178,7 +206,7 @@ extern "C" int moe_permute(const int32_t* topk_idx, int T, int k, int E, int32_t
     permute_scan_kernel<88><<<1, 1024, 0, st>>>(cc, nchunk, E, counts, offsets);
   else
     permute_scan_kernel<0><<<1, 1024, 0, st>>>(cc, nchunk, E, counts, offsets);
-  if (nchunk > 0) permute_scatter_kernel<<<nchunk, 64, 0, st>>>(topk_idx, n, E, cc, row_src, inv_row);
+  if (nchunk > 0) permute_scatter_kernel<<<nchunk, 64 * PS_WAVES, 0, st>>>(topk_idx, n, E, cc, row_src, inv_row);
   if (x_perm && n > 0) {
     const int esize = x_dtype == MOE_F32 ? 4 : 2;
     permute_gather_kernel<<<n, 256, 0, st>>>((const uint4*)x, k, H * esize / 16, row_src, (uint4*)x_perm);
