@@ -451,10 +451,11 @@ __global__ __launch_bounds__(256, 2) void gemm3_kernel(const uint16_t* __restric
     // fp16, half of one in fp32) in LDS, 16-byte unit u of row r at unit
     // u ^ (r & 7) (no bank conflicts for the 8- and 16-byte writes of 8
     // consecutive rows, nor for the reads), and writes them back 16 bytes
-    // per lane: one store instruction covers 8 rows of
-    // whole 128-byte segments (from the accumulators, 16 bytes in each of 32
-    // rows).  Written once, read once by the combine, far larger than the
-    // caches: nontemporal, so that they do not displace weights.
+    // per lane: one store instruction covers whole 128-byte segments of 8
+    // rows (straight from the accumulators it would cover 16 bytes in each
+    // of 32 rows).  The LDS accesses stay inside the wave, which executes
+    // them in order.  Written once, read once by the combine, far larger
+    // than the caches: nontemporal, so that they do not displace weights.
     __syncthreads();  // every wave is done reading the last A stage
     if (!active) return;
     const size_t ybase = (g < E ? (size_t)(gbase + m0) * H : (size_t)m0 * H) + nbase;
