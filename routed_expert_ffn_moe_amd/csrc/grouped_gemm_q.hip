@@ -10,7 +10,7 @@
 // expert g == E with rows 0..T-1): its ceil(M/32) row tiles of 32 are split as
 // evenly as possible over ceil(M/BM) workgroup tiles:
 //   gate/up pass: G|U = X_rows . [Wg|Wu]^T, h = fp16(silu(G) * U)  -> ws
-//   down pass:    Y   = h_rows . Wd^T (fp32)                       -> y_perm / y_shared
+//   down pass:    Y   = h_rows . Wd^T (fp32 sums, stored fp32 or fp16) -> y_perm / y_shared
 // MFMA v_mfma_f32_32x32x16_f16.  Weights are dequantised in registers to
 // fp16(s*q) (int4) or fp16(s*q+m) (int2), one rounding each; x (bf16) is
 // converted to fp16 (exact in fp16's normal range) once, into the workspace,
@@ -23,9 +23,10 @@
 // values and SiLU*mul happens in registers.  Tiles hold up to BM = 192 rows
 // (an expert of a chunk that routes about 160 rows to each expert is one
 // tile, and each dequantised weight operand feeds up to 6 MFMAs), K chunks of
-// 64.  A chunks are copied from global memory straight into a three-stage LDS
-// ring, two chunks ahead of the MFMAs, and the K loop is specialised on the
-// row-tile count, with no branches.
+// 64.  A chunks are copied from global memory straight into two LDS stages,
+// one chunk ahead of the MFMAs (the weight words likewise into two register
+// sets), and the K loop is specialised on the row-tile count, with no
+// branches.
 //
 // Blocks are renumbered so that consecutive work items (the column tiles of
 // one row tile, then the row tiles of one expert) land on the same XCD
