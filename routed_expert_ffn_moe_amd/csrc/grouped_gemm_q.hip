@@ -380,7 +380,9 @@ __global__ __launch_bounds__(256, 2) void gemm3_kernel(const uint16_t* __restric
   const int idx = bid >> 3;
   const int work = (bid & 7) * per_xcd + idx;
   if (idx >= per_xcd || work >= nwork) return;
-  const int tile = work / n_ntiles, nt = work % n_ntiles;
+  // tiles in reverse order: the shared expert's (all full) run first, so
+  // that the last, partly filled round of workgroups holds lighter tiles
+  const int tile = tile_start[E + 1] - 1 - work / n_ntiles, nt = work % n_ntiles;
   const int4 ti = tile_info[tile];
   const int g = ti.x, m0 = ti.y, mv = ti.z, gbase = ti.w;
   const int nrt = (mv + 31) / 32;  // row tiles present (<= g3_rt<QFMT>())
