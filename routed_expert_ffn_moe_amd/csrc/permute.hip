@@ -8,8 +8,8 @@
 //   1. per chunk: count the experts (LDS integer atomics; order-free).
 //   2. one workgroup: per expert, exclusive prefix over chunks, then an
 //      exclusive scan over experts -> offsets and each chunk's base row.
-//   3. per chunk, four waves each walk a quarter of it in order, 64 pairs at a
-//      time, from per-expert rows offset by the quarters before; lanes holding
+//   3. per chunk, eight waves each walk an eighth of it in order, 64 pairs at
+//      a time, from per-expert rows offset by the eighths before; lanes holding
 //      the same expert find each other with bit-sliced ballots, so the rank
 //      inside a batch is the number of lower lanes with that expert.
 // Every step is integer and order-deterministic, so the result is bit-exact.
@@ -97,11 +97,11 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict_
   if (e == E - 1) offsets[E] = s[e];
 }
 
-// Four waves per chunk: wave w walks pairs [256w, 256w + 256) of it, its
+// PS_WAVES waves per chunk: wave w walks pairs [128w, 128w + 128) of it, its
 // running row of expert e starting at the chunk's base row of e plus the
-// pairs of e in the quarters before it (counted in LDS first); the rows come
-// out in the same stable order as with one wave walking the whole chunk.
-#define PS_WAVES 4
+// pairs of e in the parts before it (counted in LDS first); the rows come out
+// in the same stable order as with one wave walking the whole chunk.
+#define PS_WAVES 8
 __global__ __launch_bounds__(64 * PS_WAVES) void permute_scatter_kernel(const int32_t* __restrict__ idx, int n,
                                                                         int E,
                                                                         const int32_t* __restrict__ chunk_base,
@@ -109,11 +109,11 @@ __global__ __launch_bounds__(64 * PS_WAVES) void permute_scatter_kernel(const in
                                                                         int32_t* __restrict__ inv_row) {
   __shared__ int run[PS_WAVES][MOE_MAX_E];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int QUARTER = MOE_PERMUTE_CHUNK / PS_WAVES;
-  static_assert(QUARTER % 64 == 0, "a wave walks whole batches of 64 pairs");
-  constexpr int NIT = QUARTER / 64;
-  const int base = blockIdx.x * MOE_PERMUTE_CHUNK + wave * QUARTER;
-  const int end = min(base + QUARTER, n);  // <= base when this quarter is past n
+  constexpr int PART = MOE_PERMUTE_CHUNK / PS_WAVES;
+  static_assert(PART % 64 == 0, "a wave walks whole batches of 64 pairs");
+  constexpr int NIT = PART / 64;
+  const int base = blockIdx.x * MOE_PERMUTE_CHUNK + wave * PART;
+  const int end = min(base + PART, n);  // <= base when this part is past n
   // this wave's expert ids, all requested before the first batch
   int ev[NIT];
 #pragma unroll
