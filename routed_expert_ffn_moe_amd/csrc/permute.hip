@@ -36,7 +36,7 @@ template <int NREG>
 __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict__ chunk_counts, int nchunk, int E,
                                                             int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets) {
-  __shared__ int s[1024];
+  __shared__ int wsum[16];
   const int e = threadIdx.x;
   // 8 chunk rows at a time: their loads are issued before any store (the
   // compiler cannot tell that row c + 1 is not the word just stored)
@@ -66,16 +66,20 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict_
       }
     }
   }
-  s[e] = (e < E) ? run : 0;
-  __syncthreads();
-  // inclusive Hillis-Steele scan over 1024 entries
-  for (int d = 1; d < 1024; d <<= 1) {
-    const int v = (e >= d) ? s[e - d] : 0;
-    __syncthreads();
-    s[e] += v;
-    __syncthreads();
+  // exclusive scan of the expert totals: within each wave (shuffles), then
+  // over the 16 waves' totals (one barrier)
+  const int lane = e & 63, wave = e >> 6;
+  const int own = (e < E) ? run : 0;
+  int incl = own;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
   }
-  const int excl = s[e] - ((e < E) ? run : 0);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) incl += wsum[w];
+  const int excl = incl - own;
   if (e < E) {
     counts[e] = run;
     offsets[e] = excl;
@@ -94,7 +98,7 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict_
       }
     }
   }
-  if (e == E - 1) offsets[E] = s[e];
+  if (e == E - 1) offsets[E] = incl;
 }
 
 // PS_WAVES waves per chunk: wave w walks pairs [128w, 128w + 128) of it, its
@@ -202,8 +206,8 @@ extern "C" int moe_permute(const int32_t* topk_idx, int T, int k, int E, int32_t
   hipStream_t st = moe_stream(stream);
   int32_t* cc = (int32_t*)ws;
   if (nchunk > 0) permute_hist_kernel<<<nchunk, 256, 0, st>>>(topk_idx, n, E, cc);
-  if (nchunk <= 88)  // 88 column registers fit the 128 of a 1024-thread workgroup
-    permute_scan_kernel<88><<<1, 1024, 0, st>>>(cc, nchunk, E, counts, offsets);
+  if (nchunk <= 80)  // 80 column registers fit the 128 of a 1024-thread workgroup
+    permute_scan_kernel<80><<<1, 1024, 0, st>>>(cc, nchunk, E, counts, offsets);
   else
     permute_scan_kernel<0><<<1, 1024, 0, st>>>(cc, nchunk, E, counts, offsets);
   if (nchunk > 0) permute_scatter_kernel<<<nchunk, 64 * PS_WAVES, 0, st>>>(topk_idx, n, E, cc, row_src, inv_row);
